@@ -1,0 +1,214 @@
+"""Pins for the oracle's format decoders (CPU only).
+
+Each decoder is checked against something other than itself: numpy / torch
+dtype conversions, exhaustive tables, exact rational arithmetic and the golden
+fixtures under tests/golden/ (each cites its source)."""
+
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats as F
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            rows.append(line.split())
+    return rows
+
+
+# ---------------------------------------------------------------- scalar types
+
+def test_fp16_exhaustive_against_numpy():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = F.fp16_bits_to_float(bits)
+    nan_ref = np.isnan(ref)
+    assert np.array_equal(nan_ref, np.isnan(got))
+    assert np.array_equal(ref[~nan_ref], got[~nan_ref])
+    # signed zeros keep their sign
+    assert np.array_equal(np.signbit(ref[~nan_ref]), np.signbit(got[~nan_ref]))
+
+
+def test_e4m3_exhaustive_against_torch():
+    bits = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = bits.view(torch.float8_e4m3fn).double().numpy()
+    got = F.e4m3_bits_to_float(np.arange(256))
+    nan_ref = np.isnan(ref)
+    assert nan_ref.sum() == 2  # S.1111.111 only
+    assert np.array_equal(nan_ref, np.isnan(got))
+    assert np.array_equal(ref[~nan_ref], got[~nan_ref])
+    assert np.nanmax(got) == 448.0
+
+
+def test_e2m1_against_golden_table():
+    table = _read_golden("e2m1_values.txt")
+    assert len(table) == 16
+    for code, val in table:
+        c = int(code, 16)
+        got = F.e2m1_bits_to_float(np.array([c]))[0]
+        want = float(val)
+        assert got == want and np.signbit(got) == np.signbit(want), (c, got, want)
+
+
+def test_e2m1_widened_into_e4m3_agrees_with_torch():
+    # A normal E2M1 value (s, e, m) equals the E4M3 value (s, e + 6, m << 2):
+    # both biases differ by 6.  Independent of the golden table above.
+    for c in range(16):
+        s, e, m = (c >> 3) & 1, (c >> 1) & 3, c & 1
+        if e == 0:
+            continue
+        b = (s << 7) | ((e + 6) << 3) | (m << 2)
+        ref = torch.tensor([b], dtype=torch.uint8).view(torch.float8_e4m3fn).double().item()
+        assert F.e2m1_bits_to_float(np.array([c]))[0] == ref
+
+
+def test_bf16_rounding_against_torch():
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 2 ** 32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    # add every tie pattern around a few exponents
+    ties = np.array([(e << 23) | (m << 16) | 0x8000 for e in (1, 100, 127, 200, 254) for m in range(0, 128, 7)],
+                    dtype=np.uint32)
+    bits = np.concatenate([bits, ties, ties | 0x80000000])
+    f = bits.view(np.float32)
+    keep = ~np.isnan(f)
+    f = f[keep]
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = F.f32_to_bf16_bits(f)
+    assert np.array_equal(ref, got)
+
+
+# ---------------------------------------------------------------- block formats
+
+def test_block_sizes_match_golden():
+    for fmt, n_el, n_bytes, bpw in _read_golden("format_sizes.txt"):
+        n_el, n_bytes, bpw = int(n_el), int(n_bytes), float(bpw)
+        rows, cols = 4, 128
+        total = F.bytes_per_matrix(fmt, rows, cols)
+        extra = 4 if fmt == "nvfp4" else 0  # one fp32 tensor scale per matrix
+        assert total - extra == rows * cols // n_el * n_bytes
+        assert (total - extra) * 8 / (rows * cols) == bpw
+
+
+def test_iq4_nl_codebook_matches_golden():
+    table = _read_golden("iq4_nl_codebook.txt")
+    want = np.array([int(v) for _, v in table], dtype=np.float64)
+    assert np.array_equal(F.IQ4_NL_CODEBOOK, want)
+    assert np.all(np.diff(want) > 0)
+
+
+def _fp16_exact(bits):
+    """binary16 value as an exact Fraction (independent bit decode)."""
+    b = int(bits)
+    s = -1 if b >> 15 else 1
+    e = (b >> 10) & 31
+    m = b & 1023
+    if e == 0:
+        return s * Fraction(m, 2 ** 24)
+    return s * Fraction(1024 + m) * Fraction(2) ** (e - 25)
+
+
+def test_q8_0_all_codes_times_sampled_scales_exact():
+    rng = np.random.default_rng(1)
+    finite = [b for b in range(65536) if ((b >> 10) & 31) != 31]
+    scales = rng.choice(finite, size=64, replace=False).astype(np.uint16)
+    scales = np.concatenate([scales, np.array([0x0000, 0x8000, 0x0001, 0x7BFF, 0x3C00], dtype=np.uint16)])
+    codes = np.tile(np.arange(-128, 128, dtype=np.int16), 1).astype(np.int8)  # 256 codes = 8 blocks
+    for s in scales:
+        c = codes.reshape(1, 256)
+        sc = np.full((1, 8), s, dtype=np.uint16)
+        got = F.dequant_q8_0(c, sc)[0]
+        exact = _fp16_exact(s)
+        for i in range(256):
+            assert Fraction(got[i]) == int(codes[i]) * exact
+
+
+def test_iq4_nl_nibble_order_and_exact_values():
+    # byte j of a block: low nibble = element j, high nibble = element j + 16
+    rng = np.random.default_rng(2)
+    idx = rng.integers(0, 16, size=(3, 64))  # 3 rows, 2 blocks
+    codes = np.zeros((3, 32), dtype=np.uint8)
+    for r in range(3):
+        for b in range(2):
+            for j in range(16):
+                codes[r, 16 * b + j] = idx[r, 32 * b + j] | (idx[r, 32 * b + j + 16] << 4)
+    scale_bits = np.array([[0x3C00, 0xB800], [0x1234, 0x0003], [0x0000, 0x7000]], dtype=np.uint16)
+    got = F.dequant_iq4_nl(codes, scale_bits)
+    table = [int(v) for _, v in _read_golden("iq4_nl_codebook.txt")]
+    for r in range(3):
+        for i in range(64):
+            want = table[idx[r, i]] * _fp16_exact(scale_bits[r, i // 32])
+            assert Fraction(got[r, i]) == want
+
+
+def test_iq4_nl_every_code_every_scale_class():
+    # all 256 code bytes under one scale: each byte decodes its two nibbles
+    codes = np.arange(256, dtype=np.uint8).reshape(16, 16)  # 16 rows, one block each
+    s = np.full((16, 1), 0x2E66, dtype=np.uint16)
+    got = F.dequant_iq4_nl(codes, s)
+    cb = [int(v) for _, v in _read_golden("iq4_nl_codebook.txt")]
+    d = _fp16_exact(0x2E66)
+    for r in range(16):
+        for j in range(16):
+            byte = 16 * r + j
+            assert Fraction(got[r, j]) == cb[byte & 15] * d
+            assert Fraction(got[r, j + 16]) == cb[byte >> 4] * d
+
+
+def _f32_round(fr):
+    """Round an exact Fraction to the nearest float32 (ties to even), independently
+    of numpy: scale into [2^23, 2^24) and round the integer mantissa."""
+    if fr == 0:
+        return 0.0
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)
+    q = a / Fraction(2) ** (e - 23)
+    n = q.numerator // q.denominator
+    rem = q - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sign * float(Fraction(n) * Fraction(2) ** (e - 23))
+
+
+def test_nvfp4_exact_products_then_one_fp32_rounding():
+    rng = np.random.default_rng(3)
+    cols = 64
+    codes = rng.integers(0, 256, size=(4, cols // 2), dtype=np.uint8)
+    sc = rng.integers(0, 0x7F, size=(4, cols // 16), dtype=np.uint8)  # finite, non-negative E4M3
+    sc[0, 0] = 0x7E  # 448
+    sc[1, 1] = 0x01  # smallest subnormal
+    ts = np.float32(rng.uniform(1e-5, 1e-3))
+    got = F.dequant_nvfp4(codes, sc, ts)
+    e2 = [float(v) for _, v in _read_golden("e2m1_values.txt")]
+    for r in range(4):
+        for i in range(cols):
+            byte = codes[r, i // 2]
+            nib = (byte & 15) if i % 2 == 0 else (byte >> 4)
+            sb = torch.tensor([sc[r, i // 16]], dtype=torch.uint8).view(torch.float8_e4m3fn).double().item()
+            exact = Fraction(e2[nib]) * Fraction(sb) * Fraction(float(ts))
+            assert got[r, i] == _f32_round(exact), (r, i)
+
+
+def test_zero_scale_blocks_decode_to_zero():
+    codes8 = np.random.default_rng(4).integers(-127, 128, size=(2, 64)).astype(np.int8)
+    z = np.zeros((2, 2), dtype=np.uint16)
+    assert np.all(F.dequant_q8_0(codes8, z) == 0)
+    codes4 = np.random.default_rng(5).integers(0, 256, size=(2, 32)).astype(np.uint8)
+    assert np.all(F.dequant_iq4_nl(codes4, z) == 0)
+    assert np.all(F.dequant_nvfp4(codes4, np.zeros((2, 4), np.uint8), np.float32(0.5)) == 0)

@@ -1,0 +1,206 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed-expert MoE feed-forward library.
+ *
+ * The library computes one routed-expert layer of a mixture-of-experts model:
+ *   router GEMV -> softmax over the top-k (renormalised, lower index first on
+ *   ties) -> device-side expert plan (per-expert counts, prefix scan, stable
+ *   token scatter) -> grouped dequantising gate/up projections with fused
+ *   SwiGLU -> down projection -> shared expert -> deterministic weighted combine.
+ *
+ * Sources.  "Qwen3.8-Flash-Next UD-IQ2_XS (L4 fix) for Basalt", section "What
+ * was changed": the routed experts run through a device-planned MoE tail plus
+ * grouped kernels, which only run when every layer's expert format is covered
+ * (covered down formats include IQ4_NL, NVFP4 and Q8_0; IQ4_NL is 4.5 bits per
+ * weight).  "Basalt at 665 tok/s? ...", section "RAM and VRAM Hold Different
+ * Parts of the Expert Weights": each token uses only its selected experts.
+ * The model card ("The fastest inference engine for Qwen3.8-Flash-Next on
+ * Blackwell", section "Sources"): tensors are GGUF tensors copied unchanged, so
+ * quant blocks run along each matrix row's reduction (input) dimension.  The
+ * router, top-k rule, SwiGLU, shared expert, combine and block layouts follow
+ * the workload definition of the routed-expert layer.
+ *
+ * Conventions (all entry points):
+ *  - Every pointer named "device" is GPU memory owned by the caller; the
+ *    library never allocates or frees device memory and keeps no per-call
+ *    state.  Host structs (moe_layer, moe_qmatrix, moe_plan_buf) are read
+ *    during the call only.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *    work and return without synchronising, so they may be captured into a
+ *    HIP graph.
+ *  - Arguments are validated on the host before anything is enqueued; on an
+ *    error nothing is launched and the status says why.  A failed launch
+ *    returns MOE_ERR_HIP.
+ *  - Calls that share a workspace must not overlap in time (same stream, or
+ *    ordered by events).
+ *  - Thread-safe: no mutable global state.
+ */
+#ifndef QRE_MOE_H
+#define QRE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, bad size, k > E, T < 1, ... */
+  MOE_ERR_UNSUPPORTED = -2, /* a (format, role, shape) the kernels do not cover */
+  MOE_ERR_ALIGNMENT = -3,   /* a device pointer is not suitably aligned */
+  MOE_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
+  MOE_ERR_HIP = -5          /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Block formats; all blocks run along a row's reduction dimension (cols).
+ *  MOE_Q8_0   32-element blocks; codes int8 [n][rows][cols]; scales IEEE
+ *             binary16 [n][rows][cols/32]; w = code * scale.
+ *  MOE_IQ4_NL 32-element blocks; codes uint8 [n][rows][cols/2], a block's 16
+ *             bytes hold element j in the low nibble of byte j and element
+ *             j+16 in the high nibble; scales binary16 [n][rows][cols/32];
+ *             w = codebook[nibble] * scale with the IQ4_NL codebook
+ *             {-127,-104,-83,-65,-49,-35,-22,-10,1,13,25,38,53,69,89,113}.
+ *  MOE_NVFP4  16-element blocks; codes uint8 [n][rows][cols/2] of FP4 E2M1,
+ *             element 2i in the low nibble of byte i; scales FP8 E4M3 (OCP)
+ *             [n][rows][cols/16]; tensor_scale fp32 [n];
+ *             w = fp32(e2m1 * e4m3 * tensor_scale).
+ */
+typedef enum { MOE_Q8_0 = 1, MOE_IQ4_NL = 2, MOE_NVFP4 = 3 } moe_qtype;
+
+/* One projection for n_expert experts, structure of arrays (codes and scales
+ * in separate device arrays).  rows = outputs, cols = reduction dimension.
+ * codes must be 16-byte aligned, scales 4-byte aligned, tensor_scale 4-byte. */
+typedef struct {
+  int32_t type;              /* moe_qtype */
+  int32_t n_expert;
+  int32_t rows;
+  int32_t cols;
+  const void* codes;         /* device */
+  const void* scales;        /* device */
+  const float* tensor_scale; /* device, MOE_NVFP4 only, else NULL */
+} moe_qmatrix;
+
+/* One MoE layer.  gate/up: rows = f, cols = d; down: rows = d, cols = f.
+ * gate and up share one format; the shared expert (if any) uses the routed
+ * experts' format for each role and has n_expert = 1.  Kernel coverage:
+ * d and f multiples of 128, 1 <= k <= E <= 1024, k <= 32. */
+typedef struct {
+  int32_t d, f, E, k;
+  const float* router_w;     /* device fp32 [E][d] */
+  const float* router_bias;  /* device fp32 [E], or NULL for no bias */
+  moe_qmatrix gate, up, down;
+  int32_t has_shared;        /* 0 or 1 */
+  moe_qmatrix shared_gate, shared_up, shared_down;
+} moe_layer;
+
+/* The expert plan for T tokens with k slots each (all device int32):
+ *  counts[E]        pairs routed to each expert
+ *  offsets[E+1]     exclusive prefix sum of counts; offsets[E] = valid pairs
+ *  row_token[T*k]   token of plan row r; rows of expert e are
+ *                   [offsets[e], offsets[e+1]) in ascending token order
+ *  row_slot[T*k]    slot j of plan row r
+ *  slot_row[T*k]    plan row of pair (t, j) at index t*k + j (-1 if dropped)
+ *  active[E]        ids with counts > 0, ascending, padded with -1
+ *  n_active[1]      number of active experts
+ *  error[1]         0, or a bit set: 1 = an expert id outside [0, E) was
+ *                   dropped; 2 = an SwiGLU activation exceeded the fp16 range
+ *                   of the decode path (moe_ffn_forward)
+ * Rows past offsets[E] in row_token / row_slot are set to -1. */
+typedef struct {
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* row_token;
+  int32_t* row_slot;
+  int32_t* slot_row;
+  int32_t* active;
+  int32_t* n_active;
+  int32_t* error;
+} moe_plan_buf;
+
+/* Router, top-k and gate weights for T tokens ("RAM and VRAM Hold Different
+ * Parts of the Expert Weights": each token runs only its selected experts).
+ *   logits[t][e] = fp32( sum_i router_w[e][i] * x[t][i] + bias[e] )
+ *   topk_idx[t][j]  the k largest logits, descending, lower id first on ties
+ *   topk_w[t][j]    softmax over the k selected logits (sums to 1)
+ * x: device [T][d] of x_dtype (MOE_F32 or MOE_BF16).  logits: device fp32
+ * [T][E] output, or NULL (then the workspace holds them).  The sum is
+ * accumulated in fp64 for T <= 64 and in fp32 above.  ws: device workspace of
+ * at least moe_workspace_size(layer, T) bytes, 256-byte aligned. */
+moe_status moe_route(const moe_layer* layer, const void* x, int32_t x_dtype, int32_t T,
+                     int32_t* topk_idx, float* topk_w, float* logits,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Expert plan ("device-planned MoE tail", "What was changed") from topk_idx
+ * device [T][k]: fills every array of *plan (see moe_plan_buf), in a fixed,
+ * deterministic order.  Out-of-range ids are dropped and flagged in error. */
+moe_status moe_plan(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                    const moe_plan_buf* plan, void* ws, size_t ws_bytes, void* stream);
+
+/* Routed experts + shared expert + combine ("grouped kernels", "What was
+ * changed"):
+ *   for every plan row r = (t, e):  h_r = silu(W_g[e] x_t) * (W_u[e] x_t),
+ *                                   o_r = W_d[e] h_r
+ *   s_t = the same with the shared expert (weight 1), if present
+ *   y_t = s_t + sum_j topk_w[t][j] * o_{slot_row[t*k+j]}   (slots in order j)
+ * x: device [T][d] of x_dtype; y: device [T][d] of y_dtype.  For T <= 64 the
+ * decode path runs: exact dequantisation, fp32 accumulation (activations are
+ * carried as fp16 hi/lo pairs, intermediate SwiGLU values must stay below
+ * 65504 in magnitude; error bit 2 reports otherwise).  For T > 64 the prefill
+ * path runs: weights are rounded to bf16 (RNE of the exact value) in LDS,
+ * SwiGLU activations are rounded to bf16, bf16 MFMA with fp32 accumulation.
+ * The combine never uses atomics: results are bitwise reproducible. */
+moe_status moe_ffn_forward(const moe_layer* layer, const void* x, int32_t x_dtype, int32_t T,
+                           const float* topk_w, const moe_plan_buf* plan,
+                           void* y, int32_t y_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* The four stages of moe_ffn_forward, callable one by one (same arguments and
+ * order, one stream, one workspace; the stages pass their intermediates
+ * through the workspace, whose contents are only valid between the stages of
+ * one call sequence with the same layer, T and x_dtype):
+ *  moe_ffn_prepare  activation layout for the expert products (decode: fp16
+ *                   tokens with per-token power-of-two scales; prefill: the
+ *                   device tile list over the plan)
+ *  moe_ffn_gateup   grouped gate/up projections + SwiGLU -> h rows
+ *  moe_ffn_down     grouped down projections -> o rows
+ *  moe_ffn_combine  y_t = s_t + sum_j topk_w[t][j] * o_{slot_row[t*k+j]}
+ * Each stage is one kernel launch. */
+moe_status moe_ffn_prepare(const moe_layer* layer, const void* x, int32_t x_dtype, int32_t T,
+                           const moe_plan_buf* plan, void* ws, size_t ws_bytes, void* stream);
+moe_status moe_ffn_gateup(const moe_layer* layer, const void* x, int32_t x_dtype, int32_t T,
+                          const moe_plan_buf* plan, void* ws, size_t ws_bytes, void* stream);
+moe_status moe_ffn_down(const moe_layer* layer, int32_t x_dtype, int32_t T, const moe_plan_buf* plan,
+                        void* ws, size_t ws_bytes, void* stream);
+moe_status moe_ffn_combine(const moe_layer* layer, int32_t x_dtype, int32_t T, const float* topk_w,
+                           const moe_plan_buf* plan, void* y, int32_t y_dtype, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* Test hook: dequantise expert `expert` of `m` into dst device [rows][cols] as
+ * fp32 (exact) or bf16 (round-to-nearest-even of the exact value). */
+moe_status moe_dequantize(const moe_qmatrix* m, int32_t expert, int32_t out_dtype, void* dst,
+                          void* stream);
+
+/* Pre-norm residual glue between stacked layers (the pages do not say what
+ * joins the MoE layers; this is the plain pre-norm residual chain):
+ *   if y != NULL:  h[t][i] += y[t][i]            (fp32 residual, y of y_dtype)
+ *   x[t][i] = bf16( h[t][i] / sqrt(mean_i h[t][i]^2 + eps) )
+ * h: device fp32 [T][d] (updated in place); x_out: device bf16 [T][d]. */
+moe_status moe_residual_rmsnorm(float* h, const void* y, int32_t y_dtype, int32_t T, int32_t d,
+                                float eps, void* x_out, void* stream);
+
+/* Workspace bytes needed by moe_route / moe_plan / moe_ffn_forward for up to
+ * T_max tokens on this layer shape (0 on invalid arguments). */
+size_t moe_workspace_size(const moe_layer* layer, int32_t T_max);
+
+/* Static description of a status code. */
+const char* moe_status_string(moe_status s);
+
+/* Library version string. */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QRE_MOE_H */

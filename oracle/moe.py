@@ -189,17 +189,21 @@ class DenseExperts:
     and (NVFP4) tensor_scale, each indexed by expert on the first axis.
     """
 
-    def __init__(self, mats):
+    def __init__(self, mats, cache=True):
         self.mats = mats
+        self.cache = cache
         self._cache = {}
 
     def weight(self, name, e):
         key = (name, int(e))
-        if key not in self._cache:
-            m = self.mats[name]
-            ts = None if m.get("tensor_scale") is None else m["tensor_scale"][e]
-            self._cache[key] = formats.dequant(m["type"], m["codes"][e], m["scales"][e], ts)
-        return self._cache[key]
+        if key in self._cache:
+            return self._cache[key]
+        m = self.mats[name]
+        ts = None if m.get("tensor_scale") is None else m["tensor_scale"][e]
+        w = formats.dequant(m["type"], m["codes"][e], m["scales"][e], ts)
+        if self.cache:
+            self._cache[key] = w
+        return w
 
     def ffn(self, e, x):
         return expert_ffn(self.weight("gate", e), self.weight("up", e), self.weight("down", e), x)
@@ -220,14 +224,17 @@ def moe_layer(layer, x, out_dtype="f32", return_parts=False):
     return layer_from_selection(layer, x, idx, w, p, out_dtype, return_parts, extra={"L": L, "L32": L32})
 
 
-def layer_from_selection(layer, x, idx, w, p=None, out_dtype="f32", return_parts=False, extra=None):
-    """Steps 5-7 for a given selection idx [T,k] and weights w [T,k]."""
+def layer_from_selection(layer, x, idx, w, p=None, out_dtype="f32", return_parts=False, extra=None,
+                         cache=True):
+    """Steps 5-7 for a given selection idx [T,k] and weights w [T,k].  With
+    cache=False each expert's weights are decoded, used and dropped (large
+    layers)."""
     X = np.asarray(x, dtype=np.float64)
     T, d = X.shape
     k = idx.shape[1]
     if p is None:
         p = plan(idx, layer["E"])
-    routed = DenseExperts(layer["routed"])
+    routed = DenseExperts(layer["routed"], cache=cache)
     o_rows = np.zeros((T * k, d))
     h_rows = np.zeros((T * k, layer["f"]))
     for e in range(layer["E"]):
@@ -239,7 +246,7 @@ def layer_from_selection(layer, x, idx, w, p=None, out_dtype="f32", return_parts
         o_rows[lo:hi] = o
         h_rows[lo:hi] = h
     if layer.get("shared") is not None:
-        shared = DenseExperts(layer["shared"])
+        shared = DenseExperts(layer["shared"], cache=cache)
         h_s, s = shared.ffn(0, X)
     else:
         h_s, s = None, np.zeros((T, d))

@@ -1,0 +1,217 @@
+// C ABI entry points (include/moe.h): host-side validation, workspace
+// accounting and dispatch to the kernel launchers.  Nothing here allocates
+// device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "moe.h"
+#include "moe_launch.h"
+
+using namespace qre;
+
+namespace {
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 32;
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+bool valid_qtype(int t) { return t == MOE_Q8_0 || t == MOE_IQ4_NL || t == MOE_NVFP4; }
+bool valid_dtype(int t) { return t == MOE_F32 || t == MOE_BF16; }
+
+moe_status check_qmatrix(const moe_qmatrix& m, int n_expert, int rows, int cols) {
+  if (!valid_qtype(m.type)) return MOE_ERR_UNSUPPORTED;
+  if (m.n_expert != n_expert || m.rows != rows || m.cols != cols) return MOE_ERR_INVALID_ARG;
+  if (!m.codes || !m.scales) return MOE_ERR_INVALID_ARG;
+  if (m.type == MOE_NVFP4 && !m.tensor_scale) return MOE_ERR_INVALID_ARG;
+  if (!aligned(m.codes, 16) || !aligned(m.scales, 4)) return MOE_ERR_ALIGNMENT;
+  if (m.tensor_scale && !aligned(m.tensor_scale, 4)) return MOE_ERR_ALIGNMENT;
+  return MOE_OK;
+}
+
+moe_status check_dims(const moe_layer* L) {
+  if (!L) return MOE_ERR_INVALID_ARG;
+  if (L->d <= 0 || L->f <= 0 || L->E <= 0 || L->k <= 0 || L->k > L->E) return MOE_ERR_INVALID_ARG;
+  if (L->E > kMaxE || L->k > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (L->d % 128 != 0 || L->f % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_router(const moe_layer* L) {
+  moe_status st = check_dims(L);
+  if (st != MOE_OK) return st;
+  if (!L->router_w) return MOE_ERR_INVALID_ARG;
+  if (!aligned(L->router_w, 16) || (L->router_bias && !aligned(L->router_bias, 4))) return MOE_ERR_ALIGNMENT;
+  return MOE_OK;
+}
+
+moe_status check_layer(const moe_layer* L) {
+  moe_status st = check_dims(L);
+  if (st != MOE_OK) return st;
+  if ((st = check_qmatrix(L->gate, L->E, L->f, L->d)) != MOE_OK) return st;
+  if ((st = check_qmatrix(L->up, L->E, L->f, L->d)) != MOE_OK) return st;
+  if ((st = check_qmatrix(L->down, L->E, L->d, L->f)) != MOE_OK) return st;
+  if (L->gate.type != L->up.type) return MOE_ERR_UNSUPPORTED;
+  if (L->has_shared != 0 && L->has_shared != 1) return MOE_ERR_INVALID_ARG;
+  if (L->has_shared) {
+    if ((st = check_qmatrix(L->shared_gate, 1, L->f, L->d)) != MOE_OK) return st;
+    if ((st = check_qmatrix(L->shared_up, 1, L->f, L->d)) != MOE_OK) return st;
+    if ((st = check_qmatrix(L->shared_down, 1, L->d, L->f)) != MOE_OK) return st;
+    if (L->shared_gate.type != L->gate.type || L->shared_up.type != L->up.type ||
+        L->shared_down.type != L->down.type)
+      return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+size_t route_ws(const moe_layer* L, int T) { return align_up((size_t)T * L->E * 4, 256); }
+
+size_t ffn_ws(const moe_layer* L, int T, int x_dtype) {
+  if (T <= kDecodeMaxT) return decode_ws_bytes(T, L->d, L->f, L->k, x_dtype);
+  return prefill_ws_bytes(T, L->d, L->f, L->k);
+}
+
+moe_status check_plan_buf(const moe_plan_buf* p) {
+  if (!p || !p->counts || !p->offsets || !p->row_token || !p->row_slot || !p->slot_row || !p->active ||
+      !p->n_active || !p->error)
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_version(void) { return "quantized_routed_expert_amd 0.1 (gfx950)"; }
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported format or shape";
+    case MOE_ERR_ALIGNMENT: return "misaligned device pointer";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+size_t moe_workspace_size(const moe_layer* layer, int32_t T_max) {
+  if (check_dims(layer) != MOE_OK || T_max < 1) return 0;
+  const int Td = T_max < kDecodeMaxT ? T_max : kDecodeMaxT;
+  size_t need = route_ws(layer, T_max);
+  const size_t pl = plan_ws_bytes(T_max, layer->E);
+  if (pl > need) need = pl;
+  const size_t dec = decode_ws_bytes(Td, layer->d, layer->f, layer->k, MOE_F32);
+  if (dec > need) need = dec;
+  if (T_max > kDecodeMaxT) {
+    const size_t pf = prefill_ws_bytes(T_max, layer->d, layer->f, layer->k);
+    if (pf > need) need = pf;
+  }
+  return need;
+}
+
+moe_status moe_route(const moe_layer* layer, const void* x, int32_t x_dtype, int32_t T, int32_t* topk_idx,
+                     float* topk_w, float* logits, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_router(layer);
+  if (st != MOE_OK) return st;
+  if (!x || !topk_idx || !topk_w || T < 1 || !valid_dtype(x_dtype)) return MOE_ERR_INVALID_ARG;
+  float* lg = logits;
+  if (!lg) {
+    if (!ws || ws_bytes < route_ws(layer, T)) return MOE_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
+    lg = (float*)ws;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_router_logits(layer->router_w, layer->router_bias, x, x_dtype, T, layer->E, layer->d, lg, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(launch_topk(lg, T, layer->E, layer->k, topk_idx, topk_w, s));
+}
+
+moe_status moe_plan(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, const moe_plan_buf* plan, void* ws,
+                    size_t ws_bytes, void* stream) {
+  if (!topk_idx || T < 1 || k < 1 || E < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxE || k > kMaxK) return MOE_ERR_UNSUPPORTED;
+  moe_status st = check_plan_buf(plan);
+  if (st != MOE_OK) return st;
+  if (!ws || ws_bytes < plan_ws_bytes(T, E)) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
+  return hip_status(launch_plan(topk_idx, T, k, E, plan_dev(*plan), ws, (hipStream_t)stream));
+}
+
+static moe_status ffn_checked(int stage_lo, int stage_hi, const moe_layer* layer, const void* x, int32_t x_dtype,
+                              int32_t T, const float* topk_w, const moe_plan_buf* plan, void* y, int32_t y_dtype,
+                              void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_layer(layer);
+  if (st != MOE_OK) return st;
+  if (T < 1 || !valid_dtype(x_dtype)) return MOE_ERR_INVALID_ARG;
+  const bool need_x = stage_lo <= kStageGateUp;
+  const bool need_y = stage_hi >= kStageCombine;
+  if (need_x && !x) return MOE_ERR_INVALID_ARG;
+  if (need_y && (!topk_w || !y || !valid_dtype(y_dtype))) return MOE_ERR_INVALID_ARG;
+  if ((st = check_plan_buf(plan)) != MOE_OK) return st;
+  if ((need_x && !aligned(x, 16)) || (need_y && !aligned(y, 16))) return MOE_ERR_ALIGNMENT;
+  if (!ws || ws_bytes < ffn_ws(layer, T, x_dtype)) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
+  FfnCall c{layer, x, x_dtype, T, topk_w, plan_dev(*plan), y, y_dtype, ws};
+  hipStream_t s = (hipStream_t)stream;
+  for (int stage = stage_lo; stage <= stage_hi; ++stage) {
+    const hipError_t e = T <= kDecodeMaxT ? launch_decode_stage(stage, c, s) : launch_prefill_stage(stage, c, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_ffn_forward(const moe_layer* layer, const void* x, int32_t x_dtype, int32_t T, const float* topk_w,
+                           const moe_plan_buf* plan, void* y, int32_t y_dtype, void* ws, size_t ws_bytes,
+                           void* stream) {
+  return ffn_checked(kStagePrepare, kStageCombine, layer, x, x_dtype, T, topk_w, plan, y, y_dtype, ws, ws_bytes,
+                     stream);
+}
+
+moe_status moe_ffn_prepare(const moe_layer* layer, const void* x, int32_t x_dtype, int32_t T,
+                           const moe_plan_buf* plan, void* ws, size_t ws_bytes, void* stream) {
+  return ffn_checked(kStagePrepare, kStagePrepare, layer, x, x_dtype, T, nullptr, plan, nullptr, MOE_F32, ws,
+                     ws_bytes, stream);
+}
+
+moe_status moe_ffn_gateup(const moe_layer* layer, const void* x, int32_t x_dtype, int32_t T,
+                          const moe_plan_buf* plan, void* ws, size_t ws_bytes, void* stream) {
+  return ffn_checked(kStageGateUp, kStageGateUp, layer, x, x_dtype, T, nullptr, plan, nullptr, MOE_F32, ws, ws_bytes,
+                     stream);
+}
+
+moe_status moe_ffn_down(const moe_layer* layer, int32_t x_dtype, int32_t T, const moe_plan_buf* plan, void* ws,
+                        size_t ws_bytes, void* stream) {
+  return ffn_checked(kStageDown, kStageDown, layer, nullptr, x_dtype, T, nullptr, plan, nullptr, MOE_F32, ws,
+                     ws_bytes, stream);
+}
+
+moe_status moe_ffn_combine(const moe_layer* layer, int32_t x_dtype, int32_t T, const float* topk_w,
+                           const moe_plan_buf* plan, void* y, int32_t y_dtype, void* ws, size_t ws_bytes,
+                           void* stream) {
+  return ffn_checked(kStageCombine, kStageCombine, layer, nullptr, x_dtype, T, topk_w, plan, y, y_dtype, ws,
+                     ws_bytes, stream);
+}
+
+moe_status moe_dequantize(const moe_qmatrix* m, int32_t expert, int32_t out_dtype, void* dst, void* stream) {
+  if (!m || !dst || !valid_dtype(out_dtype)) return MOE_ERR_INVALID_ARG;
+  if (!valid_qtype(m->type)) return MOE_ERR_UNSUPPORTED;
+  if (m->rows <= 0 || m->cols <= 0 || m->n_expert <= 0 || expert < 0 || expert >= m->n_expert)
+    return MOE_ERR_INVALID_ARG;
+  if (m->cols % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!m->codes || !m->scales || (m->type == MOE_NVFP4 && !m->tensor_scale)) return MOE_ERR_INVALID_ARG;
+  if (!aligned(m->codes, 16) || !aligned(m->scales, 4) || !aligned(dst, 4)) return MOE_ERR_ALIGNMENT;
+  return hip_status(launch_dequant(qmat_dev(*m), expert, out_dtype, dst, (hipStream_t)stream));
+}
+
+moe_status moe_residual_rmsnorm(float* h, const void* y, int32_t y_dtype, int32_t T, int32_t d, float eps,
+                                void* x_out, void* stream) {
+  if (!h || !x_out || T < 1 || d < 1 || !valid_dtype(y_dtype) || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_residual_rmsnorm(h, y, y_dtype, T, d, eps, x_out, (hipStream_t)stream));
+}
+
+}  // extern "C"

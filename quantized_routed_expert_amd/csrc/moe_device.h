@@ -1,0 +1,189 @@
+// Device-side helpers for the gfx950 routed-expert kernels.
+//
+// Format decoding follows the block formats declared in include/moe.h: GGUF
+// blocks along a row's reduction dimension (model card, "Sources": tensors are
+// GGUF tensors copied unchanged), Q8_0 / IQ4_NL / NVFP4-style as the covered
+// expert formats ("Qwen3.8-Flash-Next UD-IQ2_XS (L4 fix) for Basalt", section
+// "What was changed").
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace qre {
+
+typedef _Float16 f16;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- scalars
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+// OCP FP8 E4M3: bias 7, subnormal m * 2^-9, S.1111.111 = NaN, max 448.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t s = (b >> 7) & 1u, e = (b >> 3) & 15u, m = b & 7u;
+  float v = (e == 0) ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  if (e == 15u && m == 7u) v = __builtin_nanf("");
+  return s ? -v : v;
+}
+
+// float -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------- IQ4_NL
+
+// The IQ4_NL codebook biased by +128 so every entry is an unsigned byte:
+// {-127,-104,-83,-65,-49,-35,-22,-10,1,13,25,38,53,69,89,113} + 128, four
+// entries per dword, entry 0 in the low byte.
+constexpr uint32_t kIq4U0 = 0x3F2D1801u;  // 1, 24, 45, 63
+constexpr uint32_t kIq4U1 = 0x766A5D4Fu;  // 79, 93, 106, 118
+constexpr uint32_t kIq4U2 = 0xA6998D81u;  // 129, 141, 153, 166
+constexpr uint32_t kIq4U3 = 0xF1D9C5B5u;  // 181, 197, 217, 241
+
+// Four nibble indices (one per byte, values 0..15) -> four biased codebook
+// bytes.  Two 8-entry byte permutes cover entries 0..7 and 8..15; a third
+// permute keeps, per byte, the half that bit 3 of the index selects.
+__device__ __forceinline__ uint32_t iq4_lookup4(uint32_t q) {
+  const uint32_t lo = __builtin_amdgcn_perm(kIq4U1, kIq4U0, q);
+  const uint32_t hi = __builtin_amdgcn_perm(kIq4U3, kIq4U2, q ^ 0x08080808u);
+  const uint32_t sel = ((q >> 1) & 0x04040404u) | 0x03020100u;
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Two biased bytes u (= value + 128, 0..255) of U -> an fp16 pair holding the
+// exact signed values: the pattern 0x64uu is the fp16 number 1024 + u, and
+// subtracting 1152 is exact.  `sel` picks the two bytes (0x04010400 bytes 0,1;
+// 0x04030402 bytes 2,3).
+__device__ __forceinline__ uint32_t biased_bytes_to_f16x2(uint32_t U, uint32_t sel) {
+  const uint32_t p = __builtin_amdgcn_perm(0x64646464u, U, sel);
+  f16x2 v = __builtin_bit_cast(f16x2, p);
+  const f16x2 off = {(f16)-1152.0f, (f16)-1152.0f};
+  return __builtin_bit_cast(uint32_t, v + off);
+}
+
+// One dword of IQ4_NL codes (bytes 4i..4i+3 of a block) -> eight exact fp16
+// codebook values, in the element order
+//   4i, 4i+1, 4i+2, 4i+3, 16+4i, 16+4i+1, 16+4i+2, 16+4i+3
+// (the activations are stored in the same per-block order, see kPermIq4).
+__device__ __forceinline__ f16x8 iq4_dword_to_f16x8(uint32_t w) {
+  const uint32_t ulo = iq4_lookup4(w & 0x0F0F0F0Fu);
+  const uint32_t uhi = iq4_lookup4((w >> 4) & 0x0F0F0F0Fu);
+  u32x4 r;
+  r.x = biased_bytes_to_f16x2(ulo, 0x04010400u);
+  r.y = biased_bytes_to_f16x2(ulo, 0x04030402u);
+  r.z = biased_bytes_to_f16x2(uhi, 0x04010400u);
+  r.w = biased_bytes_to_f16x2(uhi, 0x04030402u);
+  return __builtin_bit_cast(f16x8, r);
+}
+
+// Position of block element e (0..31) in the IQ4_NL activation layout that
+// matches iq4_dword_to_f16x8: dword i of the codes covers positions 8i..8i+7.
+__device__ __forceinline__ int iq4_pos(int e) {
+  return ((e & 15) >> 2) * 8 + (e >> 4) * 4 + (e & 3);
+}
+
+// ---------------------------------------------------------------- Q8_0
+
+// One dword of int8 codes -> four exact fp16 values (in order).
+__device__ __forceinline__ u32x2 q8_dword_to_f16x4(uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;  // int8 c -> c + 128
+  u32x2 r;
+  r.x = biased_bytes_to_f16x2(u, 0x04010400u);
+  r.y = biased_bytes_to_f16x2(u, 0x04030402u);
+  return r;
+}
+
+__device__ __forceinline__ f16x8 q8_dwords_to_f16x8(uint32_t a, uint32_t b) {
+  const u32x2 x = q8_dword_to_f16x4(a), y = q8_dword_to_f16x4(b);
+  u32x4 r = {x.x, x.y, y.x, y.y};
+  return __builtin_bit_cast(f16x8, r);
+}
+
+// ---------------------------------------------------------------- NVFP4
+
+// One byte of two E2M1 codes (element 2i low nibble, 2i+1 high nibble) -> two
+// exact fp16 values.  Decoded arithmetically: magnitude index 0..7 maps to
+// {0, .5, 1, 1.5, 2, 3, 4, 6}.
+__device__ __forceinline__ float e2m1_to_f32(uint32_t n) {
+  const uint32_t s = (n >> 3) & 1u, e = (n >> 1) & 3u, m = n & 1u;
+  const float mag = (e == 0) ? 0.5f * (float)m : (float)(2u + m) * __uint_as_float((e + 125u) << 23);
+  return s ? -mag : mag;
+}
+
+// e2m1 magnitudes as fp16 high bytes (low byte zero): 0, .5, 1, 1.5, 2, 3, 4, 6.
+constexpr uint32_t kE2m1H0 = 0x3E3C3800u;  // idx 0..3: 0x00, 0x38, 0x3C, 0x3E
+constexpr uint32_t kE2m1H1 = 0x46444240u;  // idx 4..7: 0x40, 0x42, 0x44, 0x46
+
+// One dword of E2M1 codes (8 elements, natural order) times an fp16 block
+// scale -> eight fp16 values e2m1 * scale (exact: at most 6 significant bits).
+__device__ __forceinline__ f16x8 fp4_dword_to_f16x8(uint32_t w, f16 scale) {
+  // split nibbles: bytes of lo hold elements 0,2,4,6; bytes of hi hold 1,3,5,7
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  const uint32_t hl = __builtin_amdgcn_perm(kE2m1H1, kE2m1H0, lo & 0x07070707u) | ((lo & 0x08080808u) << 4);
+  const uint32_t hh = __builtin_amdgcn_perm(kE2m1H1, kE2m1H0, hi & 0x07070707u) | ((hi & 0x08080808u) << 4);
+  // fp16 pair (elem 2b, elem 2b+1) = [0x00, hl.byte b, 0x00, hh.byte b]
+  u32x4 r;
+  r.x = __builtin_amdgcn_perm(hh, hl, 0x040C000Cu);
+  r.y = __builtin_amdgcn_perm(hh, hl, 0x050C010Cu);
+  r.z = __builtin_amdgcn_perm(hh, hl, 0x060C020Cu);
+  r.w = __builtin_amdgcn_perm(hh, hl, 0x070C030Cu);
+  const f16x2 s2 = {scale, scale};
+  u32x4 o;
+  o.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, r.x) * s2);
+  o.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, r.y) * s2);
+  o.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, r.z) * s2);
+  o.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, r.w) * s2);
+  return __builtin_bit_cast(f16x8, o);
+}
+
+// ---------------------------------------------------------------- wave ops
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// ---------------------------------------------------------------- formats
+
+__host__ __device__ constexpr int code_row_bytes(int type, int cols) {
+  return type == MOE_Q8_0 ? cols : cols / 2;
+}
+__host__ __device__ constexpr int scale_row_bytes(int type, int cols) {
+  return type == MOE_NVFP4 ? cols / 16 : (cols / 32) * 2;
+}
+
+}  // namespace qre

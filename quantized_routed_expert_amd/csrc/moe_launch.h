@@ -1,0 +1,80 @@
+// Internal launchers: one host function per kernel family, each defined in the
+// translation unit that holds its kernels.  All return the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace qre {
+
+// Device view of one projection of one layer (pointers to expert 0).
+struct QMatDev {
+  int type;
+  int rows, cols;
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* ts;
+};
+
+inline QMatDev qmat_dev(const moe_qmatrix& m) {
+  return QMatDev{m.type, m.rows, m.cols, (const uint8_t*)m.codes, (const uint8_t*)m.scales, m.tensor_scale};
+}
+
+// Plan arrays (device).
+struct PlanDev {
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* row_token;
+  int32_t* row_slot;
+  int32_t* slot_row;
+  int32_t* active;
+  int32_t* n_active;
+  int32_t* error;
+};
+
+inline PlanDev plan_dev(const moe_plan_buf& p) {
+  return PlanDev{p.counts, p.offsets, p.row_token, p.row_slot, p.slot_row, p.active, p.n_active, p.error};
+}
+
+// moe_small.hip
+hipError_t launch_dequant(const QMatDev& m, int expert, int out_dtype, void* dst, hipStream_t s);
+hipError_t launch_router_logits(const float* W, const float* b, const void* x, int x_dtype, int T, int E, int d,
+                                float* logits, hipStream_t s);
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w, hipStream_t s);
+size_t plan_ws_bytes(int T, int E);
+hipError_t launch_plan(const int32_t* idx, int T, int k, int E, const PlanDev& p, void* ws, hipStream_t s);
+hipError_t launch_combine(const void* o, int o_bf16, const float* topk_w, const int32_t* slot_row, int T, int k,
+                          int d, int has_shared, void* y, int y_dtype, hipStream_t s);
+hipError_t launch_residual_rmsnorm(float* h, const void* y, int y_dtype, int T, int d, float eps, void* x_out,
+                                   hipStream_t s);
+
+// Expert stages (decode path for T <= kDecodeMaxT, prefill path above).
+constexpr int kDecodeMaxT = 64;
+enum FfnStage { kStagePrepare = 0, kStageGateUp = 1, kStageDown = 2, kStageCombine = 3 };
+
+struct FfnCall {
+  const moe_layer* L;
+  const void* x;
+  int x_dtype;
+  int T;
+  const float* topk_w;
+  PlanDev p;
+  void* y;
+  int y_dtype;
+  void* ws;
+};
+
+// moe_decode.hip
+size_t decode_ws_bytes(int T, int d, int f, int k, int x_dtype);
+hipError_t launch_decode_stage(int stage, const FfnCall& c, hipStream_t s);
+
+// moe_prefill.hip
+size_t prefill_ws_bytes(int T, int d, int f, int k);
+hipError_t launch_prefill_stage(int stage, const FfnCall& c, hipStream_t s);
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace qre

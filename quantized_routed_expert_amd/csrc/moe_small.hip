@@ -1,0 +1,472 @@
+// Small kernels of the routed-expert layer: dequantisation (test hook),
+// router logits, top-k + gate weights, the expert plan, the combine and the
+// residual / RMSNorm glue between stacked layers.
+#include <hip/hip_runtime.h>
+
+#include "moe_device.h"
+#include "moe_launch.h"
+
+namespace qre {
+
+// ============================================================================
+// Dequantisation (test hook).  Exact values; bf16 output is RNE of the exact
+// value.  Formats: include/moe.h.
+// ============================================================================
+
+__global__ void k_dequant(QMatDev m, int expert, int out_bf16, void* dst) {
+  const int rows = m.rows, cols = m.cols;
+  const int nb32 = cols / 32;
+  const long total = (long)rows * nb32;  // one thread per 32 elements
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int r = (int)(i / nb32), b = (int)(i % nb32);
+  const long row_e = (long)expert * rows + r;
+  const uint8_t* crow = m.codes + row_e * code_row_bytes(m.type, cols);
+  const uint8_t* srow = m.scales + row_e * scale_row_bytes(m.type, cols);
+  float v[32];
+  if (m.type == MOE_Q8_0) {
+    const float d = f16_bits_to_f32(((const uint16_t*)srow)[b]);
+    const int8_t* c = (const int8_t*)crow + b * 32;
+    for (int j = 0; j < 32; ++j) v[j] = (float)c[j] * d;
+  } else if (m.type == MOE_IQ4_NL) {
+    const float d = f16_bits_to_f32(((const uint16_t*)srow)[b]);
+    const u32x4 c = *(const u32x4*)(crow + b * 16);
+    // decode through the same helper the GEMV kernels use
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f16x8 q = iq4_dword_to_f16x8(c[i4]);
+      for (int t = 0; t < 4; ++t) {
+        v[4 * i4 + t] = (float)q[t] * d;
+        v[16 + 4 * i4 + t] = (float)q[4 + t] * d;
+      }
+    }
+  } else {  // NVFP4: two 16-element blocks
+    const float ts = m.ts[expert];
+    const u32x4 c = *(const u32x4*)(crow + b * 16);
+    for (int half = 0; half < 2; ++half) {
+      const float sb = e4m3_to_f32(srow[2 * b + half]);
+      const f16 sbh = (f16)sb;  // exact: E4M3 values are fp16 values
+      for (int i2 = 0; i2 < 2; ++i2) {
+        const f16x8 q = fp4_dword_to_f16x8(c[2 * half + i2], sbh);
+        for (int t = 0; t < 8; ++t) v[16 * half + 8 * i2 + t] = (float)q[t] * ts;
+      }
+    }
+  }
+  if (out_bf16) {
+    uint32_t* o = (uint32_t*)((uint16_t*)dst + (long)r * cols + b * 32);
+    for (int j = 0; j < 16; ++j) o[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+  } else {
+    float* o = (float*)dst + (long)r * cols + b * 32;
+    for (int j = 0; j < 32; ++j) o[j] = v[j];
+  }
+}
+
+hipError_t launch_dequant(const QMatDev& m, int expert, int out_dtype, void* dst, hipStream_t s) {
+  const long total = (long)m.rows * (m.cols / 32);
+  const int bs = 256;
+  const long grid = (total + bs - 1) / bs;
+  hipLaunchKernelGGL(k_dequant, dim3((unsigned)grid), dim3(bs), 0, s, m, expert, out_dtype == MOE_BF16 ? 1 : 0,
+                     dst);
+  return hipGetLastError();
+}
+
+// ============================================================================
+// Router logits  L[t][e] = fp32( sum_i W[e][i] x[t][i] + b[e] ).
+// ("RAM and VRAM Hold Different Parts of the Expert Weights": the router picks
+// the experts each token uses.)
+// ============================================================================
+
+__device__ __forceinline__ float load_x(const void* x, int x_bf16, long i) {
+  return x_bf16 ? bf16_bits_to_f32(((const uint16_t*)x)[i]) : ((const float*)x)[i];
+}
+
+// T <= 64: one workgroup per expert row, fp64 accumulation (products of an
+// fp32 weight and a bf16/fp32 activation are exact in fp64), up to 16 tokens
+// per pass.  Memory bound: every weight is read once per pass.
+constexpr int kRtTok = 16;
+
+__global__ __launch_bounds__(256) void k_router_gemv_f64(const float* __restrict__ W, const float* __restrict__ bias,
+                                                         const void* __restrict__ x, int x_bf16, int T, int E, int d,
+                                                         float* __restrict__ logits) {
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  __shared__ double red[4][kRtTok];
+  const float* wr = W + (long)e * d;
+  for (int t0 = 0; t0 < T; t0 += kRtTok) {
+    const int nt = min(kRtTok, T - t0);
+    double acc[kRtTok];
+#pragma unroll
+    for (int t = 0; t < kRtTok; ++t) acc[t] = 0.0;
+    for (int i = tid * 4; i < d; i += 256 * 4) {
+      const f32x4 w4 = *(const f32x4*)(wr + i);
+#pragma unroll
+      for (int t = 0; t < kRtTok; ++t) {
+        if (t < nt) {
+          const long xo = (long)(t0 + t) * d + i;
+          acc[t] += (double)w4.x * (double)load_x(x, x_bf16, xo) + (double)w4.y * (double)load_x(x, x_bf16, xo + 1) +
+                    (double)w4.z * (double)load_x(x, x_bf16, xo + 2) + (double)w4.w * (double)load_x(x, x_bf16, xo + 3);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kRtTok; ++t) {
+      if (t < nt) {
+        const double v = wave_sum_f64(acc[t]);
+        if (lane == 0) red[wid][t] = v;
+      }
+    }
+    __syncthreads();
+    if (tid < nt) {
+      double v = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+      if (bias) v += (double)bias[e];
+      logits[(long)(t0 + tid) * E + e] = (float)v;
+    }
+    __syncthreads();
+  }
+}
+
+// T > 64: fp32 tiled GEMM, 64 experts x 64 tokens per workgroup, K chunks of 32.
+__global__ __launch_bounds__(256) void k_router_gemm_f32(const float* __restrict__ W, const float* __restrict__ bias,
+                                                         const void* __restrict__ x, int x_bf16, int T, int E, int d,
+                                                         float* __restrict__ logits) {
+  __shared__ float sW[32][65];
+  __shared__ float sX[32][65];
+  const int e0 = blockIdx.x * 64, t0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  const int te = tid & 15, tt = tid >> 4;  // 4x4 outputs each: e = e0 + te + 16*i, t = t0 + tt + 16*j
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < d; k0 += 32) {
+    for (int idx = tid; idx < 64 * 32; idx += 256) {
+      const int r = idx >> 5, c = idx & 31;
+      const int e = e0 + r, t = t0 + r;
+      sW[c][r] = (e < E) ? W[(long)e * d + k0 + c] : 0.0f;
+      sX[c][r] = (t < T) ? load_x(x, x_bf16, (long)t * d + k0 + c) : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int c = 0; c < 32; ++c) {
+      float wv[4], xv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[i] = sW[c][te + 16 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xv[j] = sX[c][tt + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(wv[i], xv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = e0 + te + 16 * i;
+    if (e >= E) continue;
+    const float bv = bias ? bias[e] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = t0 + tt + 16 * j;
+      if (t < T) logits[(long)t * E + e] = acc[i][j] + bv;
+    }
+  }
+}
+
+hipError_t launch_router_logits(const float* W, const float* b, const void* x, int x_dtype, int T, int E, int d,
+                                float* logits, hipStream_t s) {
+  const int xb = x_dtype == MOE_BF16 ? 1 : 0;
+  if (T <= 64) {
+    hipLaunchKernelGGL(k_router_gemv_f64, dim3(E), dim3(256), 0, s, W, b, x, xb, T, E, d, logits);
+  } else {
+    hipLaunchKernelGGL(k_router_gemm_f32, dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, s, W, b, x, xb, T, E, d,
+                       logits);
+  }
+  return hipGetLastError();
+}
+
+// ============================================================================
+// Top-k + gate weights: one wavefront per token.  Slot order: descending
+// logit, lower expert id first on ties; weights = softmax over the k selected
+// logits.  E <= 1024 (16 logits per lane).
+// ============================================================================
+
+constexpr int kTopkPerLane = 16;
+
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
+                                              int32_t* __restrict__ idx, float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* L = logits + (long)t * E;
+  float v[kTopkPerLane];
+#pragma unroll
+  for (int i = 0; i < kTopkPerLane; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = (e < E) ? L[e] : -__builtin_inff();
+  }
+  uint32_t taken = 0;  // bit i: element lane + 64 i already selected
+  float sel_val = 0.0f;
+  int sel_idx = 0;
+  float my_val = -__builtin_inff();
+  for (int j = 0; j < k; ++j) {
+    // lane-local best among untaken: larger value, then lower index
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < kTopkPerLane; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E && !((taken >> i) & 1u)) {
+        if (v[i] > bv || (v[i] == bv && e < bi) || bi == 0x7fffffff) {
+          bv = v[i];
+          bi = e;
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (lane == j) {
+      sel_val = bv;
+      sel_idx = bi;
+    }
+    if (j == 0) my_val = bv;  // the maximum
+  }
+  // softmax over the selected logits
+  float ex = 0.0f;
+  if (lane < k) ex = __expf(sel_val - my_val);
+  const float sum = wave_sum(ex);
+  if (lane < k) {
+    idx[(long)t * k + lane] = sel_idx;
+    w[(long)t * k + lane] = ex / sum;
+  }
+}
+
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w, hipStream_t s) {
+  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, idx, w);
+  return hipGetLastError();
+}
+
+// ============================================================================
+// Expert plan ("device-planned MoE tail", UD-IQ2_XS (L4 fix) page, "What was
+// changed").  Three passes over blocks of kPlanTB tokens, no global atomics:
+//   count   per-block expert histograms (LDS atomics only count)
+//   scan    one workgroup: counts, offsets, per-block bases, active list
+//   scatter rank = base + earlier occurrences in the block (token order)
+// The result is independent of scheduling: rows of an expert are in
+// ascending token order.
+// ============================================================================
+
+constexpr int kPlanTB = 64;
+
+size_t plan_ws_bytes(int T, int E) {
+  const int nb = (T + kPlanTB - 1) / kPlanTB;
+  return align_up((size_t)nb * E * 4 + (size_t)nb * 4, 256);
+}
+
+__global__ __launch_bounds__(256) void k_plan_count(const int32_t* __restrict__ idx, int T, int k, int E,
+                                                    int32_t* __restrict__ hist, int32_t* __restrict__ blk_err) {
+  extern __shared__ int32_t sh[];
+  const int b = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) sh[e] = 0;
+  __syncthreads();
+  const int t0 = b * kPlanTB, t1 = min(T, t0 + kPlanTB);
+  int err = 0;
+  for (int p = t0 * k + threadIdx.x; p < t1 * k; p += blockDim.x) {
+    const int e = idx[p];
+    if (e >= 0 && e < E)
+      atomicAdd(&sh[e], 1);
+    else
+      err = 1;
+  }
+  err = __syncthreads_or(err);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(long)b * E + e] = sh[e];
+  if (threadIdx.x == 0) blk_err[b] = err;
+}
+
+__global__ __launch_bounds__(1024) void k_plan_scan(int T, int k, int E, int nb, int32_t* __restrict__ hist,
+                                                    const int32_t* __restrict__ blk_err, PlanDev p) {
+  extern __shared__ int32_t sh[];  // [E] counts, then scan scratch
+  const int tid = threadIdx.x;
+  // per expert: total and exclusive per-block prefix (in place)
+  for (int e = tid; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int b = 0; b < nb; ++b) {
+      const int c = hist[(long)b * E + e];
+      hist[(long)b * E + e] = run;
+      run += c;
+    }
+    sh[e] = run;
+    p.counts[e] = run;
+  }
+  __syncthreads();
+  // exclusive scan over experts (sequential per thread chunk, then across)
+  __shared__ int32_t chunk_sum[1024];
+  __shared__ int32_t chunk_act[1024];
+  const int per = (E + blockDim.x - 1) / blockDim.x;
+  const int e0 = tid * per, e1 = min(E, e0 + per);
+  int s = 0, a = 0;
+  for (int e = e0; e < e1; ++e) {
+    s += sh[e];
+    a += sh[e] > 0 ? 1 : 0;
+  }
+  chunk_sum[tid] = s;
+  chunk_act[tid] = a;
+  __syncthreads();
+  if (tid == 0) {
+    int rs = 0, ra = 0;
+    for (int i = 0; i < (int)blockDim.x; ++i) {
+      const int cs = chunk_sum[i], ca = chunk_act[i];
+      chunk_sum[i] = rs;
+      chunk_act[i] = ra;
+      rs += cs;
+      ra += ca;
+    }
+    p.offsets[E] = rs;
+    *p.n_active = ra;
+    int err = 0;
+    for (int b = 0; b < nb; ++b) err |= blk_err[b];
+    *p.error = err;
+  }
+  __syncthreads();
+  int off = chunk_sum[tid], act = chunk_act[tid];
+  for (int e = e0; e < e1; ++e) {
+    const int c = sh[e];
+    p.offsets[e] = off;
+    for (int b = 0; b < nb; ++b) hist[(long)b * E + e] += off;
+    if (c > 0) p.active[act++] = e;
+    off += c;
+  }
+  __syncthreads();
+  const int n_act = *p.n_active;
+  for (int e = n_act + tid; e < E; e += blockDim.x) p.active[e] = -1;
+  const int n_valid = p.offsets[E];
+  for (int r = n_valid + tid; r < T * k; r += blockDim.x) {
+    p.row_token[r] = -1;
+    p.row_slot[r] = -1;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_plan_scatter(const int32_t* __restrict__ idx, int T, int k, int E,
+                                                      const int32_t* __restrict__ base, PlanDev p) {
+  extern __shared__ int32_t sidx[];  // [kPlanTB * k]
+  const int b = blockIdx.x;
+  const int t0 = b * kPlanTB, t1 = min(T, t0 + kPlanTB);
+  const int npair = (t1 - t0) * k;
+  for (int i = threadIdx.x; i < npair; i += blockDim.x) sidx[i] = idx[(long)t0 * k + i];
+  __syncthreads();
+  for (int i = threadIdx.x; i < npair; i += blockDim.x) {
+    const int tl = i / k, j = i % k;
+    const int e = sidx[i];
+    const long pair = (long)(t0 + tl) * k + j;
+    if (e < 0 || e >= E) {
+      p.slot_row[pair] = -1;
+      continue;
+    }
+    int rank = 0;
+    for (int u = 0; u < tl; ++u) {
+      for (int jj = 0; jj < k; ++jj) rank += (sidx[u * k + jj] == e) ? 1 : 0;
+    }
+    const int r = base[(long)b * E + e] + rank;
+    p.row_token[r] = t0 + tl;
+    p.row_slot[r] = j;
+    p.slot_row[pair] = r;
+  }
+}
+
+hipError_t launch_plan(const int32_t* idx, int T, int k, int E, const PlanDev& p, void* ws, hipStream_t s) {
+  const int nb = (T + kPlanTB - 1) / kPlanTB;
+  int32_t* hist = (int32_t*)ws;
+  int32_t* blk_err = hist + (size_t)nb * E;
+  hipLaunchKernelGGL(k_plan_count, dim3(nb), dim3(256), E * 4, s, idx, T, k, E, hist, blk_err);
+  hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(1024), E * 4, s, T, k, E, nb, hist, blk_err, p);
+  hipLaunchKernelGGL(k_plan_scatter, dim3(nb), dim3(256), kPlanTB * k * 4, s, idx, T, k, E, hist, p);
+  return hipGetLastError();
+}
+
+// ============================================================================
+// Combine: y_t = s_t + sum_j w[t][j] * o[slot_row[t*k+j]], slots in order j,
+// fp32 arithmetic, one rounding to the output type.  o rows: plan rows
+// 0..T*k-1, then the shared expert's rows T*k + t.
+// ============================================================================
+
+__global__ __launch_bounds__(256) void k_combine(const void* __restrict__ o, int o_bf16,
+                                                 const float* __restrict__ topk_w, const int32_t* __restrict__ slot_row,
+                                                 int T, int k, int d, int has_shared, void* __restrict__ y,
+                                                 int y_bf16) {
+  const int t = blockIdx.y;
+  const int i = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= d) return;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto row4 = [&](long r) -> f32x4 {
+    if (o_bf16) {
+      const u32x2 v = *(const u32x2*)((const uint16_t*)o + r * d + i);
+      f32x4 f = {bf16_bits_to_f32(v.x & 0xffffu), bf16_bits_to_f32(v.x >> 16), bf16_bits_to_f32(v.y & 0xffffu),
+                 bf16_bits_to_f32(v.y >> 16)};
+      return f;
+    }
+    return *(const f32x4*)((const float*)o + r * d + i);
+  };
+  if (has_shared) acc = row4((long)T * k + t);
+  for (int j = 0; j < k; ++j) {
+    const int r = slot_row[(long)t * k + j];
+    if (r < 0) continue;
+    const float wj = topk_w[(long)t * k + j];
+    const f32x4 v = row4(r);
+    acc.x = fmaf(wj, v.x, acc.x);
+    acc.y = fmaf(wj, v.y, acc.y);
+    acc.z = fmaf(wj, v.z, acc.z);
+    acc.w = fmaf(wj, v.w, acc.w);
+  }
+  if (y_bf16) {
+    u32x2 r = {pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w)};
+    *(u32x2*)((uint16_t*)y + (long)t * d + i) = r;
+  } else {
+    *(f32x4*)((float*)y + (long)t * d + i) = acc;
+  }
+}
+
+hipError_t launch_combine(const void* o, int o_bf16, const float* topk_w, const int32_t* slot_row, int T, int k,
+                          int d, int has_shared, void* y, int y_dtype, hipStream_t s) {
+  const int per_blk = 256 * 4;
+  hipLaunchKernelGGL(k_combine, dim3((d + per_blk - 1) / per_blk, T), dim3(256), 0, s, o, o_bf16, topk_w, slot_row,
+                     T, k, d, has_shared, y, y_dtype == MOE_BF16 ? 1 : 0);
+  return hipGetLastError();
+}
+
+// ============================================================================
+// Stack glue: h += y; x = bf16(h / sqrt(mean(h^2) + eps)).  One workgroup per
+// token.
+// ============================================================================
+
+__global__ __launch_bounds__(256) void k_residual_rmsnorm(float* __restrict__ h, const void* __restrict__ y, int y_bf16,
+                                                          int d, float eps, uint16_t* __restrict__ x_out) {
+  const int t = blockIdx.x;
+  float* hr = h + (long)t * d;
+  __shared__ float red[4];
+  float ss = 0.0f;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    float v = hr[i];
+    if (y) v += y_bf16 ? bf16_bits_to_f32(((const uint16_t*)y)[(long)t * d + i]) : ((const float*)y)[(long)t * d + i];
+    hr[i] = v;
+    ss = fmaf(v, v, ss);
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = red[0] + red[1] + red[2] + red[3];
+  const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+  for (int i = threadIdx.x; i < d; i += blockDim.x) x_out[(long)t * d + i] = (uint16_t)f32_to_bf16_bits(hr[i] * inv);
+}
+
+hipError_t launch_residual_rmsnorm(float* h, const void* y, int y_dtype, int T, int d, float eps, void* x_out,
+                                   hipStream_t s) {
+  hipLaunchKernelGGL(k_residual_rmsnorm, dim3(T), dim3(256), 0, s, h, y, y_dtype == MOE_BF16 ? 1 : 0, d, eps,
+                     (uint16_t*)x_out);
+  return hipGetLastError();
+}
+
+}  // namespace qre

@@ -38,17 +38,19 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
   return s ? -v : v;
 }
 
-// float -> bf16 bits, round to nearest even (NaN kept quiet).
+// float -> bf16, round to nearest even (gfx950 converts in hardware:
+// v_cvt_pk_bf16_f32).
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // ---------------------------------------------------------------- IQ4_NL
@@ -85,7 +87,7 @@ __device__ __forceinline__ uint32_t biased_bytes_to_f16x2(uint32_t U, uint32_t s
 // One dword of IQ4_NL codes (bytes 4i..4i+3 of a block) -> eight exact fp16
 // codebook values, in the element order
 //   4i, 4i+1, 4i+2, 4i+3, 16+4i, 16+4i+1, 16+4i+2, 16+4i+3
-// (the activations are stored in the same per-block order, see kPermIq4).
+// (the activations are stored in the same per-block order, see iq4_pos).
 __device__ __forceinline__ f16x8 iq4_dword_to_f16x8(uint32_t w) {
   const uint32_t ulo = iq4_lookup4(w & 0x0F0F0F0Fu);
   const uint32_t uhi = iq4_lookup4((w >> 4) & 0x0F0F0F0Fu);
@@ -122,38 +124,27 @@ __device__ __forceinline__ f16x8 q8_dwords_to_f16x8(uint32_t a, uint32_t b) {
 
 // ---------------------------------------------------------------- NVFP4
 
-// One byte of two E2M1 codes (element 2i low nibble, 2i+1 high nibble) -> two
-// exact fp16 values.  Decoded arithmetically: magnitude index 0..7 maps to
-// {0, .5, 1, 1.5, 2, 3, 4, 6}.
+// E2M1 (sign bit 3, exponent bits 2..1 with bias 1, mantissa bit 0) ->
+// float: magnitude index 0..7 maps to {0, .5, 1, 1.5, 2, 3, 4, 6}.
 __device__ __forceinline__ float e2m1_to_f32(uint32_t n) {
   const uint32_t s = (n >> 3) & 1u, e = (n >> 1) & 3u, m = n & 1u;
   const float mag = (e == 0) ? 0.5f * (float)m : (float)(2u + m) * __uint_as_float((e + 125u) << 23);
   return s ? -mag : mag;
 }
 
-// e2m1 magnitudes as fp16 high bytes (low byte zero): 0, .5, 1, 1.5, 2, 3, 4, 6.
-constexpr uint32_t kE2m1H0 = 0x3E3C3800u;  // idx 0..3: 0x00, 0x38, 0x3C, 0x3E
-constexpr uint32_t kE2m1H1 = 0x46444240u;  // idx 4..7: 0x40, 0x42, 0x44, 0x46
-
-// One dword of E2M1 codes (8 elements, natural order) times an fp16 block
-// scale -> eight fp16 values e2m1 * scale (exact: at most 6 significant bits).
+// One dword of E2M1 codes (8 elements; element 2i in the low nibble of byte i)
+// times an fp16 block scale -> eight fp16 values e2m1 * scale, in element
+// order.  The products have at most 6 significant bits and are exact.  gfx950
+// converts a byte of two FP4 codes to two fp16 values in one instruction
+// (v_cvt_scalef32_pk_f16_fp4, scale 1).
 __device__ __forceinline__ f16x8 fp4_dword_to_f16x8(uint32_t w, f16 scale) {
-  // split nibbles: bytes of lo hold elements 0,2,4,6; bytes of hi hold 1,3,5,7
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-  const uint32_t hl = __builtin_amdgcn_perm(kE2m1H1, kE2m1H0, lo & 0x07070707u) | ((lo & 0x08080808u) << 4);
-  const uint32_t hh = __builtin_amdgcn_perm(kE2m1H1, kE2m1H0, hi & 0x07070707u) | ((hi & 0x08080808u) << 4);
-  // fp16 pair (elem 2b, elem 2b+1) = [0x00, hl.byte b, 0x00, hh.byte b]
-  u32x4 r;
-  r.x = __builtin_amdgcn_perm(hh, hl, 0x040C000Cu);
-  r.y = __builtin_amdgcn_perm(hh, hl, 0x050C010Cu);
-  r.z = __builtin_amdgcn_perm(hh, hl, 0x060C020Cu);
-  r.w = __builtin_amdgcn_perm(hh, hl, 0x070C030Cu);
   const f16x2 s2 = {scale, scale};
-  u32x4 o;
-  o.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, r.x) * s2);
-  o.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, r.y) * s2);
-  o.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, r.z) * s2);
-  o.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, r.w) * s2);
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+  u32x4 o = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1), __builtin_bit_cast(uint32_t, p2),
+             __builtin_bit_cast(uint32_t, p3)};
   return __builtin_bit_cast(f16x8, o);
 }
 

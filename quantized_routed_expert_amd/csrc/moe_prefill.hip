@@ -92,18 +92,11 @@ __device__ __forceinline__ void dequant32_to_lds(const uint8_t* crow, const uint
     const float d = f16_bits_to_f32(((const uint16_t*)srow)[k0 >> 5]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const u32x2 a = q8_dword_to_f16x4(c0[i]);
-      const u32x2 b = q8_dword_to_f16x4(c1[i]);
-      const f16x2 a0 = __builtin_bit_cast(f16x2, a.x), a1 = __builtin_bit_cast(f16x2, a.y);
-      const f16x2 b0 = __builtin_bit_cast(f16x2, b.x), b1 = __builtin_bit_cast(f16x2, b.y);
-      v[4 * i + 0] = (float)a0[0] * d;
-      v[4 * i + 1] = (float)a0[1] * d;
-      v[4 * i + 2] = (float)a1[0] * d;
-      v[4 * i + 3] = (float)a1[1] * d;
-      v[16 + 4 * i + 0] = (float)b0[0] * d;
-      v[16 + 4 * i + 1] = (float)b0[1] * d;
-      v[16 + 4 * i + 2] = (float)b1[0] * d;
-      v[16 + 4 * i + 3] = (float)b1[1] * d;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        v[4 * i + b] = (float)(int8_t)((c0[i] >> (8 * b)) & 0xffu) * d;
+        v[16 + 4 * i + b] = (float)(int8_t)((c1[i] >> (8 * b)) & 0xffu) * d;
+      }
     }
   } else {
     const u32x4 c = *(const u32x4*)(crow + (k0 >> 1));

@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--kernel-passes", type=int, default=3, help="instrumented passes for the kernel timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB, 5 times (HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -95,6 +97,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.copy_calibration} MiB x 5")
+        return
 
     from quantized_routed_expert_amd import lib, synth
     from quantized_routed_expert_amd.stack import Stack

@@ -190,6 +190,49 @@ moe_status moe_dequantize(const moe_qmatrix* m, int32_t expert, int32_t out_dtyp
 moe_status moe_residual_rmsnorm(float* h, const void* y, int32_t y_dtype, int32_t T, int32_t d,
                                 float eps, void* x_out, void* stream);
 
+/* Optional per-layer records of moe_decode_stack (device pointers, each NULL
+ * to skip; layer l's entries start at l * (per-layer size)). */
+typedef struct moe_stack_record {
+  float* logits;      /* [n_layers][T][E] fp32 router logits */
+  int32_t* topk_idx;  /* [n_layers][T][k] selected experts (descending logit) */
+  float* topk_w;      /* [n_layers][T][k] renormalised gate weights */
+  void* x;            /* [n_layers][T][d] bf16 layer inputs */
+  float* y;           /* [n_layers][T][d] fp32 layer outputs */
+  int32_t* error;     /* [n_layers] plan / overflow flags of each layer (bits as moe_plan_buf.error) */
+  void** events;      /* [n_layers][2] hipEvent_t handles (created by the caller), recorded on the
+                         call's stream right before and after each layer's gate/up launch; for
+                         timing that kernel in eager (not graph-captured) calls */
+} moe_stack_record;
+
+/* Fused decode step through a stack of routed-expert layers for T <= 8
+ * tokens: for each layer l in order
+ *   x_l = bf16(rmsnorm(h)),  y_l = the routed-expert layer l on x_l,  h += y_l
+ * (the same computation as moe_residual_rmsnorm -> moe_route -> moe_plan ->
+ * moe_ffn_forward(y fp32) per layer, with the glue described at
+ * moe_residual_rmsnorm; the layer itself follows the routing and expert
+ * passages cited at moe_route, moe_plan and moe_ffn_forward).  Each layer is
+ * three kernel launches for T = 1 (glue + router; top-k + plan + gate/up +
+ * SwiGLU; down) and four for T > 1 (the glue gets its own launch); the last
+ * layer's combine is folded into h by one more launch.  Routing and the plan
+ * are recomputed in every workgroup of the gate/up launch from the logits,
+ * so no launch waits on a separate plan kernel.
+ *   layers:  HOST array of n_layers descriptors of one shape (d, f, E, k,
+ *            formats and has_shared equal); all weights device-resident.
+ *   h:       device fp32 [T][d], the residual stream; updated in place.
+ *   rec:     optional records (host struct of device pointers, or NULL).
+ *   ws:      device workspace of moe_decode_stack_workspace_size bytes,
+ *            256-byte aligned; contents are scratch between calls.
+ * Coverage: 1 <= T <= 8, d a multiple of 1024 and at most 4096, activation
+ * layout and numerics as the decode path of moe_ffn_forward (bf16 inputs).
+ * Errors: validation codes as the per-layer entry points; plan or overflow
+ * flags are reported only through rec->error.  Asynchronous on `stream`. */
+moe_status moe_decode_stack(const moe_layer* layers, int32_t n_layers, float* h, int32_t T, float eps,
+                            const moe_stack_record* rec, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for moe_decode_stack on this layer shape with up to T_max
+ * tokens (0 on invalid or unsupported arguments). */
+size_t moe_decode_stack_workspace_size(const moe_layer* layer, int32_t T_max);
+
 /* Workspace bytes needed by moe_route / moe_plan / moe_ffn_forward for up to
  * T_max tokens on this layer shape (0 on invalid arguments). */
 size_t moe_workspace_size(const moe_layer* layer, int32_t T_max);

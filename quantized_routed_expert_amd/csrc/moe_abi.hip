@@ -208,6 +208,48 @@ moe_status moe_dequantize(const moe_qmatrix* m, int32_t expert, int32_t out_dtyp
   return hip_status(launch_dequant(qmat_dev(*m), expert, out_dtype, dst, (hipStream_t)stream));
 }
 
+size_t moe_decode_stack_workspace_size(const moe_layer* layer, int32_t T_max) {
+  if (check_dims(layer) != MOE_OK || T_max < 1 || T_max > kFusedMaxT) return 0;
+  if (layer->d % 1024 != 0 || layer->d > 4096) return 0;
+  return fused_ws_bytes(T_max, layer->d, layer->f, layer->k, layer->E);
+}
+
+moe_status moe_decode_stack(const moe_layer* layers, int32_t n_layers, float* h, int32_t T, float eps,
+                            const moe_stack_record* rec, void* ws, size_t ws_bytes, void* stream) {
+  if (!layers || n_layers < 1 || !h || T < 1 || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
+  if (T > kFusedMaxT) return MOE_ERR_UNSUPPORTED;
+  const moe_layer& L0 = layers[0];
+  for (int l = 0; l < n_layers; ++l) {
+    const moe_layer& L = layers[l];
+    moe_status st = check_layer(&L);
+    if (st != MOE_OK) return st;
+    if ((st = check_router(&L)) != MOE_OK) return st;
+    if (L.d != L0.d || L.f != L0.f || L.E != L0.E || L.k != L0.k || L.has_shared != L0.has_shared ||
+        L.gate.type != L0.gate.type || L.down.type != L0.down.type)
+      return MOE_ERR_UNSUPPORTED;
+  }
+  if (L0.d % 1024 != 0 || L0.d > 4096) return MOE_ERR_UNSUPPORTED;
+  if (!aligned(h, 16)) return MOE_ERR_ALIGNMENT;
+  FusedRecord r{};
+  r.eps = eps;
+  if (rec) {
+    r.logits = rec->logits;
+    r.topk_idx = rec->topk_idx;
+    r.topk_w = rec->topk_w;
+    r.x = (uint16_t*)rec->x;
+    r.y = rec->y;
+    r.error = rec->error;
+    r.events = (hipEvent_t*)rec->events;
+    if ((r.logits && !aligned(r.logits, 4)) || (r.topk_idx && !aligned(r.topk_idx, 4)) ||
+        (r.topk_w && !aligned(r.topk_w, 4)) || (r.x && !aligned(r.x, 16)) || (r.y && !aligned(r.y, 16)) ||
+        (r.error && !aligned(r.error, 4)))
+      return MOE_ERR_ALIGNMENT;
+  }
+  if (!ws || ws_bytes < fused_ws_bytes(T, L0.d, L0.f, L0.k, L0.E)) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
+  return hip_status(launch_fused_step(layers, n_layers, h, T, r, ws, (hipStream_t)stream));
+}
+
 moe_status moe_residual_rmsnorm(float* h, const void* y, int32_t y_dtype, int32_t T, int32_t d, float eps,
                                 void* x_out, void* stream) {
   if (!h || !x_out || T < 1 || d < 1 || !valid_dtype(y_dtype) || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;

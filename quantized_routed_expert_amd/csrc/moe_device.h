@@ -100,7 +100,7 @@ __device__ __forceinline__ f16x8 iq4_dword_to_f16x8(uint32_t w) {
 }
 
 // Position of block element e (0..31) in the IQ4_NL activation layout that
-// matches iq4_dword_to_f16x8: dword i of the codes covers positions 8i..8i+7.
+// matches iq4_dword_to_f16x8: code dword i covers positions 8i..8i+7.
 __device__ __forceinline__ int iq4_pos(int e) {
   return ((e & 15) >> 2) * 8 + (e >> 4) * 4 + (e & 3);
 }
@@ -166,6 +166,90 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
   return v;
+}
+
+// ---------------------------------------------------------------- top-k keys
+
+// 64-bit key whose unsigned order is "larger logit first, then lower expert
+// id": the logit's bits mapped to an order-preserving unsigned integer (-0 and
+// +0 compare equal), above the complement of the expert id.
+__device__ __forceinline__ uint64_t topk_key(float v, uint32_t e) {
+  uint32_t u = __float_as_uint(v);
+  if ((u & 0x7fffffffu) == 0u) u = 0u;
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint64_t)(0xffffffffu - e);
+}
+__device__ __forceinline__ float topk_key_value(uint64_t key) {
+  const uint32_t u = (uint32_t)(key >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+__device__ __forceinline__ uint32_t topk_key_index(uint64_t key) { return 0xffffffffu - (uint32_t)key; }
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, o, kWave), hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
+    const uint64_t w = ((uint64_t)hi << 32) | lo;
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Top-k of one token's logits L[0..E) with one wavefront (E <= 64 * NPL):
+// lane j < k receives slot j's expert id and logit.  Branch-free: each round
+// takes the wave-wide largest key and clears it in its owner lane.
+template <int NPL>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ L, int E, int k, int lane, int& sel_idx,
+                                          float& sel_val) {
+  uint64_t key[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = (e < E) ? topk_key(L[e], (uint32_t)e) : 0ull;
+  }
+  sel_idx = 0;
+  sel_val = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t m = key[0];
+#pragma unroll
+    for (int i = 1; i < NPL; ++i) m = key[i] > m ? key[i] : m;
+    m = wave_max_u64(m);
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) key[i] = key[i] == m ? 0ull : key[i];
+    if (lane == j) {
+      sel_idx = (int)topk_key_index(m);
+      sel_val = topk_key_value(m);
+    }
+  }
+}
+
+// Exclusive prefix sum over a workgroup of NT threads (NT a multiple of 64,
+// at most 1024); `tot` receives the sum.  `scratch` holds NT/64 + 1 ints.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int& tot) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += u;
+  }
+  if (lane == 63) scratch[wid] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < NT / 64; ++w) {
+      const int t = scratch[w];
+      scratch[w] = run;
+      run += t;
+    }
+    scratch[NT / 64] = run;
+  }
+  __syncthreads();
+  const int res = inc - v + scratch[wid];
+  tot = scratch[NT / 64];
+  __syncthreads();
+  return res;
 }
 
 // ---------------------------------------------------------------- formats

@@ -75,6 +75,23 @@ hipError_t launch_decode_stage(int stage, const FfnCall& c, hipStream_t s);
 size_t prefill_ws_bytes(int T, int d, int f, int k);
 hipError_t launch_prefill_stage(int stage, const FfnCall& c, hipStream_t s);
 
+// Fused decode step over a stack of layers (moe_decode.hip).  Optional
+// per-layer records (null to skip).
+constexpr int kFusedMaxT = 8;
+struct FusedRecord {
+  float* logits;      // [L][T][E]
+  int32_t* topk_idx;  // [L][T][k]
+  float* topk_w;      // [L][T][k]
+  uint16_t* x;        // [L][T][d] bf16 layer inputs
+  float* y;           // [L][T][d] layer outputs
+  int32_t* error;     // [L] plan / overflow flags
+  hipEvent_t* events; // [L][2] recorded around each layer's gate/up launch
+  float eps;
+};
+size_t fused_ws_bytes(int T, int d, int f, int k, int E);
+hipError_t launch_fused_step(const moe_layer* layers, int n_layers, float* h, int T, const FusedRecord& rec,
+                             void* ws, hipStream_t s);
+
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 }  // namespace qre

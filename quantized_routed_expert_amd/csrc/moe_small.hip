@@ -184,80 +184,50 @@ hipError_t launch_router_logits(const float* W, const float* b, const void* x, i
 // ============================================================================
 // Top-k + gate weights: one wavefront per token.  Slot order: descending
 // logit, lower expert id first on ties; weights = softmax over the k selected
-// logits.  E <= 1024 (16 logits per lane).
+// logits.  E <= 1024.
 // ============================================================================
 
-constexpr int kTopkPerLane = 16;
-
+template <int NPL>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
                                               int32_t* __restrict__ idx, float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* L = logits + (long)t * E;
-  float v[kTopkPerLane];
-#pragma unroll
-  for (int i = 0; i < kTopkPerLane; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = (e < E) ? L[e] : -__builtin_inff();
-  }
-  uint32_t taken = 0;  // bit i: element lane + 64 i already selected
-  float sel_val = 0.0f;
-  int sel_idx = 0;
-  float my_val = -__builtin_inff();
-  for (int j = 0; j < k; ++j) {
-    // lane-local best among untaken: larger value, then lower index
-    float bv = -__builtin_inff();
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < kTopkPerLane; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && !((taken >> i) & 1u)) {
-        if (v[i] > bv || (v[i] == bv && e < bi) || bi == 0x7fffffff) {
-          bv = v[i];
-          bi = e;
-        }
-      }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == j) {
-      sel_val = bv;
-      sel_idx = bi;
-    }
-    if (j == 0) my_val = bv;  // the maximum
-  }
-  // softmax over the selected logits
-  float ex = 0.0f;
-  if (lane < k) ex = __expf(sel_val - my_val);
+  int si;
+  float sv;
+  wave_topk<NPL>(logits + (long)t * E, E, k, lane, si, sv);
+  const float vmax = __shfl(sv, 0, 64);
+  const float ex = lane < k ? expf(sv - vmax) : 0.0f;
   const float sum = wave_sum(ex);
   if (lane < k) {
-    idx[(long)t * k + lane] = sel_idx;
+    idx[(long)t * k + lane] = si;
     w[(long)t * k + lane] = ex / sum;
   }
 }
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w, hipStream_t s) {
-  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, idx, w);
+  const dim3 g((T + 3) / 4), b(256);
+  if (E <= 64)
+    hipLaunchKernelGGL(k_topk<1>, g, b, 0, s, logits, T, E, k, idx, w);
+  else if (E <= 256)
+    hipLaunchKernelGGL(k_topk<4>, g, b, 0, s, logits, T, E, k, idx, w);
+  else if (E <= 512)
+    hipLaunchKernelGGL(k_topk<8>, g, b, 0, s, logits, T, E, k, idx, w);
+  else
+    hipLaunchKernelGGL(k_topk<16>, g, b, 0, s, logits, T, E, k, idx, w);
   return hipGetLastError();
 }
 
 // ============================================================================
 // Expert plan ("device-planned MoE tail", UD-IQ2_XS (L4 fix) page, "What was
-// changed").  Three passes over blocks of kPlanTB tokens, no global atomics:
-//   count   per-block expert histograms (LDS atomics only count)
-//   scan    one workgroup: counts, offsets, per-block bases, active list
-//   scatter rank = base + earlier occurrences in the block (token order)
-// The result is independent of scheduling: rows of an expert are in
+// changed").  No global atomics and no dependence on scheduling: within a
+// block of up to 64 tokens, each expert gets a 64-bit mask of the tokens that
+// picked it (LDS atomic OR is order-independent); a pair's rank among the
+// expert's rows is the number of earlier tokens in the mask, plus the rows of
+// the same expert in earlier blocks.  Rows of an expert are therefore in
 // ascending token order.
+//   T <= 64: one kernel, one workgroup.
+//   T  > 64: count (per-block histograms), scan (one workgroup), scatter.
 // ============================================================================
 
 constexpr int kPlanTB = 64;
@@ -267,84 +237,116 @@ size_t plan_ws_bytes(int T, int E) {
   return align_up((size_t)nb * E * 4 + (size_t)nb * 4, 256);
 }
 
-__global__ __launch_bounds__(256) void k_plan_count(const int32_t* __restrict__ idx, int T, int k, int E,
-                                                    int32_t* __restrict__ hist, int32_t* __restrict__ blk_err) {
-  extern __shared__ int32_t sh[];
-  const int b = blockIdx.x;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) sh[e] = 0;
+// Token masks of one block of <= 64 tokens into LDS mask[E]; returns 1 if an
+// id was out of range.
+__device__ __forceinline__ int block_token_masks(const int32_t* __restrict__ idx, int t0, int t1, int k, int E,
+                                                 unsigned long long* mask) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) mask[e] = 0ull;
   __syncthreads();
-  const int t0 = b * kPlanTB, t1 = min(T, t0 + kPlanTB);
   int err = 0;
   for (int p = t0 * k + threadIdx.x; p < t1 * k; p += blockDim.x) {
     const int e = idx[p];
     if (e >= 0 && e < E)
-      atomicAdd(&sh[e], 1);
+      atomicOr(&mask[e], 1ull << (p / k - t0));
     else
       err = 1;
   }
-  err = __syncthreads_or(err);
-  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(long)b * E + e] = sh[e];
+  return __syncthreads_or(err);
+}
+
+__device__ __forceinline__ void plan_scatter_block(const int32_t* __restrict__ idx, int t0, int t1, int k, int E,
+                                                   const unsigned long long* mask, const int32_t* base,
+                                                   const PlanDev& p) {
+  for (int q = t0 * k + threadIdx.x; q < t1 * k; q += blockDim.x) {
+    const int e = idx[q];
+    if (e < 0 || e >= E) {
+      p.slot_row[q] = -1;
+      continue;
+    }
+    const int tl = q / k - t0;
+    const int rank = __popcll(mask[e] & ((1ull << tl) - 1ull));
+    const int r = base[e] + rank;
+    p.row_token[r] = t0 + tl;
+    p.row_slot[r] = q % k;
+    p.slot_row[q] = r;
+  }
+}
+
+// T <= 64, E <= 1024: the whole plan in one workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void k_plan_small(const int32_t* __restrict__ idx, int T, int k, int E, PlanDev p) {
+  __shared__ unsigned long long mask[1024];
+  __shared__ int32_t base[1024];
+  __shared__ int32_t scratch[2][17];
+  const int err = block_token_masks(idx, 0, T, k, E, mask);
+  const int e = threadIdx.x;
+  const int cnt = e < E ? __popcll(mask[e]) : 0;
+  int n_valid, n_act;
+  const int off = block_exclusive_scan<1024>(cnt, scratch[0], n_valid);
+  const int aoff = block_exclusive_scan<1024>(cnt > 0 ? 1 : 0, scratch[1], n_act);
+  if (e < E) {
+    base[e] = off;
+    p.counts[e] = cnt;
+    p.offsets[e] = off;
+    if (cnt > 0) p.active[aoff] = e;
+    if (e >= n_act) p.active[e] = -1;
+  }
+  if (e == 0) {
+    p.offsets[E] = n_valid;
+    *p.n_active = n_act;
+    *p.error = err;
+  }
+  for (int r = n_valid + threadIdx.x; r < T * k; r += blockDim.x) {
+    p.row_token[r] = -1;
+    p.row_slot[r] = -1;
+  }
+  __syncthreads();
+  plan_scatter_block(idx, 0, T, k, E, mask, base, p);
+}
+
+__global__ __launch_bounds__(256) void k_plan_count(const int32_t* __restrict__ idx, int T, int k, int E,
+                                                    int32_t* __restrict__ hist, int32_t* __restrict__ blk_err) {
+  __shared__ unsigned long long mask[1024];
+  const int b = blockIdx.x;
+  const int t0 = b * kPlanTB, t1 = min(T, t0 + kPlanTB);
+  const int err = block_token_masks(idx, t0, t1, k, E, mask);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(long)b * E + e] = __popcll(mask[e]);
   if (threadIdx.x == 0) blk_err[b] = err;
 }
 
 __global__ __launch_bounds__(1024) void k_plan_scan(int T, int k, int E, int nb, int32_t* __restrict__ hist,
                                                     const int32_t* __restrict__ blk_err, PlanDev p) {
-  extern __shared__ int32_t sh[];  // [E] counts, then scan scratch
-  const int tid = threadIdx.x;
-  // per expert: total and exclusive per-block prefix (in place)
-  for (int e = tid; e < E; e += blockDim.x) {
-    int run = 0;
-    for (int b = 0; b < nb; ++b) {
+  __shared__ int32_t scratch[2][17];
+  __shared__ int32_t err_s;
+  const int e = threadIdx.x;
+  int cnt = 0;
+  if (e < E) {
+    for (int b = 0; b < nb; ++b) {  // per-block exclusive prefix, in place
       const int c = hist[(long)b * E + e];
-      hist[(long)b * E + e] = run;
-      run += c;
+      hist[(long)b * E + e] = cnt;
+      cnt += c;
     }
-    sh[e] = run;
-    p.counts[e] = run;
   }
-  __syncthreads();
-  // exclusive scan over experts (sequential per thread chunk, then across)
-  __shared__ int32_t chunk_sum[1024];
-  __shared__ int32_t chunk_act[1024];
-  const int per = (E + blockDim.x - 1) / blockDim.x;
-  const int e0 = tid * per, e1 = min(E, e0 + per);
-  int s = 0, a = 0;
-  for (int e = e0; e < e1; ++e) {
-    s += sh[e];
-    a += sh[e] > 0 ? 1 : 0;
-  }
-  chunk_sum[tid] = s;
-  chunk_act[tid] = a;
-  __syncthreads();
-  if (tid == 0) {
-    int rs = 0, ra = 0;
-    for (int i = 0; i < (int)blockDim.x; ++i) {
-      const int cs = chunk_sum[i], ca = chunk_act[i];
-      chunk_sum[i] = rs;
-      chunk_act[i] = ra;
-      rs += cs;
-      ra += ca;
-    }
-    p.offsets[E] = rs;
-    *p.n_active = ra;
-    int err = 0;
-    for (int b = 0; b < nb; ++b) err |= blk_err[b];
-    *p.error = err;
-  }
-  __syncthreads();
-  int off = chunk_sum[tid], act = chunk_act[tid];
-  for (int e = e0; e < e1; ++e) {
-    const int c = sh[e];
+  int n_valid, n_act;
+  const int off = block_exclusive_scan<1024>(cnt, scratch[0], n_valid);
+  const int aoff = block_exclusive_scan<1024>(cnt > 0 ? 1 : 0, scratch[1], n_act);
+  if (e < E) {
+    p.counts[e] = cnt;
     p.offsets[e] = off;
+    if (cnt > 0) p.active[aoff] = e;
+    if (e >= n_act) p.active[e] = -1;
     for (int b = 0; b < nb; ++b) hist[(long)b * E + e] += off;
-    if (c > 0) p.active[act++] = e;
-    off += c;
   }
+  if (threadIdx.x == 0) err_s = 0;
   __syncthreads();
-  const int n_act = *p.n_active;
-  for (int e = n_act + tid; e < E; e += blockDim.x) p.active[e] = -1;
-  const int n_valid = p.offsets[E];
-  for (int r = n_valid + tid; r < T * k; r += blockDim.x) {
+  for (int b = threadIdx.x; b < nb; b += blockDim.x)
+    if (blk_err[b]) atomicOr(&err_s, 1);
+  __syncthreads();
+  if (e == 0) {
+    p.offsets[E] = n_valid;
+    *p.n_active = n_act;
+    *p.error = err_s;
+  }
+  for (int r = n_valid + threadIdx.x; r < T * k; r += blockDim.x) {
     p.row_token[r] = -1;
     p.row_slot[r] = -1;
   }
@@ -352,38 +354,24 @@ __global__ __launch_bounds__(1024) void k_plan_scan(int T, int k, int E, int nb,
 
 __global__ __launch_bounds__(256) void k_plan_scatter(const int32_t* __restrict__ idx, int T, int k, int E,
                                                       const int32_t* __restrict__ base, PlanDev p) {
-  extern __shared__ int32_t sidx[];  // [kPlanTB * k]
+  __shared__ unsigned long long mask[1024];
   const int b = blockIdx.x;
   const int t0 = b * kPlanTB, t1 = min(T, t0 + kPlanTB);
-  const int npair = (t1 - t0) * k;
-  for (int i = threadIdx.x; i < npair; i += blockDim.x) sidx[i] = idx[(long)t0 * k + i];
-  __syncthreads();
-  for (int i = threadIdx.x; i < npair; i += blockDim.x) {
-    const int tl = i / k, j = i % k;
-    const int e = sidx[i];
-    const long pair = (long)(t0 + tl) * k + j;
-    if (e < 0 || e >= E) {
-      p.slot_row[pair] = -1;
-      continue;
-    }
-    int rank = 0;
-    for (int u = 0; u < tl; ++u) {
-      for (int jj = 0; jj < k; ++jj) rank += (sidx[u * k + jj] == e) ? 1 : 0;
-    }
-    const int r = base[(long)b * E + e] + rank;
-    p.row_token[r] = t0 + tl;
-    p.row_slot[r] = j;
-    p.slot_row[pair] = r;
-  }
+  block_token_masks(idx, t0, t1, k, E, mask);
+  plan_scatter_block(idx, t0, t1, k, E, mask, base + (long)b * E, p);
 }
 
 hipError_t launch_plan(const int32_t* idx, int T, int k, int E, const PlanDev& p, void* ws, hipStream_t s) {
+  if (T <= kPlanTB) {
+    hipLaunchKernelGGL(k_plan_small, dim3(1), dim3(1024), 0, s, idx, T, k, E, p);
+    return hipGetLastError();
+  }
   const int nb = (T + kPlanTB - 1) / kPlanTB;
   int32_t* hist = (int32_t*)ws;
   int32_t* blk_err = hist + (size_t)nb * E;
-  hipLaunchKernelGGL(k_plan_count, dim3(nb), dim3(256), E * 4, s, idx, T, k, E, hist, blk_err);
-  hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(1024), E * 4, s, T, k, E, nb, hist, blk_err, p);
-  hipLaunchKernelGGL(k_plan_scatter, dim3(nb), dim3(256), kPlanTB * k * 4, s, idx, T, k, E, hist, p);
+  hipLaunchKernelGGL(k_plan_count, dim3(nb), dim3(256), 0, s, idx, T, k, E, hist, blk_err);
+  hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(1024), 0, s, T, k, E, nb, hist, blk_err, p);
+  hipLaunchKernelGGL(k_plan_scatter, dim3(nb), dim3(256), 0, s, idx, T, k, E, hist, p);
   return hipGetLastError();
 }
 

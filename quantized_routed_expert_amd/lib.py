@@ -33,8 +33,8 @@ QTYPE = {"q8_0": MOE_Q8_0, "iq4_nl": MOE_IQ4_NL, "nvfp4": MOE_NVFP4}
 DTYPE = {"f32": MOE_F32, "bf16": MOE_BF16}
 
 EXPORTED = ["moe_route", "moe_plan", "moe_ffn_forward", "moe_ffn_prepare", "moe_ffn_gateup", "moe_ffn_down",
-            "moe_ffn_combine", "moe_dequantize", "moe_residual_rmsnorm", "moe_workspace_size",
-            "moe_status_string", "moe_version"]
+            "moe_ffn_combine", "moe_dequantize", "moe_residual_rmsnorm", "moe_decode_stack",
+            "moe_decode_stack_workspace_size", "moe_workspace_size", "moe_status_string", "moe_version"]
 
 
 class MoeError(RuntimeError):
@@ -62,6 +62,10 @@ class PlanBuf(ctypes.Structure):
                 ("counts", "offsets", "row_token", "row_slot", "slot_row", "active", "n_active", "error")]
 
 
+class StackRecord(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("logits", "topk_idx", "topk_w", "x", "y", "error", "events")]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
@@ -79,6 +83,8 @@ def _load():
         "moe_ffn_combine": (i32, [LP, i32, i32, vp, PP, vp, i32, vp, sz, vp]),
         "moe_dequantize": (i32, [QP, i32, i32, vp, vp]),
         "moe_residual_rmsnorm": (i32, [vp, vp, i32, i32, i32, ctypes.c_float, vp, vp]),
+        "moe_decode_stack": (i32, [LP, i32, vp, i32, ctypes.c_float, ctypes.POINTER(StackRecord), vp, sz, vp]),
+        "moe_decode_stack_workspace_size": (sz, [LP, i32]),
         "moe_workspace_size": (sz, [LP, i32]),
         "moe_status_string": (ctypes.c_char_p, [i32]),
         "moe_version": (ctypes.c_char_p, []),
@@ -239,3 +245,35 @@ def moe_residual_rmsnorm(h, y, y_dtype, T, d, eps, x_out, stream=None):
     st = _lib.moe_residual_rmsnorm(_ptr(h), _ptr(y), int(y_dtype), int(T), int(d), float(eps), _ptr(x_out),
                                    _stream(stream))
     _check(st, "moe_residual_rmsnorm")
+
+
+def moe_decode_stack_workspace_size(L, T_max):
+    return int(_lib.moe_decode_stack_workspace_size(ctypes.byref(L), int(T_max)))
+
+
+def layer_array(structs):
+    """Contiguous host array of Layer structs (moe_decode_stack's `layers`)."""
+    arr = (Layer * len(structs))()
+    for i, L in enumerate(structs):
+        arr[i] = L
+    return arr
+
+
+def stack_record(logits=None, topk_idx=None, topk_w=None, x=None, y=None, error=None, events=None):
+    """events: None, or a list of 2*n_layers torch.cuda.Event (created with
+    enable_timing=True and already initialised by a first record)."""
+    ev = None
+    if events is not None:
+        ev = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    r = StackRecord(_ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(x), _ptr(y), _ptr(error),
+                    ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None)
+    r._keep = ev  # the handle array must outlive the struct
+    return r
+
+
+def moe_decode_stack(layers, n_layers, h, T, eps, rec, ws, ws_bytes, stream=None):
+    """layers: a ctypes array from layer_array(); rec: a StackRecord or None."""
+    st = _lib.moe_decode_stack(layers, int(n_layers), _ptr(h), int(T), float(eps),
+                               ctypes.byref(rec) if rec is not None else None, _ptr(ws), int(ws_bytes),
+                               _stream(stream))
+    _check(st, "moe_decode_stack")

@@ -171,3 +171,47 @@ def test_workspace_size_monotone_and_covers_paths():
     # the prefill path needs at least the bf16 H and O rows
     R = 4096 * 8 + 4096
     assert sizes[-1] >= R * (768 + 3072) * 2
+
+
+def test_decode_stack_validation():
+    so = lib.library()
+    L = _fake_layer(d=1024, f=256, E=64, k=4, qtype=lib.MOE_IQ4_NL, down=lib.MOE_Q8_0, shared=True)
+    arr = lib.layer_array([L, L])
+    wsb = lib.moe_decode_stack_workspace_size(L, 8)
+    assert wsb > 0
+    assert lib.moe_decode_stack_workspace_size(L, 9) == 0  # more tokens than the fused step covers
+    assert lib.moe_decode_stack_workspace_size(_fake_layer(d=512), 1) == 0  # d not a multiple of 1024
+    assert lib.moe_decode_stack_workspace_size(_fake_layer(d=5120), 1) == 0  # d above 4096
+    sizes = [lib.moe_decode_stack_workspace_size(L, t) for t in range(1, 9)]
+    assert sizes == sorted(sizes)
+    wsb = sizes[3]  # T = 4
+
+    def call(arr=arr, n=2, h=1 << 30, T=4, eps=1e-6, ws=1 << 31, wsb=wsb):
+        return so.moe_decode_stack(arr, n, h, T, ctypes.c_float(eps), None, ws, wsb, None)
+
+    assert call(arr=None) == lib.MOE_ERR_INVALID_ARG
+    assert call(n=0) == lib.MOE_ERR_INVALID_ARG
+    assert call(h=0) == lib.MOE_ERR_INVALID_ARG
+    assert call(T=0) == lib.MOE_ERR_INVALID_ARG
+    assert call(T=9) == lib.MOE_ERR_UNSUPPORTED
+    assert call(eps=-1.0) == lib.MOE_ERR_INVALID_ARG
+    assert call(h=(1 << 30) + 4) == lib.MOE_ERR_ALIGNMENT
+    assert call(ws=0) == lib.MOE_ERR_WORKSPACE
+    assert call(wsb=wsb - 1) == lib.MOE_ERR_WORKSPACE
+    assert call(ws=(1 << 31) + 64) == lib.MOE_ERR_ALIGNMENT
+    # layers of different shapes or formats are not covered
+    L2 = _fake_layer(d=1024, f=256, E=64, k=4, qtype=lib.MOE_IQ4_NL, down=lib.MOE_IQ4_NL, shared=True)
+    assert call(arr=lib.layer_array([L, L2])) == lib.MOE_ERR_UNSUPPORTED
+    L3 = _fake_layer(d=1024, f=256, E=64, k=4, qtype=lib.MOE_IQ4_NL, down=lib.MOE_Q8_0, shared=False)
+    assert call(arr=lib.layer_array([L, L3])) == lib.MOE_ERR_UNSUPPORTED
+    # d outside the fused step's coverage
+    L4 = _fake_layer(d=512, f=256, E=64, k=4)
+    assert call(arr=lib.layer_array([L4]), n=1) == lib.MOE_ERR_UNSUPPORTED
+    # a bad layer anywhere in the stack is caught
+    L5 = _fake_layer(d=1024, f=256, E=64, k=4, qtype=lib.MOE_IQ4_NL, down=lib.MOE_Q8_0, shared=True)
+    L5.router_w = 0
+    assert call(arr=lib.layer_array([L, L5])) == lib.MOE_ERR_INVALID_ARG
+    # misaligned record pointers
+    rec = lib.StackRecord(None, None, None, (1 << 32) + 2, None, None, None)
+    assert so.moe_decode_stack(arr, 2, 1 << 30, 4, ctypes.c_float(1e-6), ctypes.byref(rec), 1 << 31, wsb,
+                               None) == lib.MOE_ERR_ALIGNMENT

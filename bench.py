@@ -3,7 +3,9 @@
 One step = one pass of the whole hot path over the stack for one batch of
 synthetic tokens: per layer the residual/RMSNorm glue, router + top-k, the
 expert plan and the grouped experts with combine, replayed from a HIP graph.
-Inputs are resident in HBM before the timed region starts.
+Up to 8 tokens the step is the fused entry point moe_decode_stack; above that
+it is the per-layer entry points.  Inputs are resident in HBM before the timed
+region starts.
 
 Prints one JSON line (rank 0) with the metric, the roofline of the dominant
 kernel (timed live with HIP events on its own stream) and the CPU oracle's
@@ -56,10 +58,10 @@ def source_digest(paths):
 
 DOMINANT = {
     # workload -> (kernel family, sources it is built from)
-    "decode": ("k_ffn_dq gate/up (IQ4_NL)", ["quantized_routed_expert_amd/csrc/moe_decode.hip",
-                                             "quantized_routed_expert_amd/csrc/moe_device.h"]),
-    "verify": ("k_ffn_dq gate/up (IQ4_NL)", ["quantized_routed_expert_amd/csrc/moe_decode.hip",
-                                             "quantized_routed_expert_amd/csrc/moe_device.h"]),
+    "decode": ("k_fz_gateup (top-k + plan + gate/up + SwiGLU, IQ4_NL)",
+               ["quantized_routed_expert_amd/csrc/moe_decode.hip", "quantized_routed_expert_amd/csrc/moe_device.h"]),
+    "verify": ("k_fz_gateup (top-k + plan + gate/up + SwiGLU, IQ4_NL)",
+               ["quantized_routed_expert_amd/csrc/moe_decode.hip", "quantized_routed_expert_amd/csrc/moe_device.h"]),
     "slots": ("k_ffn_dq gate/up (NVFP4)", ["quantized_routed_expert_amd/csrc/moe_decode.hip",
                                            "quantized_routed_expert_amd/csrc/moe_device.h"]),
     "prefill": ("k_pf_gemm gate/up (IQ4_NL)", ["quantized_routed_expert_amd/csrc/moe_prefill.hip",
@@ -109,7 +111,7 @@ def main():
         return
 
     from quantized_routed_expert_amd import lib, synth
-    from quantized_routed_expert_amd.stack import Stack
+    from quantized_routed_expert_amd.stack import FusedStack, Stack
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = synth.WORKLOADS[args.workload]
@@ -127,17 +129,33 @@ def main():
             torch.cuda.synchronize()
             log(f"[bench] generated {l + 1}/{wl.n_layers} layers ({time.time() - t0:.1f}s)")
     h0 = synth.make_tokens(wl, dev)
-    st = Stack(layers, wl.T, y_dtype=wl.y_dtype, x_dtype="bf16", chain=True, keep_logits=False)
+    # T <= 8 with fp32 layer outputs: the fused decode step (moe_decode_stack);
+    # otherwise the per-layer entry points (route -> plan -> ffn_forward + glue).
+    fused = wl.T <= 8 and wl.y_dtype == "f32"
+    if fused:
+        st = FusedStack(layers, wl.T, record=True, device=dev)
+    else:
+        st = Stack(layers, wl.T, y_dtype=wl.y_dtype, x_dtype="bf16", chain=True, keep_logits=False)
     st.set_tokens(h0)
     st.step()
     torch.cuda.synchronize()
-    errs = [int(b.plan.error.item()) for b in st.bufs]
+    if fused:
+        errs = st.rec_error.cpu().tolist()
+        idx_all = st.rec_idx.cpu().numpy()
+        U = [len(np.unique(idx_all[l])) for l in range(wl.n_layers)]
+    else:
+        errs = [int(b.plan.error.item()) for b in st.bufs]
+        U = [int(b.plan.n_active.item()) for b in st.bufs]
     assert not any(errs), f"plan/experts error flags {errs}"
-    U = [int(b.plan.n_active.item()) for b in st.bufs]
-    log(f"[bench] eager step ok; U per layer mean {np.mean(U):.1f} (min {min(U)}, max {max(U)})")
+    log(f"[bench] eager step ok ({'fused moe_decode_stack' if fused else 'per-layer entry points'}); "
+        f"U per layer mean {np.mean(U):.1f} (min {min(U)}, max {max(U)})")
 
     # ---------------------------------------------------------------- timed region
-    st.capture()
+    # The timed graph writes no records (the fused step's only outputs are h).
+    if fused:
+        st.capture(record=lib.stack_record())
+    else:
+        st.capture()
     for _ in range(args.warmup):
         st.replay()
     torch.cuda.synchronize()
@@ -175,7 +193,17 @@ def main():
     launch_bytes = []
     launch_flops = []
     xd = lib.MOE_BF16
-    for _ in range(args.kernel_passes):
+    for _ in range(args.kernel_passes if fused else 0):
+        evs_k = [torch.cuda.Event(enable_timing=True) for _ in range(2 * wl.n_layers)]
+        for e in evs_k:
+            e.record(stream)  # creates the underlying HIP events
+        st.step(st.timed_record(evs_k))
+        for i in range(wl.n_layers):
+            durations.append((evs_k[2 * i], evs_k[2 * i + 1]))
+            u = U[i]
+            launch_bytes.append((u + 1) * (gate_b + up_b) + T * E * 4 + T * d * 2 + T * (k + 1) * f * 4)
+            launch_flops.append(2 * T * (k + 1) * 2 * d * f)
+    for _ in range(0 if fused else args.kernel_passes):
         st.h.copy_(st.h0)
         for i in range(wl.n_layers):
             prev = None if i == 0 else st.bufs[i - 1].y

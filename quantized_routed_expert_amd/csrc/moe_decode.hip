@@ -55,6 +55,7 @@ struct DecodeArgs {
   f16* h16;                // gate/up output H16 [(T*k+T)*2][f]
   int down_type;           // gate/up: layout of H16 rows (IQ4_NL: block-permuted)
   float* o;                // down output O [(T*k+T)][d]
+  const int32_t* pair_of_row;  // fused down pass: O row of each plan row (t*k + j); null: the plan row
 };
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
@@ -105,7 +106,8 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
   constexpr int CPT = cols_per_tile<FMT>();
   constexpr int CPP = NT * CPT;                      // columns staged per pass
   constexpr int NMAT = GATEUP ? 2 : 1;
-  constexpr int PD = 4;                              // steps of codes in flight per matrix
+  constexpr int PD = 6;                              // steps of codes in flight per matrix
+  constexpr int AB = 2;                              // activation chunks per thread issued first
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int n = lane & 15, G = lane >> 4;
@@ -144,41 +146,65 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
     }
   };
 
+  const int chunks_per_col = K / 8;  // 16-byte activation chunks per column
+  // All global loads below are unconditional (out-of-range ones repeat a valid
+  // address and their result is discarded), so the waits that follow them are
+  // exact: data issued earlier never waits for data issued later.
+  // this lane's code and scale addresses at step 0; step s adds a constant
+  // (4 * EPS elements: 64 code bytes, 4 * EPS / 32 scale words)
+  const uint8_t* cl[NMAT];
+  const uint16_t* sl[NMAT];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m) {
+    cl[m] = crow[m] + (FMT == MOE_Q8_0 ? kbase : (kbase >> 1));
+    sl[m] = (const uint16_t*)srow[m] + (kbase >> 5);
+  }
+  auto load_step = [&](int m, int s, u32x4& c, uint32_t& sc) {
+    c = *(const u32x4*)(cl[m] + s * (FMT == MOE_Q8_0 ? 4 * EPS : 2 * EPS));
+    // Q8_0 / IQ4_NL: the block's fp16 scale; NVFP4: the chunk's two E4M3 scales
+    sc = sl[m][s * (4 * EPS / 32)];
+  };
   for (int c0 = 0; c0 < ncol; c0 += CPP) {
-    // ---- issue the first PD steps of weight codes (independent of the activations)
+    const int ncp = min(CPP, ncol - c0);
+    const int nch = ncp * chunks_per_col;
+    // ---- the first batch of this pass's activation chunks, issued before the
+    // weight codes so that waiting for them does not wait for the codes
+    u32x4 av[AB];
+#pragma unroll
+    for (int b = 0; b < AB; ++b) {
+      const int ch = min(tid + b * 256, nch - 1);
+      const int c = ch / chunks_per_col, kk = (ch - c * chunks_per_col) * 8;
+      av[b] = *(const u32x4*)(a.in16 + in_row_of(c0 + c) * K + kk);
+    }
+    // ---- the first PD steps of weight codes (independent of the activations)
     u32x4 cb[NMAT][PD];
     uint32_t sb[NMAT][PD];
-    auto load_step = [&](int m, int s, u32x4& c, uint32_t& sc) {
-      const int kel = kbase + s * 4 * EPS;
-      if constexpr (FMT == MOE_Q8_0)
-        c = *(const u32x4*)(crow[m] + kel);
-      else
-        c = *(const u32x4*)(crow[m] + (kel >> 1));
-      // Q8_0 / IQ4_NL: the block's fp16 scale; NVFP4: the chunk's two E4M3 scales
-      sc = ((const uint16_t*)srow[m])[kel >> 5];
-    };
 #pragma unroll
     for (int u = 0; u < PD; ++u)
-      if (u < nsteps)
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) load_step(m, u, cb[m][u], sb[m][u]);
+      for (int m = 0; m < NMAT; ++m) load_step(m, min(u, nsteps - 1), cb[m][u], sb[m][u]);
 
-    // ---- stage this pass's activation columns into LDS (one global round trip)
-    const int ncp = min(CPP, ncol - c0);
+    // ---- stage the activation columns into LDS.  Columns at or beyond ncp
+    // are never read (their A rows are zero), so they are not written.
     __syncthreads();  // the previous pass has finished reading sA
-    {
-      const int chunks_per_col = K / 8;  // 16-byte chunks
-      for (int ch = tid; ch < CPP * chunks_per_col; ch += 256) {
+#pragma unroll
+    for (int b = 0; b < AB; ++b) {
+      const int ch = tid + b * 256;
+      if (ch < nch) {
         const int c = ch / chunks_per_col, kk = (ch - c * chunks_per_col) * 8;
-        u32x4 v = {0, 0, 0, 0};
-        if (c < ncp) v = *(const u32x4*)(a.in16 + in_row_of(c0 + c) * K + kk);
-        *(u32x4*)&sA[c * K + kk] = v;
+        *(u32x4*)&sA[c * K + kk] = av[b];
       }
+    }
+    for (int ch = tid + AB * 256; ch < nch; ch += 256) {
+      const int c = ch / chunks_per_col, kk = (ch - c * chunks_per_col) * 8;
+      *(u32x4*)&sA[c * K + kk] = *(const u32x4*)(a.in16 + in_row_of(c0 + c) * K + kk);
     }
     __syncthreads();
 
-    // A-operand LDS row for each N-tile (this lane is A row m = n, K slice G); -1 = zero
+    // A-operand LDS row for each N-tile (this lane is A row m = n, K slice G);
+    // lanes without a column read column 0 and use zeros
     int acol[NT];
+    bool aval[NT];
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) {
       int c;
@@ -190,7 +216,8 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
         valid = n < CPT;
         c = jt * CPT + n;
       }
-      acol[jt] = (valid && c < ncp) ? c : -1;
+      aval[jt] = valid && c < ncp;
+      acol[jt] = aval[jt] ? c : 0;
     }
 
     f32x4 acc[NMAT][NT];
@@ -199,52 +226,72 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
 #pragma unroll
       for (int jt = 0; jt < NT; ++jt) acc[m][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int s0 = 0; s0 < nsteps; s0 += PD) {
+    auto compute_step = [&](const u32x4 (&cc)[NMAT], const uint32_t (&ss)[NMAT], int s) {
+      f16x8 ac[NT][NMF];
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt)
+#pragma unroll
+        for (int i = 0; i < NMF; ++i) {
+          const f16x8 v = *(const f16x8*)&sA[acol[jt] * K + kbase + s * 4 * EPS + 8 * i];
+          ac[jt][i] = aval[jt] ? v : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        f32x4 D[NT];
+#pragma unroll
+        for (int jt = 0; jt < NT; ++jt) D[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NMF; ++i) {
+          const f16x8 bf = decode_b<FMT>(cc[m], i, ss[m]);
+#pragma unroll
+          for (int jt = 0; jt < NT; ++jt) D[jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ac[jt][i], bf, D[jt], 0, 0, 0);
+        }
+        if constexpr (FMT == MOE_NVFP4) {
+#pragma unroll
+          for (int jt = 0; jt < NT; ++jt) acc[m][jt] += D[jt];
+        } else {
+          const float sc = f16_bits_to_f32(ss[m]);
+#pragma unroll
+          for (int jt = 0; jt < NT; ++jt) {
+            acc[m][jt].x = fmaf(sc, D[jt].x, acc[m][jt].x);
+            acc[m][jt].y = fmaf(sc, D[jt].y, acc[m][jt].y);
+            acc[m][jt].z = fmaf(sc, D[jt].z, acc[m][jt].z);
+            acc[m][jt].w = fmaf(sc, D[jt].w, acc[m][jt].w);
+          }
+        }
+      }
+    };
+
+    if (nsteps <= PD) {
+      // every step's codes are already in flight
 #pragma unroll
       for (int u = 0; u < PD; ++u) {
-        const int s = s0 + u;
-        if (s < nsteps) {
+        if (u < nsteps) {
           u32x4 cc[NMAT];
           uint32_t ss[NMAT];
 #pragma unroll
           for (int m = 0; m < NMAT; ++m) {
             cc[m] = cb[m][u];
             ss[m] = sb[m][u];
-            if (s + PD < nsteps) load_step(m, s + PD, cb[m][u], sb[m][u]);
           }
-          f16x8 ac[NT][NMF];
+          compute_step(cc, ss, u);
+        }
+      }
+    } else {
+      // rolling prefetch, PD steps ahead (past the end it repeats the last step)
+      for (int s0 = 0; s0 < nsteps; s0 += PD) {
 #pragma unroll
-          for (int jt = 0; jt < NT; ++jt)
-#pragma unroll
-            for (int i = 0; i < NMF; ++i)
-              ac[jt][i] = acol[jt] >= 0 ? *(const f16x8*)&sA[acol[jt] * K + kbase + s * 4 * EPS + 8 * i]
-                                        : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        for (int u = 0; u < PD; ++u) {
+          const int s = s0 + u;
+          u32x4 cc[NMAT];
+          uint32_t ss[NMAT];
 #pragma unroll
           for (int m = 0; m < NMAT; ++m) {
-            f32x4 D[NT];
-#pragma unroll
-            for (int jt = 0; jt < NT; ++jt) D[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int i = 0; i < NMF; ++i) {
-              const f16x8 bf = decode_b<FMT>(cc[m], i, ss[m]);
-#pragma unroll
-              for (int jt = 0; jt < NT; ++jt)
-                D[jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ac[jt][i], bf, D[jt], 0, 0, 0);
-            }
-            if constexpr (FMT == MOE_NVFP4) {
-#pragma unroll
-              for (int jt = 0; jt < NT; ++jt) acc[m][jt] += D[jt];
-            } else {
-              const float sc = f16_bits_to_f32(ss[m]);
-#pragma unroll
-              for (int jt = 0; jt < NT; ++jt) {
-                acc[m][jt].x = fmaf(sc, D[jt].x, acc[m][jt].x);
-                acc[m][jt].y = fmaf(sc, D[jt].y, acc[m][jt].y);
-                acc[m][jt].z = fmaf(sc, D[jt].z, acc[m][jt].z);
-                acc[m][jt].w = fmaf(sc, D[jt].w, acc[m][jt].w);
-              }
-            }
+            cc[m] = cb[m][u];
+            ss[m] = sb[m][u];
+            load_step(m, min(s + PD, nsteps - 1), cb[m][u], sb[m][u]);
           }
+          if (s < nsteps) compute_step(cc, ss, s);
         }
       }
     }
@@ -328,7 +375,9 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
             a.h16[((long)out_row * 2 + 0) * f + pos] = hi;
             a.h16[((long)out_row * 2 + 1) * f + pos] = lo;
           } else {
-            a.o[(long)out_row * rows + frow] = val[0];
+            // fused path: routed rows go to their (token, slot) pair's row
+            const int orow = (a.pair_of_row && !si.is_sh) ? a.pair_of_row[out_row] : out_row;
+            a.o[(long)orow * rows + frow] = val[0];
           }
         }
       }
@@ -338,7 +387,8 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
 
 // Stage kernel over a plan (global plan arrays, or the fused path's slot table).
 template <int FMT, int NT, bool GATEUP>
-__global__ __launch_bounds__(256) void k_ffn_dq(const DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1))) void k_ffn_dq(
+    const DecodeArgs a) {
   constexpr int NMAT = GATEUP ? 2 : 1;
   __shared__ f32x4 red[4 * NMAT * NT * 64];
   extern __shared__ f16 sA[];  // [CPP][K] activations of the current column pass
@@ -416,35 +466,29 @@ __global__ __launch_bounds__(256) void k_prep_x(const void* __restrict__ x, int 
 // ============================================================================
 
 struct FusedPlan {  // plan of the current layer, written by k_fz_gateup's workgroup 0
-  int32_t* counts;
-  int32_t* offsets;
-  int32_t* row_token;
-  int32_t* row_slot;
-  int32_t* slot_row;
-  int32_t* active;
-  int32_t* n_active;
+  int32_t* pair_of_row;  // [T*k] pair t*k + j of each plan row (expert-major, token order)
   int32_t* error;
-  int32_t* topk_idx;  // [T][k]
-  float* topk_w;      // [T][k]
-  SlotEnt* slots;     // [E + 1]
+  int32_t* topk_idx;     // [T][k]
+  float* topk_w;         // [T][k]
+  SlotEnt* slots;        // [T*k + 1]: shared expert first, then the active experts ascending
   int32_t* n_slots;
 };
 
 // (1) Layer input and router.
 //
-// Glue (layer l > 0): y = shared row + sum_j topk_w[t][j] * o[slot_row[t*k+j]]
-// (the previous layer's combine, slots in order j), h_new = h + y, and the
-// layer input x = bf16(h_new / sqrt(mean(h_new^2) + eps)).  The first layer
-// takes x = bf16(rmsnorm(h)).  The glue writes the new residual, x (bf16, and
-// as power-of-two scaled fp16 for the expert products) and optional records of
-// the previous layer's y and this layer's x.
+// Glue (layer l > 0): y = o[T*k + t] + sum_j topk_w[t][j] * o[t*k + j] (the
+// previous layer's combine: shared row, then the routed slots in order j; the
+// down pass writes routed rows at their pair's position), h_new = h + y, and
+// the layer input x = bf16(h_new / sqrt(mean(h_new^2) + eps)).  The first
+// layer takes x = bf16(rmsnorm(h)).  The glue writes the new residual, x (bf16,
+// and as power-of-two scaled fp16 for the expert products) and optional
+// records of the previous layer's y and this layer's x.
 struct FzGlueArgs {
   int d, T, k, has_shared;
   const float* h_in;
   float* h_out;
   const float* o;            // previous layer's expert rows, or null (first layer)
-  const int32_t* slot_row;   // previous layer's plan
-  const float* topk_w;
+  const float* topk_w;       // previous layer's gate weights
   float* rec_y;              // previous layer's y (optional)
   uint16_t* x_out;           // bf16 layer input (null: the final fold, no next layer)
   uint16_t* rec_x;           // optional record of the same
@@ -456,6 +500,7 @@ struct FzGlueArgs {
 };
 
 constexpr int kGlueMaxQ = 4;  // d <= 4096: float4 chunks per thread
+constexpr int kGlueRB = 8;    // routed rows whose loads are in flight together
 
 // Glue for one token, by one workgroup.  Returns the token's bf16 input in
 // v[] (as floats) when the caller needs it.
@@ -464,12 +509,39 @@ __device__ __forceinline__ void glue_token(const FzGlueArgs& a, int t, bool writ
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int d = a.d, T = a.T, k = a.k;
   const int nq = d / 1024;
-  float sw[32];
-  int sr[32];
+  // residual and shared row first; every routed row of a batch is in flight
+  // before the first is used
+  f32x4 y[kGlueMaxQ];
+#pragma unroll
+  for (int q = 0; q < kGlueMaxQ; ++q) {
+    if (q < nq) {
+      const int i = (q * 256 + tid) * 4;
+      v[q] = *(const f32x4*)(a.h_in + (long)t * d + i);
+      y[q] = (a.o && a.has_shared) ? *(const f32x4*)(a.o + (long)(T * k + t) * d + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
   if (a.o) {
-    for (int j = 0; j < k; ++j) {
-      sr[j] = a.slot_row[t * k + j];
-      sw[j] = a.topk_w[t * k + j];
+    for (int j0 = 0; j0 < k; j0 += kGlueRB) {
+      float wj[kGlueRB];
+      f32x4 ov[kGlueMaxQ][kGlueRB];
+#pragma unroll
+      for (int jj = 0; jj < kGlueRB; ++jj) wj[jj] = (j0 + jj < k) ? a.topk_w[t * k + j0 + jj] : 0.0f;
+#pragma unroll
+      for (int q = 0; q < kGlueMaxQ; ++q)
+#pragma unroll
+        for (int jj = 0; jj < kGlueRB; ++jj)
+          if (q < nq && j0 + jj < k)
+            ov[q][jj] = *(const f32x4*)(a.o + (long)(t * k + j0 + jj) * d + (q * 256 + tid) * 4);
+#pragma unroll
+      for (int q = 0; q < kGlueMaxQ; ++q)
+#pragma unroll
+        for (int jj = 0; jj < kGlueRB; ++jj)
+          if (q < nq && j0 + jj < k) {
+            y[q].x = fmaf(wj[jj], ov[q][jj].x, y[q].x);
+            y[q].y = fmaf(wj[jj], ov[q][jj].y, y[q].y);
+            y[q].z = fmaf(wj[jj], ov[q][jj].z, y[q].z);
+            y[q].w = fmaf(wj[jj], ov[q][jj].w, y[q].w);
+          }
     }
   }
   float ss = 0.0f;
@@ -477,20 +549,9 @@ __device__ __forceinline__ void glue_token(const FzGlueArgs& a, int t, bool writ
   for (int q = 0; q < kGlueMaxQ; ++q) {
     if (q < nq) {
       const int i = (q * 256 + tid) * 4;
-      v[q] = *(const f32x4*)(a.h_in + (long)t * d + i);
       if (a.o) {
-        f32x4 y = {0.f, 0.f, 0.f, 0.f};
-        if (a.has_shared) y = *(const f32x4*)(a.o + (long)(T * k + t) * d + i);
-        for (int j = 0; j < k; ++j) {
-          if (sr[j] < 0) continue;
-          const f32x4 ov = *(const f32x4*)(a.o + (long)sr[j] * d + i);
-          y.x = fmaf(sw[j], ov.x, y.x);
-          y.y = fmaf(sw[j], ov.y, y.y);
-          y.z = fmaf(sw[j], ov.z, y.z);
-          y.w = fmaf(sw[j], ov.w, y.w);
-        }
-        if (writer && a.rec_y) *(f32x4*)(a.rec_y + (long)t * d + i) = y;
-        v[q] += y;
+        if (writer && a.rec_y) *(f32x4*)(a.rec_y + (long)t * d + i) = y[q];
+        v[q] += y[q];
       }
       if (writer) *(f32x4*)(a.h_out + (long)t * d + i) = v[q];
       ss += v[q].x * v[q].x + v[q].y * v[q].y + v[q].z * v[q].z + v[q].w * v[q].w;
@@ -549,10 +610,10 @@ __global__ __launch_bounds__(256) void k_fz_glue(const FzGlueArgs a) {
 }
 
 // Router: logits[t][e] for T tokens, one wavefront per expert row, fp64
-// accumulation (exact products).  INLINE (a single token): every workgroup
-// forms the token's input itself with the glue (workgroup 0 writes it out),
-// so the layer needs no separate glue launch.  Otherwise x is read from the
-// glue kernel's output.
+// accumulation (exact products of fp32 weights and bf16 inputs).  INLINE (a
+// single token): every workgroup forms the token's input itself with the glue
+// (workgroup 0 writes it out), so the layer needs no separate glue launch.
+// Otherwise x is read from the glue kernel's output.
 struct FzRouteArgs {
   FzGlueArgs g;
   const float* Wr;
@@ -597,179 +658,141 @@ __global__ __launch_bounds__(256) void k_fz_route(const FzRouteArgs a) {
   }
   __syncthreads();
   if (e < a.E) {
-    for (int t = 0; t < T; ++t) {
-      double acc = 0.0;
+    // all tokens' partial sums first, then their wave reductions together
+    double acc[kFusedMaxT];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (j < nj) {
-          const int i = (j * 64 + lane) * 4;
-          const u32x2 xb = *(const u32x2*)&sx[t * 4096 + i];
-          acc += (double)wv[j].x * (double)bf16_bits_to_f32(xb.x & 0xffffu) +
-                 (double)wv[j].y * (double)bf16_bits_to_f32(xb.x >> 16) +
-                 (double)wv[j].z * (double)bf16_bits_to_f32(xb.y & 0xffffu) +
-                 (double)wv[j].w * (double)bf16_bits_to_f32(xb.y >> 16);
+    for (int t = 0; t < kFusedMaxT; ++t) acc[t] = 0.0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j < nj) {
+        const int i = (j * 64 + lane) * 4;
+#pragma unroll
+        for (int t = 0; t < kFusedMaxT; ++t) {
+          if (t < T) {
+            const u32x2 xb = *(const u32x2*)&sx[t * 4096 + i];
+            acc[t] += (double)wv[j].x * (double)bf16_bits_to_f32(xb.x & 0xffffu) +
+                      (double)wv[j].y * (double)bf16_bits_to_f32(xb.x >> 16) +
+                      (double)wv[j].z * (double)bf16_bits_to_f32(xb.y & 0xffffu) +
+                      (double)wv[j].w * (double)bf16_bits_to_f32(xb.y >> 16);
+          }
         }
       }
-      acc = wave_sum_f64(acc);
-      if (lane == 0) a.logits[(long)t * a.E + e] = (float)(acc + (a.bias ? (double)a.bias[e] : 0.0));
+    }
+    const double b = a.bias ? (double)a.bias[e] : 0.0;
+#pragma unroll
+    for (int t = 0; t < kFusedMaxT; ++t) {
+      if (t < T) {
+        const double r = wave_sum_f64(acc[t]);
+        if (lane == 0) a.logits[(long)t * a.E + e] = (float)(r + b);
+      }
     }
   }
 }
 
-// (2) Top-k + plan (in LDS, recomputed by every workgroup) + grouped gate/up.
-// Slot 0 is the shared expert (it needs no routing, so its items start
-// streaming at once); slots 1.. are the active experts in ascending id order.
+// (2) Top-k + plan (in LDS, recomputed by every workgroup that needs it) +
+// grouped gate/up.  Slot 0 is the shared expert (it needs no routing, so its
+// items start streaming at once); slots 1.. are the active experts in
+// ascending id order.  Workgroup 0 publishes the plan for the down pass and
+// the next layer's combine.
 struct FzGateArgs {
   DecodeArgs a;  // gate/up pass arguments (in16 = x16, in_scale = xs, h16, error)
   const float* logits;
   int E;
-  FusedPlan plan;  // written by workgroup 0
+  FusedPlan plan;
 };
 
+constexpr int kFusedTK = kFusedMaxT * 32;  // token-slot pairs at most
+
 template <int FMT, int NT, int NPL>
-__global__ __launch_bounds__(256) void k_fz_gateup(const FzGateArgs g) {
+// Single-tile passes (one N-tile of columns, the batch-1 case) are held to two
+// waves per SIMD so that one grid of a decode step is resident at once.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1))) void k_fz_gateup(
+    const FzGateArgs g) {
   constexpr int NMAT = 2;
   __shared__ f32x4 red[4 * NMAT * NT * 64];
-  __shared__ unsigned long long smask[1024];
-  __shared__ int32_t soff[1025];
-  __shared__ int32_t sact[1024];
-  __shared__ int32_t srow_token[kFusedMaxT * 32];
-  __shared__ int32_t sidx[kFusedMaxT * 32];
-  __shared__ float sw[kFusedMaxT * 32];
-  __shared__ int32_t scan_scr[2][5];
-  __shared__ int32_t s_nact, s_err;
+  __shared__ int32_t sidx[kFusedTK];
+  __shared__ float sw[kFusedTK];
+  __shared__ int32_t sfirst[kFusedTK];
+  __shared__ int32_t srow_token[kFusedTK];
+  __shared__ SlotEnt sslot[kFusedTK];
   extern __shared__ f16 sA[];
 
   const DecodeArgs& a = g.a;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int T = a.T, k = a.k, E = g.E;
+  const int TK = T * k;
   const int ksplit = a.ksplit;
   const int rt_per_wg = 4 / ksplit;
   const int rows = a.mat[0].rows;
   const int wg_per_slot = (rows / 16) / rt_per_wg;
   const int hs = a.has_shared;
-  const int max_slots = min(E, T * k) + hs;
-  bool planned = false;
+  const int max_slots = min(E, TK) + hs;
+  const int n_items = max_slots * wg_per_slot;
+  // The plan is needed by workgroup 0 (which publishes it) and by every
+  // workgroup with a routed item; it is built before the item loop so that
+  // none of its state stays live during the expert products.
+  const int last_item = blockIdx.x + ((n_items - 1 - (int)blockIdx.x) / (int)gridDim.x) * (int)gridDim.x;
+  int n_act = 0;
+  if (blockIdx.x == 0 || last_item >= hs * wg_per_slot) {
+    // ---- top-k per token (one wavefront per token), renormalised weights
+    for (int t = wid; t < T; t += 4) {
+      int ix;
+      float lv;
+      wave_topk<NPL>(g.logits + (long)t * E, E, k, lane, ix, lv);
+      const float vmax = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(lv), 0));
+      const float ex = lane < k ? expf(lv - vmax) : 0.0f;
+      const float sum = wave_sum(ex);
+      if (lane < k) {
+        sidx[t * k + lane] = ix;
+        sw[t * k + lane] = ex / sum;
+      }
+    }
+    __syncthreads();
+    // ---- plan: pair p (thread p) counts the pairs of smaller experts (its
+    // expert's first plan row) and the earlier pairs of its own expert (its
+    // rank); the first pair of each expert then counts the distinct smaller
+    // experts (its slot).  Rows within an expert follow token order.
+    int e = 0, less = 0, before = 0, same = 0;
+    if (tid < TK) {
+      e = sidx[tid];
+      for (int q = 0; q < TK; ++q) {
+        const int eq = sidx[q];
+        less += eq < e ? 1 : 0;
+        same += eq == e ? 1 : 0;
+        before += (eq == e && q < tid) ? 1 : 0;
+      }
+      sfirst[tid] = before == 0 ? e : 0x7fffffff;
+    }
+    __syncthreads();
+    if (tid < TK) {
+      int dl = 0;
+      for (int q = 0; q < TK; ++q) dl += sfirst[q] < e ? 1 : 0;
+      srow_token[less + before] = tid / k;
+      if (before == 0) sslot[dl] = SlotEnt{e, less, same, 0};
+    }
+    n_act = __syncthreads_count(tid < TK && before == 0);
+    if (blockIdx.x == 0) {
+      const FusedPlan& P = g.plan;
+      if (tid < TK) {
+        P.pair_of_row[less + before] = tid;
+        P.topk_idx[tid] = e;
+        P.topk_w[tid] = sw[tid];
+      }
+      for (int s = tid; s < n_act + hs; s += 256) P.slots[s] = s < hs ? SlotEnt{0, TK, T, 1} : sslot[s - hs];
+      if (tid == 0) *P.n_slots = n_act + hs;
+    }
+  }
 
-  for (int item = blockIdx.x; item < max_slots * wg_per_slot; item += gridDim.x) {
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int slot = item / wg_per_slot;
     const int tile = (item % wg_per_slot) * rt_per_wg + wid / ksplit;
-    // Workgroups of routed slots need the plan; workgroup 0 also publishes it.
-    if (!planned && (slot >= hs || blockIdx.x == 0)) {
-      {
-        // ---- top-k per token (one wavefront per token)
-        for (int t = wid; t < T; t += 4) {
-          int ix;
-          float lv;
-          wave_topk<NPL>(g.logits + (long)t * E, E, k, lane, ix, lv);
-          const float vmax = __shfl(lv, 0, 64);
-          const float ex = lane < k ? expf(lv - vmax) : 0.0f;
-          const float sum = wave_sum(ex);
-          if (lane < k) {
-            sidx[t * k + lane] = ix;
-            sw[t * k + lane] = ex / sum;
-          }
-        }
-        // ---- plan: token masks per expert (order-independent), counts, scan
-        for (int e = tid; e < E; e += 256) smask[e] = 0ull;
-        __syncthreads();
-        int err = 0;
-        for (int p = tid; p < T * k; p += 256) {
-          const int e = sidx[p];
-          if (e >= 0 && e < E)
-            atomicOr(&smask[e], 1ull << (p / k));
-          else
-            err = 1;
-        }
-        err = __syncthreads_or(err);
-        int c4[4], a4 = 0, s4 = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int e = tid * 4 + q;
-          c4[q] = e < E ? __popcll(smask[e]) : 0;
-          s4 += c4[q];
-          a4 += c4[q] > 0 ? 1 : 0;
-        }
-        int n_valid, n_act;
-        int off = block_exclusive_scan<256>(s4, scan_scr[0], n_valid);
-        int aoff = block_exclusive_scan<256>(a4, scan_scr[1], n_act);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int e = tid * 4 + q;
-          if (e < E) {
-            soff[e] = off;
-            if (c4[q] > 0) sact[aoff++] = e;
-          }
-          off += c4[q];
-        }
-        if (tid == 0) {
-          soff[E] = n_valid;
-          s_nact = n_act;
-          s_err = err;
-        }
-        __syncthreads();
-        // rows: rank = earlier tokens of the same expert
-        for (int p = tid; p < T * k; p += 256) {
-          const int e = sidx[p];
-          if (e < 0 || e >= E) continue;
-          const int t = p / k;
-          const int r = soff[e] + __popcll(smask[e] & ((1ull << t) - 1ull));
-          srow_token[r] = t;
-        }
-        __syncthreads();
-        if (blockIdx.x == 0) {
-          // publish the plan (for the down pass, the combine and records)
-          const FusedPlan& P = g.plan;
-          for (int e = tid; e < E; e += 256) {
-            P.counts[e] = soff[e + 1] - soff[e];
-            P.offsets[e] = soff[e];
-            P.active[e] = e < s_nact ? sact[e] : -1;
-          }
-          for (int p = tid; p < T * k; p += 256) {
-            const int e = sidx[p];
-            P.topk_idx[p] = e;
-            P.topk_w[p] = sw[p];
-            if (e >= 0 && e < E) {
-              const int t = p / k;
-              const int r = soff[e] + __popcll(smask[e] & ((1ull << t) - 1ull));
-              P.row_token[r] = t;
-              P.row_slot[r] = p % k;
-              P.slot_row[p] = r;
-            } else {
-              P.slot_row[p] = -1;
-            }
-          }
-          for (int r = soff[E] + tid; r < T * k; r += 256) {
-            P.row_token[r] = -1;
-            P.row_slot[r] = -1;
-          }
-          for (int s = tid; s < s_nact + hs; s += 256) {
-            SlotEnt se;
-            if (s < hs) {
-              se = SlotEnt{0, T * k, T, 1};
-            } else {
-              const int e = sact[s - hs];
-              se = SlotEnt{e, soff[e], soff[e + 1] - soff[e], 0};
-            }
-            P.slots[s] = se;
-          }
-          if (tid == 0) {
-            P.offsets[E] = soff[E];
-            *P.n_active = s_nact;
-            *P.n_slots = s_nact + hs;
-            if (s_err) atomicOr(P.error, s_err);
-          }
-        }
-      }
-      planned = true;
-    }
     SlotInfo si;
     if (slot < hs) {
-      si = SlotInfo{0, true, T * k, T};
+      si = SlotInfo{0, true, TK, T};
     } else {
-      if (slot - hs >= s_nact) break;  // items are in slot order
-      const int e = sact[slot - hs];
-      si = SlotInfo{e, false, soff[e], soff[e + 1] - soff[e]};
+      if (slot - hs >= n_act) break;  // items are in slot order
+      const SlotEnt se = sslot[slot - hs];
+      si = SlotInfo{se.e, false, se.row0, se.cnt};
     }
     dq_item<FMT, NT, true>(a, si, tile, wid % ksplit, srow_token, sA, red);
   }
@@ -878,26 +901,68 @@ DecodeArgs down_args(const moe_layer& L, int T, const DecodeWs& w) {
   return a;
 }
 
-template <int FMT, int NT>
-hipError_t launch_fz_gate(const FzGateArgs& g, int grid, size_t lds, int E, hipStream_t s) {
-  if (E <= 256)
-    hipLaunchKernelGGL((k_fz_gateup<FMT, NT, 4>), dim3(grid), dim3(256), lds, s, g);
-  else if (E <= 512)
-    hipLaunchKernelGGL((k_fz_gateup<FMT, NT, 8>), dim3(grid), dim3(256), lds, s, g);
-  else
-    hipLaunchKernelGGL((k_fz_gateup<FMT, NT, 16>), dim3(grid), dim3(256), lds, s, g);
+// Workgroups of `kern` (256 threads, `lds` dynamic bytes) resident at once on
+// the current device, or 0 if the runtime cannot tell.
+template <typename Kern>
+int resident_wgs(Kern kern, size_t lds) {
+  int dev = 0, ncu = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, lds) != hipSuccess) return 0;
+  return ncu * per_cu;
+}
+
+// Grid of a fused expert pass over `items` items: all of them when they fit
+// in one resident wave of workgroups, else one resident wave that loops.
+template <typename Kern>
+int fused_grid(Kern kern, size_t lds, int items) {
+  const int res = resident_wgs(kern, lds);
+  return (res > 0 && items > res) ? res : items;
+}
+
+template <int FMT, int NT, int NPL>
+hipError_t launch_fz_gate_npl(const FzGateArgs& g, int items, size_t lds, hipStream_t s) {
+  const int grid = fused_grid(k_fz_gateup<FMT, NT, NPL>, lds, items);
+  hipLaunchKernelGGL((k_fz_gateup<FMT, NT, NPL>), dim3(grid), dim3(256), lds, s, g);
   return hipGetLastError();
 }
 
+template <int FMT, int NT>
+hipError_t launch_fz_gate(const FzGateArgs& g, int items, size_t lds, int E, hipStream_t s) {
+  if (E <= 256) return launch_fz_gate_npl<FMT, NT, 4>(g, items, lds, s);
+  if (E <= 512) return launch_fz_gate_npl<FMT, NT, 8>(g, items, lds, s);
+  return launch_fz_gate_npl<FMT, NT, 16>(g, items, lds, s);
+}
+
 template <int FMT>
-hipError_t launch_fz_gate_fmt(const FzGateArgs& g, int grid, int E, hipStream_t s) {
+hipError_t launch_fz_gate_fmt(const FzGateArgs& g, int items, int E, hipStream_t s) {
   constexpr int CPT = cols_per_tile<FMT>();
   const int K = g.a.mat[0].cols;
   const int nt = pick_nt(CPT, g.a.T, K);
   const size_t lds = (size_t)nt * CPT * K * 2;
-  if (nt == 1) return launch_fz_gate<FMT, 1>(g, grid, lds, E, s);
-  if (nt == 2) return launch_fz_gate<FMT, 2>(g, grid, lds, E, s);
-  return launch_fz_gate<FMT, 4>(g, grid, lds, E, s);
+  if (nt == 1) return launch_fz_gate<FMT, 1>(g, items, lds, E, s);
+  if (nt == 2) return launch_fz_gate<FMT, 2>(g, items, lds, E, s);
+  return launch_fz_gate<FMT, 4>(g, items, lds, E, s);
+}
+
+// Down pass of the fused step over the slot table.
+template <int FMT>
+hipError_t launch_fz_down_fmt(const DecodeArgs& a, int items, hipStream_t s) {
+  constexpr int CPT = cols_per_tile<FMT>();
+  const int K = a.mat[0].cols;
+  const int nt = pick_nt(CPT, a.T * 2, K);
+  const size_t lds = (size_t)nt * CPT * K * 2;
+  if (nt == 1) {
+    hipLaunchKernelGGL((k_ffn_dq<FMT, 1, false>), dim3(fused_grid(k_ffn_dq<FMT, 1, false>, lds, items)), dim3(256),
+                       lds, s, a);
+  } else if (nt == 2) {
+    hipLaunchKernelGGL((k_ffn_dq<FMT, 2, false>), dim3(fused_grid(k_ffn_dq<FMT, 2, false>, lds, items)), dim3(256),
+                       lds, s, a);
+  } else {
+    hipLaunchKernelGGL((k_ffn_dq<FMT, 4, false>), dim3(fused_grid(k_ffn_dq<FMT, 4, false>, lds, items)), dim3(256),
+                       lds, s, a);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -952,7 +1017,7 @@ struct FusedWs {
 };
 
 FusedWs carve_fused(void* ws, int T, int d, int f, int k, int E) {
-  const size_t R = (size_t)T * k + T;
+  const size_t TK = (size_t)T * k;
   char* p = (char*)ws;
   FusedWs F;
   F.hb[0] = (float*)p;
@@ -966,23 +1031,15 @@ FusedWs carve_fused(void* ws, int T, int d, int f, int k, int E) {
   F.logits = (float*)p;
   p += align_up((size_t)T * E * 4, 256);
   int32_t* ints = (int32_t*)p;
-  p += align_up((size_t)(3 * E + 8) * 4, 256);
-  F.plan.counts = ints;
-  F.plan.offsets = ints + E;  // E + 1 entries
-  F.plan.active = ints + 2 * E + 1;
-  F.plan.n_active = ints + 3 * E + 1;
-  F.plan.n_slots = ints + 3 * E + 2;
-  F.plan.error = ints + 3 * E + 3;
-  F.plan.row_token = (int32_t*)p;
-  p += align_up(R * 4, 256);
-  F.plan.row_slot = (int32_t*)p;
-  p += align_up(R * 4, 256);
-  F.plan.slot_row = (int32_t*)p;
-  p += align_up(R * 4, 256);
+  p += 256;
+  F.plan.n_slots = ints;
+  F.plan.error = ints + 1;
+  F.plan.pair_of_row = (int32_t*)p;
+  p += align_up(TK * 4, 256);
   F.plan.topk_idx = (int32_t*)p;
-  p += align_up(R * 4, 256);
+  p += align_up(TK * 4, 256);
   F.plan.topk_w = (float*)p;
-  p += align_up(R * 4, 256);
+  p += align_up(TK * 4, 256);
   F.plan.slots = (SlotEnt*)p;
   return F;
 }
@@ -990,15 +1047,10 @@ FusedWs carve_fused(void* ws, int T, int d, int f, int k, int E) {
 }  // namespace
 
 size_t fused_ws_bytes(int T, int d, int f, int k, int E) {
-  const size_t R = (size_t)T * k + T;
+  const size_t TK = (size_t)T * k;
   return 2 * align_up((size_t)T * d * 4, 256) + align_up((size_t)T * d * 2, 256) +
-         decode_ws_bytes(T, d, f, k, MOE_BF16) +
-         align_up((size_t)T * E * 4, 256) + align_up((size_t)(3 * E + 8) * 4, 256) + 5 * align_up(R * 4, 256) +
-         align_up((size_t)(E + 1) * sizeof(SlotEnt), 256);
-}
-
-__global__ void k_copy_i32(const int32_t* __restrict__ src, int32_t* __restrict__ dst, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = src[i];
+         decode_ws_bytes(T, d, f, k, MOE_BF16) + align_up((size_t)T * E * 4, 256) + 256 +
+         3 * align_up(TK * 4, 256) + align_up((TK + 1) * sizeof(SlotEnt), 256);
 }
 
 hipError_t launch_fused_step(const moe_layer* layers, int n_layers, float* h, int T, const FusedRecord& rec,
@@ -1011,6 +1063,7 @@ hipError_t launch_fused_step(const moe_layer* layers, int n_layers, float* h, in
   const float* prev_w = nullptr;  // topk weights of the previous layer
   for (int l = 0; l < n_layers; ++l) {
     const moe_layer& L = layers[l];
+    int32_t* err_word = rec.error ? rec.error + l : F.plan.error;
     // (1) glue (previous layer's combine + residual + RMSNorm) and router
     FzGlueArgs g{};
     g.d = d;
@@ -1020,7 +1073,6 @@ hipError_t launch_fused_step(const moe_layer* layers, int n_layers, float* h, in
     g.h_in = l == 0 ? h : F.hb[l & 1];
     g.h_out = F.hb[(l + 1) & 1];
     g.o = l == 0 ? nullptr : F.w.o;
-    g.slot_row = F.plan.slot_row;
     g.topk_w = prev_w;
     g.rec_y = (l > 0 && rec.y) ? rec.y + (size_t)(l - 1) * T * d : nullptr;
     g.x_out = F.x;
@@ -1029,7 +1081,7 @@ hipError_t launch_fused_step(const moe_layer* layers, int n_layers, float* h, in
     g.xs = F.w.xs;
     g.gate_fmt = L.gate.type;
     g.eps = rec.eps;
-    g.error_reset = F.plan.error;
+    g.error_reset = err_word;
     FzRouteArgs ra{};
     ra.g = g;
     ra.Wr = L.router_w;
@@ -1046,37 +1098,43 @@ hipError_t launch_fused_step(const moe_layer* layers, int n_layers, float* h, in
     // (2) top-k + plan + gate/up
     FzGateArgs ga{};
     ga.a = gateup_args(L, T, 1, F.w);
-    ga.a.error = F.plan.error;
+    ga.a.error = err_word;
     ga.logits = ra.logits;
     ga.E = E;
     ga.plan = F.plan;
+    ga.plan.error = err_word;
     if (rec.topk_idx) ga.plan.topk_idx = rec.topk_idx + (size_t)l * T * k;
     if (rec.topk_w) ga.plan.topk_w = rec.topk_w + (size_t)l * T * k;
     prev_w = ga.plan.topk_w;
     {
       const int wg_per_slot = (f / 16) / (4 / ga.a.ksplit);
-      const int grid = max_slots * wg_per_slot;
+      const int items = max_slots * wg_per_slot;
       if (rec.events) (void)hipEventRecord(rec.events[2 * l], s);
       hipError_t err;
       switch (L.gate.type) {
-        case MOE_Q8_0: err = launch_fz_gate_fmt<MOE_Q8_0>(ga, grid, E, s); break;
-        case MOE_IQ4_NL: err = launch_fz_gate_fmt<MOE_IQ4_NL>(ga, grid, E, s); break;
-        default: err = launch_fz_gate_fmt<MOE_NVFP4>(ga, grid, E, s); break;
+        case MOE_Q8_0: err = launch_fz_gate_fmt<MOE_Q8_0>(ga, items, E, s); break;
+        case MOE_IQ4_NL: err = launch_fz_gate_fmt<MOE_IQ4_NL>(ga, items, E, s); break;
+        default: err = launch_fz_gate_fmt<MOE_NVFP4>(ga, items, E, s); break;
       }
       if (err != hipSuccess) return err;
       if (rec.events) (void)hipEventRecord(rec.events[2 * l + 1], s);
     }
-    // (3) down over the slot table
+    // (3) down over the slot table, rows written at their pair's position
     {
       DecodeArgs da = down_args(L, T, F.w);
       da.slots = F.plan.slots;
       da.n_slots = F.plan.n_slots;
-      da.error = F.plan.error;
-      const int wg_per_slot = (d / 16) / 4;
-      hipError_t err = launch_pass<false>(L.down.type, da, T * 2, max_slots * wg_per_slot, s);
+      da.pair_of_row = F.plan.pair_of_row;
+      da.error = err_word;
+      const int items = max_slots * ((d / 16) / 4);
+      hipError_t err;
+      switch (L.down.type) {
+        case MOE_Q8_0: err = launch_fz_down_fmt<MOE_Q8_0>(da, items, s); break;
+        case MOE_IQ4_NL: err = launch_fz_down_fmt<MOE_IQ4_NL>(da, items, s); break;
+        default: err = launch_fz_down_fmt<MOE_NVFP4>(da, items, s); break;
+      }
       if (err != hipSuccess) return err;
     }
-    if (rec.error) hipLaunchKernelGGL(k_copy_i32, dim3(1), dim3(64), 0, s, F.plan.error, rec.error + l, 1);
   }
   // the last layer's combine, folded into h
   FzGlueArgs fg{};
@@ -1087,7 +1145,6 @@ hipError_t launch_fused_step(const moe_layer* layers, int n_layers, float* h, in
   fg.h_in = F.hb[n_layers & 1];
   fg.h_out = h;
   fg.o = F.w.o;
-  fg.slot_row = F.plan.slot_row;
   fg.topk_w = prev_w;
   fg.rec_y = rec.y ? rec.y + (size_t)(n_layers - 1) * T * d : nullptr;
   fg.eps = rec.eps;

@@ -150,22 +150,68 @@ __device__ __forceinline__ f16x8 fp4_dword_to_f16x8(uint32_t w, f16 scale) {
 
 // ---------------------------------------------------------------- wave ops
 
+// Wavefront reductions with DPP row shifts and row broadcasts: an inclusive
+// prefix within each 16-lane row (row_shr 1, 2, 4, 8), then the row results
+// carried up (row_bcast 15 into rows 1 and 3, row_bcast 31 into rows 2 and 3),
+// so lane 63 holds the reduction of the wave; it is read back as a scalar.
+// Lanes without a source read the identity (zero bits).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, true);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL, ROW_MASK>(__float_as_uint(v)));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint64_t r = ((uint64_t)dpp_u32<CTRL, ROW_MASK>((uint32_t)(u >> 32)) << 32) | dpp_u32<CTRL, ROW_MASK>((uint32_t)u);
+  return __longlong_as_double((long long)r);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return ((uint64_t)dpp_u32<CTRL, ROW_MASK>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL, ROW_MASK>((uint32_t)v);
+}
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
+__device__ __forceinline__ float lane63_f32(float v) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 63));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_f32<kDppShr1, 0xf>(v);
+  v += dpp_f32<kDppShr2, 0xf>(v);
+  v += dpp_f32<kDppShr4, 0xf>(v);
+  v += dpp_f32<kDppShr8, 0xf>(v);
+  v += dpp_f32<kDppBcast15, 0xa>(v);
+  v += dpp_f32<kDppBcast31, 0xc>(v);
+  return lane63_f32(v);
 }
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_f64<kDppShr1, 0xf>(v);
+  v += dpp_f64<kDppShr2, 0xf>(v);
+  v += dpp_f64<kDppShr4, 0xf>(v);
+  v += dpp_f64<kDppShr8, 0xf>(v);
+  v += dpp_f64<kDppBcast15, 0xa>(v);
+  v += dpp_f64<kDppBcast31, 0xc>(v);
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
+// Maximum of non-negative values (zero bits are the identity).
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, dpp_f32<kDppShr1, 0xf>(v));
+  v = fmaxf(v, dpp_f32<kDppShr2, 0xf>(v));
+  v = fmaxf(v, dpp_f32<kDppShr4, 0xf>(v));
+  v = fmaxf(v, dpp_f32<kDppShr8, 0xf>(v));
+  v = fmaxf(v, dpp_f32<kDppBcast15, 0xa>(v));
+  v = fmaxf(v, dpp_f32<kDppBcast31, 0xc>(v));
+  return lane63_f32(v);
 }
 
 // ---------------------------------------------------------------- top-k keys
@@ -185,14 +231,18 @@ __device__ __forceinline__ float topk_key_value(uint64_t key) {
 }
 __device__ __forceinline__ uint32_t topk_key_index(uint64_t key) { return 0xffffffffu - (uint32_t)key; }
 
+__device__ __forceinline__ uint64_t u64_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, o, kWave), hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
-    const uint64_t w = ((uint64_t)hi << 32) | lo;
-    v = w > v ? w : v;
-  }
-  return v;
+  v = u64_max(v, dpp_u64<kDppShr1, 0xf>(v));
+  v = u64_max(v, dpp_u64<kDppShr2, 0xf>(v));
+  v = u64_max(v, dpp_u64<kDppShr4, 0xf>(v));
+  v = u64_max(v, dpp_u64<kDppShr8, 0xf>(v));
+  v = u64_max(v, dpp_u64<kDppBcast15, 0xa>(v));
+  v = u64_max(v, dpp_u64<kDppBcast31, 0xc>(v));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // Top-k of one token's logits L[0..E) with one wavefront (E <= 64 * NPL):
@@ -202,10 +252,13 @@ template <int NPL>
 __device__ __forceinline__ void wave_topk(const float* __restrict__ L, int E, int k, int lane, int& sel_idx,
                                           float& sel_val) {
   uint64_t key[NPL];
+  float lv[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) lv[i] = L[min(lane + 64 * i, E - 1)];  // unconditional loads, all in flight
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + 64 * i;
-    key[i] = (e < E) ? topk_key(L[e], (uint32_t)e) : 0ull;
+    key[i] = (e < E) ? topk_key(lv[i], (uint32_t)e) : 0ull;
   }
   sel_idx = 0;
   sel_val = 0.0f;

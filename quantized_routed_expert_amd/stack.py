@@ -158,10 +158,12 @@ class FusedStack:
         self.h0 = h0.to(self.device).contiguous()
 
     def step(self, record=None):
-        """One pass over the whole stack: h = h0, then every layer in order."""
+        """One pass over the whole stack: h = h0, then every layer in order.
+        record: a StackRecord to use instead of the stack's own (lib.stack_record()
+        for none at all)."""
         self.h.copy_(self.h0)
-        lib.moe_decode_stack(self.arr, self.n, self.h, self.T, RMS_EPS, record or self.record, self.ws_ptr,
-                             self.ws_bytes)
+        lib.moe_decode_stack(self.arr, self.n, self.h, self.T, RMS_EPS, self.record if record is None else record,
+                             self.ws_ptr, self.ws_bytes)
         return self.h
 
     def timed_record(self, events):
@@ -169,17 +171,17 @@ class FusedStack:
         r = self.record
         return lib.stack_record(r.logits, r.topk_idx, r.topk_w, r.x, r.y, r.error, events)
 
-    def capture(self, warmup=1):
+    def capture(self, warmup=1, record=None):
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
             for _ in range(warmup):
-                self.step()
+                self.step(record)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            self.step()
+            self.step(record)
         torch.cuda.synchronize()
         self.graph = g
         return g

@@ -1,0 +1,515 @@
+// Decode tile code shared by the per-layer decode / verify path (T <= 64
+// tokens, moe_decode.hip) and the fused decode step (moe_fused.hip): grouped
+// dequantising GEMV-like products over the expert plan ("grouped kernels" of
+// the device-planned MoE tail, UD-IQ2_XS (L4 fix) page, "What was changed").
+//
+// The work is HBM-bound: every weight byte of the active experts is read once.
+// Weights are the B operand of v_mfma_f32_16x16x32_f16: each lane owns one
+// weight row of a 16-row tile and one 16-byte chunk of codes per step (the
+// four lane groups read a row's four consecutive chunks, 64 contiguous bytes),
+// and decodes it in registers to exact fp16 values (IQ4_NL codebook entries,
+// Q8_0 int8 codes, or e2m1 * e4m3 products for the NVFP4-style format).
+// Activations are the A operand, staged in LDS as fp16 (with a per-token
+// power-of-two scale) or as fp16 hi/lo pairs.  For the Q8_0 and IQ4_NL formats
+// the A operand is block-diagonal: lane group G only multiplies the chunk it
+// decoded, so each accumulator row group holds the partial sum of exactly one
+// quant block and the block's fp16 scale is applied once per lane (fp32 FMA)
+// after the MFMA.  The NVFP4-style block scale is folded into the fp16 weights
+// (exact) and the tensor scale is applied at the end.  Accumulation is fp32.
+//
+// Also here: the host-side workspace layout and launch-shape helpers.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "moe_device.h"
+#include "moe_launch.h"
+
+namespace qre {
+
+// Slot table entry (fused path): expert, first plan row, rows, 1 = shared.
+struct SlotEnt {
+  int32_t e, row0, cnt, shared;
+};
+
+struct DecodeArgs {
+  QMatDev mat[2];   // routed: gate, up (gate/up pass) or down (down pass)
+  QMatDev smat[2];  // shared expert, same roles
+  int has_shared;
+  // per-layer path: plan in global memory (routed slots first, shared last)
+  const int32_t* offsets;
+  const int32_t* row_token;
+  const int32_t* active;
+  const int32_t* n_active;
+  // fused path: slot table (shared first) and its length
+  const SlotEnt* slots;
+  const int32_t* n_slots;
+  int32_t* error;
+  int T, k;
+  int P;                   // fp16 parts per column: 1 (bf16 tokens), 2 (fp32 tokens, or h hi/lo)
+  int ksplit;              // waves along K per 16-row tile (1, 2, 4)
+  const f16* in16;         // gate/up: X16 [T*P][d]; down: H16 [(T*k+T)*2][f]
+  const float* in_scale;   // gate/up: scale of each X16 row (a power of two)
+  f16* h16;                // gate/up output H16 [(T*k+T)*2][f]
+  int down_type;           // gate/up: layout of H16 rows (IQ4_NL: block-permuted)
+  float* o;                // down output O [(T*k+T)][d]
+  const int32_t* pair_of_row;  // fused down pass: O row of each plan row (t*k + j); null: the plan row
+};
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+
+template <int FMT>
+__device__ __forceinline__ f16x8 decode_b(const u32x4& c, int i, uint32_t sraw) {
+  if constexpr (FMT == MOE_IQ4_NL) {
+    return iq4_dword_to_f16x8(c[i]);
+  } else if constexpr (FMT == MOE_Q8_0) {
+    return q8_dwords_to_f16x8(c[2 * i], c[2 * i + 1]);
+  } else {
+    // dwords 0,1 hold the chunk's first 16-element block, 2,3 the second
+    const uint32_t sbyte = (i < 2) ? (sraw & 0xffu) : ((sraw >> 8) & 0xffu);
+    return fp4_dword_to_f16x8(c[i], (f16)e4m3_to_f32(sbyte));
+  }
+}
+
+// Position of element i of a row in the activation layout matching the
+// weight decode of format `fmt` (IQ4_NL reorders elements inside each block).
+__device__ __forceinline__ int act_pos(int fmt, int i) {
+  return fmt == MOE_IQ4_NL ? ((i & ~31) + iq4_pos(i & 31)) : i;
+}
+
+// Columns (token or hi/lo parts) per N-tile: block-diagonal formats use four
+// (one per lane group's block); the NVFP4-style format uses the first eight
+// rows of the dense 16-row A operand (the other eight stay zero).
+template <int FMT>
+constexpr int cols_per_tile() {
+  return FMT == MOE_NVFP4 ? 8 : 4;
+}
+
+struct SlotInfo {
+  int e;
+  bool is_sh;
+  int row0;
+  int ncolt;  // tokens of the slot
+};
+
+// One workgroup item: rows [tile*16, tile*16+16) of slot `si` (gate + up, or
+// down), this wave's K part, against all of the slot's columns.  sA: the
+// workgroup's activation staging buffer; red: [4][NMAT][NT][64] partials.
+// Steps of weight codes in flight per matrix (and per wave): the gate/up pass
+// keeps two matrices' codes in registers, the down pass one (more steps for
+// the 16-element steps of Q8_0).  A pass with more steps than that rolls the
+// prefetch forward (ROLL); otherwise every code load is issued up front.
+constexpr int dq_pd(int fmt, bool gateup) { return (!gateup && fmt == MOE_Q8_0) ? 12 : 6; }
+constexpr int dq_eps(int fmt) { return fmt == MOE_Q8_0 ? 16 : 32; }  // elements per lane per step
+inline int dq_nsteps(int fmt, int K, int ksplit) { return K / ksplit / (4 * dq_eps(fmt)); }
+
+template <int FMT, int NT, bool GATEUP, bool ROLL>
+__device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si, int tile, int kpart,
+                                        const int32_t* row_token, f16* sA, f32x4* red) {
+  constexpr int EPS = dq_eps(FMT);                   // elements per lane per step (one 16-byte load)
+  constexpr int NMF = EPS / 8;                       // MFMAs per step
+  constexpr bool BD = FMT != MOE_NVFP4;              // block-diagonal activations
+  constexpr int CPT = cols_per_tile<FMT>();
+  constexpr int CPP = NT * CPT;                      // columns staged per pass
+  constexpr int NMAT = GATEUP ? 2 : 1;
+  constexpr int PD = dq_pd(FMT, GATEUP);             // steps of codes in flight per matrix
+  constexpr int AB = NT == 1 ? 2 : 12;               // activation chunks per thread issued first
+  constexpr int RB = NT == 1 ? 2 : 8;                // later activation chunks in flight per thread
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int n = lane & 15, G = lane >> 4;
+  const int ksplit = a.ksplit;
+  const int rows = a.mat[0].rows, K = a.mat[0].cols;
+  const int kw = K / ksplit;
+  const int nsteps = kw / (4 * EPS);
+  const int crb = code_row_bytes(FMT, K), srb = scale_row_bytes(FMT, K);
+  const int P = a.P;
+  const int ncol = si.ncolt * P;
+
+  const uint8_t* crow[NMAT];
+  const uint8_t* srow[NMAT];
+  float tsc[NMAT];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m) {
+    const QMatDev& W = si.is_sh ? a.smat[m] : a.mat[m];
+    const long rw = (long)si.e * rows + tile * 16 + n;
+    crow[m] = W.codes + rw * crb;
+    srow[m] = W.scales + rw * srb;
+    tsc[m] = (FMT == MOE_NVFP4) ? W.ts[si.e] : 1.0f;
+  }
+  // K position of this lane at step s: the four lane groups take four
+  // consecutive EPS-element chunks, so a row's 16-byte code loads are
+  // contiguous across the lane groups (64 bytes per row per step).
+  const int kbase = kpart * kw + G * EPS;
+
+  // input row of column `col` (a token, or one fp16 part of it)
+  auto in_row_of = [&](int col) -> long {
+    if constexpr (GATEUP) {
+      const int tc = col / P, part = col - tc * P;
+      const int t = si.is_sh ? tc : row_token[si.row0 + tc];
+      return (long)t * P + part;
+    } else {
+      return (long)(si.row0 + col / 2) * 2 + (col & 1);
+    }
+  };
+
+  const int chunks_per_col = K / 8;  // 16-byte activation chunks per column
+  // All global loads below are unconditional (out-of-range ones repeat a valid
+  // address and their result is discarded), so the waits that follow them are
+  // exact: data issued earlier never waits for data issued later.
+  // this lane's code and scale addresses at step 0; step s adds a constant
+  // (4 * EPS elements: 64 code bytes, 4 * EPS / 32 scale words)
+  const uint8_t* cl[NMAT];
+  const uint16_t* sl[NMAT];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m) {
+    cl[m] = crow[m] + (FMT == MOE_Q8_0 ? kbase : (kbase >> 1));
+    sl[m] = (const uint16_t*)srow[m] + (kbase >> 5);
+  }
+  auto load_step = [&](int m, int s, u32x4& c, uint32_t& sc) {
+    c = *(const u32x4*)(cl[m] + s * (FMT == MOE_Q8_0 ? 4 * EPS : 2 * EPS));
+    // Q8_0 / IQ4_NL: the block's fp16 scale; NVFP4: the chunk's two E4M3 scales
+    sc = sl[m][s * (4 * EPS / 32)];
+  };
+  for (int c0 = 0; c0 < ncol; c0 += CPP) {
+    const int ncp = min(CPP, ncol - c0);
+    const int nch = ncp * chunks_per_col;
+    // ---- the first batch of this pass's activation chunks, issued before the
+    // weight codes so that waiting for them does not wait for the codes
+    u32x4 av[AB];
+#pragma unroll
+    for (int b = 0; b < AB; ++b) {
+      const int ch = min(tid + b * 256, nch - 1);
+      const int c = ch / chunks_per_col, kk = (ch - c * chunks_per_col) * 8;
+      av[b] = *(const u32x4*)(a.in16 + in_row_of(c0 + c) * K + kk);
+    }
+    // ---- the first PD steps of weight codes (independent of the activations)
+    u32x4 cb[NMAT][PD];
+    uint32_t sb[NMAT][PD];
+#pragma unroll
+    for (int u = 0; u < PD; ++u)
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) load_step(m, min(u, nsteps - 1), cb[m][u], sb[m][u]);
+
+    // ---- stage the activation columns into LDS.  Columns at or beyond ncp
+    // are never read (their A rows are zero), so they are not written.
+    __syncthreads();  // the previous pass has finished reading sA
+#pragma unroll
+    for (int b = 0; b < AB; ++b) {
+      const int ch = tid + b * 256;
+      if (ch < nch) {
+        const int c = ch / chunks_per_col, kk = (ch - c * chunks_per_col) * 8;
+        *(u32x4*)&sA[c * K + kk] = av[b];
+      }
+    }
+    // the rest in batches of RB loads in flight per thread
+    for (int ch0 = tid + AB * 256; ch0 < nch; ch0 += RB * 256) {
+      u32x4 bv[RB];
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        const int ch = min(ch0 + b * 256, nch - 1);
+        const int c = ch / chunks_per_col, kk = (ch - c * chunks_per_col) * 8;
+        bv[b] = *(const u32x4*)(a.in16 + in_row_of(c0 + c) * K + kk);
+      }
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        const int ch = ch0 + b * 256;
+        if (ch < nch) {
+          const int c = ch / chunks_per_col, kk = (ch - c * chunks_per_col) * 8;
+          *(u32x4*)&sA[c * K + kk] = bv[b];
+        }
+      }
+    }
+    __syncthreads();
+
+    // A-operand LDS row for each N-tile (this lane is A row m = n, K slice G);
+    // lanes without a column read column 0 and use zeros
+    int acol[NT];
+    bool aval[NT];
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt) {
+      int c;
+      bool valid;
+      if constexpr (BD) {
+        valid = (n >> 2) == G;
+        c = jt * CPT + (n & 3);
+      } else {
+        valid = n < CPT;
+        c = jt * CPT + n;
+      }
+      aval[jt] = valid && c < ncp;
+      acol[jt] = aval[jt] ? c : 0;
+    }
+
+    f32x4 acc[NMAT][NT];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt) acc[m][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute_step = [&](const u32x4 (&cc)[NMAT], const uint32_t (&ss)[NMAT], int s) {
+      f16x8 ac[NT][NMF];
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt)
+#pragma unroll
+        for (int i = 0; i < NMF; ++i) {
+          const f16x8 v = *(const f16x8*)&sA[acol[jt] * K + kbase + s * 4 * EPS + 8 * i];
+          ac[jt][i] = aval[jt] ? v : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        f32x4 D[NT];
+#pragma unroll
+        for (int jt = 0; jt < NT; ++jt) D[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NMF; ++i) {
+          const f16x8 bf = decode_b<FMT>(cc[m], i, ss[m]);
+#pragma unroll
+          for (int jt = 0; jt < NT; ++jt) D[jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ac[jt][i], bf, D[jt], 0, 0, 0);
+        }
+        if constexpr (FMT == MOE_NVFP4) {
+#pragma unroll
+          for (int jt = 0; jt < NT; ++jt) acc[m][jt] += D[jt];
+        } else {
+          const float sc = f16_bits_to_f32(ss[m]);
+#pragma unroll
+          for (int jt = 0; jt < NT; ++jt) {
+            acc[m][jt].x = fmaf(sc, D[jt].x, acc[m][jt].x);
+            acc[m][jt].y = fmaf(sc, D[jt].y, acc[m][jt].y);
+            acc[m][jt].z = fmaf(sc, D[jt].z, acc[m][jt].z);
+            acc[m][jt].w = fmaf(sc, D[jt].w, acc[m][jt].w);
+          }
+        }
+      }
+    };
+
+    if constexpr (!ROLL) {
+      // every step's codes are already in flight
+#pragma unroll
+      for (int u = 0; u < PD; ++u) {
+        if (u < nsteps) {
+          u32x4 cc[NMAT];
+          uint32_t ss[NMAT];
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) {
+            cc[m] = cb[m][u];
+            ss[m] = sb[m][u];
+          }
+          compute_step(cc, ss, u);
+        }
+      }
+    } else {
+      // rolling prefetch, PD steps ahead (past the end it repeats the last step)
+      for (int s0 = 0; s0 < nsteps; s0 += PD) {
+#pragma unroll
+        for (int u = 0; u < PD; ++u) {
+          const int s = s0 + u;
+          u32x4 cc[NMAT];
+          uint32_t ss[NMAT];
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) {
+            cc[m] = cb[m][u];
+            ss[m] = sb[m][u];
+            load_step(m, min(s + PD, nsteps - 1), cb[m][u], sb[m][u]);
+          }
+          if (s < nsteps) compute_step(cc, ss, s);
+        }
+      }
+    }
+
+    // block-diagonal: sum the four lane groups (one chunk each)
+    if constexpr (BD) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int jt = 0; jt < NT; ++jt) {
+          f32x4& v = acc[m][jt];
+          v.x += __shfl_xor(v.x, 16, 64);
+          v.y += __shfl_xor(v.y, 16, 64);
+          v.z += __shfl_xor(v.z, 16, 64);
+          v.w += __shfl_xor(v.w, 16, 64);
+          v.x += __shfl_xor(v.x, 32, 64);
+          v.y += __shfl_xor(v.y, 32, 64);
+          v.z += __shfl_xor(v.z, 32, 64);
+          v.w += __shfl_xor(v.w, 32, 64);
+        }
+    }
+    // reduce the K parts of this row tile through LDS
+    if (ksplit > 1) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int jt = 0; jt < NT; ++jt) red[((wid * NMAT + m) * NT + jt) * 64 + lane] = acc[m][jt];
+      __syncthreads();
+      if (kpart == 0) {
+        for (int q = 1; q < ksplit; ++q)
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int jt = 0; jt < NT; ++jt) acc[m][jt] += red[(((wid + q) * NMAT + m) * NT + jt) * 64 + lane];
+      }
+      __syncthreads();
+    }
+
+    if (kpart == 0) {
+      const int frow = tile * 16 + n;  // output feature of this lane
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt) {
+        // D row m = 4G + v.  Block-diagonal: the four lane groups hold the same
+        // sums after the reduction; group G takes column slot v == G (P == 1)
+        // or the pair v = 2G, 2G+1 (P == 2).  Dense: column 4G + v.
+        float vals[NMAT][4];
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+          vals[m][0] = acc[m][jt].x * tsc[m];
+          vals[m][1] = acc[m][jt].y * tsc[m];
+          vals[m][2] = acc[m][jt].z * tsc[m];
+          vals[m][3] = acc[m][jt].w * tsc[m];
+        }
+#pragma unroll
+        for (int v = 0; v < 4; v += 1) {
+          int cl;
+          if constexpr (BD) {
+            if (P == 1 ? (v != G) : (v != 2 * G)) continue;
+            cl = jt * CPT + v;
+          } else {
+            if (P == 2 && (v & 1)) continue;
+            cl = jt * CPT + 4 * G + v;
+            if (4 * G + v >= CPT) continue;
+          }
+          if (cl >= ncp) continue;
+          const int tc = (c0 + cl) / P;
+          float val[NMAT];
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) val[m] = (P == 2) ? vals[m][v] + vals[m][v + 1] : vals[m][v];
+          const int out_row = si.row0 + tc;
+          if constexpr (GATEUP) {
+            const int t = si.is_sh ? tc : row_token[si.row0 + tc];
+            const float xs = a.in_scale[(long)t * P];
+            const float g = val[0] * xs, u = val[1] * xs;
+            const float h = silu_f(g) * u;
+            if (!(fabsf(h) < 65504.0f)) atomicOr(a.error, 2);
+            const f16 hi = (f16)h;
+            const f16 lo = (f16)(h - (float)hi);
+            const int f = rows;
+            const int pos = act_pos(a.down_type, frow);
+            a.h16[((long)out_row * 2 + 0) * f + pos] = hi;
+            a.h16[((long)out_row * 2 + 1) * f + pos] = lo;
+          } else {
+            // fused path: routed rows go to their (token, slot) pair's row
+            const int orow = (a.pair_of_row && !si.is_sh) ? a.pair_of_row[out_row] : out_row;
+            a.o[(long)orow * rows + frow] = val[0];
+          }
+        }
+      }
+    }
+  }
+}
+
+// Exponent e such that max|x| * 2^-e lies in [2^14, 2^15) (0 for an all-zero row).
+__device__ __forceinline__ int x16_exponent(float mx) {
+  int ex = 0;
+  if (mx > 0.0f && mx < __builtin_inff()) {
+    int e2;
+    frexpf(mx, &e2);  // mx = m * 2^e2, m in [0.5, 1)
+    ex = max(-100, min(100, e2 - 15));
+  }
+  return ex;
+}
+
+// ----------------------------------------------------------------------------
+// host-side helpers
+// ----------------------------------------------------------------------------
+
+struct DecodeWs {
+  f16* x16;
+  float* xs;
+  f16* h16;
+  float* o;
+};
+
+inline DecodeWs carve(void* ws, int T, int d, int f, int k, int P) {
+  char* p = (char*)ws;
+  DecodeWs w;
+  w.x16 = (f16*)p;
+  p += align_up((size_t)T * P * d * 2, 256);
+  w.xs = (float*)p;
+  p += align_up((size_t)T * P * 4, 256);
+  const size_t R = (size_t)T * k + T;
+  w.h16 = (f16*)p;
+  p += align_up(R * 2 * f * 2, 256);
+  w.o = (float*)p;
+  return w;
+}
+
+// Waves along K per 16-row tile: as many as divide the lane-group step count.
+inline int pick_ksplit(int K, int eps) {
+  const int S = K / (4 * eps);
+  for (int ks : {4, 2})
+    if (S % ks == 0) return ks;
+  return 1;
+}
+
+// N-tiles per column pass: enough for the widest slot, within 48 KB of staged
+// activations (columns x K x 2 bytes).
+inline int pick_nt(int cpt, int ncols_max, int K) {
+  const int fit = (48 * 1024) / (cpt * K * 2);
+  int nt = (ncols_max + cpt - 1) / cpt;
+  if (nt > fit) nt = fit;
+  return nt >= 4 ? 4 : (nt >= 2 ? 2 : 1);
+}
+
+inline DecodeArgs gateup_args(const moe_layer& L, int T, int P, const DecodeWs& w) {
+  DecodeArgs a{};
+  a.has_shared = L.has_shared;
+  a.T = T;
+  a.k = L.k;
+  const int eps = dq_eps(L.gate.type);
+  a.mat[0] = qmat_dev(L.gate);
+  a.mat[1] = qmat_dev(L.up);
+  if (L.has_shared) {
+    a.smat[0] = qmat_dev(L.shared_gate);
+    a.smat[1] = qmat_dev(L.shared_up);
+  }
+  a.P = P;
+  a.ksplit = pick_ksplit(L.d, eps);
+  a.in16 = w.x16;
+  a.in_scale = w.xs;
+  a.h16 = w.h16;
+  a.down_type = L.down.type;
+  return a;
+}
+
+inline DecodeArgs down_args(const moe_layer& L, int T, const DecodeWs& w) {
+  DecodeArgs a{};
+  a.has_shared = L.has_shared;
+  a.T = T;
+  a.k = L.k;
+  a.mat[0] = qmat_dev(L.down);
+  if (L.has_shared) a.smat[0] = qmat_dev(L.shared_down);
+  a.P = 2;
+  a.ksplit = 1;
+  a.in16 = w.h16;
+  a.o = w.o;
+  return a;
+}
+
+// Workgroups of `kern` (256 threads, `lds` dynamic bytes) resident at once on
+// the current device, or 0 if the runtime cannot tell.
+template <typename Kern>
+int resident_wgs(Kern kern, size_t lds) {
+  int dev = 0, ncu = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, lds) != hipSuccess) return 0;
+  return ncu * per_cu;
+}
+
+// Grid of a fused expert pass over `items` items: all of them when they fit
+// in one resident wave of workgroups, else one resident wave that loops.
+template <typename Kern>
+int fused_grid(Kern kern, size_t lds, int items) {
+  const int res = resident_wgs(kern, lds);
+  return (res > 0 && items > res) ? res : items;
+}
+
+}  // namespace qre

@@ -1,0 +1,573 @@
+// Fused decode step (moe_decode_stack): per layer the glue and router
+// (k_fz_glue / k_fz_route), top-k + plan + grouped gate/up (k_fz_gateup), and
+// the down pass over the slot table (k_ffn_dq in moe_decode.hip).  The routing
+// and the plan are recomputed in each gate/up workgroup's LDS so that no
+// launch waits on a separate plan kernel (the "device-planned MoE tail" with
+// "grouped kernels", UD-IQ2_XS (L4 fix) page, "What was changed").
+#include <hip/hip_runtime.h>
+
+#include "moe_dq.h"
+
+namespace qre {
+
+struct FusedPlan {  // plan of the current layer, written by k_fz_gateup's workgroup 0
+  int32_t* pair_of_row;  // [T*k] pair t*k + j of each plan row (expert-major, token order)
+  int32_t* error;
+  int32_t* topk_idx;     // [T][k]
+  float* topk_w;         // [T][k]
+  SlotEnt* slots;        // [T*k + 1]: shared expert first, then the active experts ascending
+  int32_t* n_slots;
+};
+
+// (1) Layer input and router.
+//
+// Glue (layer l > 0): y = o[T*k + t] + sum_j topk_w[t][j] * o[t*k + j] (the
+// previous layer's combine: shared row, then the routed slots in order j; the
+// down pass writes routed rows at their pair's position), h_new = h + y, and
+// the layer input x = bf16(h_new / sqrt(mean(h_new^2) + eps)).  The first
+// layer takes x = bf16(rmsnorm(h)).  The glue writes the new residual, x (bf16,
+// and as power-of-two scaled fp16 for the expert products) and optional
+// records of the previous layer's y and this layer's x.
+struct FzGlueArgs {
+  int d, T, k, has_shared;
+  const float* h_in;
+  float* h_out;
+  const float* o;            // previous layer's expert rows, or null (first layer)
+  const float* topk_w;       // previous layer's gate weights
+  float* rec_y;              // previous layer's y (optional)
+  uint16_t* x_out;           // bf16 layer input (null: the final fold, no next layer)
+  uint16_t* rec_x;           // optional record of the same
+  f16* x16;
+  float* xs;
+  int gate_fmt;
+  float eps;
+  int32_t* error_reset;      // the plan's error word, cleared for the next layer
+};
+
+constexpr int kGlueMaxQ = 4;  // d <= 4096: float4 chunks per thread
+constexpr int kGlueRB = 8;    // routed rows whose loads are in flight together
+
+// Glue for one token, by one workgroup.  Returns the token's bf16 input in
+// v[] (as floats) when the caller needs it.
+__device__ __forceinline__ void glue_token(const FzGlueArgs& a, int t, bool writer, f32x4 (&v)[kGlueMaxQ]) {
+  __shared__ float red[2][4];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int d = a.d, T = a.T, k = a.k;
+  const int nq = d / 1024;
+  // residual and shared row first; every routed row of a batch is in flight
+  // before the first is used
+  f32x4 y[kGlueMaxQ];
+#pragma unroll
+  for (int q = 0; q < kGlueMaxQ; ++q) {
+    if (q < nq) {
+      const int i = (q * 256 + tid) * 4;
+      v[q] = *(const f32x4*)(a.h_in + (long)t * d + i);
+      y[q] = (a.o && a.has_shared) ? *(const f32x4*)(a.o + (long)(T * k + t) * d + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  if (a.o) {
+    for (int j0 = 0; j0 < k; j0 += kGlueRB) {
+      float wj[kGlueRB];
+      f32x4 ov[kGlueMaxQ][kGlueRB];
+#pragma unroll
+      for (int jj = 0; jj < kGlueRB; ++jj) wj[jj] = (j0 + jj < k) ? a.topk_w[t * k + j0 + jj] : 0.0f;
+#pragma unroll
+      for (int q = 0; q < kGlueMaxQ; ++q)
+#pragma unroll
+        for (int jj = 0; jj < kGlueRB; ++jj)
+          if (q < nq && j0 + jj < k)
+            ov[q][jj] = *(const f32x4*)(a.o + (long)(t * k + j0 + jj) * d + (q * 256 + tid) * 4);
+#pragma unroll
+      for (int q = 0; q < kGlueMaxQ; ++q)
+#pragma unroll
+        for (int jj = 0; jj < kGlueRB; ++jj)
+          if (q < nq && j0 + jj < k) {
+            y[q].x = fmaf(wj[jj], ov[q][jj].x, y[q].x);
+            y[q].y = fmaf(wj[jj], ov[q][jj].y, y[q].y);
+            y[q].z = fmaf(wj[jj], ov[q][jj].z, y[q].z);
+            y[q].w = fmaf(wj[jj], ov[q][jj].w, y[q].w);
+          }
+    }
+  }
+  float ss = 0.0f;
+#pragma unroll
+  for (int q = 0; q < kGlueMaxQ; ++q) {
+    if (q < nq) {
+      const int i = (q * 256 + tid) * 4;
+      if (a.o) {
+        if (writer && a.rec_y) *(f32x4*)(a.rec_y + (long)t * d + i) = y[q];
+        v[q] += y[q];
+      }
+      if (writer) *(f32x4*)(a.h_out + (long)t * d + i) = v[q];
+      ss += v[q].x * v[q].x + v[q].y * v[q].y + v[q].z * v[q].z + v[q].w * v[q].w;
+    }
+  }
+  if (!a.x_out) return;  // final fold: the residual is all that is needed
+  ss = wave_sum(ss);
+  if (lane == 0) red[0][wid] = ss;
+  __syncthreads();
+  const float inv = 1.0f / sqrtf((red[0][0] + red[0][1] + red[0][2] + red[0][3]) / (float)d + a.eps);
+  float mx = 0.0f;
+#pragma unroll
+  for (int q = 0; q < kGlueMaxQ; ++q) {
+    if (q < nq) {
+      const int i = (q * 256 + tid) * 4;
+      const uint32_t p0 = pack_bf16x2(v[q].x * inv, v[q].y * inv);
+      const uint32_t p1 = pack_bf16x2(v[q].z * inv, v[q].w * inv);
+      v[q] = f32x4{bf16_bits_to_f32(p0 & 0xffffu), bf16_bits_to_f32(p0 >> 16), bf16_bits_to_f32(p1 & 0xffffu),
+                   bf16_bits_to_f32(p1 >> 16)};
+      if (writer) {
+        const u32x2 pk = {p0, p1};
+        *(u32x2*)(a.x_out + (long)t * d + i) = pk;
+        if (a.rec_x) *(u32x2*)(a.rec_x + (long)t * d + i) = pk;
+      }
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[q].x), fabsf(v[q].y)), fmaxf(fabsf(v[q].z), fabsf(v[q].w))));
+    }
+  }
+  if (writer) {
+    // fp16 activations (power-of-two scaled) for the expert products
+    mx = wave_max(mx);
+    if (lane == 0) red[1][wid] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+    const int ex = x16_exponent(mx);
+    const float down = ldexpf(1.0f, -ex);
+#pragma unroll
+    for (int q = 0; q < kGlueMaxQ; ++q) {
+      if (q < nq) {
+        const int i = (q * 256 + tid) * 4;
+        a.x16[(long)t * d + act_pos(a.gate_fmt, i + 0)] = (f16)(v[q].x * down);
+        a.x16[(long)t * d + act_pos(a.gate_fmt, i + 1)] = (f16)(v[q].y * down);
+        a.x16[(long)t * d + act_pos(a.gate_fmt, i + 2)] = (f16)(v[q].z * down);
+        a.x16[(long)t * d + act_pos(a.gate_fmt, i + 3)] = (f16)(v[q].w * down);
+      }
+    }
+    if (tid == 0) a.xs[t] = ldexpf(1.0f, ex);
+  }
+  __syncthreads();
+}
+
+// Glue for T tokens: one workgroup per token.
+__global__ __launch_bounds__(256) void k_fz_glue(const FzGlueArgs a) {
+  f32x4 v[kGlueMaxQ];
+  if (blockIdx.x == 0 && threadIdx.x == 0 && a.error_reset) *a.error_reset = 0;
+  glue_token(a, blockIdx.x, true, v);
+}
+
+// Router: logits[t][e] for T tokens, one wavefront per expert row, fp64
+// accumulation (exact products of fp32 weights and bf16 inputs).  INLINE (a
+// single token): every workgroup forms the token's input itself with the glue
+// (workgroup 0 writes it out), so the layer needs no separate glue launch.
+// Otherwise x is read from the glue kernel's output.
+struct FzRouteArgs {
+  FzGlueArgs g;
+  const float* Wr;
+  const float* bias;
+  int E;
+  const uint16_t* x;  // bf16 [T][d] (not INLINE)
+  float* logits;      // [T][E]
+};
+
+// Experts per workgroup: four, one wavefront each (INLINE: the glue is the
+// larger cost, so fewer workgroups repeat it), or two, each split over two
+// wavefronts along d (the fp64 products of several tokens are the larger cost).
+template <bool INLINE>
+constexpr int route_experts_per_wg() {
+  return INLINE ? 4 : 2;
+}
+
+template <bool INLINE>
+__global__ __launch_bounds__(256) void k_fz_route(const FzRouteArgs a) {
+  __shared__ uint16_t sx[kFusedMaxT * 4096];  // bf16 layer inputs
+  __shared__ double pr[2][kFusedMaxT];        // second halves (two wavefronts per expert)
+  constexpr int WPE = 4 / route_experts_per_wg<INLINE>();  // wavefronts per expert
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int d = a.g.d, T = a.g.T;
+  const int e = blockIdx.x * (4 / WPE) + wid / WPE;
+  const int half = wid % WPE;
+  const int nj = d / 256;
+  const int jlo = half * nj / WPE, jhi = (half + 1) * nj / WPE;
+
+  // router row part of this wave: lane holds elements (j*64 + lane)*4 .. +3
+  f32x4 wv[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (j >= jlo && j < jhi && e < a.E) wv[j] = *(const f32x4*)(a.Wr + (long)e * d + (j * 64 + lane) * 4);
+
+  if constexpr (INLINE) {
+    if (blockIdx.x == 0 && tid == 0 && a.g.error_reset) *a.g.error_reset = 0;
+    f32x4 v[kGlueMaxQ];
+    glue_token(a.g, 0, blockIdx.x == 0, v);
+    const int nq = d / 1024;
+#pragma unroll
+    for (int q = 0; q < kGlueMaxQ; ++q) {
+      if (q < nq) {
+        const int i = (q * 256 + tid) * 4;
+        const u32x2 pk = {pack_bf16x2(v[q].x, v[q].y), pack_bf16x2(v[q].z, v[q].w)};
+        *(u32x2*)&sx[i] = pk;
+      }
+    }
+  } else {
+    const int nch = T * d / 8;
+    for (int c0 = tid; c0 < nch; c0 += 8 * 256) {
+      u32x4 bv[8];
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const int c = min(c0 + b * 256, nch - 1);
+        bv[b] = *(const u32x4*)(a.x + (long)c * 8);
+      }
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const int c = c0 + b * 256;
+        if (c < nch) {
+          const int t = (c * 8) / d, i = (c * 8) % d;
+          *(u32x4*)&sx[t * 4096 + i] = bv[b];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // all tokens' partial sums first, then their wave reductions together
+  double r[kFusedMaxT];
+  if (e < a.E) {
+    double acc[kFusedMaxT];
+#pragma unroll
+    for (int t = 0; t < kFusedMaxT; ++t) acc[t] = 0.0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j >= jlo && j < jhi) {
+        const int i = (j * 64 + lane) * 4;
+        const double w0 = wv[j].x, w1 = wv[j].y, w2 = wv[j].z, w3 = wv[j].w;
+#pragma unroll
+        for (int t = 0; t < kFusedMaxT; ++t) {
+          if (t < T) {
+            const u32x2 xb = *(const u32x2*)&sx[t * 4096 + i];
+            acc[t] += w0 * (double)bf16_bits_to_f32(xb.x & 0xffffu) + w1 * (double)bf16_bits_to_f32(xb.x >> 16) +
+                      w2 * (double)bf16_bits_to_f32(xb.y & 0xffffu) + w3 * (double)bf16_bits_to_f32(xb.y >> 16);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kFusedMaxT; ++t)
+      if (t < T) r[t] = wave_sum_f64(acc[t]);
+  }
+  if constexpr (WPE == 2) {
+    if (half == 1 && lane == 0 && e < a.E)
+      for (int t = 0; t < T; ++t) pr[wid >> 1][t] = r[t];
+    __syncthreads();
+    if (half == 0 && e < a.E)
+      for (int t = 0; t < T; ++t) r[t] += pr[wid >> 1][t];
+  }
+  if (half == 0 && lane == 0 && e < a.E) {
+    const double b = a.bias ? (double)a.bias[e] : 0.0;
+    for (int t = 0; t < T; ++t) a.logits[(long)t * a.E + e] = (float)(r[t] + b);
+  }
+}
+
+// (2) Top-k + plan (in LDS, recomputed by every workgroup that needs it) +
+// grouped gate/up.  Slot 0 is the shared expert (it needs no routing, so its
+// items start streaming at once); slots 1.. are the active experts in
+// ascending id order.  Workgroup 0 publishes the plan for the down pass and
+// the next layer's combine.
+struct FzGateArgs {
+  DecodeArgs a;  // gate/up pass arguments (in16 = x16, in_scale = xs, h16, error)
+  const float* logits;
+  int E;
+  FusedPlan plan;
+};
+
+constexpr int kFusedTK = kFusedMaxT * 32;  // token-slot pairs at most
+
+// Single-tile passes (one N-tile of columns, the batch-1 case) are held to two
+// waves per SIMD so that one grid of a decode step is resident at once.
+template <int FMT, int NT, int NPL, bool ROLL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1))) void k_fz_gateup(
+    const FzGateArgs g) {
+  constexpr int NMAT = 2;
+  __shared__ f32x4 red[4 * NMAT * NT * 64];
+  __shared__ __align__(16) int32_t sidx[kFusedTK];
+  __shared__ float sw[kFusedTK];
+  __shared__ __align__(16) int32_t sfirst[kFusedTK];
+  __shared__ int32_t srow_token[kFusedTK];
+  __shared__ SlotEnt sslot[kFusedTK];
+  extern __shared__ f16 sA[];
+
+  const DecodeArgs& a = g.a;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int T = a.T, k = a.k, E = g.E;
+  const int TK = T * k;
+  const int ksplit = a.ksplit;
+  const int rt_per_wg = 4 / ksplit;
+  const int rows = a.mat[0].rows;
+  const int wg_per_slot = (rows / 16) / rt_per_wg;
+  const int hs = a.has_shared;
+  const int max_slots = min(E, TK) + hs;
+  const int n_items = max_slots * wg_per_slot;
+  // The plan is needed by workgroup 0 (which publishes it) and by every
+  // workgroup with a routed item; it is built before the item loop so that
+  // none of its state stays live during the expert products.
+  const int last_item = blockIdx.x + ((n_items - 1 - (int)blockIdx.x) / (int)gridDim.x) * (int)gridDim.x;
+  int n_act = 0;
+  if (blockIdx.x == 0 || last_item >= hs * wg_per_slot) {
+    // ---- top-k per token (one wavefront per token), renormalised weights
+    sidx[tid] = 0x7fffffff;  // padding of the pair list
+    __syncthreads();
+    for (int t = wid; t < T; t += 4) {
+      int ix;
+      float lv;
+      wave_topk<NPL>(g.logits + (long)t * E, E, k, lane, ix, lv);
+      const float vmax = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(lv), 0));
+      const float ex = lane < k ? expf(lv - vmax) : 0.0f;
+      const float sum = wave_sum(ex);
+      if (lane < k) {
+        sidx[t * k + lane] = ix;
+        sw[t * k + lane] = ex / sum;
+      }
+    }
+    __syncthreads();
+    // ---- plan: pair p (thread p) counts the pairs of smaller experts (its
+    // expert's first plan row) and the earlier pairs of its own expert (its
+    // rank); the first pair of each expert then counts the distinct smaller
+    // experts (its slot).  Rows within an expert follow token order.
+    // (the pair lists are padded to a multiple of 4 with an id above every
+    // expert, which no count includes, and read four at a time)
+    const int TK4 = (TK + 3) & ~3;
+    int e = 0, less = 0, before = 0, same = 0;
+    if (tid < TK) {
+      e = sidx[tid];
+      for (int q0 = 0; q0 < TK4; q0 += 4) {
+        const i32x4 eq = *(const i32x4*)&sidx[q0];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          less += eq[u] < e ? 1 : 0;
+          same += eq[u] == e ? 1 : 0;
+          before += (eq[u] == e && q0 + u < tid) ? 1 : 0;
+        }
+      }
+    }
+    sfirst[tid] = (tid < TK && before == 0) ? e : 0x7fffffff;
+    __syncthreads();
+    if (tid < TK) {
+      int dl = 0;
+      for (int q0 = 0; q0 < TK4; q0 += 4) {
+        const i32x4 fq = *(const i32x4*)&sfirst[q0];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dl += fq[u] < e ? 1 : 0;
+      }
+      srow_token[less + before] = tid / k;
+      if (before == 0) sslot[dl] = SlotEnt{e, less, same, 0};
+    }
+    n_act = __syncthreads_count(tid < TK && before == 0);
+    if (blockIdx.x == 0) {
+      const FusedPlan& P = g.plan;
+      if (tid < TK) {
+        P.pair_of_row[less + before] = tid;
+        P.topk_idx[tid] = e;
+        P.topk_w[tid] = sw[tid];
+      }
+      for (int s = tid; s < n_act + hs; s += 256) P.slots[s] = s < hs ? SlotEnt{0, TK, T, 1} : sslot[s - hs];
+      if (tid == 0) *P.n_slots = n_act + hs;
+    }
+  }
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int slot = item / wg_per_slot;
+    const int tile = (item % wg_per_slot) * rt_per_wg + wid / ksplit;
+    SlotInfo si;
+    if (slot < hs) {
+      si = SlotInfo{0, true, TK, T};
+    } else {
+      if (slot - hs >= n_act) break;  // items are in slot order
+      const SlotEnt se = sslot[slot - hs];
+      si = SlotInfo{se.e, false, se.row0, se.cnt};
+    }
+    dq_item<FMT, NT, true, ROLL>(a, si, tile, wid % ksplit, srow_token, sA, red);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// host side
+// ----------------------------------------------------------------------------
+
+namespace {
+
+template <int FMT, int NT, int NPL, bool ROLL>
+hipError_t launch_fz_gate_npl(const FzGateArgs& g, int items, size_t lds, hipStream_t s) {
+  const int grid = fused_grid(k_fz_gateup<FMT, NT, NPL, ROLL>, lds, items);
+  hipLaunchKernelGGL((k_fz_gateup<FMT, NT, NPL, ROLL>), dim3(grid), dim3(256), lds, s, g);
+  return hipGetLastError();
+}
+
+template <int FMT, int NT, bool ROLL>
+hipError_t launch_fz_gate(const FzGateArgs& g, int items, size_t lds, int E, hipStream_t s) {
+  if (E <= 256) return launch_fz_gate_npl<FMT, NT, 4, ROLL>(g, items, lds, s);
+  if (E <= 512) return launch_fz_gate_npl<FMT, NT, 8, ROLL>(g, items, lds, s);
+  return launch_fz_gate_npl<FMT, NT, 16, ROLL>(g, items, lds, s);
+}
+
+template <int FMT, bool ROLL>
+hipError_t launch_fz_gate_nt(const FzGateArgs& g, int nt, int items, size_t lds, int E, hipStream_t s) {
+  if (nt == 1) return launch_fz_gate<FMT, 1, ROLL>(g, items, lds, E, s);
+  if (nt == 2) return launch_fz_gate<FMT, 2, ROLL>(g, items, lds, E, s);
+  return launch_fz_gate<FMT, 4, ROLL>(g, items, lds, E, s);
+}
+
+template <int FMT>
+hipError_t launch_fz_gate_fmt(const FzGateArgs& g, int items, int E, hipStream_t s) {
+  constexpr int CPT = cols_per_tile<FMT>();
+  const int K = g.a.mat[0].cols;
+  const int nt = pick_nt(CPT, g.a.T, K);
+  const size_t lds = (size_t)nt * CPT * K * 2;
+  if (dq_nsteps(FMT, K, g.a.ksplit) > dq_pd(FMT, true)) return launch_fz_gate_nt<FMT, true>(g, nt, items, lds, E, s);
+  return launch_fz_gate_nt<FMT, false>(g, nt, items, lds, E, s);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- fused step
+
+namespace {
+
+struct FusedWs {
+  float* hb[2];
+  uint16_t* x;  // bf16 layer input [T][d]
+  DecodeWs w;
+  float* logits;
+  FusedPlan plan;
+};
+
+FusedWs carve_fused(void* ws, int T, int d, int f, int k, int E) {
+  const size_t TK = (size_t)T * k;
+  char* p = (char*)ws;
+  FusedWs F;
+  F.hb[0] = (float*)p;
+  p += align_up((size_t)T * d * 4, 256);
+  F.hb[1] = (float*)p;
+  p += align_up((size_t)T * d * 4, 256);
+  F.x = (uint16_t*)p;
+  p += align_up((size_t)T * d * 2, 256);
+  F.w = carve(p, T, d, f, k, 1);
+  p += decode_ws_bytes(T, d, f, k, MOE_BF16);
+  F.logits = (float*)p;
+  p += align_up((size_t)T * E * 4, 256);
+  int32_t* ints = (int32_t*)p;
+  p += 256;
+  F.plan.n_slots = ints;
+  F.plan.error = ints + 1;
+  F.plan.pair_of_row = (int32_t*)p;
+  p += align_up(TK * 4, 256);
+  F.plan.topk_idx = (int32_t*)p;
+  p += align_up(TK * 4, 256);
+  F.plan.topk_w = (float*)p;
+  p += align_up(TK * 4, 256);
+  F.plan.slots = (SlotEnt*)p;
+  return F;
+}
+
+}  // namespace
+
+size_t fused_ws_bytes(int T, int d, int f, int k, int E) {
+  const size_t TK = (size_t)T * k;
+  return 2 * align_up((size_t)T * d * 4, 256) + align_up((size_t)T * d * 2, 256) +
+         decode_ws_bytes(T, d, f, k, MOE_BF16) + align_up((size_t)T * E * 4, 256) + 256 +
+         3 * align_up(TK * 4, 256) + align_up((TK + 1) * sizeof(SlotEnt), 256);
+}
+
+hipError_t launch_fused_step(const moe_layer* layers, int n_layers, float* h, int T, const FusedRecord& rec,
+                             void* ws, hipStream_t s) {
+  const moe_layer& L0 = layers[0];
+  const int d = L0.d, f = L0.f, k = L0.k, E = L0.E;
+  FusedWs F = carve_fused(ws, T, d, f, k, E);
+  const int max_slots = (T * k < E ? T * k : E) + (L0.has_shared ? 1 : 0);
+  const bool inline_glue = T == 1;
+  const float* prev_w = nullptr;  // topk weights of the previous layer
+  for (int l = 0; l < n_layers; ++l) {
+    const moe_layer& L = layers[l];
+    int32_t* err_word = rec.error ? rec.error + l : F.plan.error;
+    // (1) glue (previous layer's combine + residual + RMSNorm) and router
+    FzGlueArgs g{};
+    g.d = d;
+    g.T = T;
+    g.k = k;
+    g.has_shared = L.has_shared;
+    g.h_in = l == 0 ? h : F.hb[l & 1];
+    g.h_out = F.hb[(l + 1) & 1];
+    g.o = l == 0 ? nullptr : F.w.o;
+    g.topk_w = prev_w;
+    g.rec_y = (l > 0 && rec.y) ? rec.y + (size_t)(l - 1) * T * d : nullptr;
+    g.x_out = F.x;
+    g.rec_x = rec.x ? rec.x + (size_t)l * T * d : nullptr;
+    g.x16 = F.w.x16;
+    g.xs = F.w.xs;
+    g.gate_fmt = L.gate.type;
+    g.eps = rec.eps;
+    g.error_reset = err_word;
+    FzRouteArgs ra{};
+    ra.g = g;
+    ra.Wr = L.router_w;
+    ra.bias = L.router_bias;
+    ra.E = E;
+    ra.x = F.x;
+    ra.logits = rec.logits ? rec.logits + (size_t)l * T * E : F.logits;
+    if (inline_glue) {
+      constexpr int epw = route_experts_per_wg<true>();
+      hipLaunchKernelGGL(k_fz_route<true>, dim3((E + epw - 1) / epw), dim3(256), 0, s, ra);
+    } else {
+      constexpr int epw = route_experts_per_wg<false>();
+      hipLaunchKernelGGL(k_fz_glue, dim3(T), dim3(256), 0, s, g);
+      hipLaunchKernelGGL(k_fz_route<false>, dim3((E + epw - 1) / epw), dim3(256), 0, s, ra);
+    }
+    // (2) top-k + plan + gate/up
+    FzGateArgs ga{};
+    ga.a = gateup_args(L, T, 1, F.w);
+    ga.a.error = err_word;
+    ga.logits = ra.logits;
+    ga.E = E;
+    ga.plan = F.plan;
+    ga.plan.error = err_word;
+    if (rec.topk_idx) ga.plan.topk_idx = rec.topk_idx + (size_t)l * T * k;
+    if (rec.topk_w) ga.plan.topk_w = rec.topk_w + (size_t)l * T * k;
+    prev_w = ga.plan.topk_w;
+    {
+      const int wg_per_slot = (f / 16) / (4 / ga.a.ksplit);
+      const int items = max_slots * wg_per_slot;
+      if (rec.events) (void)hipEventRecord(rec.events[2 * l], s);
+      hipError_t err;
+      switch (L.gate.type) {
+        case MOE_Q8_0: err = launch_fz_gate_fmt<MOE_Q8_0>(ga, items, E, s); break;
+        case MOE_IQ4_NL: err = launch_fz_gate_fmt<MOE_IQ4_NL>(ga, items, E, s); break;
+        default: err = launch_fz_gate_fmt<MOE_NVFP4>(ga, items, E, s); break;
+      }
+      if (err != hipSuccess) return err;
+      if (rec.events) (void)hipEventRecord(rec.events[2 * l + 1], s);
+    }
+    // (3) down over the slot table, rows written at their pair's position
+    {
+      DecodeArgs da = down_args(L, T, F.w);
+      da.slots = F.plan.slots;
+      da.n_slots = F.plan.n_slots;
+      da.pair_of_row = F.plan.pair_of_row;
+      da.error = err_word;
+      const int items = max_slots * ((d / 16) / 4);
+      const hipError_t err = launch_dq_down_table(da, L.down.type, items, s);
+      if (err != hipSuccess) return err;
+    }
+  }
+  // the last layer's combine, folded into h
+  FzGlueArgs fg{};
+  fg.d = d;
+  fg.T = T;
+  fg.k = k;
+  fg.has_shared = layers[n_layers - 1].has_shared;
+  fg.h_in = F.hb[n_layers & 1];
+  fg.h_out = h;
+  fg.o = F.w.o;
+  fg.topk_w = prev_w;
+  fg.rec_y = rec.y ? rec.y + (size_t)(n_layers - 1) * T * d : nullptr;
+  fg.eps = rec.eps;
+  hipLaunchKernelGGL(k_fz_glue, dim3(T), dim3(256), 0, s, fg);
+  return hipGetLastError();
+}
+
+}  // namespace qre

@@ -75,7 +75,11 @@ hipError_t launch_decode_stage(int stage, const FfnCall& c, hipStream_t s);
 size_t prefill_ws_bytes(int T, int d, int f, int k);
 hipError_t launch_prefill_stage(int stage, const FfnCall& c, hipStream_t s);
 
-// Fused decode step over a stack of layers (moe_decode.hip).  Optional
+// Down pass of the fused decode step over its slot table (moe_decode.hip).
+struct DecodeArgs;
+hipError_t launch_dq_down_table(const DecodeArgs& a, int fmt, int items, hipStream_t s);
+
+// Fused decode step over a stack of layers (moe_fused.hip).  Optional
 // per-layer records (null to skip).
 constexpr int kFusedMaxT = 8;
 struct FusedRecord {

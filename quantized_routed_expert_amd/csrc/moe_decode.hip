@@ -14,7 +14,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
     const DecodeArgs a) {
   constexpr int NMAT = GATEUP ? 2 : 1;
   __shared__ f32x4 red[4 * NMAT * NT * 64];
-  extern __shared__ f16 sA[];  // [CPP][K] activations of the current column pass
+  extern __shared__ __align__(16) f16 sA[];  // [CPP][K] activations of the current column pass
 
   const int wid = threadIdx.x >> 6;
   const int ksplit = a.ksplit;

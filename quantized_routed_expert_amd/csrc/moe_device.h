@@ -217,62 +217,126 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // ---------------------------------------------------------------- top-k keys
 
-// 64-bit key whose unsigned order is "larger logit first, then lower expert
-// id": the logit's bits mapped to an order-preserving unsigned integer (-0 and
-// +0 compare equal), above the complement of the expert id.
-__device__ __forceinline__ uint64_t topk_key(float v, uint32_t e) {
+// 32-bit key whose unsigned order is the logit order: the logit's bits mapped
+// to an order-preserving unsigned integer, -0 and +0 equal.  Every real value
+// maps above 1; NaN maps to 1 (ranked below every real value, as a sort that
+// puts NaN last does); 0 marks an empty or taken entry.
+__device__ __forceinline__ uint32_t topk_key32(float v) {
   uint32_t u = __float_as_uint(v);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 1u;  // NaN
   if ((u & 0x7fffffffu) == 0u) u = 0u;
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint64_t)(0xffffffffu - e);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ float topk_key_value(uint64_t key) {
-  const uint32_t u = (uint32_t)(key >> 32);
-  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
-}
-__device__ __forceinline__ uint32_t topk_key_index(uint64_t key) { return 0xffffffffu - (uint32_t)key; }
-
-__device__ __forceinline__ uint64_t u64_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = u64_max(v, dpp_u64<kDppShr1, 0xf>(v));
-  v = u64_max(v, dpp_u64<kDppShr2, 0xf>(v));
-  v = u64_max(v, dpp_u64<kDppShr4, 0xf>(v));
-  v = u64_max(v, dpp_u64<kDppShr8, 0xf>(v));
-  v = u64_max(v, dpp_u64<kDppBcast15, 0xa>(v));
-  v = u64_max(v, dpp_u64<kDppBcast31, 0xc>(v));
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
-  return ((uint64_t)hi << 32) | lo;
+__device__ __forceinline__ float topk_key32_value(uint32_t key) {
+  if (key == 1u) return __uint_as_float(0x7fc00000u);
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
-// Top-k of one token's logits L[0..E) with one wavefront (E <= 64 * NPL):
-// lane j < k receives slot j's expert id and logit.  Branch-free: each round
-// takes the wave-wide largest key and clears it in its owner lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<kDppShr1, 0xf>(v));
+  v = max(v, dpp_u32<kDppShr2, 0xf>(v));
+  v = max(v, dpp_u32<kDppShr4, 0xf>(v));
+  v = max(v, dpp_u32<kDppShr8, 0xf>(v));
+  v = max(v, dpp_u32<kDppBcast15, 0xa>(v));
+  v = max(v, dpp_u32<kDppBcast31, 0xc>(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Top-k of one token's logits L[0..E) with one wavefront (E <= 64 * NPL,
+// 1 <= k <= min(E, 64)).  Slot j < k of the result is written to out_idx[j]
+// (expert id) and out_val[j] (logit): descending logit, the lower expert id
+// first on ties.
+//
+// A threshold first: the lanes are split into at least k groups and tau is
+// the smallest group maximum.  Those group maxima are at least k distinct
+// entries no smaller than tau, so the k-th largest entry, and every selected
+// one, is >= tau.  The entries >= tau (a few dozen for real logits) are packed
+// in index order into sk/si (per-wave LDS scratch of 64 entries each) and each
+// one's slot is its rank: the entries above it plus the equal ones with a
+// lower index.  If more than 64 entries pass the threshold (heavy ties), the
+// slots are taken one wave-wide maximum at a time instead.
 template <int NPL>
-__device__ __forceinline__ void wave_topk(const float* __restrict__ L, int E, int k, int lane, int& sel_idx,
-                                          float& sel_val) {
-  uint64_t key[NPL];
+__device__ __forceinline__ void wave_topk(const float* __restrict__ L, int E, int k, int lane, uint32_t* sk,
+                                          int32_t* si, int32_t* out_idx, float* out_val) {
+  uint32_t key[NPL];
   float lv[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) lv[i] = L[min(lane + 64 * i, E - 1)];  // unconditional loads, all in flight
 #pragma unroll
+  for (int i = 0; i < NPL; ++i) key[i] = (lane + 64 * i < E) ? topk_key32(lv[i]) : 0u;
+
+  // ---- threshold: the smallest of the group maxima (groups of g lanes, 64/g >= k groups)
+  uint32_t gm = key[0];
+#pragma unroll
+  for (int i = 1; i < NPL; ++i) gm = max(gm, key[i]);
+  int ng = 1;
+  while (ng < k) ng <<= 1;
+  const int g = 64 / ng;
+  if (g >= 2) gm = max(gm, dpp_u32<kDppShr1, 0xf>(gm));
+  if (g >= 4) gm = max(gm, dpp_u32<kDppShr2, 0xf>(gm));
+  if (g >= 8) gm = max(gm, dpp_u32<kDppShr4, 0xf>(gm));
+  if (g >= 16) gm = max(gm, dpp_u32<kDppShr8, 0xf>(gm));
+  if (g >= 32) gm = max(gm, dpp_u32<kDppBcast15, 0xa>(gm));
+  if (g >= 64) gm = max(gm, dpp_u32<kDppBcast31, 0xc>(gm));
+  const bool rep = (lane & (g - 1)) == g - 1;  // this lane holds its group's maximum
+  const uint32_t tau = ~wave_max_u32(rep ? ~gm : 0u);
+
+  // ---- the entries >= tau, packed in index order (register i, then lane)
+  int C = 0;
+#pragma unroll
   for (int i = 0; i < NPL; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = (e < E) ? topk_key(lv[i], (uint32_t)e) : 0ull;
+    const bool c = key[i] != 0u && key[i] >= tau;
+    const uint64_t mk = __ballot(c);
+    const int pos = C + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+    if (c && pos < 64) {
+      sk[pos] = key[i];
+      si[pos] = lane + 64 * i;
+    }
+    C += __popcll(mk);
   }
-  sel_idx = 0;
-  sel_val = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    uint64_t m = key[0];
+
+  if (C <= 64) {
+    // ---- slot = rank among the candidates
+    uint32_t kl = 0u;
+    int il = 0;
+    if (lane < C) {
+      kl = sk[lane];
+      il = si[lane];
+    }
+    int rank = 0;
+#pragma unroll 4
+    for (int j = 0; j < C; ++j) {
+      const uint32_t kj = sk[j];
+      rank += (kj > kl) ? 1 : 0;
+      rank += (kj == kl && j < lane) ? 1 : 0;
+    }
+    if (lane < C && rank < k) {
+      out_idx[rank] = il;
+      out_val[rank] = topk_key32_value(kl);
+    }
+    return;
+  }
+
+  // ---- many equal entries: one wave-wide maximum per round, all its holders in index order
+  int c = 0;
+  while (c < k) {
+    uint32_t m = key[0];
 #pragma unroll
-    for (int i = 1; i < NPL; ++i) m = key[i] > m ? key[i] : m;
-    m = wave_max_u64(m);
+    for (int i = 1; i < NPL; ++i) m = max(m, key[i]);
+    m = wave_max_u32(m);
+    if (m == 0u) break;  // fewer than k entries (excluded by the callers' k <= E)
+    const float v = topk_key32_value(m);
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) key[i] = key[i] == m ? 0ull : key[i];
-    if (lane == j) {
-      sel_idx = (int)topk_key_index(m);
-      sel_val = topk_key_value(m);
+    for (int i = 0; i < NPL; ++i) {
+      const bool hit = key[i] == m;
+      const uint64_t mk = __ballot(hit);
+      const int pos = c + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+      if (hit && pos < k) {
+        out_idx[pos] = lane + 64 * i;
+        out_val[pos] = v;
+      }
+      c += __popcll(mk);
+      key[i] = hit ? 0u : key[i];
     }
   }
 }

@@ -6,6 +6,8 @@
 // "grouped kernels", UD-IQ2_XS (L4 fix) page, "What was changed").
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "moe_dq.h"
 
 namespace qre {
@@ -289,9 +291,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   __shared__ __align__(16) int32_t sidx[kFusedTK];
   __shared__ float sw[kFusedTK];
   __shared__ __align__(16) int32_t sfirst[kFusedTK];
+  __shared__ uint32_t tk_key[4][64];  // top-k scratch, one row per wavefront
+  __shared__ int32_t tk_idx[4][64];
   __shared__ int32_t srow_token[kFusedTK];
   __shared__ SlotEnt sslot[kFusedTK];
-  extern __shared__ f16 sA[];
+  extern __shared__ __align__(16) f16 sA[];
 
   const DecodeArgs& a = g.a;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -310,20 +314,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   const int last_item = blockIdx.x + ((n_items - 1 - (int)blockIdx.x) / (int)gridDim.x) * (int)gridDim.x;
   int n_act = 0;
   if (blockIdx.x == 0 || last_item >= hs * wg_per_slot) {
-    // ---- top-k per token (one wavefront per token), renormalised weights
+    // ---- every token's logits into LDS (the activation buffer, unused until
+    // the item loop) with all loads in flight together
+    float* slog = (float*)sA;
+    if (((uintptr_t)g.logits & 15) != 0) {
+      // (a per-layer record slice that is not 16-byte aligned: scalar loads)
+      for (int c0 = tid; c0 < T * E; c0 += 8 * 256) {
+        float lv1[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) lv1[b] = g.logits[min(c0 + b * 256, T * E - 1)];
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+          if (c0 + b * 256 < T * E) slog[c0 + b * 256] = lv1[b];
+      }
+    } else {
+      const int n4 = (T * E) >> 2;
+      for (int c0 = tid; c0 < n4; c0 += 8 * 256) {
+        f32x4 lv4[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) lv4[b] = *(const f32x4*)(g.logits + 4 * min(c0 + b * 256, n4 - 1));
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+          if (c0 + b * 256 < n4) *(f32x4*)&slog[4 * (c0 + b * 256)] = lv4[b];
+      }
+      const int tail = 4 * n4 + tid;
+      if (tail < T * E) slog[tail] = g.logits[tail];
+    }
     sidx[tid] = 0x7fffffff;  // padding of the pair list
     __syncthreads();
+    // ---- top-k per token (one wavefront per token), renormalised weights
     for (int t = wid; t < T; t += 4) {
-      int ix;
-      float lv;
-      wave_topk<NPL>(g.logits + (long)t * E, E, k, lane, ix, lv);
-      const float vmax = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(lv), 0));
-      const float ex = lane < k ? expf(lv - vmax) : 0.0f;
+      wave_topk<NPL>(slog + t * E, E, k, lane, tk_key[wid], tk_idx[wid], sidx + t * k, sw + t * k);
+      // (the same wavefront reads back what it wrote: its LDS accesses are in order)
+      const float v = lane < k ? sw[t * k + lane] : 0.0f;
+      const float vmax = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 0));
+      const float ex = lane < k ? expf(v - vmax) : 0.0f;
       const float sum = wave_sum(ex);
-      if (lane < k) {
-        sidx[t * k + lane] = ix;
-        sw[t * k + lane] = ex / sum;
-      }
+      if (lane < k) sw[t * k + lane] = ex / sum;
     }
     __syncthreads();
     // ---- plan: pair p (thread p) counts the pairs of smaller experts (its
@@ -336,6 +363,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
     int e = 0, less = 0, before = 0, same = 0;
     if (tid < TK) {
       e = sidx[tid];
+#pragma unroll 4
       for (int q0 = 0; q0 < TK4; q0 += 4) {
         const i32x4 eq = *(const i32x4*)&sidx[q0];
 #pragma unroll
@@ -350,6 +378,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
     __syncthreads();
     if (tid < TK) {
       int dl = 0;
+#pragma unroll 4
       for (int q0 = 0; q0 < TK4; q0 += 4) {
         const i32x4 fq = *(const i32x4*)&sfirst[q0];
 #pragma unroll
@@ -418,7 +447,8 @@ hipError_t launch_fz_gate_fmt(const FzGateArgs& g, int items, int E, hipStream_t
   constexpr int CPT = cols_per_tile<FMT>();
   const int K = g.a.mat[0].cols;
   const int nt = pick_nt(CPT, g.a.T, K);
-  const size_t lds = (size_t)nt * CPT * K * 2;
+  // the activation buffer also holds the logits while the plan is built
+  const size_t lds = std::max((size_t)nt * CPT * K * 2, (size_t)g.a.T * E * 4);
   if (dq_nsteps(FMT, K, g.a.ksplit) > dq_pd(FMT, true)) return launch_fz_gate_nt<FMT, true>(g, nt, items, lds, E, s);
   return launch_fz_gate_nt<FMT, false>(g, nt, items, lds, E, s);
 }

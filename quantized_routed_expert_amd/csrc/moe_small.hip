@@ -190,17 +190,21 @@ hipError_t launch_router_logits(const float* W, const float* b, const void* x, i
 template <int NPL>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
                                               int32_t* __restrict__ idx, float* __restrict__ w) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ uint32_t sk[4][64];
+  __shared__ int32_t si[4][64];
+  __shared__ int32_t oi[4][64];
+  __shared__ float ov[4][64];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wid;
   if (t >= T) return;
-  int si;
-  float sv;
-  wave_topk<NPL>(logits + (long)t * E, E, k, lane, si, sv);
-  const float vmax = __shfl(sv, 0, 64);
-  const float ex = lane < k ? expf(sv - vmax) : 0.0f;
+  wave_topk<NPL>(logits + (long)t * E, E, k, lane, sk[wid], si[wid], oi[wid], ov[wid]);
+  // (the same wavefront reads back what it wrote: its LDS accesses are in order)
+  const float v = lane < k ? ov[wid][lane] : 0.0f;
+  const float vmax = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 0));
+  const float ex = lane < k ? expf(v - vmax) : 0.0f;
   const float sum = wave_sum(ex);
   if (lane < k) {
-    idx[(long)t * k + lane] = si;
+    idx[(long)t * k + lane] = oi[wid][lane];
     w[(long)t * k + lane] = ex / sum;
   }
 }

@@ -64,6 +64,8 @@ CASES = [
     (("q8_0", "q8_0", "q8_0"), 5, 4096, 256, 600, 6, False),
     (("nvfp4", "nvfp4", "nvfp4"), 1, 3072, 256, 1024, 8, False),
     (("q8_0", "q8_0", "iq4_nl"), 2, 1024, 128, 16, 3, True),
+    # T * E not a multiple of 4: per-layer logit records are not 16-byte aligned
+    (("q8_0", "q8_0", "q8_0"), 3, 1024, 128, 21, 3, True),
 ]
 
 
@@ -86,6 +88,23 @@ def test_fused_full_size(name):
     layers, st = _make(wl, 2)
     stats = _check_fused(wl, layers, st, TOL_DECODE)
     _say(f"[fused {name}] {stats}")
+
+
+def test_fused_heavy_ties():
+    """A zero router: every logit equal, so each token takes experts 0..k-1."""
+    wl = synth.scaled(synth.WORKLOADS["verify"], d=1024, f=256, E=512, n_layers=2, T=3)
+    layers = [synth.make_layer(wl, l, DEV) for l in range(2)]
+    for L in layers:
+        L["router_w"].zero_()
+        L["router_b"].zero_()
+    st = FusedStack(layers, wl.T, record=True, device=DEV)
+    st.set_tokens(synth.make_tokens(wl, DEV))
+    st.step()
+    torch.cuda.synchronize()
+    idx = st.rec_idx.cpu().numpy()
+    assert np.array_equal(idx, np.broadcast_to(np.arange(wl.k), idx.shape))
+    assert np.allclose(st.rec_w.cpu().numpy(), 1.0 / wl.k, rtol=1e-6)
+    _check_fused(wl, layers, st, TOL_DECODE)
 
 
 def test_fused_repeatable_and_graph_replay():

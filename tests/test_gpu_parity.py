@@ -116,6 +116,33 @@ def test_router_topk_exact(T):
     assert np.allclose(wg, M.gate_weights(L32.astype(np.float64), gi), rtol=1e-5, atol=1e-7)
 
 
+@pytest.mark.parametrize("E,k", [(16, 2), (64, 8), (512, 8), (1000, 32)])
+def test_topk_heavy_ties(E, k):
+    """All-equal logits (a zero router) and a few equal maxima: lower ids first."""
+    _say(f"[ties] E={E} k={k}")
+    wl, layer = _small_layer(40 + E, E=E, k=k)
+    layer["router_w"].zero_()
+    layer["router_b"].zero_()
+    T = 3
+    layer["router_b"][E // 2] = 1.0   # token-independent: one clear winner ...
+    layer["router_b"][E - 1] = 0.5    # ... then two equal runners-up
+    layer["router_b"][1] = 0.5
+    x = torch.randn((T, wl.d), device=DEV).to(torch.bfloat16)
+    L = lib.layer_struct(layer)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    logits = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    wsb = lib.moe_workspace_size(L, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    lib.moe_route(L, x, lib.MOE_BF16, T, idx, w, logits, ws, wsb)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    want = M.topk(logits.cpu().numpy(), k)
+    assert np.array_equal(gi, want)
+    assert list(gi[0, :min(3, k)]) == [E // 2, 1, E - 1][:k]
+    assert np.allclose(w.cpu().numpy(), M.gate_weights(logits.cpu().numpy().astype(np.float64), gi), rtol=1e-5)
+
+
 # ---------------------------------------------------------------- plan
 
 @pytest.mark.parametrize("T,k,E,bad", [(1, 8, 512, False), (8, 8, 512, False), (64, 8, 512, False),

@@ -57,15 +57,18 @@ def source_digest(paths):
 
 
 DOMINANT = {
-    # workload -> (kernel family, sources it is built from)
-    "decode": ("k_fz_gateup (top-k + plan + gate/up + SwiGLU, IQ4_NL)",
-               ["quantized_routed_expert_amd/csrc/moe_decode.hip", "quantized_routed_expert_amd/csrc/moe_device.h"]),
-    "verify": ("k_fz_gateup (top-k + plan + gate/up + SwiGLU, IQ4_NL)",
-               ["quantized_routed_expert_amd/csrc/moe_decode.hip", "quantized_routed_expert_amd/csrc/moe_device.h"]),
-    "slots": ("k_ffn_dq gate/up (NVFP4)", ["quantized_routed_expert_amd/csrc/moe_decode.hip",
-                                           "quantized_routed_expert_amd/csrc/moe_device.h"]),
-    "prefill": ("k_pf_gemm gate/up (IQ4_NL)", ["quantized_routed_expert_amd/csrc/moe_prefill.hip",
-                                               "quantized_routed_expert_amd/csrc/moe_device.h"]),
+    # workload -> (kernel, pattern of its symbol in rocprofv3 output, sources it is built from)
+    "decode": ("k_fz_gateup (top-k + plan + gate/up + SwiGLU, IQ4_NL)", r"qre::k_fz_gateup<",
+               ["quantized_routed_expert_amd/csrc/moe_fused.hip", "quantized_routed_expert_amd/csrc/moe_dq.h",
+                "quantized_routed_expert_amd/csrc/moe_device.h"]),
+    "verify": ("k_fz_gateup (top-k + plan + gate/up + SwiGLU, IQ4_NL)", r"qre::k_fz_gateup<",
+               ["quantized_routed_expert_amd/csrc/moe_fused.hip", "quantized_routed_expert_amd/csrc/moe_dq.h",
+                "quantized_routed_expert_amd/csrc/moe_device.h"]),
+    "slots": ("k_ffn_dq gate/up (NVFP4)", r"qre::k_ffn_dq<3, \d, true",
+              ["quantized_routed_expert_amd/csrc/moe_decode.hip", "quantized_routed_expert_amd/csrc/moe_dq.h",
+               "quantized_routed_expert_amd/csrc/moe_device.h"]),
+    "prefill": ("k_pf_gemm gate/up (IQ4_NL)", r"qre::k_pf_gemm<2, true>",
+                ["quantized_routed_expert_amd/csrc/moe_prefill.hip", "quantized_routed_expert_amd/csrc/moe_device.h"]),
 }
 
 
@@ -225,7 +228,7 @@ def main():
     torch.cuda.synchronize()
     dur_ms = np.array([a.elapsed_time(b) for a, b in durations])
     avg_ms = float(dur_ms.mean())
-    kname, ksrc = DOMINANT[args.workload]
+    kname, _, ksrc = DOMINANT[args.workload]
     digest = source_digest(ksrc)
     if args.workload == "prefill":
         achieved = float(np.mean(launch_flops)) / (avg_ms / 1e3) / 1e12

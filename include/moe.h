@@ -199,9 +199,9 @@ typedef struct moe_stack_record {
   void* x;            /* [n_layers][T][d] bf16 layer inputs */
   float* y;           /* [n_layers][T][d] fp32 layer outputs */
   int32_t* error;     /* [n_layers] plan / overflow flags of each layer (bits as moe_plan_buf.error) */
-  void** events;      /* [n_layers][2] hipEvent_t handles (created by the caller), recorded on the
-                         call's stream right before and after each layer's gate/up launch; for
-                         timing that kernel in eager (not graph-captured) calls */
+  void** events;      /* [n_layers][2] hipEvent_t handles (created by the caller), attached to each
+                         layer's gate/up launch so that they carry that kernel's start and end; for
+                         timing the kernel in eager (not graph-captured) calls */
 } moe_stack_record;
 
 /* Fused decode step through a stack of routed-expert layers for T <= 8

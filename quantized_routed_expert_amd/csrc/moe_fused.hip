@@ -4,6 +4,7 @@
 // and the plan are recomputed in each gate/up workgroup's LDS so that no
 // launch waits on a separate plan kernel (the "device-planned MoE tail" with
 // "grouped kernels", UD-IQ2_XS (L4 fix) page, "What was changed").
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -421,36 +422,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
 
 namespace {
 
+// With timing events, the kernel is launched with them attached (they then
+// carry the kernel's own start and end, as a profiler's kernel trace does).
 template <int FMT, int NT, int NPL, bool ROLL>
-hipError_t launch_fz_gate_npl(const FzGateArgs& g, int items, size_t lds, hipStream_t s) {
+hipError_t launch_fz_gate_npl(const FzGateArgs& g, int items, size_t lds, hipStream_t s, hipEvent_t e0,
+                              hipEvent_t e1) {
   const int grid = fused_grid(k_fz_gateup<FMT, NT, NPL, ROLL>, lds, items);
-  hipLaunchKernelGGL((k_fz_gateup<FMT, NT, NPL, ROLL>), dim3(grid), dim3(256), lds, s, g);
+  if (e0)
+    hipExtLaunchKernelGGL((k_fz_gateup<FMT, NT, NPL, ROLL>), dim3(grid), dim3(256), (uint32_t)lds, s, e0, e1, 0, g);
+  else
+    hipLaunchKernelGGL((k_fz_gateup<FMT, NT, NPL, ROLL>), dim3(grid), dim3(256), lds, s, g);
   return hipGetLastError();
 }
 
 template <int FMT, int NT, bool ROLL>
-hipError_t launch_fz_gate(const FzGateArgs& g, int items, size_t lds, int E, hipStream_t s) {
-  if (E <= 256) return launch_fz_gate_npl<FMT, NT, 4, ROLL>(g, items, lds, s);
-  if (E <= 512) return launch_fz_gate_npl<FMT, NT, 8, ROLL>(g, items, lds, s);
-  return launch_fz_gate_npl<FMT, NT, 16, ROLL>(g, items, lds, s);
+hipError_t launch_fz_gate(const FzGateArgs& g, int items, size_t lds, int E, hipStream_t s, hipEvent_t e0,
+                          hipEvent_t e1) {
+  if (E <= 256) return launch_fz_gate_npl<FMT, NT, 4, ROLL>(g, items, lds, s, e0, e1);
+  if (E <= 512) return launch_fz_gate_npl<FMT, NT, 8, ROLL>(g, items, lds, s, e0, e1);
+  return launch_fz_gate_npl<FMT, NT, 16, ROLL>(g, items, lds, s, e0, e1);
 }
 
 template <int FMT, bool ROLL>
-hipError_t launch_fz_gate_nt(const FzGateArgs& g, int nt, int items, size_t lds, int E, hipStream_t s) {
-  if (nt == 1) return launch_fz_gate<FMT, 1, ROLL>(g, items, lds, E, s);
-  if (nt == 2) return launch_fz_gate<FMT, 2, ROLL>(g, items, lds, E, s);
-  return launch_fz_gate<FMT, 4, ROLL>(g, items, lds, E, s);
+hipError_t launch_fz_gate_nt(const FzGateArgs& g, int nt, int items, size_t lds, int E, hipStream_t s,
+                             hipEvent_t e0, hipEvent_t e1) {
+  if (nt == 1) return launch_fz_gate<FMT, 1, ROLL>(g, items, lds, E, s, e0, e1);
+  if (nt == 2) return launch_fz_gate<FMT, 2, ROLL>(g, items, lds, E, s, e0, e1);
+  return launch_fz_gate<FMT, 4, ROLL>(g, items, lds, E, s, e0, e1);
 }
 
 template <int FMT>
-hipError_t launch_fz_gate_fmt(const FzGateArgs& g, int items, int E, hipStream_t s) {
+hipError_t launch_fz_gate_fmt(const FzGateArgs& g, int items, int E, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   constexpr int CPT = cols_per_tile<FMT>();
   const int K = g.a.mat[0].cols;
   const int nt = pick_nt(CPT, g.a.T, K);
   // the activation buffer also holds the logits while the plan is built
   const size_t lds = std::max((size_t)nt * CPT * K * 2, (size_t)g.a.T * E * 4);
-  if (dq_nsteps(FMT, K, g.a.ksplit) > dq_pd(FMT, true)) return launch_fz_gate_nt<FMT, true>(g, nt, items, lds, E, s);
-  return launch_fz_gate_nt<FMT, false>(g, nt, items, lds, E, s);
+  if (dq_nsteps(FMT, K, g.a.ksplit) > dq_pd(FMT, true))
+    return launch_fz_gate_nt<FMT, true>(g, nt, items, lds, E, s, e0, e1);
+  return launch_fz_gate_nt<FMT, false>(g, nt, items, lds, E, s, e0, e1);
 }
 
 }  // namespace
@@ -562,15 +572,14 @@ hipError_t launch_fused_step(const moe_layer* layers, int n_layers, float* h, in
     {
       const int wg_per_slot = (f / 16) / (4 / ga.a.ksplit);
       const int items = max_slots * wg_per_slot;
-      if (rec.events) (void)hipEventRecord(rec.events[2 * l], s);
+      hipEvent_t e0 = rec.events ? rec.events[2 * l] : nullptr, e1 = rec.events ? rec.events[2 * l + 1] : nullptr;
       hipError_t err;
       switch (L.gate.type) {
-        case MOE_Q8_0: err = launch_fz_gate_fmt<MOE_Q8_0>(ga, items, E, s); break;
-        case MOE_IQ4_NL: err = launch_fz_gate_fmt<MOE_IQ4_NL>(ga, items, E, s); break;
-        default: err = launch_fz_gate_fmt<MOE_NVFP4>(ga, items, E, s); break;
+        case MOE_Q8_0: err = launch_fz_gate_fmt<MOE_Q8_0>(ga, items, E, s, e0, e1); break;
+        case MOE_IQ4_NL: err = launch_fz_gate_fmt<MOE_IQ4_NL>(ga, items, E, s, e0, e1); break;
+        default: err = launch_fz_gate_fmt<MOE_NVFP4>(ga, items, E, s, e0, e1); break;
       }
       if (err != hipSuccess) return err;
-      if (rec.events) (void)hipEventRecord(rec.events[2 * l + 1], s);
     }
     // (3) down over the slot table, rows written at their pair's position
     {

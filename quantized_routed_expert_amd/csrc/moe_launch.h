@@ -89,7 +89,7 @@ struct FusedRecord {
   uint16_t* x;        // [L][T][d] bf16 layer inputs
   float* y;           // [L][T][d] layer outputs
   int32_t* error;     // [L] plan / overflow flags
-  hipEvent_t* events; // [L][2] recorded around each layer's gate/up launch
+  hipEvent_t* events; // [L][2] attached to each layer's gate/up launch (its start and end)
   float eps;
 };
 size_t fused_ws_bytes(int T, int d, int f, int k, int E);

@@ -149,8 +149,9 @@ moe_status moe_plan(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
  * decode path runs: exact dequantisation, fp32 accumulation (activations are
  * carried as fp16 hi/lo pairs, intermediate SwiGLU values must stay below
  * 65504 in magnitude; error bit 2 reports otherwise).  For T > 64 the prefill
- * path runs: weights are rounded to bf16 (RNE of the exact value) in LDS,
- * SwiGLU activations are rounded to bf16, bf16 MFMA with fp32 accumulation.
+ * path runs: weights are rounded to bf16 (RNE of the exact value) in
+ * registers, fp32 tokens and SwiGLU activations are rounded to bf16, bf16
+ * MFMA with fp32 accumulation.
  * The combine never uses atomics: results are bitwise reproducible. */
 moe_status moe_ffn_forward(const moe_layer* layer, const void* x, int32_t x_dtype, int32_t T,
                            const float* topk_w, const moe_plan_buf* plan,

@@ -8,14 +8,14 @@
 // "grouped kernels", UD-IQ2_XS (L4 fix) page, "What was changed").
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "moe_device.h"
 #include "moe_launch.h"
 
 namespace qre {
 
 constexpr int kBM = 128;   // plan rows per tile
-constexpr int kBK = 64;    // K per LDS stage (two quant blocks)
-constexpr int kLdsK = kBK + 8;  // padded LDS row (bf16 elements)
 
 struct PrefillArgs {
   QMatDev mat[2];
@@ -68,54 +68,6 @@ __global__ __launch_bounds__(1024) void k_pf_tiles(const int32_t* __restrict__ o
   }
 }
 
-// Dequantise 32 elements (one 32-element group of a row) to bf16 (RNE of the
-// exact value) and store them to LDS as 16 packed dwords.
-template <int FMT>
-__device__ __forceinline__ void dequant32_to_lds(const uint8_t* crow, const uint8_t* srow, float ts, int k0,
-                                                 uint32_t* dst) {
-  float v[32];
-  if constexpr (FMT == MOE_IQ4_NL) {
-    const u32x4 c = *(const u32x4*)(crow + (k0 >> 1));
-    const float d = f16_bits_to_f32(((const uint16_t*)srow)[k0 >> 5]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f16x8 q = iq4_dword_to_f16x8(c[i]);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        v[4 * i + t] = (float)q[t] * d;
-        v[16 + 4 * i + t] = (float)q[4 + t] * d;
-      }
-    }
-  } else if constexpr (FMT == MOE_Q8_0) {
-    const u32x4 c0 = *(const u32x4*)(crow + k0);
-    const u32x4 c1 = *(const u32x4*)(crow + k0 + 16);
-    const float d = f16_bits_to_f32(((const uint16_t*)srow)[k0 >> 5]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        v[4 * i + b] = (float)(int8_t)((c0[i] >> (8 * b)) & 0xffu) * d;
-        v[16 + 4 * i + b] = (float)(int8_t)((c1[i] >> (8 * b)) & 0xffu) * d;
-      }
-    }
-  } else {
-    const u32x4 c = *(const u32x4*)(crow + (k0 >> 1));
-    const uint32_t sraw = ((const uint16_t*)srow)[k0 >> 5];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const f16 sb = (f16)e4m3_to_f32((sraw >> (8 * h)) & 0xffu);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const f16x8 q = fp4_dword_to_f16x8(c[2 * h + i], sb);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) v[16 * h + 8 * i + t] = (float)q[t] * ts;
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 16; ++j) dst[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
-}
-
 __device__ __forceinline__ int find_slot(const int32_t* mstart, int n_slots, int mt) {
   int lo = 0, hi = n_slots - 1;
   while (lo < hi) {
@@ -125,25 +77,124 @@ __device__ __forceinline__ int find_slot(const int32_t* mstart, int n_slots, int
   return lo;
 }
 
-// GATEUP: N-tile = 64 gate rows + the same 64 up rows; waves split M (32 rows each).
-// DOWN:   N-tile = 128 output rows; waves split M.
-template <int FMT, bool GATEUP>
-__global__ __launch_bounds__(256) void k_pf_gemm(const PrefillArgs a) {
-  constexpr int BN = 128;  // weight rows staged per tile (gate/up: 64 + 64)
-  __shared__ uint32_t sA[kBM * kLdsK / 2];
-  __shared__ uint32_t sB[BN * kLdsK / 2];
+// ----------------------------------------------------------------------------
+// Grouped GEMM tile: 128 plan rows (M) x 64 * NF weight rows (N), K in
+// stages of 128.
+//
+// Activations (A operand of v_mfma_f32_16x16x32_bf16, bf16) are copied
+// global -> LDS by 16-byte LDS-DMA loads (no registers), double-buffered: the
+// next stage's copies are in flight while the current stage computes.  The
+// LDS tile is [128 rows][16 chunks of 8 elements], chunk c of row r stored at
+// c ^ (r & 15) so that the 16 rows a fragment read touches fall in distinct
+// banks; each lane of a copy picks the source chunk that lands at its LDS slot.
+//
+// Weights (B operand) never pass through LDS: lane (n, G) of a wavefront loads,
+// for each of its NF row fragments, the codes of quant block G of the stage
+// (row n of the fragment) and decodes them in registers to bf16 = RNE(exact
+// value); MFMA i of the stage takes elements 8i .. 8i+7 of each lane group's
+// block, and the A fragment reads the matching activation chunk.  One MFMA
+// thus reduces over four blocks; the K order of a sum is immaterial to the
+// GEMM, so this is the plain product with exactly the oracle's bf16 weights.
+//
+// Eight wavefronts (two per SIMD, so that one's decode and LDS reads overlap
+// the other's MFMAs) each hold all 128 M rows and NF weight-row fragments:
+// GATEUP: wave w holds f-rows [16w, 16w+16) of the tile's 128, as a gate and
+//         an up fragment (NF = 2), so SwiGLU is formed in registers.
+// DOWN:   wave w holds 16 * NF consecutive d-rows.
+// ----------------------------------------------------------------------------
+constexpr int kPfBK = 128;                       // K per stage
+constexpr int kPfMF = kBM / 16;                  // M fragments
+constexpr int kPfBuf = kBM * kPfBK * 2;          // bytes of one activation buffer
+constexpr int kXcds = 8;                         // accelerator complex dies of an MI355X
+constexpr int kPfWaves = 8;                      // wavefronts per workgroup (two per SIMD)
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kPfCopies = kBM * kPfBK * 2 / (16 * kPfThreads);  // 16-byte copies per thread per stage
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Code bytes of one lane's block-sized chunk per stage: IQ4_NL / NVFP4 16 (32
+// elements), Q8_0 32.
+template <int FMT>
+struct PfCodes {
+  u32x4 c[FMT == MOE_Q8_0 ? 2 : 1];
+  uint32_t sc;  // fp16 block scale, or two E4M3 scales (NVFP4)
+};
+
+template <int FMT>
+__device__ __forceinline__ void pf_load_codes(const uint8_t* crow, const uint8_t* srow, int kel, PfCodes<FMT>& pc) {
+  if constexpr (FMT == MOE_Q8_0) {
+    pc.c[0] = *(const u32x4*)(crow + kel);
+    pc.c[1] = *(const u32x4*)(crow + kel + 16);
+  } else {
+    pc.c[0] = *(const u32x4*)(crow + (kel >> 1));
+  }
+  pc.sc = ((const uint16_t*)srow)[kel >> 5];
+}
+
+// Four biased bytes u (= value + 128) times scale d, rounded once to bf16: the
+// products (u - 128) * d are exact in fp32 (at most 19 significant bits), so
+// fma(u, d, -128 d) is exact and the bf16 rounding is the only one.
+__device__ __forceinline__ u32x2 pf_biased4_to_bf16(uint32_t u, float d) {
+  const float nd = -128.0f * d;
+  const float v0 = fmaf((float)(u & 0xffu), d, nd);
+  const float v1 = fmaf((float)((u >> 8) & 0xffu), d, nd);
+  const float v2 = fmaf((float)((u >> 16) & 0xffu), d, nd);
+  const float v3 = fmaf((float)(u >> 24), d, nd);
+  return u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+}
+
+// bf16 weights of MFMA i: elements 8i .. 8i+7 of the lane's 32-element chunk,
+// in natural order.
+template <int FMT>
+__device__ __forceinline__ bf16x8 pf_decode(const PfCodes<FMT>& pc, int i, float ts) {
+  if constexpr (FMT == MOE_IQ4_NL) {
+    // elements 0..15 are the low nibbles of bytes 0..15, elements 16..31 the high ones
+    const uint32_t w0 = pc.c[0][2 * (i & 1)], w1 = pc.c[0][2 * (i & 1) + 1];
+    const int sh = (i >> 1) * 4;
+    const float d = f16_bits_to_f32(pc.sc);
+    const u32x2 a = pf_biased4_to_bf16(iq4_lookup4((w0 >> sh) & 0x0F0F0F0Fu), d);
+    const u32x2 b = pf_biased4_to_bf16(iq4_lookup4((w1 >> sh) & 0x0F0F0F0Fu), d);
+    return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
+  } else if constexpr (FMT == MOE_Q8_0) {
+    const float d = f16_bits_to_f32(pc.sc);
+    const u32x2 a = pf_biased4_to_bf16(pc.c[i >> 1][2 * (i & 1)] ^ 0x80808080u, d);
+    const u32x2 b = pf_biased4_to_bf16(pc.c[i >> 1][2 * (i & 1) + 1] ^ 0x80808080u, d);
+    return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
+  } else {
+    // e2m1 * e4m3 is exact in fp16; times the tensor scale rounds once in fp32
+    const uint32_t sbyte = (i < 2) ? (pc.sc & 0xffu) : ((pc.sc >> 8) & 0xffu);
+    const f16x8 q = fp4_dword_to_f16x8(pc.c[0][i], (f16)e4m3_to_f32(sbyte));
+    u32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = pack_bf16x2((float)q[2 * j] * ts, (float)q[2 * j + 1] * ts);
+    return __builtin_bit_cast(bf16x8, r);
+  }
+}
+
+template <int FMT, bool GATEUP, int NF>
+__global__ __launch_bounds__(kPfThreads) void k_pf_gemm(const PrefillArgs a) {
+  extern __shared__ __align__(16) uint8_t sAbuf[];  // [2][kBM][16 chunks][16 B]
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int n = lane & 15, G = lane >> 4;
   const QMatDev& M0 = a.mat[0];
   const int rows = M0.rows, K = M0.cols;
-  const int n_ntiles = GATEUP ? rows / 64 : rows / BN;
+  const int n_ntiles = GATEUP ? rows / (kPfWaves * 8 * NF) : rows / (kPfWaves * 16 * NF);
   const int n_act = *a.n_active;
   const int n_slots = n_act + a.has_shared;
   const int total = a.mstart[n_slots] * n_ntiles;
   const int crb = code_row_bytes(FMT, K), srb = scale_row_bytes(FMT, K);
+  const int nstages = K / kPfBK;
+  const uint16_t* act = GATEUP ? (const uint16_t*)a.x : a.hin;  // bf16 [rows][K]
 
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+  // Workgroups are dealt to the XCDs round-robin by index; each XCD takes a
+  // contiguous run of items (the N-tiles of an M-tile, then the next M-tiles
+  // of the same expert) so that activations and weights are shared in its L2.
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int grid_per_xcd = (int)gridDim.x / kXcds;
+  const int xcd = blockIdx.x % kXcds, lane_in_xcd = blockIdx.x / kXcds;
+  for (int it = lane_in_xcd; it < per_xcd; it += grid_per_xcd) {
+    const int item = xcd * per_xcd + it;
+    if (item >= total) break;
     const int mt = item / n_ntiles, nt = item % n_ntiles;
     const int slot = find_slot(a.mstart, n_slots, mt);
     const bool is_sh = slot >= n_act;
@@ -159,136 +210,149 @@ __global__ __launch_bounds__(256) void k_pf_gemm(const PrefillArgs a) {
     }
     const int m0 = (mt - a.mstart[slot]) * kBM;  // first row of this tile within the slot
 
-    // ---- per-thread staging roles
-    // A: 128 rows x 64 elements = 1024 chunks of 8 elements; 4 per thread
-    // B: 128 weight rows x 2 groups of 32 elements; 1 per thread
-    const int brow = tid >> 1, bgrp = tid & 1;
-    const uint8_t* bcrow;
-    const uint8_t* bsrow;
-    float bts = 1.0f;
-    {
+    // ---- this lane's weight rows (one per fragment)
+    const uint8_t* bc[NF];
+    const uint8_t* bs[NF];
+    float ts[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
       int mi = 0, wr;
       if constexpr (GATEUP) {
-        mi = brow >> 6;
-        wr = nt * 64 + (brow & 63);
+        mi = f / (NF / 2);                                                // gate, then up
+        wr = nt * (kPfWaves * 8 * NF) + wid * (8 * NF) + (f % (NF / 2)) * 16 + n;   // same f-rows for both
       } else {
-        wr = nt * BN + brow;
+        wr = nt * (kPfWaves * 16 * NF) + wid * (16 * NF) + f * 16 + n;
       }
       const QMatDev& W = is_sh ? a.smat[mi] : a.mat[mi];
       const long rw = (long)e * rows + wr;
-      bcrow = W.codes + rw * crb;
-      bsrow = W.scales + rw * srb;
-      if (FMT == MOE_NVFP4) bts = W.ts[e];
+      bc[f] = W.codes + rw * crb;
+      bs[f] = W.scales + rw * srb;
+      ts[f] = (FMT == MOE_NVFP4) ? W.ts[e] : 1.0f;
     }
-    // A source rows for this thread's 4 chunks
-    long asrc[4];
-    bool aval[4];
+
+    // ---- activation copies: wave w, copy q covers LDS chunks (w*C+q)*64 + lane,
+    // i.e. tile row (w*C+q)*4 + lane/16, stored chunk lane%16 = logical chunk ^ (row%16).
+    int asrc[kPfCopies];   // element offset of the source row (rows past the slot's end copy its first row)
+    int acol[kPfCopies];   // element offset of the logical chunk
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int ch = tid + 256 * q;
-      const int r = ch >> 3;
+    for (int q = 0; q < kPfCopies; ++q) {
+      const int r = (wid * kPfCopies + q) * 4 + (lane >> 4);
       const int rr = m0 + r;
-      aval[q] = rr < cnt;
-      long src = 0;
-      if (aval[q]) {
-        if constexpr (GATEUP) {
-          const int t = is_sh ? rr : a.row_token[row0 + rr];
-          src = (long)t * K;
-        } else {
-          src = (long)(row0 + rr) * K;
-        }
+      const int rs = rr < cnt ? rr : 0;
+      if constexpr (GATEUP) {
+        const int t = is_sh ? rs : a.row_token[row0 + rs];
+        asrc[q] = t * K;
+      } else {
+        asrc[q] = (row0 + rs) * K;
       }
-      asrc[q] = src;
+      acol[q] = ((lane & 15) ^ (r & 15)) * 8;
     }
+    auto copy_a = [&](int s, int buf) {
+      uint8_t* base = sAbuf + buf * kPfBuf + (wid * kPfCopies) * 64 * 16;
+#pragma unroll
+      for (int q = 0; q < kPfCopies; ++q)
+        __builtin_amdgcn_global_load_lds((const void*)(act + asrc[q] + s * kPfBK + acol[q]),
+                                         (lds_void*)(base + q * 64 * 16), 16, 0, 0);
+    };
+    auto load_b = [&](int s, PfCodes<FMT> (&pc)[NF]) {
+#pragma unroll
+      for (int f = 0; f < NF; ++f) pf_load_codes<FMT>(bc[f], bs[f], s * kPfBK + 32 * G, pc[f]);
+    };
 
-    f32x4 acc[2][2][4];  // [matrix or N half][M sub-tile][N sub-tile]
+    f32x4 acc[kPfMF][NF];
 #pragma unroll
-    for (int x0 = 0; x0 < 2; ++x0)
+    for (int mi = 0; mi < kPfMF; ++mi)
 #pragma unroll
-      for (int x1 = 0; x1 < 2; ++x1)
-#pragma unroll
-        for (int x2 = 0; x2 < 4; ++x2) acc[x0][x1][x2] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int f = 0; f < NF; ++f) acc[mi][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int k0 = 0; k0 < K; k0 += kBK) {
-      // stage A
+    PfCodes<FMT> pc[NF], pn[NF];
+    copy_a(0, 0);
+    load_b(0, pc);
+    for (int s = 0; s < nstages; ++s) {
+      __builtin_amdgcn_s_waitcnt(0);  // this stage's copies and codes have landed
+      __syncthreads();                // ... for every wave; the other buffer is free
+      if (s + 1 < nstages) {
+        copy_a(s + 1, (s + 1) & 1);
+        load_b(s + 1, pn);
+      }
+      const uint8_t* sa = sAbuf + (s & 1) * kPfBuf;
+      // Software pipeline over the stage's four MFMA steps: step i+1's A
+      // fragments (LDS) and B fragments (decoded in registers) are produced
+      // while step i's MFMAs run; the scheduling groups below interleave one
+      // MFMA with a few VALU decode instructions and LDS reads.
+      auto read_a = [&](int i, bf16x8 (&af)[kPfMF]) {
+        const int c = 4 * G + i;  // logical chunk of MFMA step i
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int ch = tid + 256 * q;
-        const int r = ch >> 3, c8 = (ch & 7) * 8;
-        u32x4 v = {0, 0, 0, 0};
-        if (aval[q]) {
-          if constexpr (GATEUP) {
-            if (a.x_bf16) {
-              v = *(const u32x4*)((const uint16_t*)a.x + asrc[q] + k0 + c8);
-            } else {
-              const float* xf = (const float*)a.x + asrc[q] + k0 + c8;
-              const f32x4 f0 = *(const f32x4*)xf, f1 = *(const f32x4*)(xf + 4);
-              v = u32x4{pack_bf16x2(f0.x, f0.y), pack_bf16x2(f0.z, f0.w), pack_bf16x2(f1.x, f1.y),
-                        pack_bf16x2(f1.z, f1.w)};
-            }
-          } else {
-            v = *(const u32x4*)(a.hin + asrc[q] + k0 + c8);
+        for (int mi = 0; mi < kPfMF; ++mi)
+          af[mi] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sa + ((mi * 16 + n) * 16 + (c ^ n)) * 16));
+      };
+      bf16x8 afc[kPfMF], afn[kPfMF], bwc[NF], bwn[NF];
+      read_a(0, afc);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) bwc[f] = pf_decode<FMT>(pc[f], 0, ts[f]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < 3) {
+          read_a(i + 1, afn);
+#pragma unroll
+          for (int f = 0; f < NF; ++f) bwn[f] = pf_decode<FMT>(pc[f], i + 1, ts[f]);
+        }
+#pragma unroll
+        for (int mi = 0; mi < kPfMF; ++mi)
+#pragma unroll
+          for (int f = 0; f < NF; ++f)
+            acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afc[mi], bwc[f], acc[mi][f], 0, 0, 0);
+        if (i < 3) {
+#pragma unroll
+          for (int g = 0; g < kPfMF * NF; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // up to four VALU
+            if (g % 4 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
           }
-        }
-        *(u32x4*)&sA[(r * kLdsK + c8) / 2] = v;
-      }
-      // stage B (dequantise)
-      {
-        uint32_t tmp[16];
-        dequant32_to_lds<FMT>(bcrow, bsrow, bts, k0 + 32 * bgrp, tmp);
-        uint32_t* dst = &sB[(brow * kLdsK + 32 * bgrp) / 2];
 #pragma unroll
-        for (int j = 0; j < 16; j += 4) *(u32x4*)&dst[j] = u32x4{tmp[j], tmp[j + 1], tmp[j + 2], tmp[j + 3]};
-      }
-      __syncthreads();
+          for (int mi = 0; mi < kPfMF; ++mi) afc[mi] = afn[mi];
 #pragma unroll
-      for (int kk = 0; kk < kBK; kk += 32) {
-        bf16x8 af[2];
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
-          const int r = wid * 32 + mi * 16 + n;
-          af[mi] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sA[(r * kLdsK + kk + 8 * G) / 2]);
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-          for (int ni = 0; ni < 4; ++ni) {
-            const int br = h * 64 + ni * 16 + n;
-            const bf16x8 bfr = __builtin_bit_cast(bf16x8, *(const u32x4*)&sB[(br * kLdsK + kk + 8 * G) / 2]);
-#pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-              acc[h][mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mi], bfr, acc[h][mi][ni], 0, 0, 0);
-          }
+          for (int f = 0; f < NF; ++f) bwc[f] = bwn[f];
         }
       }
-      __syncthreads();
+#pragma unroll
+      for (int f = 0; f < NF; ++f) pc[f] = pn[f];
     }
+    __syncthreads();  // the next item's first copy must not overwrite a buffer still being read
 
-    // ---- epilogue: D row m = 4G + v of the 16x16 tile, column n
+    // ---- epilogue: D row (M) = mi*16 + 4G + v, column (N) = fragment row n
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
+    for (int mi = 0; mi < kPfMF; ++mi) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int rr = m0 + wid * 32 + mi * 16 + 4 * G + v;
+        const int rr = m0 + mi * 16 + 4 * G + v;
         if (rr >= cnt) continue;
         const long orow = row0 + rr;
+        if constexpr (GATEUP) {
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          if constexpr (GATEUP) {
-            const float g = acc[0][mi][ni][v], u = acc[1][mi][ni][v];
+          for (int f = 0; f < NF / 2; ++f) {
+            const float g = acc[mi][f][v], u = acc[mi][f + NF / 2][v];
             const float hv = g / (1.0f + __expf(-g)) * u;
-            const int fcol = nt * 64 + ni * 16 + n;
+            const int fcol = nt * (kPfWaves * 8 * NF) + wid * (8 * NF) + f * 16 + n;
             a.hout[orow * rows + fcol] = (uint16_t)f32_to_bf16_bits(hv);
-          } else {
+          }
+        } else {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const int dcol = nt * BN + h * 64 + ni * 16 + n;
-              a.o[orow * rows + dcol] = (uint16_t)f32_to_bf16_bits(acc[h][mi][ni][v]);
-            }
+          for (int f = 0; f < NF; ++f) {
+            const int dcol = nt * (kPfWaves * 16 * NF) + wid * (16 * NF) + f * 16 + n;
+            a.o[orow * rows + dcol] = (uint16_t)f32_to_bf16_bits(acc[mi][f][v]);
           }
         }
       }
     }
+  }
+}
+
+// fp32 tokens -> bf16 (RNE), for the prefill products.
+__global__ __launch_bounds__(256) void k_pf_x_bf16(const float* __restrict__ x, long n4, uint16_t* __restrict__ xb) {
+  for (long i = blockIdx.x * 256L + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
+    const f32x4 v = ((const f32x4*)x)[i];
+    ((u32x2*)xb)[i] = u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
   }
 }
 
@@ -298,6 +362,7 @@ struct PrefillWs {
   int32_t* mstart;
   uint16_t* h;
   uint16_t* o;
+  uint16_t* xb;  // bf16 copy of fp32 tokens
 };
 
 PrefillWs carve(void* ws, int T, int d, int f, int k, int E) {
@@ -309,24 +374,40 @@ PrefillWs carve(void* ws, int T, int d, int f, int k, int E) {
   w.h = (uint16_t*)p;
   p += align_up(R * f * 2, 256);
   w.o = (uint16_t*)p;
+  p += align_up(R * d * 2, 256);
+  w.xb = (uint16_t*)p;
   return w;
 }
 
-template <bool GATEUP>
-hipError_t launch_gemm(int fmt, const PrefillArgs& a, int grid, hipStream_t s) {
-  switch (fmt) {
-    case MOE_Q8_0: hipLaunchKernelGGL((k_pf_gemm<MOE_Q8_0, GATEUP>), dim3(grid), dim3(256), 0, s, a); break;
-    case MOE_IQ4_NL: hipLaunchKernelGGL((k_pf_gemm<MOE_IQ4_NL, GATEUP>), dim3(grid), dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_pf_gemm<MOE_NVFP4, GATEUP>), dim3(grid), dim3(256), 0, s, a); break;
-  }
+constexpr size_t kPfLds = 2 * kPfBuf;  // double-buffered activation tile
+
+template <int FMT, bool GATEUP, int NF>
+hipError_t launch_gemm_nf(const PrefillArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((k_pf_gemm<FMT, GATEUP, NF>), dim3(grid), dim3(kPfThreads), kPfLds, s, a);
   return hipGetLastError();
+}
+
+template <int FMT, bool GATEUP>
+hipError_t launch_gemm_fmt(int nf, const PrefillArgs& a, int grid, hipStream_t s) {
+  if constexpr (GATEUP) return launch_gemm_nf<FMT, true, 2>(a, grid, s);  // a gate and an up fragment
+  return nf == 2 ? launch_gemm_nf<FMT, false, 2>(a, grid, s) : launch_gemm_nf<FMT, false, 1>(a, grid, s);
+}
+
+template <bool GATEUP>
+hipError_t launch_gemm(int fmt, int nf, const PrefillArgs& a, int grid, hipStream_t s) {
+  switch (fmt) {
+    case MOE_Q8_0: return launch_gemm_fmt<MOE_Q8_0, GATEUP>(nf, a, grid, s);
+    case MOE_IQ4_NL: return launch_gemm_fmt<MOE_IQ4_NL, GATEUP>(nf, a, grid, s);
+    default: return launch_gemm_fmt<MOE_NVFP4, GATEUP>(nf, a, grid, s);
+  }
 }
 
 }  // namespace
 
 size_t prefill_ws_bytes(int T, int d, int f, int k) {
   const size_t R = (size_t)T * k + T;
-  return align_up((size_t)(4096 + 2) * 4, 256) + align_up(R * f * 2, 256) + align_up(R * d * 2, 256);
+  return align_up((size_t)(4096 + 2) * 4, 256) + align_up(R * f * 2, 256) + align_up(R * d * 2, 256) +
+         align_up((size_t)T * d * 2, 256);
 }
 
 hipError_t launch_prefill_stage(int stage, const FfnCall& c, hipStream_t s) {
@@ -336,6 +417,11 @@ hipError_t launch_prefill_stage(int stage, const FfnCall& c, hipStream_t s) {
   if (stage == kStagePrepare) {
     hipLaunchKernelGGL(k_pf_tiles, dim3(1), dim3(1024), 0, s, c.p.offsets, c.p.active, c.p.n_active, L.has_shared, T,
                        w.mstart);
+    if (c.x_dtype == MOE_F32) {
+      const long n4 = (long)T * L.d / 4;
+      hipLaunchKernelGGL(k_pf_x_bf16, dim3((unsigned)std::min<long>((n4 + 255) / 256, 4096)), dim3(256), 0, s,
+                         (const float*)c.x, n4, w.xb);
+    }
     return hipGetLastError();
   }
   if (stage == kStageCombine)
@@ -358,20 +444,23 @@ hipError_t launch_prefill_stage(int stage, const FfnCall& c, hipStream_t s) {
       a.smat[0] = qmat_dev(L.shared_gate);
       a.smat[1] = qmat_dev(L.shared_up);
     }
-    a.x = c.x;
-    a.x_bf16 = c.x_dtype == MOE_BF16 ? 1 : 0;
+    a.x = c.x_dtype == MOE_BF16 ? c.x : (const void*)w.xb;
+    a.x_bf16 = 1;
     a.hout = w.h;
-    const long items = max_mtiles * (L.f / 64);
-    const int grid = (int)(items < 8192 ? items : 8192);
-    return launch_gemm<true>(L.gate.type, a, grid, s);
+    // a gate and an up fragment per wavefront: a tile of 128 f-rows
+    const long items = max_mtiles * (L.f / 128);
+    const int grid = (int)(items < 8192 ? items : 8192) / kXcds * kXcds + kXcds;
+    return launch_gemm<true>(L.gate.type, 2, a, grid, s);
   }
   a.mat[0] = qmat_dev(L.down);
   if (L.has_shared) a.smat[0] = qmat_dev(L.shared_down);
   a.hin = w.h;
   a.o = w.o;
-  const long items = max_mtiles * (L.d / 128);
-  const int grid = (int)(items < 8192 ? items : 8192);
-  return launch_gemm<false>(L.down.type, a, grid, s);
+  // 256 d-rows per tile where d allows, else 128
+  const int nf = (L.d % 256 == 0) ? 2 : 1;
+  const long items = max_mtiles * (L.d / (128 * nf));
+  const int grid = (int)(items < 8192 ? items : 8192) / kXcds * kXcds + kXcds;
+  return launch_gemm<false>(L.down.type, nf, a, grid, s);
 }
 
 }  // namespace qre

@@ -72,7 +72,7 @@ typedef enum { MOE_Q8_0 = 1, MOE_IQ4_NL = 2, MOE_NVFP4 = 3 } moe_qtype;
 
 /* One projection for n_expert experts, structure of arrays (codes and scales
  * in separate device arrays).  rows = outputs, cols = reduction dimension.
- * codes must be 16-byte aligned, scales 4-byte aligned, tensor_scale 4-byte. */
+ * codes and scales must be 16-byte aligned, tensor_scale 4-byte. */
 typedef struct {
   int32_t type;              /* moe_qtype */
   int32_t n_expert;

@@ -27,7 +27,7 @@ moe_status check_qmatrix(const moe_qmatrix& m, int n_expert, int rows, int cols)
   if (m.n_expert != n_expert || m.rows != rows || m.cols != cols) return MOE_ERR_INVALID_ARG;
   if (!m.codes || !m.scales) return MOE_ERR_INVALID_ARG;
   if (m.type == MOE_NVFP4 && !m.tensor_scale) return MOE_ERR_INVALID_ARG;
-  if (!aligned(m.codes, 16) || !aligned(m.scales, 4)) return MOE_ERR_ALIGNMENT;
+  if (!aligned(m.codes, 16) || !aligned(m.scales, 16)) return MOE_ERR_ALIGNMENT;
   if (m.tensor_scale && !aligned(m.tensor_scale, 4)) return MOE_ERR_ALIGNMENT;
   return MOE_OK;
 }
@@ -204,7 +204,7 @@ moe_status moe_dequantize(const moe_qmatrix* m, int32_t expert, int32_t out_dtyp
     return MOE_ERR_INVALID_ARG;
   if (m->cols % 32 != 0) return MOE_ERR_UNSUPPORTED;
   if (!m->codes || !m->scales || (m->type == MOE_NVFP4 && !m->tensor_scale)) return MOE_ERR_INVALID_ARG;
-  if (!aligned(m->codes, 16) || !aligned(m->scales, 4) || !aligned(dst, 4)) return MOE_ERR_ALIGNMENT;
+  if (!aligned(m->codes, 16) || !aligned(m->scales, 16) || !aligned(dst, 4)) return MOE_ERR_ALIGNMENT;
   return hip_status(launch_dequant(qmat_dev(*m), expert, out_dtype, dst, (hipStream_t)stream));
 }
 

@@ -8,29 +8,31 @@
 
 namespace qre {
 
-// Stage kernel over a plan (global plan arrays, or the fused path's slot table).
-template <int FMT, int NT, bool GATEUP, bool ROLL>
+// Stage kernel over a plan: global plan arrays, or (TABLE) the fused step's
+// slot table, whose routed rows go to their pair's output row.
+template <int FMT, int NT, bool GATEUP, bool ROLL, bool TABLE = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1))) void k_ffn_dq(
     const DecodeArgs a) {
-  constexpr int NMAT = GATEUP ? 2 : 1;
-  __shared__ f32x4 red[4 * NMAT * NT * 64];
-  extern __shared__ __align__(16) f16 sA[];  // [CPP][K] activations of the current column pass
+  extern __shared__ __align__(16) f16 sA[];  // activations of the current column pass, then scales
 
+  dq_pin_args(a);
   const int wid = threadIdx.x >> 6;
   const int ksplit = a.ksplit;
   const int rt_per_wg = 4 / ksplit;
   const int rows = a.mat[0].rows;
   const int wg_per_slot = (rows / 16) / rt_per_wg;
-  const bool table = a.slots != nullptr;
-  const int n_act = table ? 0 : *a.n_active;
-  const int total = (table ? *a.n_slots : n_act + a.has_shared) * wg_per_slot;
+  // table: the slot count and the first item's entry are read together (the
+  // table has T*k + 1 entries; one past the count is read but not used)
+  const int n_act = TABLE ? 0 : *a.n_active;
+  const SlotEnt se0 = TABLE ? a.slots[min((int)blockIdx.x / wg_per_slot, a.T * a.k)] : SlotEnt{};
+  const int total = (TABLE ? *a.n_slots : n_act + a.has_shared) * wg_per_slot;
 
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const int slot = item / wg_per_slot;
     const int tile = (item % wg_per_slot) * rt_per_wg + wid / ksplit;
     SlotInfo si;
-    if (table) {
-      const SlotEnt se = a.slots[slot];
+    if constexpr (TABLE) {
+      const SlotEnt se = item == (int)blockIdx.x ? se0 : a.slots[slot];
       si = SlotInfo{se.e, se.shared != 0, se.row0, se.cnt};
     } else if (slot < n_act) {
       const int e = a.active[slot];
@@ -38,7 +40,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
     } else {
       si = SlotInfo{0, true, a.T * a.k, a.T};
     }
-    dq_item<FMT, NT, GATEUP, ROLL>(a, si, tile, wid % ksplit, a.row_token, sA, red);
+    dq_item<FMT, NT, GATEUP, ROLL, TABLE>(a, si, tile, wid % ksplit, a.row_token, sA);
   }
 }
 
@@ -95,7 +97,7 @@ hipError_t launch_fmt(const DecodeArgs& a, int ncols_max, int grid, hipStream_t 
   constexpr int CPT = cols_per_tile<FMT>();
   const int K = a.mat[0].cols;
   const int nt = pick_nt(CPT, ncols_max, K);
-  const size_t lds = (size_t)nt * CPT * K * 2;
+  const size_t lds = dq_lds_bytes(CPT, nt, K, a.ksplit, GATEUP ? 2 : 1);
   if (dq_nsteps(FMT, K, a.ksplit) > dq_pd(FMT, GATEUP)) return launch_fmt_roll<FMT, GATEUP, true>(a, nt, lds, grid, s);
   return launch_fmt_roll<FMT, GATEUP, false>(a, nt, lds, grid, s);
 }
@@ -113,18 +115,20 @@ hipError_t launch_pass(int fmt, const DecodeArgs& a, int ncols_max, int grid, hi
 
 // Down pass of the fused step over the slot table: a grid of at most one
 // resident wave of workgroups that loops over the items.
+template <int FMT, int NT, bool ROLL>
+static void launch_fz_down_nt(const DecodeArgs& a, size_t lds, int items, hipStream_t s) {
+  auto kern = k_ffn_dq<FMT, NT, false, ROLL, true>;
+  hipLaunchKernelGGL(kern, dim3(fused_grid(kern, lds, items)), dim3(256), lds, s, a);
+}
+
 template <int FMT, bool ROLL>
 static hipError_t launch_fz_down_roll(const DecodeArgs& a, int nt, size_t lds, int items, hipStream_t s) {
-  if (nt == 1) {
-    hipLaunchKernelGGL((k_ffn_dq<FMT, 1, false, ROLL>), dim3(fused_grid(k_ffn_dq<FMT, 1, false, ROLL>, lds, items)),
-                       dim3(256), lds, s, a);
-  } else if (nt == 2) {
-    hipLaunchKernelGGL((k_ffn_dq<FMT, 2, false, ROLL>), dim3(fused_grid(k_ffn_dq<FMT, 2, false, ROLL>, lds, items)),
-                       dim3(256), lds, s, a);
-  } else {
-    hipLaunchKernelGGL((k_ffn_dq<FMT, 4, false, ROLL>), dim3(fused_grid(k_ffn_dq<FMT, 4, false, ROLL>, lds, items)),
-                       dim3(256), lds, s, a);
-  }
+  if (nt == 1)
+    launch_fz_down_nt<FMT, 1, ROLL>(a, lds, items, s);
+  else if (nt == 2)
+    launch_fz_down_nt<FMT, 2, ROLL>(a, lds, items, s);
+  else
+    launch_fz_down_nt<FMT, 4, ROLL>(a, lds, items, s);
   return hipGetLastError();
 }
 
@@ -133,7 +137,7 @@ static hipError_t launch_fz_down_fmt(const DecodeArgs& a, int items, hipStream_t
   constexpr int CPT = cols_per_tile<FMT>();
   const int K = a.mat[0].cols;
   const int nt = pick_nt(CPT, a.T * 2, K);
-  const size_t lds = (size_t)nt * CPT * K * 2;
+  const size_t lds = dq_lds_bytes(CPT, nt, K, a.ksplit, 1);
   if (dq_nsteps(FMT, K, a.ksplit) > dq_pd(FMT, false)) return launch_fz_down_roll<FMT, true>(a, nt, lds, items, s);
   return launch_fz_down_roll<FMT, false>(a, nt, lds, items, s);
 }

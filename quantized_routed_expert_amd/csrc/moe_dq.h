@@ -55,6 +55,41 @@ struct DecodeArgs {
   const int32_t* pair_of_row;  // fused down pass: O row of each plan row (t*k + j); null: the plan row
 };
 
+// Kernel arguments are fetched through the scalar cache at their first use;
+// a first use inside the item path puts a memory round trip on every item's
+// critical path.  Touching every field the item path reads at kernel entry
+// fetches them all together, once.
+template <typename V>
+__device__ __forceinline__ void pin_arg(V v) {
+  asm volatile("" ::"s"(v));
+}
+
+__device__ __forceinline__ void dq_pin_args(const DecodeArgs& a) {
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    pin_arg(a.mat[m].codes);
+    pin_arg(a.mat[m].scales);
+    pin_arg(a.mat[m].ts);
+    pin_arg(a.smat[m].codes);
+    pin_arg(a.smat[m].scales);
+    pin_arg(a.smat[m].ts);
+  }
+  pin_arg(a.mat[0].rows);
+  pin_arg(a.mat[0].cols);
+  pin_arg(a.has_shared);
+  pin_arg(a.T);
+  pin_arg(a.k);
+  pin_arg(a.P);
+  pin_arg(a.ksplit);
+  pin_arg(a.down_type);
+  pin_arg(a.in16);
+  pin_arg(a.in_scale);
+  pin_arg(a.h16);
+  pin_arg(a.o);
+  pin_arg(a.pair_of_row);
+  pin_arg(a.error);
+}
+
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
 template <int FMT>
@@ -93,7 +128,8 @@ struct SlotInfo {
 
 // One workgroup item: rows [tile*16, tile*16+16) of slot `si` (gate + up, or
 // down), this wave's K part, against all of the slot's columns.  sA: the
-// workgroup's activation staging buffer; red: [4][NMAT][NT][64] partials.
+// workgroup's dynamic LDS: the activation staging buffer (which also holds the
+// [4][NMAT][NT][64] partial sums of the K reduction), then the scale rows.
 // Steps of weight codes in flight per matrix (and per wave): the gate/up pass
 // keeps two matrices' codes in registers, the down pass one (more steps for
 // the 16-element steps of Q8_0).  A pass with more steps than that rolls the
@@ -102,9 +138,14 @@ constexpr int dq_pd(int fmt, bool gateup) { return (!gateup && fmt == MOE_Q8_0) 
 constexpr int dq_eps(int fmt) { return fmt == MOE_Q8_0 ? 16 : 32; }  // elements per lane per step
 inline int dq_nsteps(int fmt, int K, int ksplit) { return K / ksplit / (4 * dq_eps(fmt)); }
 
-template <int FMT, int NT, bool GATEUP, bool ROLL>
+// PAIRS (down pass of the fused step): routed rows are written at the output
+// row pair_of_row gives their plan row.
+template <int FMT, int NT, bool GATEUP, bool ROLL, bool PAIRS = false>
 __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si, int tile, int kpart,
-                                        const int32_t* row_token, f16* sA, f32x4* red) {
+                                        const int32_t* row_token, f16* sA) {
+  // one word per column of a pass for the epilogue: the token's activation
+  // scale (gate/up) or the output row (PAIRS)
+  __shared__ uint32_t s_colw[4 * 8];
   constexpr int EPS = dq_eps(FMT);                   // elements per lane per step (one 16-byte load)
   constexpr int NMF = EPS / 8;                       // MFMAs per step
   constexpr bool BD = FMT != MOE_NVFP4;              // block-diagonal activations
@@ -126,14 +167,16 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
   const int ncol = si.ncolt * P;
 
   const uint8_t* crow[NMAT];
-  const uint8_t* srow[NMAT];
+  const uint8_t* sreg[NMAT];  // the workgroup's scale rows (contiguous)
   float tsc[NMAT];
+  const int wg_rows = 64 / ksplit;            // rows of the workgroup's tiles
+  const int tile0 = tile - wid / ksplit;      // its first tile
 #pragma unroll
   for (int m = 0; m < NMAT; ++m) {
     const QMatDev& W = si.is_sh ? a.smat[m] : a.mat[m];
     const long rw = (long)si.e * rows + tile * 16 + n;
     crow[m] = W.codes + rw * crb;
-    srow[m] = W.scales + rw * srb;
+    sreg[m] = W.scales + ((long)si.e * rows + tile0 * 16) * srb;
     tsc[m] = (FMT == MOE_NVFP4) ? W.ts[si.e] : 1.0f;
   }
   // K position of this lane at step s: the four lane groups take four
@@ -159,17 +202,38 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
   // this lane's code and scale addresses at step 0; step s adds a constant
   // (4 * EPS elements: 64 code bytes, 4 * EPS / 32 scale words)
   const uint8_t* cl[NMAT];
-  const uint16_t* sl[NMAT];
 #pragma unroll
-  for (int m = 0; m < NMAT; ++m) {
-    cl[m] = crow[m] + (FMT == MOE_Q8_0 ? kbase : (kbase >> 1));
-    sl[m] = (const uint16_t*)srow[m] + (kbase >> 5);
-  }
-  auto load_step = [&](int m, int s, u32x4& c, uint32_t& sc) {
-    c = *(const u32x4*)(cl[m] + s * (FMT == MOE_Q8_0 ? 4 * EPS : 2 * EPS));
-    // Q8_0 / IQ4_NL: the block's fp16 scale; NVFP4: the chunk's two E4M3 scales
-    sc = sl[m][s * (4 * EPS / 32)];
+  for (int m = 0; m < NMAT; ++m) cl[m] = crow[m] + (FMT == MOE_Q8_0 ? kbase : (kbase >> 1));
+  // Weight codes are read once: non-temporal loads, which stream from HBM at a
+  // far higher rate than loads that allocate for reuse.
+  auto load_step = [&](int m, int s, u32x4& c) {
+    c = __builtin_nontemporal_load((const u32x4*)(cl[m] + s * (FMT == MOE_Q8_0 ? 4 * EPS : 2 * EPS)));
   };
+
+  // The scales of the workgroup's rows (wg_rows x srb bytes per matrix, one
+  // contiguous region) go to LDS through coalesced 16-byte loads: per-step
+  // scale loads of a few bytes per lane would cost as many memory requests
+  // as the codes themselves.  sS follows the activation buffer.
+  constexpr int RED_BYTES = 4 * NMAT * NT * 64 * 16;
+  uint8_t* sS = (uint8_t*)sA + max(NT * CPT * K * 2, RED_BYTES);
+  f32x4* red = (f32x4*)sA;
+  const int s_chunks_m = wg_rows * srb / 16;  // per matrix (srb is a multiple of 8, wg_rows of 16)
+  const int s_chunks = NMAT * s_chunks_m;
+  constexpr int SB = 2;  // scale chunks per thread issued before the codes
+  auto s_src = [&](int ch) -> const u32x4* {
+    const int m = ch >= s_chunks_m ? 1 : 0;
+    return (const u32x4*)(sreg[NMAT > 1 ? m : 0] + (ch - m * s_chunks_m) * 16);
+  };
+  u32x4 sv[SB];
+#pragma unroll
+  for (int b = 0; b < SB; ++b) sv[b] = __builtin_nontemporal_load(s_src(min(tid + b * 256, s_chunks - 1)));
+  // A rows that hold no column read zeros from kw halves after the scales
+  const int zoff = (int)(sS + s_chunks * 16 - (uint8_t*)sA) / 2;
+  // this lane's scale words in LDS: row (wid / ksplit) * 16 + n, the step-0 block
+  const uint16_t* ssl[NMAT];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+    ssl[m] = (const uint16_t*)(sS + m * s_chunks_m * 16 + ((wid / ksplit) * 16 + n) * srb) + (kbase >> 5);
   for (int c0 = 0; c0 < ncol; c0 += CPP) {
     const int ncp = min(CPP, ncol - c0);
     const int nch = ncp * chunks_per_col;
@@ -182,13 +246,22 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
       const int c = ch / chunks_per_col, kk = (ch - c * chunks_per_col) * 8;
       av[b] = *(const u32x4*)(a.in16 + in_row_of(c0 + c) * K + kk);
     }
+    uint32_t cw = 0;
+    {
+      const int c = min(tid, ncp - 1);
+      if constexpr (GATEUP) {
+        cw = __float_as_uint(a.in_scale[in_row_of(c0 + c)]);
+      } else if constexpr (PAIRS) {
+        // (the shared slot's rows are past the pair list; its value is unused)
+        cw = (uint32_t)a.pair_of_row[min(si.row0 + (c0 + c) / 2, a.T * a.k - 1)];
+      }
+    }
     // ---- the first PD steps of weight codes (independent of the activations)
     u32x4 cb[NMAT][PD];
-    uint32_t sb[NMAT][PD];
 #pragma unroll
     for (int u = 0; u < PD; ++u)
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) load_step(m, min(u, nsteps - 1), cb[m][u], sb[m][u]);
+      for (int m = 0; m < NMAT; ++m) load_step(m, min(u, nsteps - 1), cb[m][u]);
 
     // ---- stage the activation columns into LDS.  Columns at or beyond ncp
     // are never read (their A rows are zero), so they are not written.
@@ -200,6 +273,15 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
         const int c = ch / chunks_per_col, kk = (ch - c * chunks_per_col) * 8;
         *(u32x4*)&sA[c * K + kk] = av[b];
       }
+    }
+    if (tid < ncp) s_colw[tid] = cw;
+    if (c0 == 0) {
+      // the item's scales (the first chunks were loaded with the activations)
+#pragma unroll
+      for (int b = 0; b < SB; ++b)
+        if (tid + b * 256 < s_chunks) *(u32x4*)(sS + (tid + b * 256) * 16) = sv[b];
+      for (int ch = tid + SB * 256; ch < s_chunks; ch += 256) *(u32x4*)(sS + ch * 16) = *s_src(ch);
+      for (int z = tid; z < kw / 8; z += 256) *(u32x4*)&sA[zoff + z * 8] = u32x4{0u, 0u, 0u, 0u};
     }
     // the rest in batches of RB loads in flight per thread
     for (int ch0 = tid + AB * 256; ch0 < nch; ch0 += RB * 256) {
@@ -221,10 +303,9 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
     }
     __syncthreads();
 
-    // A-operand LDS row for each N-tile (this lane is A row m = n, K slice G);
-    // lanes without a column read column 0 and use zeros
-    int acol[NT];
-    bool aval[NT];
+    // A-operand LDS position for each N-tile (this lane is A row m = n, K
+    // slice G); lanes without a column read the zero region instead
+    int abase[NT];
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) {
       int c;
@@ -236,8 +317,7 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
         valid = n < CPT;
         c = jt * CPT + n;
       }
-      aval[jt] = valid && c < ncp;
-      acol[jt] = aval[jt] ? c : 0;
+      abase[jt] = (valid && c < ncp) ? c * K + kbase : zoff;
     }
 
     f32x4 acc[NMAT][NT];
@@ -246,14 +326,17 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
 #pragma unroll
       for (int jt = 0; jt < NT; ++jt) acc[m][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute_step = [&](const u32x4 (&cc)[NMAT], const uint32_t (&ss)[NMAT], int s) {
+    auto compute_step = [&](const u32x4 (&cc)[NMAT], int s) {
+      // Q8_0 / IQ4_NL: the block's fp16 scale; NVFP4: the chunk's two E4M3 scales
+      uint32_t ss[NMAT];
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) ss[m] = ssl[m][s * (4 * EPS / 32)];
       f16x8 ac[NT][NMF];
 #pragma unroll
       for (int jt = 0; jt < NT; ++jt)
 #pragma unroll
         for (int i = 0; i < NMF; ++i) {
-          const f16x8 v = *(const f16x8*)&sA[acol[jt] * K + kbase + s * 4 * EPS + 8 * i];
-          ac[jt][i] = aval[jt] ? v : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+          ac[jt][i] = *(const f16x8*)&sA[abase[jt] + s * 4 * EPS + 8 * i];
         }
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
@@ -288,13 +371,9 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
       for (int u = 0; u < PD; ++u) {
         if (u < nsteps) {
           u32x4 cc[NMAT];
-          uint32_t ss[NMAT];
 #pragma unroll
-          for (int m = 0; m < NMAT; ++m) {
-            cc[m] = cb[m][u];
-            ss[m] = sb[m][u];
-          }
-          compute_step(cc, ss, u);
+          for (int m = 0; m < NMAT; ++m) cc[m] = cb[m][u];
+          compute_step(cc, u);
         }
       }
     } else {
@@ -304,14 +383,12 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
         for (int u = 0; u < PD; ++u) {
           const int s = s0 + u;
           u32x4 cc[NMAT];
-          uint32_t ss[NMAT];
 #pragma unroll
           for (int m = 0; m < NMAT; ++m) {
             cc[m] = cb[m][u];
-            ss[m] = sb[m][u];
-            load_step(m, min(s + PD, nsteps - 1), cb[m][u], sb[m][u]);
+            load_step(m, min(s + PD, nsteps - 1), cb[m][u]);
           }
-          if (s < nsteps) compute_step(cc, ss, s);
+          if (s < nsteps) compute_step(cc, s);
         }
       }
     }
@@ -333,8 +410,10 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
           v.w += __shfl_xor(v.w, 32, 64);
         }
     }
-    // reduce the K parts of this row tile through LDS
+    // reduce the K parts of this row tile through LDS (over the activations,
+    // once every wave has finished reading them)
     if (ksplit > 1) {
+      __syncthreads();
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -384,7 +463,7 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
           const int out_row = si.row0 + tc;
           if constexpr (GATEUP) {
             const int t = si.is_sh ? tc : row_token[si.row0 + tc];
-            const float xs = a.in_scale[(long)t * P];
+            const float xs = __uint_as_float(s_colw[cl]);
             const float g = val[0] * xs, u = val[1] * xs;
             const float h = silu_f(g) * u;
             if (!(fabsf(h) < 65504.0f)) atomicOr(a.error, 2);
@@ -396,7 +475,7 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
             a.h16[((long)out_row * 2 + 1) * f + pos] = lo;
           } else {
             // fused path: routed rows go to their (token, slot) pair's row
-            const int orow = (a.pair_of_row && !si.is_sh) ? a.pair_of_row[out_row] : out_row;
+            const int orow = (PAIRS && !si.is_sh) ? (int)s_colw[cl] : out_row;
             a.o[(long)orow * rows + frow] = val[0];
           }
         }
@@ -439,6 +518,14 @@ inline DecodeWs carve(void* ws, int T, int d, int f, int k, int P) {
   p += align_up(R * 2 * f * 2, 256);
   w.o = (float*)p;
   return w;
+}
+
+// Dynamic LDS of a decode pass: nt N-tiles of staged activations (or the K
+// reduction's partial sums), the scale rows of the workgroup's tiles for each
+// of nmat matrices, and K / ksplit zero halves.
+inline size_t dq_lds_bytes(int cpt, int nt, int K, int ksplit, int nmat) {
+  const size_t act = (size_t)nt * cpt * K * 2, red = (size_t)4 * nmat * nt * 64 * 16;
+  return (act > red ? act : red) + (size_t)nmat * (64 / ksplit) * (K / 16) + (size_t)(K / ksplit) * 2;
 }
 
 // Waves along K per 16-row tile: as many as divide the lane-group step count.

@@ -150,8 +150,28 @@ __device__ __forceinline__ void glue_token(const FzGlueArgs& a, int t, bool writ
   __syncthreads();
 }
 
+__device__ __forceinline__ void glue_pin_args(const FzGlueArgs& a) {
+  pin_arg(a.d);
+  pin_arg(a.T);
+  pin_arg(a.k);
+  pin_arg(a.has_shared);
+  pin_arg(a.h_in);
+  pin_arg(a.h_out);
+  pin_arg(a.o);
+  pin_arg(a.topk_w);
+  pin_arg(a.rec_y);
+  pin_arg(a.x_out);
+  pin_arg(a.rec_x);
+  pin_arg(a.x16);
+  pin_arg(a.xs);
+  pin_arg(a.gate_fmt);
+  pin_arg(a.eps);
+  pin_arg(a.error_reset);
+}
+
 // Glue for T tokens: one workgroup per token.
 __global__ __launch_bounds__(256) void k_fz_glue(const FzGlueArgs a) {
+  glue_pin_args(a);
   f32x4 v[kGlueMaxQ];
   if (blockIdx.x == 0 && threadIdx.x == 0 && a.error_reset) *a.error_reset = 0;
   glue_token(a, blockIdx.x, true, v);
@@ -183,6 +203,12 @@ template <bool INLINE>
 __global__ __launch_bounds__(256) void k_fz_route(const FzRouteArgs a) {
   __shared__ uint16_t sx[kFusedMaxT * 4096];  // bf16 layer inputs
   __shared__ double pr[2][kFusedMaxT];        // second halves (two wavefronts per expert)
+  glue_pin_args(a.g);
+  pin_arg(a.Wr);
+  pin_arg(a.bias);
+  pin_arg(a.E);
+  pin_arg(a.x);
+  pin_arg(a.logits);
   constexpr int WPE = 4 / route_experts_per_wg<INLINE>();  // wavefronts per expert
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int d = a.g.d, T = a.g.T;
@@ -195,7 +221,10 @@ __global__ __launch_bounds__(256) void k_fz_route(const FzRouteArgs a) {
   f32x4 wv[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j)
-    if (j >= jlo && j < jhi && e < a.E) wv[j] = *(const f32x4*)(a.Wr + (long)e * d + (j * 64 + lane) * 4);
+    if (j >= jlo && j < jhi && e < a.E)
+      wv[j] = __builtin_nontemporal_load((const f32x4*)(a.Wr + (long)e * d + (j * 64 + lane) * 4));
+  // the bias with the weights, so that the end of the product waits for nothing
+  const float bias_e = (a.bias && e < a.E) ? a.bias[e] : 0.0f;
 
   if constexpr (INLINE) {
     if (blockIdx.x == 0 && tid == 0 && a.g.error_reset) *a.g.error_reset = 0;
@@ -263,7 +292,7 @@ __global__ __launch_bounds__(256) void k_fz_route(const FzRouteArgs a) {
       for (int t = 0; t < T; ++t) r[t] += pr[wid >> 1][t];
   }
   if (half == 0 && lane == 0 && e < a.E) {
-    const double b = a.bias ? (double)a.bias[e] : 0.0;
+    const double b = (double)bias_e;
     for (int t = 0; t < T; ++t) a.logits[(long)t * a.E + e] = (float)(r[t] + b);
   }
 }
@@ -287,8 +316,6 @@ constexpr int kFusedTK = kFusedMaxT * 32;  // token-slot pairs at most
 template <int FMT, int NT, int NPL, bool ROLL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1))) void k_fz_gateup(
     const FzGateArgs g) {
-  constexpr int NMAT = 2;
-  __shared__ f32x4 red[4 * NMAT * NT * 64];
   __shared__ __align__(16) int32_t sidx[kFusedTK];
   __shared__ float sw[kFusedTK];
   __shared__ __align__(16) int32_t sfirst[kFusedTK];
@@ -299,6 +326,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   extern __shared__ __align__(16) f16 sA[];
 
   const DecodeArgs& a = g.a;
+  dq_pin_args(a);
+  pin_arg(g.logits);
+  pin_arg(g.plan.pair_of_row);
+  pin_arg(g.plan.topk_idx);
+  pin_arg(g.plan.topk_w);
+  pin_arg(g.plan.slots);
+  pin_arg(g.plan.n_slots);
+  pin_arg(g.E);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int T = a.T, k = a.k, E = g.E;
   const int TK = T * k;
@@ -412,7 +447,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
       const SlotEnt se = sslot[slot - hs];
       si = SlotInfo{se.e, false, se.row0, se.cnt};
     }
-    dq_item<FMT, NT, true, ROLL>(a, si, tile, wid % ksplit, srow_token, sA, red);
+    dq_item<FMT, NT, true, ROLL>(a, si, tile, wid % ksplit, srow_token, sA);
   }
 }
 
@@ -457,7 +492,7 @@ hipError_t launch_fz_gate_fmt(const FzGateArgs& g, int items, int E, hipStream_t
   const int K = g.a.mat[0].cols;
   const int nt = pick_nt(CPT, g.a.T, K);
   // the activation buffer also holds the logits while the plan is built
-  const size_t lds = std::max((size_t)nt * CPT * K * 2, (size_t)g.a.T * E * 4);
+  const size_t lds = std::max(dq_lds_bytes(CPT, nt, K, g.a.ksplit, 2), (size_t)g.a.T * E * 4);
   if (dq_nsteps(FMT, K, g.a.ksplit) > dq_pd(FMT, true))
     return launch_fz_gate_nt<FMT, true>(g, nt, items, lds, E, s, e0, e1);
   return launch_fz_gate_nt<FMT, false>(g, nt, items, lds, E, s, e0, e1);

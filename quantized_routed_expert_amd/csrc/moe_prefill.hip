@@ -122,13 +122,14 @@ struct PfCodes {
 
 template <int FMT>
 __device__ __forceinline__ void pf_load_codes(const uint8_t* crow, const uint8_t* srow, int kel, PfCodes<FMT>& pc) {
+  // (non-temporal: each weight tile is read by few workgroups, close together)
   if constexpr (FMT == MOE_Q8_0) {
-    pc.c[0] = *(const u32x4*)(crow + kel);
-    pc.c[1] = *(const u32x4*)(crow + kel + 16);
+    pc.c[0] = __builtin_nontemporal_load((const u32x4*)(crow + kel));
+    pc.c[1] = __builtin_nontemporal_load((const u32x4*)(crow + kel + 16));
   } else {
-    pc.c[0] = *(const u32x4*)(crow + (kel >> 1));
+    pc.c[0] = __builtin_nontemporal_load((const u32x4*)(crow + (kel >> 1)));
   }
-  pc.sc = ((const uint16_t*)srow)[kel >> 5];
+  pc.sc = __builtin_nontemporal_load((const uint16_t*)srow + (kel >> 5));
 }
 
 // Four biased bytes u (= value + 128) times scale d, rounded once to bf16: the

@@ -79,33 +79,66 @@ __device__ __forceinline__ float load_x(const void* x, int x_bf16, long i) {
   return x_bf16 ? bf16_bits_to_f32(((const uint16_t*)x)[i]) : ((const float*)x)[i];
 }
 
+// Four consecutive activations x[i .. i+3] (i a multiple of 4).
+template <bool XB>
+__device__ __forceinline__ f32x4 load4_x(const void* x, long i) {
+  if constexpr (XB) {
+    const u32x2 v = *(const u32x2*)((const uint16_t*)x + i);
+    return f32x4{bf16_bits_to_f32(v.x & 0xffffu), bf16_bits_to_f32(v.x >> 16), bf16_bits_to_f32(v.y & 0xffffu),
+                 bf16_bits_to_f32(v.y >> 16)};
+  } else {
+    return *(const f32x4*)((const float*)x + i);
+  }
+}
+
 // T <= 64: one workgroup per expert row, fp64 accumulation (products of an
 // fp32 weight and a bf16/fp32 activation are exact in fp64), up to 16 tokens
-// per pass.  Memory bound: every weight is read once per pass.
+// per pass.  The row is streamed from HBM once (held in registers for
+// d <= 4096); the activations are shared by every workgroup and come from L2.
 constexpr int kRtTok = 16;
+constexpr int kRtJ = 4;  // 1024-element chunks of the row held in registers
 
+template <bool XB>
 __global__ __launch_bounds__(256) void k_router_gemv_f64(const float* __restrict__ W, const float* __restrict__ bias,
-                                                         const void* __restrict__ x, int x_bf16, int T, int E, int d,
+                                                         const void* __restrict__ x, int T, int E, int d,
                                                          float* __restrict__ logits) {
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   __shared__ double red[4][kRtTok];
   const float* wr = W + (long)e * d;
+  const int nj = (d + 1023) / 1024;
+  const float bv = bias ? bias[e] : 0.0f;
+  // elements j*1024 + 4*tid .. +3 (out-of-row lanes load a valid address and
+  // leave it unused)
+  f32x4 wv[kRtJ];
+#pragma unroll
+  for (int j = 0; j < kRtJ; ++j)
+    wv[j] = __builtin_nontemporal_load((const f32x4*)(wr + min(j * 1024 + tid * 4, d - 4)));
+
+  auto accumulate = [&](const f32x4& w4, int i, int t0, int nt, double (&acc)[kRtTok]) {
+    f32x4 xv[kRtTok];
+#pragma unroll
+    for (int t = 0; t < kRtTok; ++t) xv[t] = load4_x<XB>(x, (long)(t0 + min(t, nt - 1)) * d + i);
+#pragma unroll
+    for (int t = 0; t < kRtTok; ++t)
+      if (t < nt)
+        acc[t] += (double)w4.x * (double)xv[t].x + (double)w4.y * (double)xv[t].y + (double)w4.z * (double)xv[t].z +
+                  (double)w4.w * (double)xv[t].w;
+  };
+
   for (int t0 = 0; t0 < T; t0 += kRtTok) {
     const int nt = min(kRtTok, T - t0);
     double acc[kRtTok];
 #pragma unroll
     for (int t = 0; t < kRtTok; ++t) acc[t] = 0.0;
-    for (int i = tid * 4; i < d; i += 256 * 4) {
-      const f32x4 w4 = *(const f32x4*)(wr + i);
 #pragma unroll
-      for (int t = 0; t < kRtTok; ++t) {
-        if (t < nt) {
-          const long xo = (long)(t0 + t) * d + i;
-          acc[t] += (double)w4.x * (double)load_x(x, x_bf16, xo) + (double)w4.y * (double)load_x(x, x_bf16, xo + 1) +
-                    (double)w4.z * (double)load_x(x, x_bf16, xo + 2) + (double)w4.w * (double)load_x(x, x_bf16, xo + 3);
-        }
-      }
+    for (int j = 0; j < kRtJ; ++j) {
+      const int i = j * 1024 + tid * 4;
+      if (j < nj && i < d) accumulate(wv[j], i, t0, nt, acc);
+    }
+    for (int j = kRtJ; j < nj; ++j) {  // rows longer than 4096: re-read per pass
+      const int i = j * 1024 + tid * 4;
+      if (i < d) accumulate(*(const f32x4*)(wr + i), i, t0, nt, acc);
     }
 #pragma unroll
     for (int t = 0; t < kRtTok; ++t) {
@@ -116,8 +149,7 @@ __global__ __launch_bounds__(256) void k_router_gemv_f64(const float* __restrict
     }
     __syncthreads();
     if (tid < nt) {
-      double v = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
-      if (bias) v += (double)bias[e];
+      const double v = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid] + (double)bv;
       logits[(long)(t0 + tid) * E + e] = (float)v;
     }
     __syncthreads();
@@ -173,7 +205,10 @@ hipError_t launch_router_logits(const float* W, const float* b, const void* x, i
                                 float* logits, hipStream_t s) {
   const int xb = x_dtype == MOE_BF16 ? 1 : 0;
   if (T <= 64) {
-    hipLaunchKernelGGL(k_router_gemv_f64, dim3(E), dim3(256), 0, s, W, b, x, xb, T, E, d, logits);
+    if (xb)
+      hipLaunchKernelGGL(k_router_gemv_f64<true>, dim3(E), dim3(256), 0, s, W, b, x, T, E, d, logits);
+    else
+      hipLaunchKernelGGL(k_router_gemv_f64<false>, dim3(E), dim3(256), 0, s, W, b, x, T, E, d, logits);
   } else {
     hipLaunchKernelGGL(k_router_gemm_f32, dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, s, W, b, x, xb, T, E, d,
                        logits);

@@ -50,45 +50,73 @@ struct FzGlueArgs {
 constexpr int kGlueMaxQ = 4;  // d <= 4096: float4 chunks per thread
 constexpr int kGlueRB = 8;    // routed rows whose loads are in flight together
 
-// Glue for one token, by one workgroup.  Returns the token's bf16 input in
-// v[] (as floats) when the caller needs it.
-__device__ __forceinline__ void glue_token(const FzGlueArgs& a, int t, bool writer, f32x4 (&v)[kGlueMaxQ]) {
-  __shared__ float red[2][4];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+// Glue for one token, by one workgroup, in two parts so that a caller can put
+// other loads in flight between them: glue_load issues the token's residual,
+// shared row, gate weights and first kGlueRB routed rows; glue_finish forms y,
+// the new residual and the bf16 input, which it returns in v[] (as floats).
+struct GlueLoads {
+  f32x4 v[kGlueMaxQ];              // residual
+  f32x4 y[kGlueMaxQ];              // shared row (or zero)
+  float wj[kGlueRB];               // gate weights of the first routed rows
+  f32x4 ov[kGlueMaxQ][kGlueRB];    // the first routed rows
+};
+
+__device__ __forceinline__ void glue_load(const FzGlueArgs& a, int t, GlueLoads& g) {
+  const int tid = threadIdx.x;
   const int d = a.d, T = a.T, k = a.k;
   const int nq = d / 1024;
-  // residual and shared row first; every routed row of a batch is in flight
-  // before the first is used
-  f32x4 y[kGlueMaxQ];
 #pragma unroll
   for (int q = 0; q < kGlueMaxQ; ++q) {
     if (q < nq) {
       const int i = (q * 256 + tid) * 4;
-      v[q] = *(const f32x4*)(a.h_in + (long)t * d + i);
-      y[q] = (a.o && a.has_shared) ? *(const f32x4*)(a.o + (long)(T * k + t) * d + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+      g.v[q] = *(const f32x4*)(a.h_in + (long)t * d + i);
+      g.y[q] = (a.o && a.has_shared) ? *(const f32x4*)(a.o + (long)(T * k + t) * d + i) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
   if (a.o) {
+#pragma unroll
+    for (int jj = 0; jj < kGlueRB; ++jj) g.wj[jj] = (jj < k) ? a.topk_w[t * k + jj] : 0.0f;
+#pragma unroll
+    for (int q = 0; q < kGlueMaxQ; ++q)
+#pragma unroll
+      for (int jj = 0; jj < kGlueRB; ++jj)
+        if (q < nq && jj < k) g.ov[q][jj] = *(const f32x4*)(a.o + (long)(t * k + jj) * d + (q * 256 + tid) * 4);
+  }
+}
+
+__device__ __forceinline__ void glue_finish(const FzGlueArgs& a, int t, bool writer, GlueLoads& g,
+                                            f32x4 (&v)[kGlueMaxQ]) {
+  __shared__ float red[2][4];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int d = a.d, k = a.k;
+  const int nq = d / 1024;
+  f32x4 y[kGlueMaxQ];
+#pragma unroll
+  for (int q = 0; q < kGlueMaxQ; ++q) {
+    v[q] = g.v[q];
+    y[q] = g.y[q];
+  }
+  if (a.o) {
     for (int j0 = 0; j0 < k; j0 += kGlueRB) {
-      float wj[kGlueRB];
-      f32x4 ov[kGlueMaxQ][kGlueRB];
+      if (j0 > 0) {  // (k > kGlueRB) the next batch of routed rows
 #pragma unroll
-      for (int jj = 0; jj < kGlueRB; ++jj) wj[jj] = (j0 + jj < k) ? a.topk_w[t * k + j0 + jj] : 0.0f;
+        for (int jj = 0; jj < kGlueRB; ++jj) g.wj[jj] = (j0 + jj < k) ? a.topk_w[t * k + j0 + jj] : 0.0f;
 #pragma unroll
-      for (int q = 0; q < kGlueMaxQ; ++q)
+        for (int q = 0; q < kGlueMaxQ; ++q)
 #pragma unroll
-        for (int jj = 0; jj < kGlueRB; ++jj)
-          if (q < nq && j0 + jj < k)
-            ov[q][jj] = *(const f32x4*)(a.o + (long)(t * k + j0 + jj) * d + (q * 256 + tid) * 4);
+          for (int jj = 0; jj < kGlueRB; ++jj)
+            if (q < nq && j0 + jj < k)
+              g.ov[q][jj] = *(const f32x4*)(a.o + (long)(t * k + j0 + jj) * d + (q * 256 + tid) * 4);
+      }
 #pragma unroll
       for (int q = 0; q < kGlueMaxQ; ++q)
 #pragma unroll
         for (int jj = 0; jj < kGlueRB; ++jj)
           if (q < nq && j0 + jj < k) {
-            y[q].x = fmaf(wj[jj], ov[q][jj].x, y[q].x);
-            y[q].y = fmaf(wj[jj], ov[q][jj].y, y[q].y);
-            y[q].z = fmaf(wj[jj], ov[q][jj].z, y[q].z);
-            y[q].w = fmaf(wj[jj], ov[q][jj].w, y[q].w);
+            y[q].x = fmaf(g.wj[jj], g.ov[q][jj].x, y[q].x);
+            y[q].y = fmaf(g.wj[jj], g.ov[q][jj].y, y[q].y);
+            y[q].z = fmaf(g.wj[jj], g.ov[q][jj].z, y[q].z);
+            y[q].w = fmaf(g.wj[jj], g.ov[q][jj].w, y[q].w);
           }
     }
   }
@@ -148,6 +176,12 @@ __device__ __forceinline__ void glue_token(const FzGlueArgs& a, int t, bool writ
     if (tid == 0) a.xs[t] = ldexpf(1.0f, ex);
   }
   __syncthreads();
+}
+
+__device__ __forceinline__ void glue_token(const FzGlueArgs& a, int t, bool writer, f32x4 (&v)[kGlueMaxQ]) {
+  GlueLoads g;
+  glue_load(a, t, g);
+  glue_finish(a, t, writer, g, v);
 }
 
 __device__ __forceinline__ void glue_pin_args(const FzGlueArgs& a) {
@@ -217,6 +251,10 @@ __global__ __launch_bounds__(256) void k_fz_route(const FzRouteArgs a) {
   const int nj = d / 256;
   const int jlo = half * nj / WPE, jhi = (half + 1) * nj / WPE;
 
+  // INLINE: the glue's loads go first, so that forming the input waits for
+  // them alone while the router row streams in
+  GlueLoads gl;
+  if constexpr (INLINE) glue_load(a.g, 0, gl);
   // router row part of this wave: lane holds elements (j*64 + lane)*4 .. +3
   f32x4 wv[16];
 #pragma unroll
@@ -229,7 +267,7 @@ __global__ __launch_bounds__(256) void k_fz_route(const FzRouteArgs a) {
   if constexpr (INLINE) {
     if (blockIdx.x == 0 && tid == 0 && a.g.error_reset) *a.g.error_reset = 0;
     f32x4 v[kGlueMaxQ];
-    glue_token(a.g, 0, blockIdx.x == 0, v);
+    glue_finish(a.g, 0, blockIdx.x == 0, gl, v);
     const int nq = d / 1024;
 #pragma unroll
     for (int q = 0; q < kGlueMaxQ; ++q) {

@@ -67,7 +67,7 @@ DOMINANT = {
     "slots": ("k_ffn_dq gate/up (NVFP4)", r"qre::k_ffn_dq<3, \d, true",
               ["quantized_routed_expert_amd/csrc/moe_decode.hip", "quantized_routed_expert_amd/csrc/moe_dq.h",
                "quantized_routed_expert_amd/csrc/moe_device.h"]),
-    "prefill": ("k_pf_gemm gate/up (IQ4_NL)", r"qre::k_pf_gemm<2, true>",
+    "prefill": ("k_pf_gemm gate/up (IQ4_NL)", r"qre::k_pf_gemm<2, true",
                 ["quantized_routed_expert_amd/csrc/moe_prefill.hip", "quantized_routed_expert_amd/csrc/moe_device.h"]),
 }
 
@@ -263,7 +263,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if args.workload == "prefill" else "f16",
+        "dtype": "f16",
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: {wl.n_layers}-layer routed-expert stack, T={T} tokens/step",

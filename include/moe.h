@@ -107,7 +107,7 @@ typedef struct {
  *  n_active[1]      number of active experts
  *  error[1]         0, or a bit set: 1 = an expert id outside [0, E) was
  *                   dropped; 2 = an SwiGLU activation exceeded the fp16 range
- *                   of the decode path (moe_ffn_forward)
+ *                   (moe_ffn_forward, moe_decode_stack)
  * Rows past offsets[E] in row_token / row_slot are set to -1. */
 typedef struct {
   int32_t* counts;
@@ -149,9 +149,11 @@ moe_status moe_plan(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
  * decode path runs: exact dequantisation, fp32 accumulation (activations are
  * carried as fp16 hi/lo pairs, intermediate SwiGLU values must stay below
  * 65504 in magnitude; error bit 2 reports otherwise).  For T > 64 the prefill
- * path runs: weights are rounded to bf16 (RNE of the exact value) in
- * registers, fp32 tokens and SwiGLU activations are rounded to bf16, bf16
- * MFMA with fp32 accumulation.
+ * path runs: weights are rounded to fp16 (code times block scale, rounded
+ * once; NVFP4-style weights are exact and their tensor scale is applied in
+ * fp32), tokens are scaled by a power of two per token into fp16 (exact for
+ * bf16 tokens), SwiGLU activations are rounded to fp16 (error bit 2 if one
+ * exceeds 65504 in magnitude), fp16 MFMA with fp32 accumulation.
  * The combine never uses atomics: results are bitwise reproducible. */
 moe_status moe_ffn_forward(const moe_layer* layer, const void* x, int32_t x_dtype, int32_t T,
                            const float* topk_w, const moe_plan_buf* plan,
@@ -161,8 +163,8 @@ moe_status moe_ffn_forward(const moe_layer* layer, const void* x, int32_t x_dtyp
  * order, one stream, one workspace; the stages pass their intermediates
  * through the workspace, whose contents are only valid between the stages of
  * one call sequence with the same layer, T and x_dtype):
- *  moe_ffn_prepare  activation layout for the expert products (decode: fp16
- *                   tokens with per-token power-of-two scales; prefill: the
+ *  moe_ffn_prepare  activation layout for the expert products: fp16 tokens
+ *                   with per-token power-of-two scales (and, prefill, the
  *                   device tile list over the plan)
  *  moe_ffn_gateup   grouped gate/up projections + SwiGLU -> h rows
  *  moe_ffn_down     grouped down projections -> o rows

@@ -106,6 +106,23 @@ __device__ __forceinline__ int iq4_pos(int e) {
   return ((e & 15) >> 2) * 8 + (e >> 4) * 4 + (e & 3);
 }
 
+// Position of element i of a row in the activation layout matching the
+// weight decode of format `fmt` (IQ4_NL reorders elements inside each block).
+__device__ __forceinline__ int act_pos(int fmt, int i) {
+  return fmt == MOE_IQ4_NL ? ((i & ~31) + iq4_pos(i & 31)) : i;
+}
+
+// Exponent e such that max|x| * 2^-e lies in [2^14, 2^15) (0 for an all-zero row).
+__device__ __forceinline__ int x16_exponent(float mx) {
+  int ex = 0;
+  if (mx > 0.0f && mx < __builtin_inff()) {
+    int e2;
+    frexpf(mx, &e2);  // mx = m * 2^e2, m in [0.5, 1)
+    ex = max(-100, min(100, e2 - 15));
+  }
+  return ex;
+}
+
 // ---------------------------------------------------------------- Q8_0
 
 // One dword of int8 codes -> four exact fp16 values (in order).

@@ -105,12 +105,6 @@ __device__ __forceinline__ f16x8 decode_b(const u32x4& c, int i, uint32_t sraw) 
   }
 }
 
-// Position of element i of a row in the activation layout matching the
-// weight decode of format `fmt` (IQ4_NL reorders elements inside each block).
-__device__ __forceinline__ int act_pos(int fmt, int i) {
-  return fmt == MOE_IQ4_NL ? ((i & ~31) + iq4_pos(i & 31)) : i;
-}
-
 // Columns (token or hi/lo parts) per N-tile: block-diagonal formats use four
 // (one per lane group's block); the NVFP4-style format uses the first eight
 // rows of the dense 16-row A operand (the other eight stay zero).
@@ -482,17 +476,6 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
       }
     }
   }
-}
-
-// Exponent e such that max|x| * 2^-e lies in [2^14, 2^15) (0 for an all-zero row).
-__device__ __forceinline__ int x16_exponent(float mx) {
-  int ex = 0;
-  if (mx > 0.0f && mx < __builtin_inff()) {
-    int e2;
-    frexpf(mx, &e2);  // mx = m * 2^e2, m in [0.5, 1)
-    ex = max(-100, min(100, e2 - 15));
-  }
-  return ex;
 }
 
 // ----------------------------------------------------------------------------

@@ -1,11 +1,12 @@
 // Prefill path of the routed experts (T > 64): grouped GEMMs over the expert
-// plan, the one place the layer is a dense contraction.  Tiles of quantised
-// weights are dequantised to bf16 (round to nearest even of the exact value)
-// into LDS and multiplied with bf16 activations on v_mfma_f32_16x16x32_bf16
-// with fp32 accumulation.  The device-side tile list walks (slot, M-tile)
-// pairs, one slot per active expert plus the shared expert, so hot experts get
-// many tiles and cold ones a single ragged tile ("device-planned MoE tail" +
-// "grouped kernels", UD-IQ2_XS (L4 fix) page, "What was changed").
+// plan, the one place the layer is a dense contraction.  Quantised weights are
+// decoded in registers to fp16 (the exact code times the block scale, rounded
+// once) and multiplied with fp16 activations (tokens scaled by a power of two
+// per token, so bf16 tokens are exact) on v_mfma_f32_16x16x32_f16 with fp32
+// accumulation.  The device-side tile list walks (slot, M-tile) pairs, one
+// slot per active expert plus the shared expert, so hot experts get many tiles
+// and cold ones a single ragged tile ("device-planned MoE tail" + "grouped
+// kernels", UD-IQ2_XS (L4 fix) page, "What was changed").
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -15,7 +16,7 @@
 
 namespace qre {
 
-constexpr int kBM = 128;   // plan rows per tile
+constexpr int kBM = 96;    // plan rows per tile
 
 struct PrefillArgs {
   QMatDev mat[2];
@@ -27,32 +28,59 @@ struct PrefillArgs {
   const int32_t* n_active;
   const int32_t* mstart;   // [n_slots + 1] first M-tile of each slot
   int T, k;
-  const void* x;           // gate/up: tokens [T][d] (bf16 or fp32)
-  int x_bf16;
-  const uint16_t* hin;     // down: H bf16 [(T*k+T)][f]
-  uint16_t* hout;          // gate/up: H bf16
+  const f16* x16;          // gate/up: scaled fp16 tokens [T][d] (weight-decode layout)
+  const float* xs;         // gate/up: scale of each token row (a power of two)
+  int down_type;           // gate/up: layout of the H rows
+  const f16* hin;          // down: H fp16 [(T*k+T)][f]
+  f16* hout;               // gate/up: H
   uint16_t* o;             // down: O bf16 [(T*k+T)][d]
+  int32_t* error;
 };
 
-// Build the tile list: mstart[s] = sum over earlier slots of ceil(rows / kBM).
-__global__ __launch_bounds__(1024) void k_pf_tiles(const int32_t* __restrict__ offsets,
-                                                   const int32_t* __restrict__ active,
-                                                   const int32_t* __restrict__ n_active, int has_shared, int T,
-                                                   int32_t* __restrict__ mstart) {
-  __shared__ int32_t part[1024];
+// Preparation, one launch: workgroups 0 .. T-1 write the scaled fp16 copy of
+// their token (max |x| scaled into [2^14, 2^15), elements in the layout the
+// gate/up weights decode to); workgroup T builds the tile list,
+// mstart[s] = sum over earlier slots of ceil(rows / kBM).
+template <bool XB>
+__global__ __launch_bounds__(256) void k_pf_prepare(const void* __restrict__ x, int T, int d, int gate_fmt,
+                                                    f16* __restrict__ x16, float* __restrict__ xs,
+                                                    const int32_t* __restrict__ offsets,
+                                                    const int32_t* __restrict__ active,
+                                                    const int32_t* __restrict__ n_active, int has_shared,
+                                                    int32_t* __restrict__ mstart) {
+  __shared__ int32_t part[256];
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  if ((int)blockIdx.x < T) {
+    const long t = blockIdx.x;
+    auto ld = [&](int i) -> float {
+      return XB ? bf16_bits_to_f32(((const uint16_t*)x)[t * d + i]) : ((const float*)x)[t * d + i];
+    };
+    float mx = 0.0f;
+    for (int i = tid; i < d; i += 256) mx = fmaxf(mx, fabsf(ld(i)));
+    mx = wave_max(mx);
+    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const int ex = x16_exponent(mx);
+    const float down = ldexpf(1.0f, -ex);
+    for (int i = tid; i < d; i += 256) x16[t * d + act_pos(gate_fmt, i)] = (f16)(ld(i) * down);
+    if (tid == 0) xs[t] = ldexpf(1.0f, ex);
+    return;
+  }
   const int n_slots = *n_active + has_shared;
-  const int per = (n_slots + blockDim.x - 1) / blockDim.x;
-  const int s0 = threadIdx.x * per, s1 = min(n_slots, s0 + per);
+  const int per = (n_slots + 255) / 256;
+  const int s0 = tid * per, s1 = min(n_slots, s0 + per);
   int sum = 0;
   for (int s = s0; s < s1; ++s) {
     const int cnt = (s < *n_active) ? offsets[active[s] + 1] - offsets[active[s]] : T;
     sum += (cnt + kBM - 1) / kBM;
   }
-  part[threadIdx.x] = sum;
+  part[tid] = sum;
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     int run = 0;
-    for (int i = 0; i < (int)blockDim.x; ++i) {
+    for (int i = 0; i < 256; ++i) {
       const int v = part[i];
       part[i] = run;
       run += v;
@@ -60,7 +88,7 @@ __global__ __launch_bounds__(1024) void k_pf_tiles(const int32_t* __restrict__ o
     mstart[n_slots] = run;
   }
   __syncthreads();
-  int run = part[threadIdx.x];
+  int run = part[tid];
   for (int s = s0; s < s1; ++s) {
     mstart[s] = run;
     const int cnt = (s < *n_active) ? offsets[active[s] + 1] - offsets[active[s]] : T;
@@ -78,35 +106,38 @@ __device__ __forceinline__ int find_slot(const int32_t* mstart, int n_slots, int
 }
 
 // ----------------------------------------------------------------------------
-// Grouped GEMM tile: 128 plan rows (M) x 64 * NF weight rows (N), K in
+// Grouped GEMM tile: kBM = 96 plan rows (M) x 64 * NF weight rows (N), K in
 // stages of 128.
 //
-// Activations (A operand of v_mfma_f32_16x16x32_bf16, bf16) are copied
-// global -> LDS by 16-byte LDS-DMA loads (no registers), double-buffered: the
-// next stage's copies are in flight while the current stage computes.  The
-// LDS tile is [128 rows][16 chunks of 8 elements], chunk c of row r stored at
-// c ^ (r & 15) so that the 16 rows a fragment read touches fall in distinct
-// banks; each lane of a copy picks the source chunk that lands at its LDS slot.
+// Activations (A operand of v_mfma_f32_16x16x32_f16) are copied global -> LDS
+// by 16-byte LDS-DMA loads (no registers), double-buffered: the next stage's
+// copies are in flight while the current stage computes.  The LDS tile is
+// [96 rows][16 chunks of 8 elements], chunk c of row r stored at c ^ (r & 15)
+// so that the 16 rows a fragment read touches fall in distinct banks; each
+// lane of a copy picks the source chunk that lands at its LDS slot.
 //
 // Weights (B operand) never pass through LDS: lane (n, G) of a wavefront loads,
 // for each of its NF row fragments, the codes of quant block G of the stage
-// (row n of the fragment) and decodes them in registers to bf16 = RNE(exact
-// value); MFMA i of the stage takes elements 8i .. 8i+7 of each lane group's
-// block, and the A fragment reads the matching activation chunk.  One MFMA
-// thus reduces over four blocks; the K order of a sum is immaterial to the
-// GEMM, so this is the plain product with exactly the oracle's bf16 weights.
+// (row n of the fragment) and decodes them in registers to fp16; MFMA i of the
+// stage takes code dword i of each lane group's block, and the A fragment
+// reads the activation chunk holding the same elements (the activation rows
+// are stored in the order the weights decode to).  One MFMA thus reduces over
+// four blocks; the K order of a sum is immaterial to the GEMM.
 //
-// Eight wavefronts (two per SIMD, so that one's decode and LDS reads overlap
-// the other's MFMAs) each hold all 128 M rows and NF weight-row fragments:
-// GATEUP: wave w holds f-rows [16w, 16w+16) of the tile's 128, as a gate and
-//         an up fragment (NF = 2), so SwiGLU is formed in registers.
+// Four wavefronts each hold all 96 M rows and NF = 4 weight-row fragments, so
+// that every A fragment read from LDS feeds four MFMAs; two workgroups share a
+// CU (IQ4_NL: at most 256 registers per lane), so that one wavefront's MFMAs
+// overlap the other's LDS reads and weight decode on each SIMD.  (96 rows
+// measured faster than 112 within that budget.)
+// GATEUP: wave w holds f-rows [32w, 32w+32) of the tile's 128, as two gate and
+//         two up fragments, so SwiGLU is formed in registers.
 // DOWN:   wave w holds 16 * NF consecutive d-rows.
 // ----------------------------------------------------------------------------
 constexpr int kPfBK = 128;                       // K per stage
 constexpr int kPfMF = kBM / 16;                  // M fragments
 constexpr int kPfBuf = kBM * kPfBK * 2;          // bytes of one activation buffer
 constexpr int kXcds = 8;                         // accelerator complex dies of an MI355X
-constexpr int kPfWaves = 8;                      // wavefronts per workgroup (two per SIMD)
+constexpr int kPfWaves = 4;                      // wavefronts per workgroup
 constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfCopies = kBM * kPfBK * 2 / (16 * kPfThreads);  // 16-byte copies per thread per stage
 
@@ -122,59 +153,36 @@ struct PfCodes {
 
 template <int FMT>
 __device__ __forceinline__ void pf_load_codes(const uint8_t* crow, const uint8_t* srow, int kel, PfCodes<FMT>& pc) {
-  // (non-temporal: each weight tile is read by few workgroups, close together)
   if constexpr (FMT == MOE_Q8_0) {
-    pc.c[0] = __builtin_nontemporal_load((const u32x4*)(crow + kel));
-    pc.c[1] = __builtin_nontemporal_load((const u32x4*)(crow + kel + 16));
+    pc.c[0] = *(const u32x4*)(crow + kel);
+    pc.c[1] = *(const u32x4*)(crow + kel + 16);
   } else {
-    pc.c[0] = __builtin_nontemporal_load((const u32x4*)(crow + (kel >> 1)));
+    pc.c[0] = *(const u32x4*)(crow + (kel >> 1));
   }
-  pc.sc = __builtin_nontemporal_load((const uint16_t*)srow + (kel >> 5));
+  pc.sc = ((const uint16_t*)srow)[kel >> 5];
 }
 
-// Four biased bytes u (= value + 128) times scale d, rounded once to bf16: the
-// products (u - 128) * d are exact in fp32 (at most 19 significant bits), so
-// fma(u, d, -128 d) is exact and the bf16 rounding is the only one.
-__device__ __forceinline__ u32x2 pf_biased4_to_bf16(uint32_t u, float d) {
-  const float nd = -128.0f * d;
-  const float v0 = fmaf((float)(u & 0xffu), d, nd);
-  const float v1 = fmaf((float)((u >> 8) & 0xffu), d, nd);
-  const float v2 = fmaf((float)((u >> 16) & 0xffu), d, nd);
-  const float v3 = fmaf((float)(u >> 24), d, nd);
-  return u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-}
-
-// bf16 weights of MFMA i: elements 8i .. 8i+7 of the lane's 32-element chunk,
-// in natural order.
+// fp16 weights of MFMA i (code dword i of the lane's block-sized chunk):
+// Q8_0 / IQ4_NL: the exact code values (fp16 integers) times the fp16 block
+// scale, rounded once; NVFP4: e2m1 * e4m3, exact in fp16 (the tensor scale is
+// applied to the fp32 result).
 template <int FMT>
-__device__ __forceinline__ bf16x8 pf_decode(const PfCodes<FMT>& pc, int i, float ts) {
-  if constexpr (FMT == MOE_IQ4_NL) {
-    // elements 0..15 are the low nibbles of bytes 0..15, elements 16..31 the high ones
-    const uint32_t w0 = pc.c[0][2 * (i & 1)], w1 = pc.c[0][2 * (i & 1) + 1];
-    const int sh = (i >> 1) * 4;
-    const float d = f16_bits_to_f32(pc.sc);
-    const u32x2 a = pf_biased4_to_bf16(iq4_lookup4((w0 >> sh) & 0x0F0F0F0Fu), d);
-    const u32x2 b = pf_biased4_to_bf16(iq4_lookup4((w1 >> sh) & 0x0F0F0F0Fu), d);
-    return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
-  } else if constexpr (FMT == MOE_Q8_0) {
-    const float d = f16_bits_to_f32(pc.sc);
-    const u32x2 a = pf_biased4_to_bf16(pc.c[i >> 1][2 * (i & 1)] ^ 0x80808080u, d);
-    const u32x2 b = pf_biased4_to_bf16(pc.c[i >> 1][2 * (i & 1) + 1] ^ 0x80808080u, d);
-    return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
-  } else {
-    // e2m1 * e4m3 is exact in fp16; times the tensor scale rounds once in fp32
+__device__ __forceinline__ f16x8 pf_decode(const PfCodes<FMT>& pc, int i) {
+  if constexpr (FMT == MOE_NVFP4) {
     const uint32_t sbyte = (i < 2) ? (pc.sc & 0xffu) : ((pc.sc >> 8) & 0xffu);
-    const f16x8 q = fp4_dword_to_f16x8(pc.c[0][i], (f16)e4m3_to_f32(sbyte));
-    u32x4 r;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = pack_bf16x2((float)q[2 * j] * ts, (float)q[2 * j + 1] * ts);
-    return __builtin_bit_cast(bf16x8, r);
+    return fp4_dword_to_f16x8(pc.c[0][i], (f16)e4m3_to_f32(sbyte));
+  } else {
+    const f16 d = __builtin_bit_cast(f16, (uint16_t)pc.sc);
+    const f16x8 dd = {d, d, d, d, d, d, d, d};
+    if constexpr (FMT == MOE_IQ4_NL) return iq4_dword_to_f16x8(pc.c[0][i]) * dd;
+    return q8_dwords_to_f16x8(pc.c[i >> 1][2 * (i & 1)], pc.c[i >> 1][2 * (i & 1) + 1]) * dd;
   }
 }
 
 template <int FMT, bool GATEUP, int NF>
-__global__ __launch_bounds__(kPfThreads) void k_pf_gemm(const PrefillArgs a) {
+__global__ __launch_bounds__(kPfThreads, FMT == MOE_IQ4_NL ? 2 : 1) void k_pf_gemm(const PrefillArgs a) {
   extern __shared__ __align__(16) uint8_t sAbuf[];  // [2][kBM][16 chunks][16 B]
+  __shared__ float s_rsx[kBM];                      // gate/up: token scale of each tile row
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int n = lane & 15, G = lane >> 4;
   const QMatDev& M0 = a.mat[0];
@@ -185,7 +193,13 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(const PrefillArgs a) {
   const int total = a.mstart[n_slots] * n_ntiles;
   const int crb = code_row_bytes(FMT, K), srb = scale_row_bytes(FMT, K);
   const int nstages = K / kPfBK;
-  const uint16_t* act = GATEUP ? (const uint16_t*)a.x : a.hin;  // bf16 [rows][K]
+  const f16* act = GATEUP ? a.x16 : a.hin;  // fp16 [rows][K]
+
+  // A fragment of step i: row mi*16 + n, logical chunk 4G + i, stored at
+  // chunk (4G + i) ^ n; the fragment index adds mi * 4096 bytes
+  int aoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) aoff[i] = (n * 16 + ((4 * G + i) ^ n)) * 16;
 
   // Workgroups are dealt to the XCDs round-robin by index; each XCD takes a
   // contiguous run of items (the N-tiles of an M-tile, then the next M-tiles
@@ -214,13 +228,12 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(const PrefillArgs a) {
     // ---- this lane's weight rows (one per fragment)
     const uint8_t* bc[NF];
     const uint8_t* bs[NF];
-    float ts[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       int mi = 0, wr;
       if constexpr (GATEUP) {
-        mi = f / (NF / 2);                                                // gate, then up
-        wr = nt * (kPfWaves * 8 * NF) + wid * (8 * NF) + (f % (NF / 2)) * 16 + n;   // same f-rows for both
+        mi = f / (NF / 2);                                                       // gate, then up
+        wr = nt * (kPfWaves * 8 * NF) + wid * (8 * NF) + (f % (NF / 2)) * 16 + n;  // same f-rows for both
       } else {
         wr = nt * (kPfWaves * 16 * NF) + wid * (16 * NF) + f * 16 + n;
       }
@@ -228,7 +241,11 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(const PrefillArgs a) {
       const long rw = (long)e * rows + wr;
       bc[f] = W.codes + rw * crb;
       bs[f] = W.scales + rw * srb;
-      ts[f] = (FMT == MOE_NVFP4) ? W.ts[e] : 1.0f;
+    }
+    float tsg = 1.0f, tsu = 1.0f;  // NVFP4 tensor scales (gate, up / down)
+    if constexpr (FMT == MOE_NVFP4) {
+      tsg = (is_sh ? a.smat[0] : a.mat[0]).ts[e];
+      if constexpr (GATEUP) tsu = (is_sh ? a.smat[1] : a.mat[1]).ts[e];
     }
 
     // ---- activation copies: wave w, copy q covers LDS chunks (w*C+q)*64 + lane,
@@ -269,6 +286,15 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(const PrefillArgs a) {
     PfCodes<FMT> pc[NF], pn[NF];
     copy_a(0, 0);
     load_b(0, pc);
+    // gate/up: the token scale of tile row tid, kept for the epilogue
+    float rsx = 0.0f;
+    if constexpr (GATEUP) {
+      if (tid < kBM) {
+        const int rr = m0 + tid;
+        const int rs = rr < cnt ? rr : 0;
+        rsx = a.xs[is_sh ? rs : a.row_token[row0 + rs]];
+      }
+    }
     for (int s = 0; s < nstages; ++s) {
       __builtin_amdgcn_s_waitcnt(0);  // this stage's copies and codes have landed
       __syncthreads();                // ... for every wave; the other buffer is free
@@ -277,48 +303,27 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(const PrefillArgs a) {
         load_b(s + 1, pn);
       }
       const uint8_t* sa = sAbuf + (s & 1) * kPfBuf;
-      // Software pipeline over the stage's four MFMA steps: step i+1's A
-      // fragments (LDS) and B fragments (decoded in registers) are produced
-      // while step i's MFMAs run; the scheduling groups below interleave one
-      // MFMA with a few VALU decode instructions and LDS reads.
-      auto read_a = [&](int i, bf16x8 (&af)[kPfMF]) {
-        const int c = 4 * G + i;  // logical chunk of MFMA step i
-#pragma unroll
-        for (int mi = 0; mi < kPfMF; ++mi)
-          af[mi] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sa + ((mi * 16 + n) * 16 + (c ^ n)) * 16));
-      };
-      bf16x8 afc[kPfMF], afn[kPfMF], bwc[NF], bwn[NF];
-      read_a(0, afc);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) bwc[f] = pf_decode<FMT>(pc[f], 0, ts[f]);
+      // The stage's four MFMA steps; the SIMD's other wavefront (two
+      // workgroups per CU) overlaps its MFMAs with this one's LDS reads and
+      // weight decode.
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (i < 3) {
-          read_a(i + 1, afn);
+        const uint8_t* p = sa + aoff[i];
+        f16x8 af[kPfMF], bw[NF];
 #pragma unroll
-          for (int f = 0; f < NF; ++f) bwn[f] = pf_decode<FMT>(pc[f], i + 1, ts[f]);
-        }
+        for (int mi = 0; mi < kPfMF; ++mi) af[mi] = __builtin_bit_cast(f16x8, *(const u32x4*)(p + mi * 4096));
+#pragma unroll
+        for (int f = 0; f < NF; ++f) bw[f] = pf_decode<FMT>(pc[f], i);
 #pragma unroll
         for (int mi = 0; mi < kPfMF; ++mi)
 #pragma unroll
           for (int f = 0; f < NF; ++f)
-            acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afc[mi], bwc[f], acc[mi][f], 0, 0, 0);
-        if (i < 3) {
-#pragma unroll
-          for (int g = 0; g < kPfMF * NF; ++g) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // up to four VALU
-            if (g % 4 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-          }
-#pragma unroll
-          for (int mi = 0; mi < kPfMF; ++mi) afc[mi] = afn[mi];
-#pragma unroll
-          for (int f = 0; f < NF; ++f) bwc[f] = bwn[f];
-        }
+            acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mi], bw[f], acc[mi][f], 0, 0, 0);
       }
 #pragma unroll
       for (int f = 0; f < NF; ++f) pc[f] = pn[f];
     }
+    if (GATEUP && tid < kBM) s_rsx[tid] = rsx;
     __syncthreads();  // the next item's first copy must not overwrite a buffer still being read
 
     // ---- epilogue: D row (M) = mi*16 + 4G + v, column (N) = fragment row n
@@ -330,18 +335,20 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(const PrefillArgs a) {
         if (rr >= cnt) continue;
         const long orow = row0 + rr;
         if constexpr (GATEUP) {
+          const float sx = s_rsx[mi * 16 + 4 * G + v];
 #pragma unroll
           for (int f = 0; f < NF / 2; ++f) {
-            const float g = acc[mi][f][v], u = acc[mi][f + NF / 2][v];
+            const float g = acc[mi][f][v] * sx * tsg, u = acc[mi][f + NF / 2][v] * sx * tsu;
             const float hv = g / (1.0f + __expf(-g)) * u;
+            if (!(fabsf(hv) < 65504.0f)) atomicOr(a.error, 2);
             const int fcol = nt * (kPfWaves * 8 * NF) + wid * (8 * NF) + f * 16 + n;
-            a.hout[orow * rows + fcol] = (uint16_t)f32_to_bf16_bits(hv);
+            a.hout[orow * rows + act_pos(a.down_type, fcol)] = (f16)hv;
           }
         } else {
 #pragma unroll
           for (int f = 0; f < NF; ++f) {
             const int dcol = nt * (kPfWaves * 16 * NF) + wid * (16 * NF) + f * 16 + n;
-            a.o[orow * rows + dcol] = (uint16_t)f32_to_bf16_bits(acc[mi][f][v]);
+            a.o[orow * rows + dcol] = (uint16_t)f32_to_bf16_bits(acc[mi][f][v] * tsg);
           }
         }
       }
@@ -349,21 +356,14 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gemm(const PrefillArgs a) {
   }
 }
 
-// fp32 tokens -> bf16 (RNE), for the prefill products.
-__global__ __launch_bounds__(256) void k_pf_x_bf16(const float* __restrict__ x, long n4, uint16_t* __restrict__ xb) {
-  for (long i = blockIdx.x * 256L + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
-    const f32x4 v = ((const f32x4*)x)[i];
-    ((u32x2*)xb)[i] = u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
-  }
-}
-
 namespace {
 
 struct PrefillWs {
   int32_t* mstart;
-  uint16_t* h;
+  f16* h;
   uint16_t* o;
-  uint16_t* xb;  // bf16 copy of fp32 tokens
+  f16* x16;   // scaled fp16 tokens
+  float* xs;  // their scales
 };
 
 PrefillWs carve(void* ws, int T, int d, int f, int k, int E) {
@@ -372,11 +372,13 @@ PrefillWs carve(void* ws, int T, int d, int f, int k, int E) {
   w.mstart = (int32_t*)p;
   p += align_up((size_t)(E + 2) * 4, 256);
   const size_t R = (size_t)T * k + T;
-  w.h = (uint16_t*)p;
+  w.h = (f16*)p;
   p += align_up(R * f * 2, 256);
   w.o = (uint16_t*)p;
   p += align_up(R * d * 2, 256);
-  w.xb = (uint16_t*)p;
+  w.x16 = (f16*)p;
+  p += align_up((size_t)T * d * 2, 256);
+  w.xs = (float*)p;
   return w;
 }
 
@@ -390,8 +392,8 @@ hipError_t launch_gemm_nf(const PrefillArgs& a, int grid, hipStream_t s) {
 
 template <int FMT, bool GATEUP>
 hipError_t launch_gemm_fmt(int nf, const PrefillArgs& a, int grid, hipStream_t s) {
-  if constexpr (GATEUP) return launch_gemm_nf<FMT, true, 2>(a, grid, s);  // a gate and an up fragment
-  return nf == 2 ? launch_gemm_nf<FMT, false, 2>(a, grid, s) : launch_gemm_nf<FMT, false, 1>(a, grid, s);
+  if constexpr (GATEUP) return launch_gemm_nf<FMT, true, 4>(a, grid, s);  // two gate and two up fragments
+  return nf == 4 ? launch_gemm_nf<FMT, false, 4>(a, grid, s) : launch_gemm_nf<FMT, false, 2>(a, grid, s);
 }
 
 template <bool GATEUP>
@@ -408,7 +410,7 @@ hipError_t launch_gemm(int fmt, int nf, const PrefillArgs& a, int grid, hipStrea
 size_t prefill_ws_bytes(int T, int d, int f, int k) {
   const size_t R = (size_t)T * k + T;
   return align_up((size_t)(4096 + 2) * 4, 256) + align_up(R * f * 2, 256) + align_up(R * d * 2, 256) +
-         align_up((size_t)T * d * 2, 256);
+         align_up((size_t)T * d * 2, 256) + align_up((size_t)T * 4, 256);
 }
 
 hipError_t launch_prefill_stage(int stage, const FfnCall& c, hipStream_t s) {
@@ -416,13 +418,12 @@ hipError_t launch_prefill_stage(int stage, const FfnCall& c, hipStream_t s) {
   const int T = c.T;
   PrefillWs w = carve(c.ws, T, L.d, L.f, L.k, 4096);
   if (stage == kStagePrepare) {
-    hipLaunchKernelGGL(k_pf_tiles, dim3(1), dim3(1024), 0, s, c.p.offsets, c.p.active, c.p.n_active, L.has_shared, T,
-                       w.mstart);
-    if (c.x_dtype == MOE_F32) {
-      const long n4 = (long)T * L.d / 4;
-      hipLaunchKernelGGL(k_pf_x_bf16, dim3((unsigned)std::min<long>((n4 + 255) / 256, 4096)), dim3(256), 0, s,
-                         (const float*)c.x, n4, w.xb);
-    }
+    if (c.x_dtype == MOE_BF16)
+      hipLaunchKernelGGL(k_pf_prepare<true>, dim3(T + 1), dim3(256), 0, s, c.x, T, L.d, L.gate.type, w.x16, w.xs,
+                         c.p.offsets, c.p.active, c.p.n_active, L.has_shared, w.mstart);
+    else
+      hipLaunchKernelGGL(k_pf_prepare<false>, dim3(T + 1), dim3(256), 0, s, c.x, T, L.d, L.gate.type, w.x16, w.xs,
+                         c.p.offsets, c.p.active, c.p.n_active, L.has_shared, w.mstart);
     return hipGetLastError();
   }
   if (stage == kStageCombine)
@@ -436,6 +437,7 @@ hipError_t launch_prefill_stage(int stage, const FfnCall& c, hipStream_t s) {
   a.mstart = w.mstart;
   a.T = T;
   a.k = L.k;
+  a.error = c.p.error;
   const int max_slots = (T * L.k < L.E ? T * L.k : L.E) + (L.has_shared ? 1 : 0);
   const long max_mtiles = ((long)T * L.k + kBM - 1) / kBM + max_slots + (T + kBM - 1) / kBM;
   if (stage == kStageGateUp) {
@@ -445,21 +447,22 @@ hipError_t launch_prefill_stage(int stage, const FfnCall& c, hipStream_t s) {
       a.smat[0] = qmat_dev(L.shared_gate);
       a.smat[1] = qmat_dev(L.shared_up);
     }
-    a.x = c.x_dtype == MOE_BF16 ? c.x : (const void*)w.xb;
-    a.x_bf16 = 1;
+    a.x16 = w.x16;
+    a.xs = w.xs;
+    a.down_type = L.down.type;
     a.hout = w.h;
-    // a gate and an up fragment per wavefront: a tile of 128 f-rows
+    // two gate and two up fragments per wavefront: a tile of 128 f-rows
     const long items = max_mtiles * (L.f / 128);
     const int grid = (int)(items < 8192 ? items : 8192) / kXcds * kXcds + kXcds;
-    return launch_gemm<true>(L.gate.type, 2, a, grid, s);
+    return launch_gemm<true>(L.gate.type, 4, a, grid, s);
   }
   a.mat[0] = qmat_dev(L.down);
   if (L.has_shared) a.smat[0] = qmat_dev(L.shared_down);
   a.hin = w.h;
   a.o = w.o;
   // 256 d-rows per tile where d allows, else 128
-  const int nf = (L.d % 256 == 0) ? 2 : 1;
-  const long items = max_mtiles * (L.d / (128 * nf));
+  const int nf = (L.d % 256 == 0) ? 4 : 2;
+  const long items = max_mtiles * (L.d / (64 * nf));
   const int grid = (int)(items < 8192 ? items : 8192) / kXcds * kXcds + kXcds;
   return launch_gemm<false>(L.down.type, nf, a, grid, s);
 }

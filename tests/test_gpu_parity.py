@@ -3,7 +3,8 @@ CPU oracle on the same seeded inputs.
 
 Bars: bit-exact dequantised weights, top-k indices (near-tie rule in
 parity_common) and expert plan; rel-L2 <= 1e-4 for the fp32-accumulated decode
-path and <= 1e-2 for the bf16-MFMA prefill path."""
+path and <= 1e-2 for the fp16-MFMA prefill path (weights and SwiGLU
+activations rounded to fp16)."""
 
 import numpy as np
 import pytest
@@ -239,15 +240,15 @@ def test_prefill_path_small(types, T, y_dtype):
 @pytest.mark.parametrize("types", [("q8_0", "q8_0", "iq4_nl"), ("iq4_nl", "iq4_nl", "nvfp4")], ids=lambda t: "-".join(t))
 def test_prefill_narrow_shapes_fp32_tokens(types):
     """d not a multiple of 256 (half-width down tiles), f = 128 (one gate/up
-    tile), fp32 tokens converted to bf16 when staged, many ragged M-tiles."""
+    tile), fp32 tokens rounded to fp16 when staged, many ragged M-tiles."""
     T = 200
     _say(f"[prefill narrow] {types} T={T}")
     wl, layer = _small_layer(500, d=384, f=128, E=24, k=3, types=types)
     x = torch.randn((T, wl.d), generator=torch.Generator().manual_seed(7))
     st, gpu = _run_single(layer, x, "f32", "f32")
     lnp = synth.layer_to_numpy(layer)
-    # the router sees the fp32 tokens; the bf16 expert products see them rounded to
-    # bf16, an error of the same order as the bf16 weights', inside the prefill bar
+    # the router sees the fp32 tokens; the fp16 expert products see them rounded to
+    # fp16, an error of the same order as the fp16 weights', inside the prefill bar
     stats = check_layer(lnp, x.numpy().astype(np.float64), gpu, "f64", TOL_PREFILL)
     _say(f"[prefill narrow] {stats}")
 

@@ -201,6 +201,108 @@ __global__ __launch_bounds__(256) void k_router_gemm_f32(const float* __restrict
   }
 }
 
+// T > 64 with bf16 tokens: logits on bf16 MFMA.  Each fp32 router weight is
+// the exact sum of three bf16 parts (its top 8 significand bits, the next 8,
+// the last 8: each remainder is exact in fp32), and a bf16 token times a bf16
+// part is exact in fp32, so three MFMAs per product give fp32-accumulated
+// dot products of the fp32 weights with the bf16 tokens.  A workgroup covers
+// 64 tokens x 128 experts; wavefront w holds all 64 tokens (four M fragments)
+// and experts [32w, 32w+32) (two N fragments).  Operands come straight from
+// global memory (the four wavefronts read the same token fragments, which L1
+// serves), K in chunks of 32, the next chunk's loads in flight.
+constexpr int kRmTok = 64, kRmExp = 128;
+
+__device__ __forceinline__ void split_bf16x3(const f32x4 (&w)[2], bf16x8& p1, bf16x8& p2, bf16x8& p3) {
+  uint32_t u[8], r1[8], r2[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    u[j] = __float_as_uint(w[j >> 2][j & 3]);
+    const float a = __uint_as_float(u[j]) - __uint_as_float(u[j] & 0xffff0000u);
+    r1[j] = __float_as_uint(a);
+    r2[j] = __float_as_uint(a - __uint_as_float(r1[j] & 0xffff0000u));
+  }
+  u32x4 q1, q2, q3;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // the upper halves of elements 2j, 2j+1
+    q1[j] = __builtin_amdgcn_perm(u[2 * j + 1], u[2 * j], 0x07060302u);
+    q2[j] = __builtin_amdgcn_perm(r1[2 * j + 1], r1[2 * j], 0x07060302u);
+    q3[j] = __builtin_amdgcn_perm(r2[2 * j + 1], r2[2 * j], 0x07060302u);
+  }
+  p1 = __builtin_bit_cast(bf16x8, q1);
+  p2 = __builtin_bit_cast(bf16x8, q2);
+  p3 = __builtin_bit_cast(bf16x8, q3);
+}
+
+__global__ __launch_bounds__(256) void k_router_mfma(const float* __restrict__ W, const float* __restrict__ bias,
+                                                     const uint16_t* __restrict__ x, int T, int E, int d,
+                                                     float* __restrict__ logits) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int n = lane & 15, G = lane >> 4;
+  const int t0 = blockIdx.y * kRmTok, e0 = blockIdx.x * kRmExp + wid * 32;
+  // this lane's rows (rows past the end repeat the last one and are not stored)
+  const uint16_t* xr[4];
+  const float* wr[2];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) xr[mi] = x + (long)min(t0 + mi * 16 + n, T - 1) * d + 8 * G;
+#pragma unroll
+  for (int f = 0; f < 2; ++f) wr[f] = W + (long)min(e0 + f * 16 + n, E - 1) * d + 8 * G;
+
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int f = 0; f < 2; ++f) acc[mi][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto load = [&](int kc, u32x4 (&xa)[4], f32x4 (&wb)[2][2]) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) xa[mi] = *(const u32x4*)(xr[mi] + kc);
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      wb[f][0] = *(const f32x4*)(wr[f] + kc);
+      wb[f][1] = *(const f32x4*)(wr[f] + kc + 4);
+    }
+  };
+  auto compute = [&](const u32x4 (&xa)[4], const f32x4 (&wb)[2][2]) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      bf16x8 p1, p2, p3;
+      split_bf16x3(wb[f], p1, p2, p3);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, xa[mi]);
+        acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, p1, acc[mi][f], 0, 0, 0);
+        acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, p2, acc[mi][f], 0, 0, 0);
+        acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, p3, acc[mi][f], 0, 0, 0);
+      }
+    }
+  };
+  // two chunks per iteration (d is a multiple of 128); past the end the
+  // prefetch repeats the last chunk and is not used
+  u32x4 xa0[4], xa1[4];
+  f32x4 wb0[2][2], wb1[2][2];
+  load(0, xa0, wb0);
+  for (int kc = 0; kc < d; kc += 64) {
+    load(kc + 32, xa1, wb1);
+    compute(xa0, wb0);
+    load(min(kc + 64, d - 32), xa0, wb0);
+    compute(xa1, wb1);
+  }
+  // D row 4G + v of fragment (mi, f): token t0 + mi*16 + 4G + v, expert e0 + f*16 + n
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int e = e0 + f * 16 + n;
+    if (e >= E) continue;
+    const float bv = bias ? bias[e] : 0.0f;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = t0 + mi * 16 + 4 * G + v;
+        if (t < T) logits[(long)t * E + e] = acc[mi][f][v] + bv;
+      }
+  }
+}
+
 hipError_t launch_router_logits(const float* W, const float* b, const void* x, int x_dtype, int T, int E, int d,
                                 float* logits, hipStream_t s) {
   const int xb = x_dtype == MOE_BF16 ? 1 : 0;
@@ -209,6 +311,9 @@ hipError_t launch_router_logits(const float* W, const float* b, const void* x, i
       hipLaunchKernelGGL(k_router_gemv_f64<true>, dim3(E), dim3(256), 0, s, W, b, x, T, E, d, logits);
     else
       hipLaunchKernelGGL(k_router_gemv_f64<false>, dim3(E), dim3(256), 0, s, W, b, x, T, E, d, logits);
+  } else if (xb) {
+    hipLaunchKernelGGL(k_router_mfma, dim3((E + kRmExp - 1) / kRmExp, (T + kRmTok - 1) / kRmTok), dim3(256), 0, s, W,
+                       b, (const uint16_t*)x, T, E, d, logits);
   } else {
     hipLaunchKernelGGL(k_router_gemm_f32, dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, s, W, b, x, xb, T, E, d,
                        logits);

@@ -216,8 +216,9 @@ typedef struct moe_stack_record {
  * moe_residual_rmsnorm; the layer itself follows the routing and expert
  * passages cited at moe_route, moe_plan and moe_ffn_forward).  Each layer is
  * three kernel launches for T = 1 (glue + router; top-k + plan + gate/up +
- * SwiGLU; down) and four for T > 1 (the glue gets its own launch); the last
- * layer's combine is folded into h by one more launch.  Routing and the plan
+ * SwiGLU; down, whose last workgroup per 64-column tile forms the combine and
+ * the new residual) and four for T > 1 (the glue gets its own launch).
+ * Routing and the plan
  * are recomputed in every workgroup of the gate/up launch from the logits,
  * so no launch waits on a separate plan kernel.
  *   layers:  HOST array of n_layers descriptors of one shape (d, f, E, k,

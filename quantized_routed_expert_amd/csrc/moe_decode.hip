@@ -8,8 +8,63 @@
 
 namespace qre {
 
+// Fused step, down pass: the combine of one 64-column tile, by the last
+// workgroup to finish the tile.  Wavefront w takes tokens w, w+4, ...; lane c
+// column 64*ct + c.  y sums the shared row, then the routed slots in order j;
+// the tile's sum of squares of the new residual is a wavefront reduction.
+__device__ __forceinline__ void fz_combine_tile(const DecodeArgs& a, int ct) {
+  const int d = a.mat[0].rows, T = a.T, k = a.k, TK = T * k;
+  const int n_ct = d / 64;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int col = ct * 64 + lane;
+  auto ld_o = [&](long i) { return __hip_atomic_load(a.o + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  // tokens wid and wid + 4 together (T <= 8), all loads of a batch in flight
+  // before any is used; rows past T or k repeat a valid one and are unused
+  for (int t0 = wid; t0 < T; t0 += 8) {
+    const int tt[2] = {t0, min(t0 + 4, T - 1)};
+    float y[2], r[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      y[u] = a.has_shared ? ld_o((long)(TK + tt[u]) * d + col) : 0.0f;
+      r[u] = a.r_in[(long)tt[u] * d + col];
+    }
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      float wj[2][8], oj[2][8];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int j = min(j0 + jj, k - 1);
+          wj[u][jj] = a.gate_w[tt[u] * k + j];
+          oj[u][jj] = ld_o((long)(tt[u] * k + j) * d + col);
+        }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          if (j0 + jj < k) y[u] = fmaf(wj[u][jj], oj[u][jj], y[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (u == 1 && t0 + 4 >= T) break;  // (wavefront-uniform)
+      const int t = tt[u];
+      const float rn = r[u] + y[u];
+      a.r_out[(long)t * d + col] = rn;
+      if (a.rec_y) a.rec_y[(long)t * d + col] = y[u];
+      const float ss = wave_sum(rn * rn);
+      if (lane == 0) a.ss_part[t * n_ct + ct] = ss;
+    }
+  }
+}
+
 // Stage kernel over a plan: global plan arrays, or (TABLE) the fused step's
-// slot table, whose routed rows go to their pair's output row.
+// slot table, whose routed rows go to their pair's output row; there the
+// workgroups of each 64-column tile count themselves done, and the last one
+// forms the tile's combine.  The o rows are written and read with agent-scope
+// atomic accesses, which bypass the XCDs' private L2 caches, and every store
+// has completed (s_waitcnt) before the count: no cache-wide fence is needed
+// (a __threadfence writes back and invalidates whole L2 caches, which costs
+// more than the combine saves).
 template <int FMT, int NT, bool GATEUP, bool ROLL, bool TABLE = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1))) void k_ffn_dq(
     const DecodeArgs a) {
@@ -41,6 +96,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
       si = SlotInfo{0, true, a.T * a.k, a.T};
     }
     dq_item<FMT, NT, GATEUP, ROLL, TABLE>(a, si, tile, wid % ksplit, a.row_token, sA);
+    if constexpr (TABLE && !GATEUP) {
+      if (a.tile_cnt) {
+        __shared__ int s_last;
+        const int ct = item % wg_per_slot;  // 64-column tile (four 16-row tiles)
+        __builtin_amdgcn_s_waitcnt(0);      // this workgroup's o rows have landed
+        __syncthreads();
+        if (threadIdx.x == 0) s_last = atomicAdd(&a.tile_cnt[ct], 1) == total / wg_per_slot - 1;
+        __syncthreads();
+        if (s_last) {
+          fz_combine_tile(a, ct);
+          if (threadIdx.x == 0) a.tile_cnt[ct] = 0;
+        }
+      }
+    }
   }
 }
 

@@ -53,6 +53,15 @@ struct DecodeArgs {
   int down_type;           // gate/up: layout of H16 rows (IQ4_NL: block-permuted)
   float* o;                // down output O [(T*k+T)][d]
   const int32_t* pair_of_row;  // fused down pass: O row of each plan row (t*k + j); null: the plan row
+  // fused down pass: the combine, formed by the last workgroup of each
+  // 64-column tile: r_out = r_in + y with y = o[T*k + t] + sum_j gate_w[t][j] *
+  // o[t*k + j], and each tile's sum of squares of r_out
+  int32_t* tile_cnt;       // [d/64] workgroups finished per tile (0 on entry, left 0)
+  const float* r_in;
+  float* r_out;
+  float* ss_part;          // [T][d/64]
+  float* rec_y;            // optional record of y
+  const float* gate_w;     // [T][k]
 };
 
 // Kernel arguments are fetched through the scalar cache at their first use;
@@ -470,7 +479,13 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
           } else {
             // fused path: routed rows go to their (token, slot) pair's row
             const int orow = (PAIRS && !si.is_sh) ? (int)s_colw[cl] : out_row;
-            a.o[(long)orow * rows + frow] = val[0];
+            if constexpr (PAIRS) {
+              // coherent across the XCDs' L2 caches: the tile's last
+              // workgroup reads these rows in this launch
+              __hip_atomic_store(a.o + (long)orow * rows + frow, val[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+              a.o[(long)orow * rows + frow] = val[0];
+            }
           }
         }
       }

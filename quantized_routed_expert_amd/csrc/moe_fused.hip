@@ -24,120 +24,74 @@ struct FusedPlan {  // plan of the current layer, written by k_fz_gateup's workg
 
 // (1) Layer input and router.
 //
-// Glue (layer l > 0): y = o[T*k + t] + sum_j topk_w[t][j] * o[t*k + j] (the
-// previous layer's combine: shared row, then the routed slots in order j; the
-// down pass writes routed rows at their pair's position), h_new = h + y, and
-// the layer input x = bf16(h_new / sqrt(mean(h_new^2) + eps)).  The first
-// layer takes x = bf16(rmsnorm(h)).  The glue writes the new residual, x (bf16,
-// and as power-of-two scaled fp16 for the expert products) and optional
-// records of the previous layer's y and this layer's x.
+// The residual r_l entering layer l is complete when the layer starts: the
+// previous layer's down pass formed its combine, y = o[T*k + t] + sum_j
+// topk_w[t][j] * o[t*k + j] (shared row, then the routed slots in order j),
+// and wrote r_l = r_{l-1} + y together with each 64-column tile's sum of
+// squares.  The glue forms the layer input x = bf16(r_l / sqrt(mean(r_l^2) +
+// eps)) from r_l and those tile sums (the first layer sums the squares
+// itself), writes x (bf16, and as power-of-two scaled fp16 for the expert
+// products) and an optional record of x, and clears the layer's error word
+// and down-pass tile counters.
 struct FzGlueArgs {
-  int d, T, k, has_shared;
-  const float* h_in;
-  float* h_out;
-  const float* o;            // previous layer's expert rows, or null (first layer)
-  const float* topk_w;       // previous layer's gate weights
-  float* rec_y;              // previous layer's y (optional)
-  uint16_t* x_out;           // bf16 layer input (null: the final fold, no next layer)
+  int d, T;
+  const float* r;            // residual entering the layer [T][d]
+  const float* ss_part;      // [T][d/64] tile sums of squares of r, or null (first layer)
+  uint16_t* x_out;           // bf16 layer input
   uint16_t* rec_x;           // optional record of the same
   f16* x16;
   float* xs;
   int gate_fmt;
   float eps;
-  int32_t* error_reset;      // the plan's error word, cleared for the next layer
+  int32_t* error_reset;      // the plan's error word, cleared for this layer
+  int32_t* tile_cnt;         // [d/64] down-pass tile counters, cleared for this layer
 };
 
 constexpr int kGlueMaxQ = 4;  // d <= 4096: float4 chunks per thread
-constexpr int kGlueRB = 8;    // routed rows whose loads are in flight together
 
 // Glue for one token, by one workgroup, in two parts so that a caller can put
-// other loads in flight between them: glue_load issues the token's residual,
-// shared row, gate weights and first kGlueRB routed rows; glue_finish forms y,
-// the new residual and the bf16 input, which it returns in v[] (as floats).
+// other loads in flight between them: glue_load issues the token's residual
+// and tile sums; glue_finish forms the bf16 input, which it returns in v[]
+// (as floats).
 struct GlueLoads {
-  f32x4 v[kGlueMaxQ];              // residual
-  f32x4 y[kGlueMaxQ];              // shared row (or zero)
-  float wj[kGlueRB];               // gate weights of the first routed rows
-  f32x4 ov[kGlueMaxQ][kGlueRB];    // the first routed rows
+  f32x4 v[kGlueMaxQ];  // residual
+  float ssp;           // tile sum of squares of lane (lanes past the tiles: 0)
 };
 
 __device__ __forceinline__ void glue_load(const FzGlueArgs& a, int t, GlueLoads& g) {
-  const int tid = threadIdx.x;
-  const int d = a.d, T = a.T, k = a.k;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int d = a.d;
   const int nq = d / 1024;
 #pragma unroll
   for (int q = 0; q < kGlueMaxQ; ++q) {
-    if (q < nq) {
-      const int i = (q * 256 + tid) * 4;
-      g.v[q] = *(const f32x4*)(a.h_in + (long)t * d + i);
-      g.y[q] = (a.o && a.has_shared) ? *(const f32x4*)(a.o + (long)(T * k + t) * d + i) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    if (q < nq) g.v[q] = *(const f32x4*)(a.r + (long)t * d + (q * 256 + tid) * 4);
   }
-  if (a.o) {
-#pragma unroll
-    for (int jj = 0; jj < kGlueRB; ++jj) g.wj[jj] = (jj < k) ? a.topk_w[t * k + jj] : 0.0f;
-#pragma unroll
-    for (int q = 0; q < kGlueMaxQ; ++q)
-#pragma unroll
-      for (int jj = 0; jj < kGlueRB; ++jj)
-        if (q < nq && jj < k) g.ov[q][jj] = *(const f32x4*)(a.o + (long)(t * k + jj) * d + (q * 256 + tid) * 4);
-  }
+  const int n_ct = d / 64;
+  g.ssp = (a.ss_part && lane < n_ct) ? a.ss_part[t * n_ct + lane] : 0.0f;
 }
 
 __device__ __forceinline__ void glue_finish(const FzGlueArgs& a, int t, bool writer, GlueLoads& g,
                                             f32x4 (&v)[kGlueMaxQ]) {
   __shared__ float red[2][4];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int d = a.d, k = a.k;
+  const int d = a.d;
   const int nq = d / 1024;
-  f32x4 y[kGlueMaxQ];
 #pragma unroll
-  for (int q = 0; q < kGlueMaxQ; ++q) {
-    v[q] = g.v[q];
-    y[q] = g.y[q];
+  for (int q = 0; q < kGlueMaxQ; ++q) v[q] = g.v[q];
+  float tot;
+  if (a.ss_part) {
+    tot = wave_sum(g.ssp);  // every wavefront sums the tiles in the same order
+  } else {
+    float ss = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kGlueMaxQ; ++q)
+      if (q < nq) ss += v[q].x * v[q].x + v[q].y * v[q].y + v[q].z * v[q].z + v[q].w * v[q].w;
+    ss = wave_sum(ss);
+    if (lane == 0) red[0][wid] = ss;
+    __syncthreads();
+    tot = red[0][0] + red[0][1] + red[0][2] + red[0][3];
   }
-  if (a.o) {
-    for (int j0 = 0; j0 < k; j0 += kGlueRB) {
-      if (j0 > 0) {  // (k > kGlueRB) the next batch of routed rows
-#pragma unroll
-        for (int jj = 0; jj < kGlueRB; ++jj) g.wj[jj] = (j0 + jj < k) ? a.topk_w[t * k + j0 + jj] : 0.0f;
-#pragma unroll
-        for (int q = 0; q < kGlueMaxQ; ++q)
-#pragma unroll
-          for (int jj = 0; jj < kGlueRB; ++jj)
-            if (q < nq && j0 + jj < k)
-              g.ov[q][jj] = *(const f32x4*)(a.o + (long)(t * k + j0 + jj) * d + (q * 256 + tid) * 4);
-      }
-#pragma unroll
-      for (int q = 0; q < kGlueMaxQ; ++q)
-#pragma unroll
-        for (int jj = 0; jj < kGlueRB; ++jj)
-          if (q < nq && j0 + jj < k) {
-            y[q].x = fmaf(g.wj[jj], g.ov[q][jj].x, y[q].x);
-            y[q].y = fmaf(g.wj[jj], g.ov[q][jj].y, y[q].y);
-            y[q].z = fmaf(g.wj[jj], g.ov[q][jj].z, y[q].z);
-            y[q].w = fmaf(g.wj[jj], g.ov[q][jj].w, y[q].w);
-          }
-    }
-  }
-  float ss = 0.0f;
-#pragma unroll
-  for (int q = 0; q < kGlueMaxQ; ++q) {
-    if (q < nq) {
-      const int i = (q * 256 + tid) * 4;
-      if (a.o) {
-        if (writer && a.rec_y) *(f32x4*)(a.rec_y + (long)t * d + i) = y[q];
-        v[q] += y[q];
-      }
-      if (writer) *(f32x4*)(a.h_out + (long)t * d + i) = v[q];
-      ss += v[q].x * v[q].x + v[q].y * v[q].y + v[q].z * v[q].z + v[q].w * v[q].w;
-    }
-  }
-  if (!a.x_out) return;  // final fold: the residual is all that is needed
-  ss = wave_sum(ss);
-  if (lane == 0) red[0][wid] = ss;
-  __syncthreads();
-  const float inv = 1.0f / sqrtf((red[0][0] + red[0][1] + red[0][2] + red[0][3]) / (float)d + a.eps);
+  const float inv = 1.0f / sqrtf(tot / (float)d + a.eps);
   float mx = 0.0f;
 #pragma unroll
   for (int q = 0; q < kGlueMaxQ; ++q) {
@@ -184,16 +138,18 @@ __device__ __forceinline__ void glue_token(const FzGlueArgs& a, int t, bool writ
   glue_finish(a, t, writer, g, v);
 }
 
+// Clears of the layer's error word and down-pass tile counters (block 0).
+__device__ __forceinline__ void glue_clear(const FzGlueArgs& a) {
+  if (blockIdx.x != 0) return;
+  if (threadIdx.x == 0 && a.error_reset) *a.error_reset = 0;
+  if (a.tile_cnt && (int)threadIdx.x < a.d / 64) a.tile_cnt[threadIdx.x] = 0;
+}
+
 __device__ __forceinline__ void glue_pin_args(const FzGlueArgs& a) {
   pin_arg(a.d);
   pin_arg(a.T);
-  pin_arg(a.k);
-  pin_arg(a.has_shared);
-  pin_arg(a.h_in);
-  pin_arg(a.h_out);
-  pin_arg(a.o);
-  pin_arg(a.topk_w);
-  pin_arg(a.rec_y);
+  pin_arg(a.r);
+  pin_arg(a.ss_part);
   pin_arg(a.x_out);
   pin_arg(a.rec_x);
   pin_arg(a.x16);
@@ -201,13 +157,14 @@ __device__ __forceinline__ void glue_pin_args(const FzGlueArgs& a) {
   pin_arg(a.gate_fmt);
   pin_arg(a.eps);
   pin_arg(a.error_reset);
+  pin_arg(a.tile_cnt);
 }
 
 // Glue for T tokens: one workgroup per token.
 __global__ __launch_bounds__(256) void k_fz_glue(const FzGlueArgs a) {
   glue_pin_args(a);
+  glue_clear(a);
   f32x4 v[kGlueMaxQ];
-  if (blockIdx.x == 0 && threadIdx.x == 0 && a.error_reset) *a.error_reset = 0;
   glue_token(a, blockIdx.x, true, v);
 }
 
@@ -265,7 +222,7 @@ __global__ __launch_bounds__(256) void k_fz_route(const FzRouteArgs a) {
   const float bias_e = (a.bias && e < a.E) ? a.bias[e] : 0.0f;
 
   if constexpr (INLINE) {
-    if (blockIdx.x == 0 && tid == 0 && a.g.error_reset) *a.g.error_reset = 0;
+    glue_clear(a.g);
     f32x4 v[kGlueMaxQ];
     glue_finish(a.g, 0, blockIdx.x == 0, gl, v);
     const int nq = d / 1024;
@@ -548,6 +505,8 @@ struct FusedWs {
   DecodeWs w;
   float* logits;
   FusedPlan plan;
+  float* ss_part;     // [T][d/64] tile sums of squares of the residual
+  int32_t* tile_cnt;  // [d/64] down-pass tile counters
 };
 
 FusedWs carve_fused(void* ws, int T, int d, int f, int k, int E) {
@@ -575,6 +534,10 @@ FusedWs carve_fused(void* ws, int T, int d, int f, int k, int E) {
   F.plan.topk_w = (float*)p;
   p += align_up(TK * 4, 256);
   F.plan.slots = (SlotEnt*)p;
+  p += align_up((TK + 1) * sizeof(SlotEnt), 256);
+  F.ss_part = (float*)p;
+  p += align_up((size_t)T * (d / 64) * 4, 256);
+  F.tile_cnt = (int32_t*)p;
   return F;
 }
 
@@ -584,7 +547,8 @@ size_t fused_ws_bytes(int T, int d, int f, int k, int E) {
   const size_t TK = (size_t)T * k;
   return 2 * align_up((size_t)T * d * 4, 256) + align_up((size_t)T * d * 2, 256) +
          decode_ws_bytes(T, d, f, k, MOE_BF16) + align_up((size_t)T * E * 4, 256) + 256 +
-         3 * align_up(TK * 4, 256) + align_up((TK + 1) * sizeof(SlotEnt), 256);
+         3 * align_up(TK * 4, 256) + align_up((TK + 1) * sizeof(SlotEnt), 256) +
+         align_up((size_t)T * (d / 64) * 4, 256) + align_up((size_t)(d / 64) * 4, 256);
 }
 
 hipError_t launch_fused_step(const moe_layer* layers, int n_layers, float* h, int T, const FusedRecord& rec,
@@ -594,21 +558,18 @@ hipError_t launch_fused_step(const moe_layer* layers, int n_layers, float* h, in
   FusedWs F = carve_fused(ws, T, d, f, k, E);
   const int max_slots = (T * k < E ? T * k : E) + (L0.has_shared ? 1 : 0);
   const bool inline_glue = T == 1;
-  const float* prev_w = nullptr;  // topk weights of the previous layer
   for (int l = 0; l < n_layers; ++l) {
     const moe_layer& L = layers[l];
     int32_t* err_word = rec.error ? rec.error + l : F.plan.error;
-    // (1) glue (previous layer's combine + residual + RMSNorm) and router
+    // residual entering the layer and leaving it (the down pass forms the latter)
+    float* r_in = l == 0 ? h : F.hb[l & 1];
+    float* r_out = l == n_layers - 1 ? h : F.hb[(l + 1) & 1];
+    // (1) layer input (RMSNorm of the residual) and router
     FzGlueArgs g{};
     g.d = d;
     g.T = T;
-    g.k = k;
-    g.has_shared = L.has_shared;
-    g.h_in = l == 0 ? h : F.hb[l & 1];
-    g.h_out = F.hb[(l + 1) & 1];
-    g.o = l == 0 ? nullptr : F.w.o;
-    g.topk_w = prev_w;
-    g.rec_y = (l > 0 && rec.y) ? rec.y + (size_t)(l - 1) * T * d : nullptr;
+    g.r = r_in;
+    g.ss_part = l == 0 ? nullptr : F.ss_part;
     g.x_out = F.x;
     g.rec_x = rec.x ? rec.x + (size_t)l * T * d : nullptr;
     g.x16 = F.w.x16;
@@ -616,6 +577,7 @@ hipError_t launch_fused_step(const moe_layer* layers, int n_layers, float* h, in
     g.gate_fmt = L.gate.type;
     g.eps = rec.eps;
     g.error_reset = err_word;
+    g.tile_cnt = F.tile_cnt;
     FzRouteArgs ra{};
     ra.g = g;
     ra.Wr = L.router_w;
@@ -641,7 +603,6 @@ hipError_t launch_fused_step(const moe_layer* layers, int n_layers, float* h, in
     ga.plan.error = err_word;
     if (rec.topk_idx) ga.plan.topk_idx = rec.topk_idx + (size_t)l * T * k;
     if (rec.topk_w) ga.plan.topk_w = rec.topk_w + (size_t)l * T * k;
-    prev_w = ga.plan.topk_w;
     {
       const int wg_per_slot = (f / 16) / (4 / ga.a.ksplit);
       const int items = max_slots * wg_per_slot;
@@ -654,31 +615,25 @@ hipError_t launch_fused_step(const moe_layer* layers, int n_layers, float* h, in
       }
       if (err != hipSuccess) return err;
     }
-    // (3) down over the slot table, rows written at their pair's position
+    // (3) down over the slot table, rows written at their pair's position; the
+    // last workgroup of each 64-column tile forms the combine and the residual
     {
       DecodeArgs da = down_args(L, T, F.w);
       da.slots = F.plan.slots;
       da.n_slots = F.plan.n_slots;
       da.pair_of_row = F.plan.pair_of_row;
       da.error = err_word;
+      da.tile_cnt = F.tile_cnt;
+      da.r_in = r_in;
+      da.r_out = r_out;
+      da.ss_part = F.ss_part;
+      da.rec_y = rec.y ? rec.y + (size_t)l * T * d : nullptr;
+      da.gate_w = ga.plan.topk_w;
       const int items = max_slots * ((d / 16) / 4);
       const hipError_t err = launch_dq_down_table(da, L.down.type, items, s);
       if (err != hipSuccess) return err;
     }
   }
-  // the last layer's combine, folded into h
-  FzGlueArgs fg{};
-  fg.d = d;
-  fg.T = T;
-  fg.k = k;
-  fg.has_shared = layers[n_layers - 1].has_shared;
-  fg.h_in = F.hb[n_layers & 1];
-  fg.h_out = h;
-  fg.o = F.w.o;
-  fg.topk_w = prev_w;
-  fg.rec_y = rec.y ? rec.y + (size_t)(n_layers - 1) * T * d : nullptr;
-  fg.eps = rec.eps;
-  hipLaunchKernelGGL(k_fz_glue, dim3(T), dim3(256), 0, s, fg);
   return hipGetLastError();
 }
 

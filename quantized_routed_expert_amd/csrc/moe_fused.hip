@@ -182,18 +182,19 @@ struct FzRouteArgs {
   float* logits;      // [T][E]
 };
 
-// Experts per workgroup: four, one wavefront each (INLINE: the glue is the
-// larger cost, so fewer workgroups repeat it), or two, each split over two
-// wavefronts along d (the fp64 products of several tokens are the larger cost).
+// Experts per workgroup: one, split over the four wavefronts along d (INLINE:
+// a single token, so the router rows stream through every CU), or two, each
+// split over two wavefronts (the fp64 products of several tokens are the
+// larger cost).
 template <bool INLINE>
 constexpr int route_experts_per_wg() {
-  return INLINE ? 4 : 2;
+  return INLINE ? 1 : 2;
 }
 
 template <bool INLINE>
 __global__ __launch_bounds__(256) void k_fz_route(const FzRouteArgs a) {
   __shared__ uint16_t sx[kFusedMaxT * 4096];  // bf16 layer inputs
-  __shared__ double pr[2][kFusedMaxT];        // second halves (two wavefronts per expert)
+  __shared__ double pr[4][kFusedMaxT];        // partial sums of the other wavefronts of an expert
   glue_pin_args(a.g);
   pin_arg(a.Wr);
   pin_arg(a.bias);
@@ -279,12 +280,13 @@ __global__ __launch_bounds__(256) void k_fz_route(const FzRouteArgs a) {
     for (int t = 0; t < kFusedMaxT; ++t)
       if (t < T) r[t] = wave_sum_f64(acc[t]);
   }
-  if constexpr (WPE == 2) {
-    if (half == 1 && lane == 0 && e < a.E)
-      for (int t = 0; t < T; ++t) pr[wid >> 1][t] = r[t];
+  if constexpr (WPE > 1) {
+    if (half != 0 && lane == 0 && e < a.E)
+      for (int t = 0; t < T; ++t) pr[wid][t] = r[t];
     __syncthreads();
     if (half == 0 && e < a.E)
-      for (int t = 0; t < T; ++t) r[t] += pr[wid >> 1][t];
+      for (int q = 1; q < WPE; ++q)
+        for (int t = 0; t < T; ++t) r[t] += pr[wid + q][t];
   }
   if (half == 0 && lane == 0 && e < a.E) {
     const double b = (double)bias_e;

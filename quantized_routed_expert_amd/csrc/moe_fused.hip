@@ -376,7 +376,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
     sidx[tid] = 0x7fffffff;  // padding of the pair list
     __syncthreads();
     // ---- top-k per token (one wavefront per token), renormalised weights
-    for (int t = wid; t < T; t += 4) {
+    auto topk_token = [&](int t) {
       wave_topk<NPL>(slog + t * E, E, k, lane, tk_key[wid], tk_idx[wid], sidx + t * k, sw + t * k);
       // (the same wavefront reads back what it wrote: its LDS accesses are in order)
       const float v = lane < k ? sw[t * k + lane] : 0.0f;
@@ -384,52 +384,84 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
       const float ex = lane < k ? expf(v - vmax) : 0.0f;
       const float sum = wave_sum(ex);
       if (lane < k) sw[t * k + lane] = ex / sum;
-    }
-    __syncthreads();
-    // ---- plan: pair p (thread p) counts the pairs of smaller experts (its
-    // expert's first plan row) and the earlier pairs of its own expert (its
-    // rank); the first pair of each expert then counts the distinct smaller
-    // experts (its slot).  Rows within an expert follow token order.
-    // (the pair lists are padded to a multiple of 4 with an id above every
-    // expert, which no count includes, and read four at a time)
-    const int TK4 = (TK + 3) & ~3;
-    int e = 0, less = 0, before = 0, same = 0;
-    if (tid < TK) {
-      e = sidx[tid];
-#pragma unroll 4
-      for (int q0 = 0; q0 < TK4; q0 += 4) {
-        const i32x4 eq = *(const i32x4*)&sidx[q0];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          less += eq[u] < e ? 1 : 0;
-          same += eq[u] == e ? 1 : 0;
-          before += (eq[u] == e && q0 + u < tid) ? 1 : 0;
+    };
+    if (T == 1) {
+      // One token: the plan is the order of its k distinct experts, formed by
+      // the same wavefront without further barriers (row = slot = the number
+      // of selected experts with a smaller id).
+      if (wid == 0) {
+        topk_token(0);
+        const int e = lane < k ? sidx[lane] : 0x7fffffff;
+        int less = 0;
+        for (int i = 0; i < k; ++i) less += __shfl(e, i, 64) < e ? 1 : 0;
+        if (lane < k) {
+          srow_token[less] = 0;
+          sslot[less] = SlotEnt{e, less, 1, 0};
+        }
+        if (blockIdx.x == 0) {
+          const FusedPlan& P = g.plan;
+          if (lane < k) {
+            P.pair_of_row[less] = lane;
+            P.topk_idx[lane] = e;
+            P.topk_w[lane] = sw[lane];
+            P.slots[hs + less] = SlotEnt{e, less, 1, 0};
+          }
+          if (lane == 0) {
+            if (hs) P.slots[0] = SlotEnt{0, TK, T, 1};
+            *P.n_slots = k + hs;
+          }
         }
       }
-    }
-    sfirst[tid] = (tid < TK && before == 0) ? e : 0x7fffffff;
-    __syncthreads();
-    if (tid < TK) {
-      int dl = 0;
-#pragma unroll 4
-      for (int q0 = 0; q0 < TK4; q0 += 4) {
-        const i32x4 fq = *(const i32x4*)&sfirst[q0];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) dl += fq[u] < e ? 1 : 0;
-      }
-      srow_token[less + before] = tid / k;
-      if (before == 0) sslot[dl] = SlotEnt{e, less, same, 0};
-    }
-    n_act = __syncthreads_count(tid < TK && before == 0);
-    if (blockIdx.x == 0) {
-      const FusedPlan& P = g.plan;
+      n_act = k;
+      __syncthreads();
+    } else {
+      for (int t = wid; t < T; t += 4) topk_token(t);
+      __syncthreads();
+      // ---- plan: pair p (thread p) counts the pairs of smaller experts (its
+      // expert's first plan row) and the earlier pairs of its own expert (its
+      // rank); the first pair of each expert then counts the distinct smaller
+      // experts (its slot).  Rows within an expert follow token order.
+      // (the pair lists are padded to a multiple of 4 with an id above every
+      // expert, which no count includes, and read four at a time)
+      const int TK4 = (TK + 3) & ~3;
+      int e = 0, less = 0, before = 0, same = 0;
       if (tid < TK) {
-        P.pair_of_row[less + before] = tid;
-        P.topk_idx[tid] = e;
-        P.topk_w[tid] = sw[tid];
+        e = sidx[tid];
+  #pragma unroll 4
+        for (int q0 = 0; q0 < TK4; q0 += 4) {
+          const i32x4 eq = *(const i32x4*)&sidx[q0];
+  #pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            less += eq[u] < e ? 1 : 0;
+            same += eq[u] == e ? 1 : 0;
+            before += (eq[u] == e && q0 + u < tid) ? 1 : 0;
+          }
+        }
       }
-      for (int s = tid; s < n_act + hs; s += 256) P.slots[s] = s < hs ? SlotEnt{0, TK, T, 1} : sslot[s - hs];
-      if (tid == 0) *P.n_slots = n_act + hs;
+      sfirst[tid] = (tid < TK && before == 0) ? e : 0x7fffffff;
+      __syncthreads();
+      if (tid < TK) {
+        int dl = 0;
+  #pragma unroll 4
+        for (int q0 = 0; q0 < TK4; q0 += 4) {
+          const i32x4 fq = *(const i32x4*)&sfirst[q0];
+  #pragma unroll
+          for (int u = 0; u < 4; ++u) dl += fq[u] < e ? 1 : 0;
+        }
+        srow_token[less + before] = tid / k;
+        if (before == 0) sslot[dl] = SlotEnt{e, less, same, 0};
+      }
+      n_act = __syncthreads_count(tid < TK && before == 0);
+      if (blockIdx.x == 0) {
+        const FusedPlan& P = g.plan;
+        if (tid < TK) {
+          P.pair_of_row[less + before] = tid;
+          P.topk_idx[tid] = e;
+          P.topk_w[tid] = sw[tid];
+        }
+        for (int s = tid; s < n_act + hs; s += 256) P.slots[s] = s < hs ? SlotEnt{0, TK, T, 1} : sslot[s - hs];
+        if (tid == 0) *P.n_slots = n_act + hs;
+      }
     }
   }
 

@@ -66,6 +66,13 @@ CASES = [
     (("q8_0", "q8_0", "iq4_nl"), 2, 1024, 128, 16, 3, True),
     # T * E not a multiple of 4: per-layer logit records are not 16-byte aligned
     (("q8_0", "q8_0", "q8_0"), 3, 1024, 128, 21, 3, True),
+    # one token, other format pairs of the single-launch gate/up + down path
+    (("q8_0", "q8_0", "q8_0"), 1, 2048, 256, 128, 6, True),
+    (("iq4_nl", "iq4_nl", "q8_0"), 1, 3072, 768, 256, 8, True),
+    (("nvfp4", "nvfp4", "iq4_nl"), 1, 1024, 512, 64, 2, True),
+    # one token whose gate/up pass has more steps than are issued up front
+    # (the separate gate/up and down launches)
+    (("q8_0", "q8_0", "q8_0"), 1, 4096, 256, 600, 6, False),
 ]
 
 
@@ -90,9 +97,10 @@ def test_fused_full_size(name):
     _say(f"[fused {name}] {stats}")
 
 
-def test_fused_heavy_ties():
+@pytest.mark.parametrize("T", [1, 3])
+def test_fused_heavy_ties(T):
     """A zero router: every logit equal, so each token takes experts 0..k-1."""
-    wl = synth.scaled(synth.WORKLOADS["verify"], d=1024, f=256, E=512, n_layers=2, T=3)
+    wl = synth.scaled(synth.WORKLOADS["verify"], d=1024, f=256, E=512, n_layers=2, T=T)
     layers = [synth.make_layer(wl, l, DEV) for l in range(2)]
     for L in layers:
         L["router_w"].zero_()
@@ -107,9 +115,10 @@ def test_fused_heavy_ties():
     _check_fused(wl, layers, st, TOL_DECODE)
 
 
-def test_fused_repeatable_and_graph_replay():
-    _say("[fused graph]")
-    wl = synth.scaled(synth.WORKLOADS["verify"], d=1024, f=256, E=64, n_layers=4, T=4)
+@pytest.mark.parametrize("T", [1, 4])
+def test_fused_repeatable_and_graph_replay(T):
+    _say(f"[fused graph] T={T}")
+    wl = synth.scaled(synth.WORKLOADS["verify"], d=1024, f=256, E=64, n_layers=4, T=T)
     layers, st = _make(wl, 4)
     ref = st.h.clone()
     ref_idx = st.rec_idx.clone()

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
     } else {
       si = SlotInfo{0, true, a.T * a.k, a.T};
     }
-    dq_item<FMT, NT, GATEUP, ROLL, TABLE>(a, si, tile, wid % ksplit, a.row_token, sA);
+    dq_item<FMT, NT, GATEUP, ROLL, TABLE, !TABLE>(a, si, tile, wid % ksplit, a.row_token, sA);
     if constexpr (TABLE && !GATEUP) {
       if (a.tile_cnt) {
         __shared__ int s_last;

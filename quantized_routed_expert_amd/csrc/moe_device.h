@@ -239,10 +239,11 @@ __device__ __forceinline__ float wave_max(float v) {
 // maps above 1; NaN maps to 1 (ranked below every real value, as a sort that
 // puts NaN last does); 0 marks an empty or taken entry.
 __device__ __forceinline__ uint32_t topk_key32(float v) {
-  uint32_t u = __float_as_uint(v);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 1u;  // NaN
-  if ((u & 0x7fffffffu) == 0u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  // (selects, not branches: callers convert many entries back to back)
+  const uint32_t u = __float_as_uint(v), a = u & 0x7fffffffu;
+  uint32_t key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  key = a == 0u ? 0x80000000u : key;  // -0 as +0
+  return a > 0x7f800000u ? 1u : key;  // NaN
 }
 __device__ __forceinline__ float topk_key32_value(uint32_t key) {
   if (key == 1u) return __uint_as_float(0x7fc00000u);
@@ -280,7 +281,7 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ L, int E, in
 #pragma unroll
   for (int i = 0; i < NPL; ++i) lv[i] = L[min(lane + 64 * i, E - 1)];  // unconditional loads, all in flight
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) key[i] = (lane + 64 * i < E) ? topk_key32(lv[i]) : 0u;
+  for (int i = 0; i < NPL; ++i) key[i] = topk_key32(lv[i]) & (lane + 64 * i < E ? 0xffffffffu : 0u);
 
   // ---- threshold: the smallest of the group maxima (groups of g lanes, 64/g >= k groups)
   uint32_t gm = key[0];

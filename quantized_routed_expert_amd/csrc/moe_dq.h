@@ -143,7 +143,7 @@ inline int dq_nsteps(int fmt, int K, int ksplit) { return K / ksplit / (4 * dq_e
 
 // PAIRS (down pass of the fused step): routed rows are written at the output
 // row pair_of_row gives their plan row.
-template <int FMT, int NT, bool GATEUP, bool ROLL, bool PAIRS = false>
+template <int FMT, int NT, bool GATEUP, bool ROLL, bool PAIRS = false, bool REUSE = false>
 __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si, int tile, int kpart,
                                         const int32_t* row_token, f16* sA) {
   // one word per column of a pass for the epilogue: the token's activation
@@ -237,6 +237,9 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
 #pragma unroll
   for (int m = 0; m < NMAT; ++m)
     ssl[m] = (const uint16_t*)(sS + m * s_chunks_m * 16 + ((wid / ksplit) * 16 + n) * srb) + (kbase >> 5);
+  // REUSE (without ROLL): the codes of every step, loaded in the first pass,
+  // stay in registers for the later passes instead of being read again.
+  u32x4 cb_keep[NMAT][PD];
   for (int c0 = 0; c0 < ncol; c0 += CPP) {
     const int ncp = min(CPP, ncol - c0);
     const int nch = ncp * chunks_per_col;
@@ -260,11 +263,14 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
       }
     }
     // ---- the first PD steps of weight codes (independent of the activations)
-    u32x4 cb[NMAT][PD];
+    u32x4 cb_pass[NMAT][PD];
+    u32x4(&cb)[NMAT][PD] = (REUSE && !ROLL) ? cb_keep : cb_pass;
+    if (!(REUSE && !ROLL) || c0 == 0) {
 #pragma unroll
-    for (int u = 0; u < PD; ++u)
+      for (int u = 0; u < PD; ++u)
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) load_step(m, min(u, nsteps - 1), cb[m][u]);
+        for (int m = 0; m < NMAT; ++m) load_step(m, min(u, nsteps - 1), cb[m][u]);
+    }
 
     // ---- stage the activation columns into LDS.  Columns at or beyond ncp
     // are never read (their A rows are zero), so they are not written.

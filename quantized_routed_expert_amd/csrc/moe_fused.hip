@@ -294,6 +294,95 @@ __global__ __launch_bounds__(256) void k_fz_route(const FzRouteArgs a) {
   }
 }
 
+// Top-k of one token's logits L[0..E) by a whole workgroup of 256 threads
+// (E <= 64 * NPL, 1 <= k <= 32), with the result of wave_topk: slot j < k in
+// out_idx[j] / out_val[j], descending logit, the lower expert id first on
+// ties.  Thread t holds entries t + 256 i.  The threshold tau is the smallest
+// of ng >= k group maxima (groups of 256 / ng consecutive threads, never
+// spanning two wavefronts), so every selected entry is >= tau.  Each wavefront
+// packs its entries >= tau into its own list, and each list entry counts the
+// entries of all lists above it (64-bit keys: the order-preserving logit key,
+// then the complement of the expert id, so that no two keys are equal and the
+// count is the slot).  If a list would exceed 64 entries (heavy ties),
+// wavefront 0 runs wave_topk instead.  Ends with a barrier, after which the
+// result is visible to every wavefront.
+template <int NPL>
+__device__ __forceinline__ void wg_topk1(const float* __restrict__ L, int E, int k, uint32_t* smax,
+                                         uint64_t (*ck)[64], int32_t* cnt, uint32_t* tk_key, int32_t* tk_idx,
+                                         int32_t* out_idx, float* out_val) {
+  constexpr int PT = NPL / 4;  // entries per thread
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  uint32_t key[PT];
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    const int e = tid + 256 * i;
+    key[i] = topk_key32(L[min(e, E - 1)]) & (e < E ? 0xffffffffu : 0u);
+  }
+  int ng = 4;
+  while (ng < k) ng <<= 1;
+  const int gs = 256 / ng;  // 64 .. 8 threads per group
+  uint32_t gm = key[0];
+#pragma unroll
+  for (int i = 1; i < PT; ++i) gm = max(gm, key[i]);
+  if (gs >= 2) gm = max(gm, dpp_u32<kDppShr1, 0xf>(gm));
+  if (gs >= 4) gm = max(gm, dpp_u32<kDppShr2, 0xf>(gm));
+  if (gs >= 8) gm = max(gm, dpp_u32<kDppShr4, 0xf>(gm));
+  if (gs >= 16) gm = max(gm, dpp_u32<kDppShr8, 0xf>(gm));
+  if (gs >= 32) gm = max(gm, dpp_u32<kDppBcast15, 0xa>(gm));
+  if (gs >= 64) gm = max(gm, dpp_u32<kDppBcast31, 0xc>(gm));
+  if ((lane & (gs - 1)) == gs - 1) smax[tid / gs] = gm;  // the group's last thread holds its maximum
+  __syncthreads();
+  uint32_t tau = 0xffffffffu;
+  for (int j0 = 0; j0 < ng; j0 += 4) {
+    const u32x4 q = *(const u32x4*)&smax[j0];
+    tau = min(tau, min(min(q.x, q.y), min(q.z, q.w)));
+  }
+  // ---- this wavefront's entries >= tau, in index order
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    const bool in = key[i] != 0u && key[i] >= tau;
+    const uint64_t mk = __ballot(in);
+    const int pos = c + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+    if (in && pos < 64) ck[wid][pos] = ((uint64_t)key[i] << 32) | (uint32_t)~(uint32_t)(tid + 256 * i);
+    c += __popcll(mk);
+  }
+  // zero keys pad the list to a multiple of 8 (they count for nothing)
+  if (c <= 64 && lane >= c && lane < ((c + 7) & ~7)) ck[wid][lane] = 0ull;
+  if (lane == 0) cnt[wid] = c;
+  __syncthreads();
+  const int c0 = cnt[0], c1 = cnt[1], c2 = cnt[2], c3 = cnt[3];
+  const int cmax = max(max(c0, c1), max(c2, c3));
+  if (cmax <= 64) {
+    const int cw = cnt[wid];
+    const uint64_t kl = lane < cw ? ck[wid][lane] : 0ull;
+    int rank = 0;
+    for (int j0 = 0; j0 < cmax; j0 += 8) {
+      u32x4 q[4][4];
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          q[w2][u] = j0 < cnt[w2] ? *(const u32x4*)&ck[w2][j0 + 2 * u] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint64_t x0 = ((uint64_t)q[w2][u].y << 32) | q[w2][u].x;
+          const uint64_t x1 = ((uint64_t)q[w2][u].w << 32) | q[w2][u].z;
+          rank += (x0 > kl ? 1 : 0) + (x1 > kl ? 1 : 0);
+        }
+    }
+    if (lane < cw && rank < k) {
+      out_idx[rank] = (int32_t)~(uint32_t)kl;
+      out_val[rank] = topk_key32_value((uint32_t)(kl >> 32));
+    }
+  } else if (wid == 0) {
+    wave_topk<NPL>(L, E, k, lane, tk_key, tk_idx, out_idx, out_val);
+  }
+  __syncthreads();
+}
+
 // (2) Top-k + plan (in LDS, recomputed by every workgroup that needs it) +
 // grouped gate/up.  Slot 0 is the shared expert (it needs no routing, so its
 // items start streaming at once); slots 1.. are the active experts in
@@ -318,6 +407,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   __shared__ __align__(16) int32_t sfirst[kFusedTK];
   __shared__ uint32_t tk_key[4][64];  // top-k scratch, one row per wavefront
   __shared__ int32_t tk_idx[4][64];
+  __shared__ __align__(16) uint32_t tk_max[32];      // workgroup top-k (one token): group maxima,
+  __shared__ __align__(16) uint64_t tk_list[4][64];  // per-wavefront candidate lists,
+  __shared__ int32_t tk_cnt[4];                      // and their lengths
   __shared__ int32_t srow_token[kFusedTK];
   __shared__ SlotEnt sslot[kFusedTK];
   extern __shared__ __align__(16) f16 sA[];
@@ -386,34 +478,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
       if (lane < k) sw[t * k + lane] = ex / sum;
     };
     if (T == 1) {
-      // One token: the plan is the order of its k distinct experts, formed by
-      // the same wavefront without further barriers (row = slot = the number
-      // of selected experts with a smaller id).
-      if (wid == 0) {
-        topk_token(0);
-        const int e = lane < k ? sidx[lane] : 0x7fffffff;
-        int less = 0;
-        for (int i = 0; i < k; ++i) less += __shfl(e, i, 64) < e ? 1 : 0;
+      // One token: top-k over the whole workgroup, then every wavefront forms
+      // the weights and the plan itself (the same values, so no further
+      // barrier): the plan is the order of the k distinct experts, row = slot
+      // = the number of selected experts with a smaller id.
+      wg_topk1<NPL>(slog, E, k, tk_max, tk_list, tk_cnt, tk_key[0], tk_idx[0], sidx, sw);
+      const float v = lane < k ? sw[lane] : 0.0f;
+      const float vmax = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 0));
+      const float ex = lane < k ? expf(v - vmax) : 0.0f;
+      const float sum = wave_sum(ex);
+      const float w = ex / sum;
+      const int e = lane < k ? sidx[lane] : 0x7fffffff;
+      int less = 0;
+      for (int i0 = 0; i0 < k; i0 += 4) {
+        const i32x4 q = *(const i32x4*)&sidx[i0];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) less += (i0 + u < k && q[u] < e) ? 1 : 0;
+      }
+      if (lane < k) {
+        srow_token[less] = 0;
+        sslot[less] = SlotEnt{e, less, 1, 0};
+      }
+      if (blockIdx.x == 0 && wid == 0) {
+        const FusedPlan& P = g.plan;
         if (lane < k) {
-          srow_token[less] = 0;
-          sslot[less] = SlotEnt{e, less, 1, 0};
+          P.pair_of_row[less] = lane;
+          P.topk_idx[lane] = e;
+          P.topk_w[lane] = w;
+          P.slots[hs + less] = SlotEnt{e, less, 1, 0};
         }
-        if (blockIdx.x == 0) {
-          const FusedPlan& P = g.plan;
-          if (lane < k) {
-            P.pair_of_row[less] = lane;
-            P.topk_idx[lane] = e;
-            P.topk_w[lane] = sw[lane];
-            P.slots[hs + less] = SlotEnt{e, less, 1, 0};
-          }
-          if (lane == 0) {
-            if (hs) P.slots[0] = SlotEnt{0, TK, T, 1};
-            *P.n_slots = k + hs;
-          }
+        if (lane == 0) {
+          if (hs) P.slots[0] = SlotEnt{0, TK, T, 1};
+          *P.n_slots = k + hs;
         }
       }
       n_act = k;
-      __syncthreads();
     } else {
       for (int t = wid; t < T; t += 4) topk_token(t);
       __syncthreads();

@@ -89,11 +89,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
     if constexpr (TABLE) {
       const SlotEnt se = item == (int)blockIdx.x ? se0 : a.slots[slot];
       si = SlotInfo{se.e, se.shared != 0, se.row0, se.cnt};
-    } else if (slot < n_act) {
-      const int e = a.active[slot];
-      si = SlotInfo{e, false, a.offsets[e], a.offsets[e + 1] - a.offsets[e]};
-    } else {
+    } else if (slot < a.has_shared) {
+      // the shared expert first: its items carry every token
       si = SlotInfo{0, true, a.T * a.k, a.T};
+    } else {
+      const int e = a.active[slot - a.has_shared];
+      si = SlotInfo{e, false, a.offsets[e], a.offsets[e + 1] - a.offsets[e]};
     }
     dq_item<FMT, NT, GATEUP, ROLL, TABLE, !TABLE>(a, si, tile, wid % ksplit, a.row_token, sA);
     if constexpr (TABLE && !GATEUP) {
@@ -150,33 +151,39 @@ __global__ __launch_bounds__(256) void k_prep_x(const void* __restrict__ x, int 
 
 namespace {
 
-template <int FMT, bool GATEUP, bool ROLL>
-hipError_t launch_fmt_roll(const DecodeArgs& a, int nt, size_t lds, int grid, hipStream_t s) {
-  if (nt == 1)
-    hipLaunchKernelGGL((k_ffn_dq<FMT, 1, GATEUP, ROLL>), dim3(grid), dim3(256), lds, s, a);
-  else if (nt == 2)
-    hipLaunchKernelGGL((k_ffn_dq<FMT, 2, GATEUP, ROLL>), dim3(grid), dim3(256), lds, s, a);
-  else
-    hipLaunchKernelGGL((k_ffn_dq<FMT, 4, GATEUP, ROLL>), dim3(grid), dim3(256), lds, s, a);
+// One workgroup per item (up to 4096, which then loop): workgroups are
+// dispatched in index order as earlier ones finish, so the items are balanced
+// dynamically and the long items of the first slots (the shared expert, which
+// carries every token) start at once.
+template <int FMT, int NT, bool GATEUP, bool ROLL>
+hipError_t launch_fmt_nt(const DecodeArgs& a, size_t lds, int items, hipStream_t s) {
+  hipLaunchKernelGGL((k_ffn_dq<FMT, NT, GATEUP, ROLL>), dim3(items < 4096 ? items : 4096), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
+template <int FMT, bool GATEUP, bool ROLL>
+hipError_t launch_fmt_roll(const DecodeArgs& a, int nt, size_t lds, int items, hipStream_t s) {
+  if (nt == 1) return launch_fmt_nt<FMT, 1, GATEUP, ROLL>(a, lds, items, s);
+  if (nt == 2) return launch_fmt_nt<FMT, 2, GATEUP, ROLL>(a, lds, items, s);
+  return launch_fmt_nt<FMT, 4, GATEUP, ROLL>(a, lds, items, s);
+}
+
 template <int FMT, bool GATEUP>
-hipError_t launch_fmt(const DecodeArgs& a, int ncols_max, int grid, hipStream_t s) {
+hipError_t launch_fmt(const DecodeArgs& a, int ncols_max, int items, hipStream_t s) {
   constexpr int CPT = cols_per_tile<FMT>();
   const int K = a.mat[0].cols;
   const int nt = pick_nt(CPT, ncols_max, K);
   const size_t lds = dq_lds_bytes(CPT, nt, K, a.ksplit, GATEUP ? 2 : 1);
-  if (dq_nsteps(FMT, K, a.ksplit) > dq_pd(FMT, GATEUP)) return launch_fmt_roll<FMT, GATEUP, true>(a, nt, lds, grid, s);
-  return launch_fmt_roll<FMT, GATEUP, false>(a, nt, lds, grid, s);
+  if (dq_nsteps(FMT, K, a.ksplit) > dq_pd(FMT, GATEUP)) return launch_fmt_roll<FMT, GATEUP, true>(a, nt, lds, items, s);
+  return launch_fmt_roll<FMT, GATEUP, false>(a, nt, lds, items, s);
 }
 
 template <bool GATEUP>
-hipError_t launch_pass(int fmt, const DecodeArgs& a, int ncols_max, int grid, hipStream_t s) {
+hipError_t launch_pass(int fmt, const DecodeArgs& a, int ncols_max, int items, hipStream_t s) {
   switch (fmt) {
-    case MOE_Q8_0: return launch_fmt<MOE_Q8_0, GATEUP>(a, ncols_max, grid, s);
-    case MOE_IQ4_NL: return launch_fmt<MOE_IQ4_NL, GATEUP>(a, ncols_max, grid, s);
-    default: return launch_fmt<MOE_NVFP4, GATEUP>(a, ncols_max, grid, s);
+    case MOE_Q8_0: return launch_fmt<MOE_Q8_0, GATEUP>(a, ncols_max, items, s);
+    case MOE_IQ4_NL: return launch_fmt<MOE_IQ4_NL, GATEUP>(a, ncols_max, items, s);
+    default: return launch_fmt<MOE_NVFP4, GATEUP>(a, ncols_max, items, s);
   }
 }
 
@@ -249,11 +256,11 @@ hipError_t launch_decode_stage(int stage, const FfnCall& c, hipStream_t s) {
   if (stage == kStageGateUp) {
     const int wg_per_slot = (L.f / 16) / (4 / a.ksplit);
     const long items = (long)max_slots * wg_per_slot;
-    return launch_pass<true>(L.gate.type, a, T * P, (int)(items < 4096 ? items : 4096), s);
+    return launch_pass<true>(L.gate.type, a, T * P, (int)items, s);
   }
   const int wg_per_slot = (L.d / 16) / 4;
   const long items = (long)max_slots * wg_per_slot;
-  return launch_pass<false>(L.down.type, a, T * 2, (int)(items < 4096 ? items : 4096), s);
+  return launch_pass<false>(L.down.type, a, T * 2, (int)items, s);
 }
 
 }  // namespace qre

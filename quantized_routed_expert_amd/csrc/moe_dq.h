@@ -245,12 +245,15 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
     const int nch = ncp * chunks_per_col;
     // ---- the first batch of this pass's activation chunks, issued before the
     // weight codes so that waiting for them does not wait for the codes
-    u32x4 av[AB];
+    // (REUSE: the chunks go straight to LDS below instead)
+    u32x4 av[REUSE ? 1 : AB];
+    if constexpr (!REUSE) {
 #pragma unroll
-    for (int b = 0; b < AB; ++b) {
-      const int ch = min(tid + b * 256, nch - 1);
-      const int c = ch / chunks_per_col, kk = (ch - c * chunks_per_col) * 8;
-      av[b] = *(const u32x4*)(a.in16 + in_row_of(c0 + c) * K + kk);
+      for (int b = 0; b < AB; ++b) {
+        const int ch = min(tid + b * 256, nch - 1);
+        const int c = ch / chunks_per_col, kk = (ch - c * chunks_per_col) * 8;
+        av[b] = *(const u32x4*)(a.in16 + in_row_of(c0 + c) * K + kk);
+      }
     }
     uint32_t cw = 0;
     {
@@ -275,12 +278,26 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
     // ---- stage the activation columns into LDS.  Columns at or beyond ncp
     // are never read (their A rows are zero), so they are not written.
     __syncthreads();  // the previous pass has finished reading sA
+    if constexpr (REUSE) {
+      // every chunk of the pass by LDS DMA (16 bytes a lane, 1 KB a wavefront
+      // instruction, contiguous in LDS), all in flight at once and no registers
+      typedef __attribute__((address_space(3))) void lds_void_t;
+      for (int q = wid; q * 64 < nch; q += 4) {
+        const int ch = q * 64 + lane;
+        if (ch < nch) {
+          const int c = ch / chunks_per_col, kk = (ch - c * chunks_per_col) * 8;
+          __builtin_amdgcn_global_load_lds((const void*)(a.in16 + in_row_of(c0 + c) * K + kk),
+                                           (lds_void_t*)(sA + q * 512), 16, 0, 0);
+        }
+      }
+    } else {
 #pragma unroll
-    for (int b = 0; b < AB; ++b) {
-      const int ch = tid + b * 256;
-      if (ch < nch) {
-        const int c = ch / chunks_per_col, kk = (ch - c * chunks_per_col) * 8;
-        *(u32x4*)&sA[c * K + kk] = av[b];
+      for (int b = 0; b < AB; ++b) {
+        const int ch = tid + b * 256;
+        if (ch < nch) {
+          const int c = ch / chunks_per_col, kk = (ch - c * chunks_per_col) * 8;
+          *(u32x4*)&sA[c * K + kk] = av[b];
+        }
       }
     }
     if (tid < ncp) s_colw[tid] = cw;
@@ -293,7 +310,8 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
       for (int z = tid; z < kw / 8; z += 256) *(u32x4*)&sA[zoff + z * 8] = u32x4{0u, 0u, 0u, 0u};
     }
     // the rest in batches of RB loads in flight per thread
-    for (int ch0 = tid + AB * 256; ch0 < nch; ch0 += RB * 256) {
+    if constexpr (REUSE) __builtin_amdgcn_s_waitcnt(0);  // the DMA chunks (and the codes) have landed
+    for (int ch0 = tid + AB * 256; !REUSE && ch0 < nch; ch0 += RB * 256) {
       u32x4 bv[RB];
 #pragma unroll
       for (int b = 0; b < RB; ++b) {

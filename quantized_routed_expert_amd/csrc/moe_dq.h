@@ -109,8 +109,8 @@ __device__ __forceinline__ f16x8 decode_b(const u32x4& c, int i, uint32_t sraw) 
     return q8_dwords_to_f16x8(c[2 * i], c[2 * i + 1]);
   } else {
     // dwords 0,1 hold the chunk's first 16-element block, 2,3 the second
-    const uint32_t sbyte = (i < 2) ? (sraw & 0xffu) : ((sraw >> 8) & 0xffu);
-    return fp4_dword_to_f16x8(c[i], (f16)e4m3_to_f32(sbyte));
+    const float sc = i < 2 ? e4m3_byte_to_f32<0>(sraw) : e4m3_byte_to_f32<1>(sraw);
+    return fp4_dword_to_f16x8(c[i], (f16)sc);
   }
 }
 

@@ -169,8 +169,8 @@ __device__ __forceinline__ void pf_load_codes(const uint8_t* crow, const uint8_t
 template <int FMT>
 __device__ __forceinline__ f16x8 pf_decode(const PfCodes<FMT>& pc, int i) {
   if constexpr (FMT == MOE_NVFP4) {
-    const uint32_t sbyte = (i < 2) ? (pc.sc & 0xffu) : ((pc.sc >> 8) & 0xffu);
-    return fp4_dword_to_f16x8(pc.c[0][i], (f16)e4m3_to_f32(sbyte));
+    const float sc = i < 2 ? e4m3_byte_to_f32<0>(pc.sc) : e4m3_byte_to_f32<1>(pc.sc);
+    return fp4_dword_to_f16x8(pc.c[0][i], (f16)sc);
   } else {
     const f16 d = __builtin_bit_cast(f16, (uint16_t)pc.sc);
     const f16x8 dd = {d, d, d, d, d, d, d, d};

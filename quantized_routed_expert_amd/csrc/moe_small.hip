@@ -303,10 +303,71 @@ __global__ __launch_bounds__(256) void k_router_mfma(const float* __restrict__ W
   }
 }
 
+// 8 < T <= 64 with bf16 tokens: the same exact-product MFMA logits, shaped
+// for few tokens: a workgroup of 16 wavefronts takes 16 experts and 16 tokens
+// (one fragment each way), wavefront w the w-th sixteenth of K, with all of
+// its chunks in flight at once; the sixteen partial sums are added in
+// wavefront order through LDS.
+constexpr int kRsWaves = 16;
+constexpr int kRsMaxChunks = 8;  // K / 16 <= 256
+
+__global__ __launch_bounds__(64 * kRsWaves) void k_router_mfma_small(const float* __restrict__ W,
+                                                                    const float* __restrict__ bias,
+                                                                    const uint16_t* __restrict__ x, int T, int E,
+                                                                    int d, float* __restrict__ logits) {
+  __shared__ f32x4 red[kRsWaves][64];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int n = lane & 15, G = lane >> 4;
+  const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
+  const int kw = d / kRsWaves, kb = wid * kw;
+  const int nc = kw / 32;
+  const uint16_t* xr = x + (long)min(t0 + n, T - 1) * d + kb + 8 * G;
+  const float* wr = W + (long)min(e0 + n, E - 1) * d + kb + 8 * G;
+  u32x4 xa[kRsMaxChunks];
+  f32x4 wb[kRsMaxChunks][2];
+#pragma unroll
+  for (int c = 0; c < kRsMaxChunks; ++c) {
+    const int cc = min(c, nc - 1);  // past the end: a repeated chunk, unused
+    wb[c][0] = __builtin_nontemporal_load((const f32x4*)(wr + cc * 32));
+    wb[c][1] = __builtin_nontemporal_load((const f32x4*)(wr + cc * 32 + 4));
+    xa[c] = *(const u32x4*)(xr + cc * 32);
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < kRsMaxChunks; ++c) {
+    if (c < nc) {
+      bf16x8 p1, p2, p3;
+      split_bf16x3(wb[c], p1, p2, p3);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, xa[c]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, p1, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, p2, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, p3, acc, 0, 0, 0);
+    }
+  }
+  red[wid][lane] = acc;
+  __syncthreads();
+  // thread o < 256: lane o / 4 of the fragment, row v = o % 4, i.e. token
+  // t0 + 4G + v and expert e0 + n (D layout of the MFMA)
+  const int o = threadIdx.x;
+  if (o < 256) {
+    const int ol = o >> 2, v = o & 3;
+    const int t = t0 + 4 * (ol >> 4) + v, e = e0 + (ol & 15);
+    if (t < T && e < E) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kRsWaves; ++w) sum += red[w][ol][v];
+      logits[(long)t * E + e] = sum + (bias ? bias[e] : 0.0f);
+    }
+  }
+}
+
 hipError_t launch_router_logits(const float* W, const float* b, const void* x, int x_dtype, int T, int E, int d,
                                 float* logits, hipStream_t s) {
   const int xb = x_dtype == MOE_BF16 ? 1 : 0;
-  if (T <= 64) {
+  if (xb && T > 8 && T <= 64 && d % (32 * kRsWaves) == 0 && d / kRsWaves <= 32 * kRsMaxChunks) {
+    hipLaunchKernelGGL(k_router_mfma_small, dim3((E + 15) / 16, (T + 15) / 16), dim3(64 * kRsWaves), 0, s, W, b,
+                       (const uint16_t*)x, T, E, d, logits);
+  } else if (T <= 64) {
     if (xb)
       hipLaunchKernelGGL(k_router_gemv_f64<true>, dim3(E), dim3(256), 0, s, W, b, x, T, E, d, logits);
     else

@@ -87,10 +87,10 @@ def _small_layer(seed, d=256, f=128, E=16, k=4, types=("iq4_nl", "iq4_nl", "iq4_
     return wl, synth.make_layer(wl, 0, DEV)
 
 
-@pytest.mark.parametrize("T", [1, 7, 64, 200])
-def test_router_topk_exact(T):
-    _say(f"[route] T={T}")
-    wl, layer = _small_layer(10 + T, E=64, k=6)
+@pytest.mark.parametrize("T,d", [(1, 256), (7, 256), (64, 256), (200, 256), (37, 1024), (64, 3072)])
+def test_router_topk_exact(T, d):
+    _say(f"[route] T={T} d={d}")
+    wl, layer = _small_layer(10 + T, d=d, E=64, k=6)
     # duplicate router rows -> exact ties, lower id must win
     layer["router_w"][9] = layer["router_w"][3]
     layer["router_b"][9] = layer["router_b"][3]
@@ -106,7 +106,9 @@ def test_router_topk_exact(T):
     L64 = M.router_logits(layer["router_w"].cpu().numpy(), layer["router_b"].cpu().numpy(), to_np(x))
     L32 = logits.cpu().numpy()
     err = np.abs(L32.astype(np.float64) - L64)
-    if T <= 64:  # fp64 accumulation: the rounded result equals the oracle's rounding
+    # fp64 sums (T <= 8, or rows that the small-batch MFMA router does not
+    # take): the rounded result equals the oracle's rounding
+    if T <= 8 or (T <= 64 and d % 512 != 0):
         assert np.mean(L32 == L64.astype(np.float32)) > 0.999
     assert np.all(err <= 1e-5 * (1 + np.abs(L64)))
     gi = idx.cpu().numpy()

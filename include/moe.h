@@ -165,8 +165,10 @@ moe_status moe_ffn_forward(const moe_layer* layer, const void* x, int32_t x_dtyp
  * through the workspace, whose contents are only valid between the stages of
  * one call sequence with the same layer, T and x_dtype):
  *  moe_ffn_prepare  activation layout for the expert products: fp16 tokens
- *                   with per-token power-of-two scales (and, prefill, the
- *                   device tile list over the plan)
+ *                   with per-token power-of-two scales, and the order in
+ *                   which the expert passes take the active experts (T <= 64:
+ *                   by descending token count; prefill: the device tile list
+ *                   over the plan)
  *  moe_ffn_gateup   grouped gate/up projections + SwiGLU -> h rows
  *  moe_ffn_down     grouped down projections -> o rows
  *  moe_ffn_combine  y_t = s_t + sum_j topk_w[t][j] * o_{slot_row[t*k+j]}

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
       // the shared expert first: its items carry every token
       si = SlotInfo{0, true, a.T * a.k, a.T};
     } else {
-      const int e = a.active[slot - a.has_shared];
+      const int e = a.order[slot - a.has_shared];
       si = SlotInfo{e, false, a.offsets[e], a.offsets[e + 1] - a.offsets[e]};
     }
     dq_item<FMT, NT, GATEUP, ROLL, TABLE, !TABLE>(a, si, tile, wid % ksplit, a.row_token, sA);
@@ -119,9 +119,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
 // tokens as hi/lo pairs), in the block layout the gate/up weights decode to.
 // ----------------------------------------------------------------------------
 
+// The workgroup past the last token orders the active experts by descending
+// token count (a counting sort over counts 0..T; the order within a count is
+// immaterial), so that the expert passes start their longest items first.
 __global__ __launch_bounds__(256) void k_prep_x(const void* __restrict__ x, int x_bf16, int d, int P, int gate_fmt,
-                                                f16* __restrict__ x16, float* __restrict__ xs) {
+                                                f16* __restrict__ x16, float* __restrict__ xs,
+                                                const int32_t* __restrict__ offsets,
+                                                const int32_t* __restrict__ active,
+                                                const int32_t* __restrict__ n_active, int32_t* __restrict__ order,
+                                                int T) {
   const int t = blockIdx.x;
+  if (t == T) {
+    __shared__ int32_t hist[kDecodeMaxT + 2];
+    __shared__ int32_t start[kDecodeMaxT + 2];
+    const int tid = threadIdx.x;
+    const int n = *n_active;
+    if (tid <= T + 1) hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += 256) {
+      const int e = active[i];
+      atomicAdd(&hist[min(offsets[e + 1] - offsets[e], T)], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int run = 0;
+      for (int c = T; c >= 0; --c) {
+        start[c] = run;
+        run += hist[c];
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += 256) {
+      const int e = active[i];
+      order[atomicAdd(&start[min(offsets[e + 1] - offsets[e], T)], 1)] = e;
+    }
+    return;
+  }
   __shared__ float red[4];
   float mx = 0.0f;
   for (int i = threadIdx.x; i < d; i += blockDim.x) {
@@ -230,7 +263,7 @@ size_t decode_ws_bytes(int T, int d, int f, int k, int x_dtype) {
   const int P = x_dtype == MOE_F32 ? 2 : 1;
   const size_t R = (size_t)T * k + T;
   return align_up((size_t)T * P * d * 2, 256) + align_up((size_t)T * P * 4, 256) + align_up(R * 2 * f * 2, 256) +
-         align_up(R * d * 4, 256);
+         align_up(R * d * 4, 256) + align_up((size_t)T * k * 4, 256);
 }
 
 hipError_t launch_decode_stage(int stage, const FfnCall& c, hipStream_t s) {
@@ -239,8 +272,8 @@ hipError_t launch_decode_stage(int stage, const FfnCall& c, hipStream_t s) {
   const int P = c.x_dtype == MOE_F32 ? 2 : 1;
   DecodeWs w = carve(c.ws, T, L.d, L.f, L.k, P);
   if (stage == kStagePrepare) {
-    hipLaunchKernelGGL(k_prep_x, dim3(T), dim3(256), 0, s, c.x, c.x_dtype == MOE_BF16 ? 1 : 0, L.d, P, L.gate.type,
-                       w.x16, w.xs);
+    hipLaunchKernelGGL(k_prep_x, dim3(T + 1), dim3(256), 0, s, c.x, c.x_dtype == MOE_BF16 ? 1 : 0, L.d, P,
+                       L.gate.type, w.x16, w.xs, c.p.offsets, c.p.active, c.p.n_active, w.order, T);
     return hipGetLastError();
   }
   if (stage == kStageCombine)
@@ -251,6 +284,7 @@ hipError_t launch_decode_stage(int stage, const FfnCall& c, hipStream_t s) {
   a.offsets = c.p.offsets;
   a.row_token = c.p.row_token;
   a.active = c.p.active;
+  a.order = w.order;
   a.n_active = c.p.n_active;
   a.error = c.p.error;
   if (stage == kStageGateUp) {

@@ -76,26 +76,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
   const int rt_per_wg = 4 / ksplit;
   const int rows = a.mat[0].rows;
   const int wg_per_slot = (rows / 16) / rt_per_wg;
-  // table: the slot count and the first item's entry are read together (the
-  // table has T*k + 1 entries; one past the count is read but not used)
-  const int n_act = TABLE ? 0 : *a.n_active;
-  const SlotEnt se0 = TABLE ? a.slots[min((int)blockIdx.x / wg_per_slot, a.T * a.k)] : SlotEnt{};
-  const int total = (TABLE ? *a.n_slots : n_act + a.has_shared) * wg_per_slot;
+  // the slot count and the first item's entry are read together (the table
+  // has T*k + 1 entries at least; one past the count is read but not used)
+  const SlotEnt se0 = a.slots[min((int)blockIdx.x / wg_per_slot, a.T * a.k)];
+  const int total = *a.n_slots * wg_per_slot;
 
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const int slot = item / wg_per_slot;
     const int tile = (item % wg_per_slot) * rt_per_wg + wid / ksplit;
-    SlotInfo si;
-    if constexpr (TABLE) {
-      const SlotEnt se = item == (int)blockIdx.x ? se0 : a.slots[slot];
-      si = SlotInfo{se.e, se.shared != 0, se.row0, se.cnt};
-    } else if (slot < a.has_shared) {
-      // the shared expert first: its items carry every token
-      si = SlotInfo{0, true, a.T * a.k, a.T};
-    } else {
-      const int e = a.order[slot - a.has_shared];
-      si = SlotInfo{e, false, a.offsets[e], a.offsets[e + 1] - a.offsets[e]};
-    }
+    const SlotEnt se = item == (int)blockIdx.x ? se0 : a.slots[slot];
+    const SlotInfo si{se.e, se.shared != 0, se.row0, se.cnt};
     dq_item<FMT, NT, GATEUP, ROLL, TABLE, !TABLE>(a, si, tile, wid % ksplit, a.row_token, sA);
     if constexpr (TABLE && !GATEUP) {
       if (a.tile_cnt) {
@@ -119,39 +109,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
 // tokens as hi/lo pairs), in the block layout the gate/up weights decode to.
 // ----------------------------------------------------------------------------
 
-// The workgroup past the last token orders the active experts by descending
-// token count (a counting sort over counts 0..T; the order within a count is
-// immaterial), so that the expert passes start their longest items first.
+// The workgroup past the last token builds the slot table of the expert
+// passes: the shared expert, then the active experts by descending token
+// count (a counting sort over counts 0..T; the order within a count is
+// immaterial), so that the passes start their longest items first and read
+// an item's expert, rows and count in one load.
 __global__ __launch_bounds__(256) void k_prep_x(const void* __restrict__ x, int x_bf16, int d, int P, int gate_fmt,
                                                 f16* __restrict__ x16, float* __restrict__ xs,
                                                 const int32_t* __restrict__ offsets,
                                                 const int32_t* __restrict__ active,
-                                                const int32_t* __restrict__ n_active, int32_t* __restrict__ order,
-                                                int T) {
+                                                const int32_t* __restrict__ n_active, int has_shared, int k,
+                                                SlotEnt* __restrict__ slots, int32_t* __restrict__ n_slots, int T) {
   const int t = blockIdx.x;
   if (t == T) {
     __shared__ int32_t hist[kDecodeMaxT + 2];
     __shared__ int32_t start[kDecodeMaxT + 2];
     const int tid = threadIdx.x;
     const int n = *n_active;
+    const int hs = has_shared ? 1 : 0;
+    auto count_of = [&](int e) { return min(offsets[e + 1] - offsets[e], T); };
     if (tid <= T + 1) hist[tid] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += 256) {
-      const int e = active[i];
-      atomicAdd(&hist[min(offsets[e + 1] - offsets[e], T)], 1);
-    }
+    for (int i = tid; i < n; i += 256) atomicAdd(&hist[count_of(active[i])], 1);
     __syncthreads();
     if (tid == 0) {
-      int run = 0;
+      int run = hs;
       for (int c = T; c >= 0; --c) {
         start[c] = run;
         run += hist[c];
       }
+      if (hs) slots[0] = SlotEnt{0, T * k, T, 1};
+      *n_slots = run;
     }
     __syncthreads();
     for (int i = tid; i < n; i += 256) {
       const int e = active[i];
-      order[atomicAdd(&start[min(offsets[e + 1] - offsets[e], T)], 1)] = e;
+      const int c = count_of(e);
+      slots[atomicAdd(&start[c], 1)] = SlotEnt{e, offsets[e], c, 0};
     }
     return;
   }
@@ -263,7 +257,7 @@ size_t decode_ws_bytes(int T, int d, int f, int k, int x_dtype) {
   const int P = x_dtype == MOE_F32 ? 2 : 1;
   const size_t R = (size_t)T * k + T;
   return align_up((size_t)T * P * d * 2, 256) + align_up((size_t)T * P * 4, 256) + align_up(R * 2 * f * 2, 256) +
-         align_up(R * d * 4, 256) + align_up((size_t)T * k * 4, 256);
+         align_up(R * d * 4, 256) + align_up(((size_t)T * k + 2) * sizeof(SlotEnt), 256) + 256;
 }
 
 hipError_t launch_decode_stage(int stage, const FfnCall& c, hipStream_t s) {
@@ -273,7 +267,8 @@ hipError_t launch_decode_stage(int stage, const FfnCall& c, hipStream_t s) {
   DecodeWs w = carve(c.ws, T, L.d, L.f, L.k, P);
   if (stage == kStagePrepare) {
     hipLaunchKernelGGL(k_prep_x, dim3(T + 1), dim3(256), 0, s, c.x, c.x_dtype == MOE_BF16 ? 1 : 0, L.d, P,
-                       L.gate.type, w.x16, w.xs, c.p.offsets, c.p.active, c.p.n_active, w.order, T);
+                       L.gate.type, w.x16, w.xs, c.p.offsets, c.p.active, c.p.n_active, L.has_shared, L.k, w.slots,
+                       w.n_slots, T);
     return hipGetLastError();
   }
   if (stage == kStageCombine)
@@ -284,7 +279,8 @@ hipError_t launch_decode_stage(int stage, const FfnCall& c, hipStream_t s) {
   a.offsets = c.p.offsets;
   a.row_token = c.p.row_token;
   a.active = c.p.active;
-  a.order = w.order;
+  a.slots = w.slots;
+  a.n_slots = w.n_slots;
   a.n_active = c.p.n_active;
   a.error = c.p.error;
   if (stage == kStageGateUp) {

@@ -35,14 +35,13 @@ struct DecodeArgs {
   QMatDev mat[2];   // routed: gate, up (gate/up pass) or down (down pass)
   QMatDev smat[2];  // shared expert, same roles
   int has_shared;
-  // per-layer path: plan in global memory (the shared slot first, then the
-  // active experts in `order`: by descending token count)
+  // per-layer path: plan in global memory
   const int32_t* offsets;
   const int32_t* row_token;
   const int32_t* active;
   const int32_t* n_active;
-  const int32_t* order;
-  // fused path: slot table (shared first) and its length
+  // slot table (the shared expert first; per-layer path: then the active
+  // experts by descending token count) and its length
   const SlotEnt* slots;
   const int32_t* n_slots;
   int32_t* error;
@@ -99,7 +98,6 @@ __device__ __forceinline__ void dq_pin_args(const DecodeArgs& a) {
   pin_arg(a.o);
   pin_arg(a.pair_of_row);
   pin_arg(a.error);
-  pin_arg(a.order);
 }
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
@@ -529,7 +527,8 @@ struct DecodeWs {
   float* xs;
   f16* h16;
   float* o;
-  int32_t* order;  // active experts by descending token count
+  SlotEnt* slots;    // per-layer slot table (see DecodeArgs::slots), T*k + 2 entries
+  int32_t* n_slots;
 };
 
 inline DecodeWs carve(void* ws, int T, int d, int f, int k, int P) {
@@ -544,7 +543,9 @@ inline DecodeWs carve(void* ws, int T, int d, int f, int k, int P) {
   p += align_up(R * 2 * f * 2, 256);
   w.o = (float*)p;
   p += align_up(R * d * 4, 256);
-  w.order = (int32_t*)p;
+  w.slots = (SlotEnt*)p;
+  p += align_up(((size_t)T * k + 2) * sizeof(SlotEnt), 256);
+  w.n_slots = (int32_t*)p;
   return w;
 }
 

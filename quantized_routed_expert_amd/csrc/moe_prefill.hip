@@ -18,6 +18,17 @@ namespace qre {
 
 constexpr int kBM = 96;    // plan rows per tile
 
+// One M-tile of the grouped GEMM: its expert (-1: the shared expert), the
+// slot's first plan row and row count, and the tile's first row in the slot.
+struct PfTile {
+  int32_t e, row0, cnt, m0;
+};
+// M-tiles at most: one per kBM plan rows of the routed pairs, plus one
+// partial tile per active expert, plus the shared expert's.
+inline int pf_tile_cap(int T, int k, int E) {
+  return (T * k + kBM - 1) / kBM + (T * k < E ? T * k : E) + (T + kBM - 1) / kBM + 1;
+}
+
 struct PrefillArgs {
   QMatDev mat[2];
   QMatDev smat[2];
@@ -27,6 +38,8 @@ struct PrefillArgs {
   const int32_t* active;
   const int32_t* n_active;
   const int32_t* mstart;   // [n_slots + 1] first M-tile of each slot
+  const PfTile* tiles;     // [M-tiles] the M-tile table
+  const int32_t* n_mtiles; // its length
   int T, k;
   const f16* x16;          // gate/up: scaled fp16 tokens [T][d] (weight-decode layout)
   const float* xs;         // gate/up: scale of each token row (a power of two)
@@ -40,14 +53,16 @@ struct PrefillArgs {
 // Preparation, one launch: workgroups 0 .. T-1 write the scaled fp16 copy of
 // their token (max |x| scaled into [2^14, 2^15), elements in the layout the
 // gate/up weights decode to); workgroup T builds the tile list,
-// mstart[s] = sum over earlier slots of ceil(rows / kBM).
+// mstart[s] = sum over earlier slots of ceil(rows / kBM), and the M-tile
+// table (so that a GEMM item finds its expert and rows in one load).
 template <bool XB>
 __global__ __launch_bounds__(256) void k_pf_prepare(const void* __restrict__ x, int T, int d, int gate_fmt,
                                                     f16* __restrict__ x16, float* __restrict__ xs,
                                                     const int32_t* __restrict__ offsets,
                                                     const int32_t* __restrict__ active,
                                                     const int32_t* __restrict__ n_active, int has_shared,
-                                                    int32_t* __restrict__ mstart) {
+                                                    int32_t* __restrict__ mstart, PfTile* __restrict__ tiles,
+                                                    int32_t* __restrict__ n_mtiles, int k) {
   __shared__ int32_t part[256];
   __shared__ float red[4];
   const int tid = threadIdx.x;
@@ -86,23 +101,18 @@ __global__ __launch_bounds__(256) void k_pf_prepare(const void* __restrict__ x, 
       run += v;
     }
     mstart[n_slots] = run;
+    *n_mtiles = run;
   }
   __syncthreads();
   int run = part[tid];
   for (int s = s0; s < s1; ++s) {
     mstart[s] = run;
-    const int cnt = (s < *n_active) ? offsets[active[s] + 1] - offsets[active[s]] : T;
-    run += (cnt + kBM - 1) / kBM;
+    const bool routed = s < *n_active;
+    const int e = routed ? active[s] : -1;
+    const int row0 = routed ? offsets[e] : T * k;
+    const int cnt = routed ? offsets[e + 1] - row0 : T;
+    for (int m0 = 0; m0 < cnt; m0 += kBM) tiles[run++] = PfTile{e, row0, cnt, m0};
   }
-}
-
-__device__ __forceinline__ int find_slot(const int32_t* mstart, int n_slots, int mt) {
-  int lo = 0, hi = n_slots - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (mstart[mid] <= mt) lo = mid; else hi = mid - 1;
-  }
-  return lo;
 }
 
 // ----------------------------------------------------------------------------
@@ -188,9 +198,7 @@ __global__ __launch_bounds__(kPfThreads, FMT == MOE_IQ4_NL ? 2 : 1) void k_pf_ge
   const QMatDev& M0 = a.mat[0];
   const int rows = M0.rows, K = M0.cols;
   const int n_ntiles = GATEUP ? rows / (kPfWaves * 8 * NF) : rows / (kPfWaves * 16 * NF);
-  const int n_act = *a.n_active;
-  const int n_slots = n_act + a.has_shared;
-  const int total = a.mstart[n_slots] * n_ntiles;
+  const int total = *a.n_mtiles * n_ntiles;
   const int crb = code_row_bytes(FMT, K), srb = scale_row_bytes(FMT, K);
   const int nstages = K / kPfBK;
   const f16* act = GATEUP ? a.x16 : a.hin;  // fp16 [rows][K]
@@ -211,19 +219,10 @@ __global__ __launch_bounds__(kPfThreads, FMT == MOE_IQ4_NL ? 2 : 1) void k_pf_ge
     const int item = xcd * per_xcd + it;
     if (item >= total) break;
     const int mt = item / n_ntiles, nt = item % n_ntiles;
-    const int slot = find_slot(a.mstart, n_slots, mt);
-    const bool is_sh = slot >= n_act;
-    int e, row0, cnt;
-    if (!is_sh) {
-      e = a.active[slot];
-      row0 = a.offsets[e];
-      cnt = a.offsets[e + 1] - row0;
-    } else {
-      e = 0;
-      row0 = a.T * a.k;
-      cnt = a.T;
-    }
-    const int m0 = (mt - a.mstart[slot]) * kBM;  // first row of this tile within the slot
+    const PfTile tl = a.tiles[mt];
+    const bool is_sh = tl.e < 0;
+    const int e = is_sh ? 0 : tl.e, row0 = tl.row0, cnt = tl.cnt;
+    const int m0 = tl.m0;  // first row of this tile within the slot
 
     // ---- this lane's weight rows (one per fragment)
     const uint8_t* bc[NF];
@@ -360,6 +359,8 @@ namespace {
 
 struct PrefillWs {
   int32_t* mstart;
+  PfTile* tiles;
+  int32_t* n_mtiles;
   f16* h;
   uint16_t* o;
   f16* x16;   // scaled fp16 tokens
@@ -371,6 +372,10 @@ PrefillWs carve(void* ws, int T, int d, int f, int k, int E) {
   PrefillWs w;
   w.mstart = (int32_t*)p;
   p += align_up((size_t)(E + 2) * 4, 256);
+  w.tiles = (PfTile*)p;
+  p += align_up((size_t)pf_tile_cap(T, k, E) * sizeof(PfTile), 256);
+  w.n_mtiles = (int32_t*)p;
+  p += 256;
   const size_t R = (size_t)T * k + T;
   w.h = (f16*)p;
   p += align_up(R * f * 2, 256);
@@ -409,7 +414,8 @@ hipError_t launch_gemm(int fmt, int nf, const PrefillArgs& a, int grid, hipStrea
 
 size_t prefill_ws_bytes(int T, int d, int f, int k) {
   const size_t R = (size_t)T * k + T;
-  return align_up((size_t)(4096 + 2) * 4, 256) + align_up(R * f * 2, 256) + align_up(R * d * 2, 256) +
+  return align_up((size_t)(4096 + 2) * 4, 256) + align_up((size_t)pf_tile_cap(T, k, 4096) * sizeof(PfTile), 256) +
+         256 + align_up(R * f * 2, 256) + align_up(R * d * 2, 256) +
          align_up((size_t)T * d * 2, 256) + align_up((size_t)T * 4, 256);
 }
 
@@ -420,10 +426,10 @@ hipError_t launch_prefill_stage(int stage, const FfnCall& c, hipStream_t s) {
   if (stage == kStagePrepare) {
     if (c.x_dtype == MOE_BF16)
       hipLaunchKernelGGL(k_pf_prepare<true>, dim3(T + 1), dim3(256), 0, s, c.x, T, L.d, L.gate.type, w.x16, w.xs,
-                         c.p.offsets, c.p.active, c.p.n_active, L.has_shared, w.mstart);
+                         c.p.offsets, c.p.active, c.p.n_active, L.has_shared, w.mstart, w.tiles, w.n_mtiles, L.k);
     else
       hipLaunchKernelGGL(k_pf_prepare<false>, dim3(T + 1), dim3(256), 0, s, c.x, T, L.d, L.gate.type, w.x16, w.xs,
-                         c.p.offsets, c.p.active, c.p.n_active, L.has_shared, w.mstart);
+                         c.p.offsets, c.p.active, c.p.n_active, L.has_shared, w.mstart, w.tiles, w.n_mtiles, L.k);
     return hipGetLastError();
   }
   if (stage == kStageCombine)
@@ -435,6 +441,8 @@ hipError_t launch_prefill_stage(int stage, const FfnCall& c, hipStream_t s) {
   a.active = c.p.active;
   a.n_active = c.p.n_active;
   a.mstart = w.mstart;
+  a.tiles = w.tiles;
+  a.n_mtiles = w.n_mtiles;
   a.T = T;
   a.k = L.k;
   a.error = c.p.error;

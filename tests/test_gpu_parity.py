@@ -227,6 +227,24 @@ def test_decode_path_small(types, T, x_dtype):
     _say(f"[decode] {stats}")
 
 
+@pytest.mark.parametrize("T,x_dtype", [(40, "bf16"), (23, "f32")])
+def test_decode_path_long_rows(T, x_dtype):
+    """Rows longer than the codes kept in registers (Q8_0, d = 4096: 16 steps
+    per wave, rolled forward) with several column passes per item, and a
+    router row length the small-batch MFMA router takes (bf16 tokens)."""
+    _say(f"[decode long] T={T} x={x_dtype}")
+    wl, layer = _small_layer(300 + T, d=4096, f=256, E=32, k=6, types=("q8_0", "q8_0", "q8_0"))
+    x = torch.randn((T, wl.d), generator=torch.Generator().manual_seed(T))
+    if x_dtype == "bf16":
+        x = x.to(torch.bfloat16)
+    st, gpu = _run_single(layer, x, x_dtype, "f32")
+    lnp = synth.layer_to_numpy(layer)
+    xn = x.float().numpy().astype(np.float64)
+    stats = check_layer(lnp, xn, gpu, "f32", TOL_DECODE)
+    assert int(st.bufs[0].plan.error.item()) == 0
+    _say(f"[decode long] {stats}")
+
+
 @pytest.mark.parametrize("types", FORMATS, ids=lambda t: "-".join(t))
 @pytest.mark.parametrize("T,y_dtype", [(65, "bf16"), (300, "f32")])
 def test_prefill_path_small(types, T, y_dtype):

@@ -523,12 +523,18 @@ __global__ __launch_bounds__(1024) void k_plan_scan(int T, int k, int E, int nb,
   __shared__ int32_t scratch[2][17];
   __shared__ int32_t err_s;
   const int e = threadIdx.x;
+  constexpr int kB = 16;  // block counts per batch, all loads of a batch in flight together
   int cnt = 0;
   if (e < E) {
-    for (int b = 0; b < nb; ++b) {  // per-block exclusive prefix, in place
-      const int c = hist[(long)b * E + e];
-      hist[(long)b * E + e] = cnt;
-      cnt += c;
+    for (int b0 = 0; b0 < nb; b0 += kB) {  // per-block exclusive prefix, in place
+      int c[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) c[u] = b0 + u < nb ? hist[(long)(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        if (b0 + u < nb) hist[(long)(b0 + u) * E + e] = cnt;
+        cnt += c[u];
+      }
     }
   }
   int n_valid, n_act;
@@ -539,7 +545,14 @@ __global__ __launch_bounds__(1024) void k_plan_scan(int T, int k, int E, int nb,
     p.offsets[e] = off;
     if (cnt > 0) p.active[aoff] = e;
     if (e >= n_act) p.active[e] = -1;
-    for (int b = 0; b < nb; ++b) hist[(long)b * E + e] += off;
+    for (int b0 = 0; b0 < nb; b0 += kB) {
+      int c[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) c[u] = b0 + u < nb ? hist[(long)(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        if (b0 + u < nb) hist[(long)(b0 + u) * E + e] = c[u] + off;
+    }
   }
   if (threadIdx.x == 0) err_s = 0;
   __syncthreads();

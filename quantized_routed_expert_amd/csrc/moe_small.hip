@@ -207,9 +207,11 @@ __global__ __launch_bounds__(256) void k_router_gemm_f32(const float* __restrict
 // part is exact in fp32, so three MFMAs per product give fp32-accumulated
 // dot products of the fp32 weights with the bf16 tokens.  A workgroup covers
 // 64 tokens x 128 experts; wavefront w holds all 64 tokens (four M fragments)
-// and experts [32w, 32w+32) (two N fragments).  Operands come straight from
-// global memory (the four wavefronts read the same token fragments, which L1
-// serves), K in chunks of 32, the next chunk's loads in flight.
+// and experts [32w, 32w+32) (two N fragments).  The token tile of each
+// 128-element K group is copied once per workgroup into LDS (16-byte LDS
+// DMA) and read from there by the four wavefronts; each wavefront loads its
+// router words itself.  The next group's copies and loads are in flight while
+// the current group's products run.
 constexpr int kRmTok = 64, kRmExp = 128;
 
 __device__ __forceinline__ void split_bf16x3(const f32x4 (&w)[2], bf16x8& p1, bf16x8& p2, bf16x8& p3) {
@@ -233,19 +235,45 @@ __device__ __forceinline__ void split_bf16x3(const f32x4 (&w)[2], bf16x8& p1, bf
   p3 = __builtin_bit_cast(bf16x8, q3);
 }
 
-__global__ __launch_bounds__(256) void k_router_mfma(const float* __restrict__ W, const float* __restrict__ bias,
-                                                     const uint16_t* __restrict__ x, int T, int E, int d,
-                                                     float* __restrict__ logits) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_router_mfma(
+    const float* __restrict__ W, const float* __restrict__ bias, const uint16_t* __restrict__ x, int T, int E, int d,
+    float* __restrict__ logits) {
+  // the token tile of a 128-element K group: [64 rows][16 chunks of 8], chunk
+  // c of row r at c ^ (r & 15) (the 16 rows of a fragment read fall in
+  // distinct banks); two buffers, the next group's copy in flight
+  __shared__ __align__(16) uint8_t sx[2][kRmTok * 16 * 16];
+  typedef __attribute__((address_space(3))) void lds_void_t;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int n = lane & 15, G = lane >> 4;
   const int t0 = blockIdx.y * kRmTok, e0 = blockIdx.x * kRmExp + wid * 32;
-  // this lane's rows (rows past the end repeat the last one and are not stored)
-  const uint16_t* xr[4];
+  // this thread's four 16-byte copies per group: LDS slot q*256 + tid holds
+  // row (q*256 + tid) / 16, stored chunk (q*256 + tid) % 16, i.e. logical
+  // chunk (stored ^ row % 16); rows past T repeat the last one
+  const uint16_t* xsrc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int slot = q * 256 + tid, r = slot >> 4, c = (slot & 15) ^ (r & 15);
+    xsrc[q] = x + (long)min(t0 + r, T - 1) * d + c * 8;
+  }
+  auto copy_x = [&](int kg, int buf) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(xsrc[q] + kg), (lds_void_t*)(&sx[buf][(q * 256 + wid * 64) * 16]),
+                                       16, 0, 0);
+  };
+  // this lane's router rows (rows past the end repeat the last one and are not stored)
   const float* wr[2];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) xr[mi] = x + (long)min(t0 + mi * 16 + n, T - 1) * d + 8 * G;
-#pragma unroll
   for (int f = 0; f < 2; ++f) wr[f] = W + (long)min(e0 + f * 16 + n, E - 1) * d + 8 * G;
+  auto load_w = [&](int kg, f32x4 (&wb)[4][2][2]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        wb[j][f][0] = *(const f32x4*)(wr[f] + kg + 32 * j);
+        wb[j][f][1] = *(const f32x4*)(wr[f] + kg + 32 * j + 4);
+      }
+  };
 
   f32x4 acc[4][2];
 #pragma unroll
@@ -253,39 +281,50 @@ __global__ __launch_bounds__(256) void k_router_mfma(const float* __restrict__ W
 #pragma unroll
     for (int f = 0; f < 2; ++f) acc[mi][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto load = [&](int kc, u32x4 (&xa)[4], f32x4 (&wb)[2][2]) {
+  auto compute = [&](int buf, const f32x4 (&wb)[4][2][2]) {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) xa[mi] = *(const u32x4*)(xr[mi] + kc);
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      wb[f][0] = *(const f32x4*)(wr[f] + kc);
-      wb[f][1] = *(const f32x4*)(wr[f] + kc + 4);
-    }
-  };
-  auto compute = [&](const u32x4 (&xa)[4], const f32x4 (&wb)[2][2]) {
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      bf16x8 p1, p2, p3;
-      split_bf16x3(wb[f], p1, p2, p3);
+    for (int j = 0; j < 4; ++j) {
+      u32x4 xa[4];
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, xa[mi]);
-        acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, p1, acc[mi][f], 0, 0, 0);
-        acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, p2, acc[mi][f], 0, 0, 0);
-        acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, p3, acc[mi][f], 0, 0, 0);
+        const int r = mi * 16 + n;
+        xa[mi] = *(const u32x4*)&sx[buf][(r * 16 + ((4 * j + G) ^ n)) * 16];
+      }
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        bf16x8 p1, p2, p3;
+        split_bf16x3(wb[j][f], p1, p2, p3);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, xa[mi]);
+          acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, p1, acc[mi][f], 0, 0, 0);
+          acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, p2, acc[mi][f], 0, 0, 0);
+          acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, p3, acc[mi][f], 0, 0, 0);
+        }
       }
     }
   };
-  // two chunks per iteration (d is a multiple of 128); past the end the
-  // prefetch repeats the last chunk and is not used
-  u32x4 xa0[4], xa1[4];
-  f32x4 wb0[2][2], wb1[2][2];
-  load(0, xa0, wb0);
-  for (int kc = 0; kc < d; kc += 64) {
-    load(kc + 32, xa1, wb1);
-    compute(xa0, wb0);
-    load(min(kc + 64, d - 32), xa0, wb0);
-    compute(xa1, wb1);
+  // K in groups of 128 (d is a multiple of 128): the group's token tile and
+  // router words were requested during the previous group
+  f32x4 wb0[4][2][2], wb1[4][2][2];
+  copy_x(0, 0);
+  load_w(0, wb0);
+  for (int kg = 0; kg < d; kg += 256) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // group kg is in LDS for every wave; buffer 1 is free
+    if (kg + 128 < d) {
+      copy_x(kg + 128, 1);
+      load_w(kg + 128, wb1);
+    }
+    compute(0, wb0);
+    if (kg + 128 >= d) break;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // group kg + 128 is in LDS; buffer 0 is free
+    if (kg + 256 < d) {
+      copy_x(kg + 256, 0);
+      load_w(kg + 256, wb0);
+    }
+    compute(1, wb1);
   }
   // D row 4G + v of fragment (mi, f): token t0 + mi*16 + 4G + v, expert e0 + f*16 + n
 #pragma unroll

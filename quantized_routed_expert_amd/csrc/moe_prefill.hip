@@ -71,15 +71,29 @@ __global__ __launch_bounds__(256) void k_pf_prepare(const void* __restrict__ x, 
     auto ld = [&](int i) -> float {
       return XB ? bf16_bits_to_f32(((const uint16_t*)x)[t * d + i]) : ((const float*)x)[t * d + i];
     };
+    // the token is read once: d <= 16 * 256 elements stay in registers
+    constexpr int kPerThread = 16;
+    float v[kPerThread];
     float mx = 0.0f;
-    for (int i = tid; i < d; i += 256) mx = fmaxf(mx, fabsf(ld(i)));
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int i = tid + j * 256;
+      v[j] = i < d ? ld(i) : 0.0f;
+      mx = fmaxf(mx, fabsf(v[j]));
+    }
+    for (int i = tid + kPerThread * 256; i < d; i += 256) mx = fmaxf(mx, fabsf(ld(i)));
     mx = wave_max(mx);
     if ((tid & 63) == 0) red[tid >> 6] = mx;
     __syncthreads();
     mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const int ex = x16_exponent(mx);
     const float down = ldexpf(1.0f, -ex);
-    for (int i = tid; i < d; i += 256) x16[t * d + act_pos(gate_fmt, i)] = (f16)(ld(i) * down);
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int i = tid + j * 256;
+      if (i < d) x16[t * d + act_pos(gate_fmt, i)] = (f16)(v[j] * down);
+    }
+    for (int i = tid + kPerThread * 256; i < d; i += 256) x16[t * d + act_pos(gate_fmt, i)] = (f16)(ld(i) * down);
     if (tid == 0) xs[t] = ldexpf(1.0f, ex);
     return;
   }

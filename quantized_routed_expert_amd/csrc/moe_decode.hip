@@ -119,7 +119,8 @@ __global__ __launch_bounds__(256) void k_prep_x(const void* __restrict__ x, int 
                                                 const int32_t* __restrict__ offsets,
                                                 const int32_t* __restrict__ active,
                                                 const int32_t* __restrict__ n_active, int has_shared, int k,
-                                                SlotEnt* __restrict__ slots, int32_t* __restrict__ n_slots, int T) {
+                                                SlotEnt* __restrict__ slots, int32_t* __restrict__ n_slots, int T,
+                                                const int32_t* __restrict__ slot_row) {
   const int t = blockIdx.x;
   if (t == T) {
     __shared__ int32_t hist[kDecodeMaxT + 2];
@@ -161,15 +162,51 @@ __global__ __launch_bounds__(256) void k_prep_x(const void* __restrict__ x, int 
   mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const int ex = x16_exponent(mx);
   const float down = ldexpf(1.0f, -ex);
-  for (int i = threadIdx.x; i < d; i += blockDim.x) {
-    const float v = x_bf16 ? bf16_bits_to_f32(((const uint16_t*)x)[(long)t * d + i]) : ((const float*)x)[(long)t * d + i];
-    const float sv = v * down;
-    const int pos = act_pos(gate_fmt, i);
-    const f16 hi = (f16)sv;
-    x16[((long)t * P) * d + pos] = hi;
-    if (P == 2) x16[((long)t * P + 1) * d + pos] = (f16)(sv - (float)hi);
+  // the token's rows: its shared-expert row T*k + t, then the plan row of
+  // each of its k pairs (the expert passes read a slot's rows consecutively)
+  __shared__ int32_t rows[33];  // k <= 32
+  if ((int)threadIdx.x <= k) rows[threadIdx.x] = threadIdx.x == 0 ? T * k + t : slot_row[t * k + threadIdx.x - 1];
+  __syncthreads();
+  // one 8-position output chunk per step: positions 8c .. 8c+7 hold two runs
+  // of four consecutive elements (IQ4_NL block order: elements 4q.. and
+  // 16+4q.. of the block for quarter q; other formats: in order), stored as
+  // one 16-byte word per row
+  for (int c = threadIdx.x; c < d / 8; c += blockDim.x) {
+    const int e0 = gate_fmt == MOE_IQ4_NL ? (c >> 2) * 32 + 4 * (c & 3) : 8 * c;
+    const int e1 = gate_fmt == MOE_IQ4_NL ? e0 + 16 : e0 + 4;
+    float v[8];
+    if (x_bf16) {
+      const u32x2 a = *(const u32x2*)((const uint16_t*)x + (long)t * d + e0);
+      const u32x2 b = *(const u32x2*)((const uint16_t*)x + (long)t * d + e1);
+      const uint32_t w[4] = {a.x, a.y, b.x, b.y};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = bf16_bits_to_f32(w[q] & 0xffffu);
+        v[2 * q + 1] = bf16_bits_to_f32(w[q] >> 16);
+      }
+    } else {
+      const f32x4 a = *(const f32x4*)((const float*)x + (long)t * d + e0);
+      const f32x4 b = *(const f32x4*)((const float*)x + (long)t * d + e1);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    f16x8 hi, lo;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float sv = v[q] * down;
+      hi[q] = (f16)sv;
+      lo[q] = (f16)(sv - (float)hi[q]);
+    }
+    for (int j = 0; j <= k; ++j) {
+      const long r = rows[j];
+      *(f16x8*)&x16[(r * P) * d + 8 * c] = hi;
+      if (P == 2) *(f16x8*)&x16[(r * P + 1) * d + 8 * c] = lo;
+    }
   }
-  if (threadIdx.x < P) xs[(long)t * P + threadIdx.x] = ldexpf(1.0f, ex);
+  if ((int)threadIdx.x < (k + 1) * P) {
+    const int j = threadIdx.x / P, part = threadIdx.x - j * P;
+    xs[(long)rows[j] * P + part] = ldexpf(1.0f, ex);
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -256,7 +293,7 @@ hipError_t launch_dq_down_table(const DecodeArgs& a, int fmt, int items, hipStre
 size_t decode_ws_bytes(int T, int d, int f, int k, int x_dtype) {
   const int P = x_dtype == MOE_F32 ? 2 : 1;
   const size_t R = (size_t)T * k + T;
-  return align_up((size_t)T * P * d * 2, 256) + align_up((size_t)T * P * 4, 256) + align_up(R * 2 * f * 2, 256) +
+  return align_up(R * P * d * 2, 256) + align_up(R * P * 4, 256) + align_up(R * 2 * f * 2, 256) +
          align_up(R * d * 4, 256) + align_up(((size_t)T * k + 2) * sizeof(SlotEnt), 256) + 256;
 }
 
@@ -268,7 +305,7 @@ hipError_t launch_decode_stage(int stage, const FfnCall& c, hipStream_t s) {
   if (stage == kStagePrepare) {
     hipLaunchKernelGGL(k_prep_x, dim3(T + 1), dim3(256), 0, s, c.x, c.x_dtype == MOE_BF16 ? 1 : 0, L.d, P,
                        L.gate.type, w.x16, w.xs, c.p.offsets, c.p.active, c.p.n_active, L.has_shared, L.k, w.slots,
-                       w.n_slots, T);
+                       w.n_slots, T, c.p.slot_row);
     return hipGetLastError();
   }
   if (stage == kStageCombine)

@@ -188,10 +188,14 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
   // contiguous across the lane groups (64 bytes per row per step).
   const int kbase = kpart * kw + G * EPS;
 
-  // input row of column `col` (a token, or one fp16 part of it)
+  // input row of column `col` (a token, or one fp16 part of it).  Per-layer
+  // path (REUSE): the preparation wrote the gate/up input in plan-row order
+  // (rows T*k + t: the shared expert's), so a slot's rows are consecutive;
+  // fused path: one row per token, found through the plan.
   auto in_row_of = [&](int col) -> long {
     if constexpr (GATEUP) {
       const int tc = col / P, part = col - tc * P;
+      if constexpr (REUSE) return (long)(si.row0 + tc) * P + part;
       const int t = si.is_sh ? tc : row_token[si.row0 + tc];
       return (long)t * P + part;
     } else {
@@ -534,11 +538,13 @@ struct DecodeWs {
 inline DecodeWs carve(void* ws, int T, int d, int f, int k, int P) {
   char* p = (char*)ws;
   DecodeWs w;
-  w.x16 = (f16*)p;
-  p += align_up((size_t)T * P * d * 2, 256);
-  w.xs = (float*)p;
-  p += align_up((size_t)T * P * 4, 256);
+  // x16 / xs: per-layer path, one row per plan row and per token (the
+  // shared expert's, after the plan rows); fused path: rows 0..T-1 only
   const size_t R = (size_t)T * k + T;
+  w.x16 = (f16*)p;
+  p += align_up(R * P * d * 2, 256);
+  w.xs = (float*)p;
+  p += align_up(R * P * 4, 256);
   w.h16 = (f16*)p;
   p += align_up(R * 2 * f * 2, 256);
   w.o = (float*)p;

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2
     const int tile = (item % wg_per_slot) * rt_per_wg + wid / ksplit;
     const SlotEnt se = item == (int)blockIdx.x ? se0 : a.slots[slot];
     const SlotInfo si{se.e, se.shared != 0, se.row0, se.cnt};
-    dq_item<FMT, NT, GATEUP, ROLL, TABLE, !TABLE>(a, si, tile, wid % ksplit, a.row_token, sA);
+    dq_item<FMT, NT, GATEUP, ROLL, TABLE, !TABLE, !TABLE>(a, si, tile, wid % ksplit, a.row_token, sA);
     if constexpr (TABLE && !GATEUP) {
       if (a.tile_cnt) {
         __shared__ int s_last;

@@ -144,7 +144,7 @@ inline int dq_nsteps(int fmt, int K, int ksplit) { return K / ksplit / (4 * dq_e
 
 // PAIRS (down pass of the fused step): routed rows are written at the output
 // row pair_of_row gives their plan row.
-template <int FMT, int NT, bool GATEUP, bool ROLL, bool PAIRS = false, bool REUSE = false>
+template <int FMT, int NT, bool GATEUP, bool ROLL, bool PAIRS = false, bool REUSE = false, bool GATHER = false>
 __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si, int tile, int kpart,
                                         const int32_t* row_token, f16* sA) {
   // one word per column of a pass for the epilogue: the token's activation
@@ -188,14 +188,14 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
   // contiguous across the lane groups (64 bytes per row per step).
   const int kbase = kpart * kw + G * EPS;
 
-  // input row of column `col` (a token, or one fp16 part of it).  Per-layer
-  // path (REUSE): the preparation wrote the gate/up input in plan-row order
-  // (rows T*k + t: the shared expert's), so a slot's rows are consecutive;
-  // fused path: one row per token, found through the plan.
+  // input row of column `col` (a token, or one fp16 part of it).  GATHER
+  // (per-layer path): the preparation wrote the gate/up input in plan-row
+  // order (rows T*k + t: the shared expert's), so a slot's rows are
+  // consecutive; fused path: one row per token, found through the plan.
   auto in_row_of = [&](int col) -> long {
     if constexpr (GATEUP) {
       const int tc = col / P, part = col - tc * P;
-      if constexpr (REUSE) return (long)(si.row0 + tc) * P + part;
+      if constexpr (GATHER) return (long)(si.row0 + tc) * P + part;
       const int t = si.is_sh ? tc : row_token[si.row0 + tc];
       return (long)t * P + part;
     } else {

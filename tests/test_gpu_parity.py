@@ -227,6 +227,21 @@ def test_decode_path_small(types, T, x_dtype):
     _say(f"[decode] {stats}")
 
 
+def test_decode_path_many_experts():
+    """The largest per-layer decode batch over the widest router: T = 64,
+    k = 32, E = 1000 (up to 1000 active experts in the slot table, counts
+    from 1 to 64 in the counting sort)."""
+    T = 64
+    _say(f"[decode many] T={T} k=32 E=1000")
+    wl, layer = _small_layer(77, d=512, f=128, E=1000, k=32, types=("iq4_nl", "iq4_nl", "q8_0"))
+    x = torch.randn((T, wl.d), generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    st, gpu = _run_single(layer, x, "bf16", "f32")
+    lnp = synth.layer_to_numpy(layer)
+    stats = check_layer(lnp, x.float().numpy().astype(np.float64), gpu, "f32", TOL_DECODE)
+    assert int(st.bufs[0].plan.error.item()) == 0
+    _say(f"[decode many] {stats}")
+
+
 @pytest.mark.parametrize("T,x_dtype", [(40, "bf16"), (23, "f32")])
 def test_decode_path_long_rows(T, x_dtype):
     """Rows longer than the codes kept in registers (Q8_0, d = 4096: 16 steps

@@ -16,7 +16,7 @@
 
 namespace qre {
 
-constexpr int kBM = 96;    // plan rows per tile
+constexpr int kBM = 128;   // plan rows per tile
 
 // One M-tile of the grouped GEMM: its expert (-1: the shared expert), the
 // slot's first plan row and row count, and the tile's first row in the slot.
@@ -130,13 +130,13 @@ __global__ __launch_bounds__(256) void k_pf_prepare(const void* __restrict__ x, 
 }
 
 // ----------------------------------------------------------------------------
-// Grouped GEMM tile: kBM = 96 plan rows (M) x 64 * NF weight rows (N), K in
+// Grouped GEMM tile: kBM = 128 plan rows (M) x 64 * NF weight rows (N), K in
 // stages of 128.
 //
 // Activations (A operand of v_mfma_f32_16x16x32_f16) are copied global -> LDS
 // by 16-byte LDS-DMA loads (no registers), double-buffered: the next stage's
 // copies are in flight while the current stage computes.  The LDS tile is
-// [96 rows][16 chunks of 8 elements], chunk c of row r stored at c ^ (r & 15)
+// [128 rows][16 chunks of 8 elements], chunk c of row r stored at c ^ (r & 15)
 // so that the 16 rows a fragment read touches fall in distinct banks; each
 // lane of a copy picks the source chunk that lands at its LDS slot.
 //
@@ -148,22 +148,24 @@ __global__ __launch_bounds__(256) void k_pf_prepare(const void* __restrict__ x, 
 // are stored in the order the weights decode to).  One MFMA thus reduces over
 // four blocks; the K order of a sum is immaterial to the GEMM.
 //
-// Four wavefronts each hold all 96 M rows and NF = 4 weight-row fragments, so
-// that every A fragment read from LDS feeds four MFMAs; two workgroups share a
-// CU (IQ4_NL: at most 256 registers per lane), so that one wavefront's MFMAs
-// overlap the other's LDS reads and weight decode on each SIMD.  (96 rows
-// measured faster than 112 within that budget.)
+// Four wavefronts each hold all M rows of the tile and NF = 4 weight-row
+// fragments, so a decoded weight fragment feeds up to eight MFMAs and an A
+// fragment read from LDS feeds four; two workgroups share a CU (IQ4_NL: at
+// most 256 registers per lane), so that one wavefront's MFMAs overlap the
+// other's LDS reads and weight decode on each SIMD.  A tile is computed over
+// its first NMF = 2, 4 or 8 M fragments only (enough for its rows): rows past
+// the slot's end in the last fragments are copied from its first row and
+// never stored.
 // GATEUP: wave w holds f-rows [32w, 32w+32) of the tile's 128, as two gate and
 //         two up fragments, so SwiGLU is formed in registers.
 // DOWN:   wave w holds 16 * NF consecutive d-rows.
 // ----------------------------------------------------------------------------
 constexpr int kPfBK = 128;                       // K per stage
-constexpr int kPfMF = kBM / 16;                  // M fragments
+constexpr int kPfMF = kBM / 16;                  // M fragments of a full tile
 constexpr int kPfBuf = kBM * kPfBK * 2;          // bytes of one activation buffer
 constexpr int kXcds = 8;                         // accelerator complex dies of an MI355X
 constexpr int kPfWaves = 4;                      // wavefronts per workgroup
 constexpr int kPfThreads = 64 * kPfWaves;
-constexpr int kPfCopies = kBM * kPfBK * 2 / (16 * kPfThreads);  // 16-byte copies per thread per stage
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -203,25 +205,165 @@ __device__ __forceinline__ f16x8 pf_decode(const PfCodes<FMT>& pc, int i) {
   }
 }
 
-template <int FMT, bool GATEUP, int NF>
-__global__ __launch_bounds__(kPfThreads, FMT == MOE_IQ4_NL ? 2 : 1) void k_pf_gemm(const PrefillArgs a) {
-  extern __shared__ __align__(16) uint8_t sAbuf[];  // [2][kBM][16 chunks][16 B]
-  __shared__ float s_rsx[kBM];                      // gate/up: token scale of each tile row
+// One work item (M-tile x N-tile) over its first NMF M fragments.
+template <int FMT, bool GATEUP, int NF, int NMF>
+__device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sAbuf, float* s_rsx, const PfTile tl,
+                                        int nt, int rows, int K) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int n = lane & 15, G = lane >> 4;
-  const QMatDev& M0 = a.mat[0];
-  const int rows = M0.rows, K = M0.cols;
-  const int n_ntiles = GATEUP ? rows / (kPfWaves * 8 * NF) : rows / (kPfWaves * 16 * NF);
-  const int total = *a.n_mtiles * n_ntiles;
   const int crb = code_row_bytes(FMT, K), srb = scale_row_bytes(FMT, K);
   const int nstages = K / kPfBK;
   const f16* act = GATEUP ? a.x16 : a.hin;  // fp16 [rows][K]
+  const bool is_sh = tl.e < 0;
+  const int e = is_sh ? 0 : tl.e, row0 = tl.row0, cnt = tl.cnt;
+  const int m0 = tl.m0;  // first row of this tile within the slot
 
   // A fragment of step i: row mi*16 + n, logical chunk 4G + i, stored at
   // chunk (4G + i) ^ n; the fragment index adds mi * 4096 bytes
   int aoff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) aoff[i] = (n * 16 + ((4 * G + i) ^ n)) * 16;
+
+  // ---- this lane's weight rows (one per fragment)
+  const uint8_t* bc[NF];
+  const uint8_t* bs[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    int mi = 0, wr;
+    if constexpr (GATEUP) {
+      mi = f / (NF / 2);                                                       // gate, then up
+      wr = nt * (kPfWaves * 8 * NF) + wid * (8 * NF) + (f % (NF / 2)) * 16 + n;  // same f-rows for both
+    } else {
+      wr = nt * (kPfWaves * 16 * NF) + wid * (16 * NF) + f * 16 + n;
+    }
+    const QMatDev& W = is_sh ? a.smat[mi] : a.mat[mi];
+    const long rw = (long)e * rows + wr;
+    bc[f] = W.codes + rw * crb;
+    bs[f] = W.scales + rw * srb;
+  }
+  float tsg = 1.0f, tsu = 1.0f;  // NVFP4 tensor scales (gate, up / down)
+  if constexpr (FMT == MOE_NVFP4) {
+    tsg = (is_sh ? a.smat[0] : a.mat[0]).ts[e];
+    if constexpr (GATEUP) tsu = (is_sh ? a.smat[1] : a.mat[1]).ts[e];
+  }
+
+  // ---- activation copies: copy c = 4q + w (wave w, q < NMF) fills LDS bytes
+  // [1024c, 1024c + 1024), i.e. tile row 4c + lane/16, stored chunk lane%16 =
+  // logical chunk ^ (row%16).
+  int asrc[NMF];  // element offset of the source row (rows past the slot's end copy its first row)
+  int acol[NMF];  // element offset of the logical chunk
+#pragma unroll
+  for (int q = 0; q < NMF; ++q) {
+    const int r = (q * kPfWaves + wid) * 4 + (lane >> 4);
+    const int rr = m0 + r;
+    const int rs = rr < cnt ? rr : 0;
+    if constexpr (GATEUP) {
+      const int t = is_sh ? rs : a.row_token[row0 + rs];
+      asrc[q] = t * K;
+    } else {
+      asrc[q] = (row0 + rs) * K;
+    }
+    acol[q] = ((lane & 15) ^ (r & 15)) * 8;
+  }
+  auto copy_a = [&](int s, int buf) {
+    uint8_t* base = sAbuf + buf * kPfBuf + wid * 1024;
+#pragma unroll
+    for (int q = 0; q < NMF; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(act + asrc[q] + s * kPfBK + acol[q]),
+                                       (lds_void*)(base + q * kPfWaves * 1024), 16, 0, 0);
+  };
+  auto load_b = [&](int s, PfCodes<FMT> (&pc)[NF]) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) pf_load_codes<FMT>(bc[f], bs[f], s * kPfBK + 32 * G, pc[f]);
+  };
+
+  f32x4 acc[NMF][NF];
+#pragma unroll
+  for (int mi = 0; mi < NMF; ++mi)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[mi][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  PfCodes<FMT> pc[NF], pn[NF];
+  copy_a(0, 0);
+  load_b(0, pc);
+  // gate/up: the token scale of tile row tid, kept for the epilogue
+  float rsx = 0.0f;
+  if constexpr (GATEUP) {
+    if (tid < NMF * 16) {
+      const int rr = m0 + tid;
+      const int rs = rr < cnt ? rr : 0;
+      rsx = a.xs[is_sh ? rs : a.row_token[row0 + rs]];
+    }
+  }
+  for (int s = 0; s < nstages; ++s) {
+    __builtin_amdgcn_s_waitcnt(0);  // this stage's copies and codes have landed
+    __syncthreads();                // ... for every wave; the other buffer is free
+    if (s + 1 < nstages) {
+      copy_a(s + 1, (s + 1) & 1);
+      load_b(s + 1, pn);
+    }
+    const uint8_t* sa = sAbuf + (s & 1) * kPfBuf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint8_t* p = sa + aoff[i];
+      f16x8 bw[NF];
+#pragma unroll
+      for (int f = 0; f < NF; ++f) bw[f] = pf_decode<FMT>(pc[f], i);
+#pragma unroll
+      for (int mi = 0; mi < NMF; ++mi) {
+        const f16x8 af = __builtin_bit_cast(f16x8, *(const u32x4*)(p + mi * 4096));
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+          acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bw[f], acc[mi][f], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int f = 0; f < NF; ++f) pc[f] = pn[f];
+  }
+  if (GATEUP && tid < NMF * 16) s_rsx[tid] = rsx;
+  __syncthreads();  // the next item's first copy must not overwrite a buffer still being read
+
+  // ---- epilogue: D row (M) = mi*16 + 4G + v, column (N) = fragment row n
+  bool bad = false;  // an h value beyond fp16 range
+#pragma unroll
+  for (int mi = 0; mi < NMF; ++mi) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int rr = m0 + mi * 16 + 4 * G + v;
+      if (rr >= cnt) continue;
+      const long orow = row0 + rr;
+      if constexpr (GATEUP) {
+        const float sx = s_rsx[mi * 16 + 4 * G + v];
+#pragma unroll
+        for (int f = 0; f < NF / 2; ++f) {
+          const float g = acc[mi][f][v] * sx * tsg, u = acc[mi][f + NF / 2][v] * sx * tsu;
+          // silu(g) * u with the hardware reciprocal (about 1 ulp); h is then
+          // rounded to fp16
+          const float hv = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+          bad |= !(fabsf(hv) < 65504.0f);
+          const int fcol = nt * (kPfWaves * 8 * NF) + wid * (8 * NF) + f * 16 + n;
+          a.hout[orow * rows + act_pos(a.down_type, fcol)] = (f16)hv;
+        }
+      } else {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const int dcol = nt * (kPfWaves * 16 * NF) + wid * (16 * NF) + f * 16 + n;
+          a.o[orow * rows + dcol] = (uint16_t)f32_to_bf16_bits(acc[mi][f][v] * tsg);
+        }
+      }
+    }
+  }
+  if (GATEUP && bad) atomicOr(a.error, 2);
+}
+
+template <int FMT, bool GATEUP, int NF>
+__global__ __launch_bounds__(kPfThreads, FMT == MOE_IQ4_NL ? 2 : 1) void k_pf_gemm(const PrefillArgs a) {
+  __shared__ __align__(16) uint8_t sAbuf[2 * kPfBuf];  // [2][kBM][16 chunks][16 B]
+  __shared__ float s_rsx[kBM];                         // gate/up: token scale of each tile row
+  const QMatDev& M0 = a.mat[0];
+  const int rows = M0.rows, K = M0.cols;
+  const int n_ntiles = GATEUP ? rows / (kPfWaves * 8 * NF) : rows / (kPfWaves * 16 * NF);
+  const int total = *a.n_mtiles * n_ntiles;
 
   // Workgroups are dealt to the XCDs round-robin by index; each XCD takes a
   // contiguous run of items (the N-tiles of an M-tile, then the next M-tiles
@@ -234,138 +376,13 @@ __global__ __launch_bounds__(kPfThreads, FMT == MOE_IQ4_NL ? 2 : 1) void k_pf_ge
     if (item >= total) break;
     const int mt = item / n_ntiles, nt = item % n_ntiles;
     const PfTile tl = a.tiles[mt];
-    const bool is_sh = tl.e < 0;
-    const int e = is_sh ? 0 : tl.e, row0 = tl.row0, cnt = tl.cnt;
-    const int m0 = tl.m0;  // first row of this tile within the slot
-
-    // ---- this lane's weight rows (one per fragment)
-    const uint8_t* bc[NF];
-    const uint8_t* bs[NF];
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      int mi = 0, wr;
-      if constexpr (GATEUP) {
-        mi = f / (NF / 2);                                                       // gate, then up
-        wr = nt * (kPfWaves * 8 * NF) + wid * (8 * NF) + (f % (NF / 2)) * 16 + n;  // same f-rows for both
-      } else {
-        wr = nt * (kPfWaves * 16 * NF) + wid * (16 * NF) + f * 16 + n;
-      }
-      const QMatDev& W = is_sh ? a.smat[mi] : a.mat[mi];
-      const long rw = (long)e * rows + wr;
-      bc[f] = W.codes + rw * crb;
-      bs[f] = W.scales + rw * srb;
-    }
-    float tsg = 1.0f, tsu = 1.0f;  // NVFP4 tensor scales (gate, up / down)
-    if constexpr (FMT == MOE_NVFP4) {
-      tsg = (is_sh ? a.smat[0] : a.mat[0]).ts[e];
-      if constexpr (GATEUP) tsu = (is_sh ? a.smat[1] : a.mat[1]).ts[e];
-    }
-
-    // ---- activation copies: wave w, copy q covers LDS chunks (w*C+q)*64 + lane,
-    // i.e. tile row (w*C+q)*4 + lane/16, stored chunk lane%16 = logical chunk ^ (row%16).
-    int asrc[kPfCopies];   // element offset of the source row (rows past the slot's end copy its first row)
-    int acol[kPfCopies];   // element offset of the logical chunk
-#pragma unroll
-    for (int q = 0; q < kPfCopies; ++q) {
-      const int r = (wid * kPfCopies + q) * 4 + (lane >> 4);
-      const int rr = m0 + r;
-      const int rs = rr < cnt ? rr : 0;
-      if constexpr (GATEUP) {
-        const int t = is_sh ? rs : a.row_token[row0 + rs];
-        asrc[q] = t * K;
-      } else {
-        asrc[q] = (row0 + rs) * K;
-      }
-      acol[q] = ((lane & 15) ^ (r & 15)) * 8;
-    }
-    auto copy_a = [&](int s, int buf) {
-      uint8_t* base = sAbuf + buf * kPfBuf + (wid * kPfCopies) * 64 * 16;
-#pragma unroll
-      for (int q = 0; q < kPfCopies; ++q)
-        __builtin_amdgcn_global_load_lds((const void*)(act + asrc[q] + s * kPfBK + acol[q]),
-                                         (lds_void*)(base + q * 64 * 16), 16, 0, 0);
-    };
-    auto load_b = [&](int s, PfCodes<FMT> (&pc)[NF]) {
-#pragma unroll
-      for (int f = 0; f < NF; ++f) pf_load_codes<FMT>(bc[f], bs[f], s * kPfBK + 32 * G, pc[f]);
-    };
-
-    f32x4 acc[kPfMF][NF];
-#pragma unroll
-    for (int mi = 0; mi < kPfMF; ++mi)
-#pragma unroll
-      for (int f = 0; f < NF; ++f) acc[mi][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    PfCodes<FMT> pc[NF], pn[NF];
-    copy_a(0, 0);
-    load_b(0, pc);
-    // gate/up: the token scale of tile row tid, kept for the epilogue
-    float rsx = 0.0f;
-    if constexpr (GATEUP) {
-      if (tid < kBM) {
-        const int rr = m0 + tid;
-        const int rs = rr < cnt ? rr : 0;
-        rsx = a.xs[is_sh ? rs : a.row_token[row0 + rs]];
-      }
-    }
-    for (int s = 0; s < nstages; ++s) {
-      __builtin_amdgcn_s_waitcnt(0);  // this stage's copies and codes have landed
-      __syncthreads();                // ... for every wave; the other buffer is free
-      if (s + 1 < nstages) {
-        copy_a(s + 1, (s + 1) & 1);
-        load_b(s + 1, pn);
-      }
-      const uint8_t* sa = sAbuf + (s & 1) * kPfBuf;
-      // The stage's four MFMA steps; the SIMD's other wavefront (two
-      // workgroups per CU) overlaps its MFMAs with this one's LDS reads and
-      // weight decode.
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint8_t* p = sa + aoff[i];
-        f16x8 af[kPfMF], bw[NF];
-#pragma unroll
-        for (int mi = 0; mi < kPfMF; ++mi) af[mi] = __builtin_bit_cast(f16x8, *(const u32x4*)(p + mi * 4096));
-#pragma unroll
-        for (int f = 0; f < NF; ++f) bw[f] = pf_decode<FMT>(pc[f], i);
-#pragma unroll
-        for (int mi = 0; mi < kPfMF; ++mi)
-#pragma unroll
-          for (int f = 0; f < NF; ++f)
-            acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mi], bw[f], acc[mi][f], 0, 0, 0);
-      }
-#pragma unroll
-      for (int f = 0; f < NF; ++f) pc[f] = pn[f];
-    }
-    if (GATEUP && tid < kBM) s_rsx[tid] = rsx;
-    __syncthreads();  // the next item's first copy must not overwrite a buffer still being read
-
-    // ---- epilogue: D row (M) = mi*16 + 4G + v, column (N) = fragment row n
-#pragma unroll
-    for (int mi = 0; mi < kPfMF; ++mi) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int rr = m0 + mi * 16 + 4 * G + v;
-        if (rr >= cnt) continue;
-        const long orow = row0 + rr;
-        if constexpr (GATEUP) {
-          const float sx = s_rsx[mi * 16 + 4 * G + v];
-#pragma unroll
-          for (int f = 0; f < NF / 2; ++f) {
-            const float g = acc[mi][f][v] * sx * tsg, u = acc[mi][f + NF / 2][v] * sx * tsu;
-            const float hv = g / (1.0f + __expf(-g)) * u;
-            if (!(fabsf(hv) < 65504.0f)) atomicOr(a.error, 2);
-            const int fcol = nt * (kPfWaves * 8 * NF) + wid * (8 * NF) + f * 16 + n;
-            a.hout[orow * rows + act_pos(a.down_type, fcol)] = (f16)hv;
-          }
-        } else {
-#pragma unroll
-          for (int f = 0; f < NF; ++f) {
-            const int dcol = nt * (kPfWaves * 16 * NF) + wid * (16 * NF) + f * 16 + n;
-            a.o[orow * rows + dcol] = (uint16_t)f32_to_bf16_bits(acc[mi][f][v] * tsg);
-          }
-        }
-      }
-    }
+    const int nrow = min(kBM, tl.cnt - tl.m0);  // rows of this tile, 1 .. kBM
+    if (nrow > 64)
+      pf_item<FMT, GATEUP, NF, 8>(a, sAbuf, s_rsx, tl, nt, rows, K);
+    else if (nrow > 32)
+      pf_item<FMT, GATEUP, NF, 4>(a, sAbuf, s_rsx, tl, nt, rows, K);
+    else
+      pf_item<FMT, GATEUP, NF, 2>(a, sAbuf, s_rsx, tl, nt, rows, K);
   }
 }
 
@@ -401,11 +418,9 @@ PrefillWs carve(void* ws, int T, int d, int f, int k, int E) {
   return w;
 }
 
-constexpr size_t kPfLds = 2 * kPfBuf;  // double-buffered activation tile
-
 template <int FMT, bool GATEUP, int NF>
 hipError_t launch_gemm_nf(const PrefillArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_pf_gemm<FMT, GATEUP, NF>), dim3(grid), dim3(kPfThreads), kPfLds, s, a);
+  hipLaunchKernelGGL((k_pf_gemm<FMT, GATEUP, NF>), dim3(grid), dim3(kPfThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -127,9 +127,12 @@ typedef struct {
  *   topk_w[t][j]    softmax over the k selected logits (sums to 1)
  * x: device [T][d] of x_dtype (MOE_F32 or MOE_BF16).  logits: device fp32
  * [T][E] output, or NULL (then the workspace holds them).  The sum is
- * accumulated in fp64 for T <= 64 and in fp32 above (bf16 tokens: exact
- * products with three bf16 parts of each weight, on MFMA).  ws: device workspace of
- * at least moe_workspace_size(layer, T) bytes, 256-byte aligned. */
+ * accumulated in fp64 for T <= 8 and for fp32 tokens up to T = 64; otherwise
+ * in fp32 (bf16 tokens: exact products with three bf16 parts of each weight,
+ * on MFMA; for 8 < T <= 64 over slices of d added in a fixed order).  ws:
+ * device workspace of at least moe_workspace_size(layer, T) bytes, 256-byte
+ * aligned; it may be NULL only where logits is given and no slices are used
+ * (MOE_ERR_WORKSPACE otherwise). */
 moe_status moe_route(const moe_layer* layer, const void* x, int32_t x_dtype, int32_t T,
                      int32_t* topk_idx, float* topk_w, float* logits,
                      void* ws, size_t ws_bytes, void* stream);

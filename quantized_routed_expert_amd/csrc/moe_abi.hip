@@ -67,7 +67,11 @@ moe_status check_layer(const moe_layer* L) {
   return MOE_OK;
 }
 
-size_t route_ws(const moe_layer* L, int T) { return align_up((size_t)T * L->E * 4, 256); }
+// moe_route's workspace: the logits when the caller passes none, then the
+// K-split router's slices (bf16 tokens, 8 < T <= 64).
+size_t route_ws(const moe_layer* L, int T, int x_dtype) {
+  return align_up((size_t)T * L->E * 4, 256) + align_up(router_partials_bytes(T, L->E, L->d, x_dtype), 256);
+}
 
 size_t ffn_ws(const moe_layer* L, int T, int x_dtype) {
   if (T <= kDecodeMaxT) return decode_ws_bytes(T, L->d, L->f, L->k, x_dtype);
@@ -102,7 +106,9 @@ const char* moe_status_string(moe_status s) {
 size_t moe_workspace_size(const moe_layer* layer, int32_t T_max) {
   if (check_dims(layer) != MOE_OK || T_max < 1) return 0;
   const int Td = T_max < kDecodeMaxT ? T_max : kDecodeMaxT;
-  size_t need = route_ws(layer, T_max);
+  // the router's slices grow with T up to 64 tokens
+  size_t need = align_up((size_t)T_max * layer->E * 4, 256) +
+                align_up(router_partials_bytes(T_max < 64 ? T_max : 64, layer->E, layer->d, MOE_BF16), 256);
   const size_t pl = plan_ws_bytes(T_max, layer->E);
   if (pl > need) need = pl;
   const size_t dec = decode_ws_bytes(Td, layer->d, layer->f, layer->k, MOE_F32);
@@ -120,15 +126,17 @@ moe_status moe_route(const moe_layer* layer, const void* x, int32_t x_dtype, int
   if (st != MOE_OK) return st;
   if (!x || !topk_idx || !topk_w || T < 1 || !valid_dtype(x_dtype)) return MOE_ERR_INVALID_ARG;
   float* lg = logits;
-  if (!lg) {
-    if (!ws || ws_bytes < route_ws(layer, T)) return MOE_ERR_WORKSPACE;
+  float* partials = nullptr;
+  const bool slices = router_partials_bytes(T, layer->E, layer->d, x_dtype) > 0;
+  if (!lg || slices) {
+    if (!ws || ws_bytes < route_ws(layer, T, x_dtype)) return MOE_ERR_WORKSPACE;
     if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
-    lg = (float*)ws;
+    if (!lg) lg = (float*)ws;
+    partials = (float*)((char*)ws + align_up((size_t)T * layer->E * 4, 256));
   }
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_router_logits(layer->router_w, layer->router_bias, x, x_dtype, T, layer->E, layer->d, lg, s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(launch_topk(lg, T, layer->E, layer->k, topk_idx, topk_w, s));
+  return hip_status(launch_route(layer->router_w, layer->router_bias, x, x_dtype, T, layer->E, layer->d, layer->k, lg,
+                                 partials, topk_idx, topk_w, s));
 }
 
 moe_status moe_plan(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, const moe_plan_buf* plan, void* ws,

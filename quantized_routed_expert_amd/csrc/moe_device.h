@@ -281,13 +281,12 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // one's slot is its rank: the entries above it plus the equal ones with a
 // lower index.  If more than 64 entries pass the threshold (heavy ties), the
 // slots are taken one wave-wide maximum at a time instead.
+// wave_topk_vals takes the logits in registers (lv[i] = L[lane + 64 i]; the
+// entries at E and beyond are ignored).
 template <int NPL>
-__device__ __forceinline__ void wave_topk(const float* __restrict__ L, int E, int k, int lane, uint32_t* sk,
-                                          int32_t* si, int32_t* out_idx, float* out_val) {
+__device__ __forceinline__ void wave_topk_vals(const float (&lv)[NPL], int E, int k, int lane, uint32_t* sk,
+                                               int32_t* si, int32_t* out_idx, float* out_val) {
   uint32_t key[NPL];
-  float lv[NPL];
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) lv[i] = L[min(lane + 64 * i, E - 1)];  // unconditional loads, all in flight
 #pragma unroll
   for (int i = 0; i < NPL; ++i) key[i] = topk_key32(lv[i]) & (lane + 64 * i < E ? 0xffffffffu : 0u);
 
@@ -365,6 +364,15 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ L, int E, in
       key[i] = hit ? 0u : key[i];
     }
   }
+}
+
+template <int NPL>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ L, int E, int k, int lane, uint32_t* sk,
+                                          int32_t* si, int32_t* out_idx, float* out_val) {
+  float lv[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) lv[i] = L[min(lane + 64 * i, E - 1)];  // unconditional loads, all in flight
+  wave_topk_vals<NPL>(lv, E, k, lane, sk, si, out_idx, out_val);
 }
 
 // Exclusive prefix sum over a workgroup of NT threads (NT a multiple of 64,

@@ -44,6 +44,11 @@ hipError_t launch_dequant(const QMatDev& m, int expert, int out_dtype, void* dst
 hipError_t launch_router_logits(const float* W, const float* b, const void* x, int x_dtype, int T, int E, int d,
                                 float* logits, hipStream_t s);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w, hipStream_t s);
+// Router logits + top-k for the per-layer path; partials: device scratch of
+// router_partials_bytes (the K-split router's slices; unused when that is 0).
+size_t router_partials_bytes(int T, int E, int d, int x_dtype);
+hipError_t launch_route(const float* W, const float* b, const void* x, int x_dtype, int T, int E, int d, int k,
+                        float* logits, float* partials, int32_t* idx, float* w, hipStream_t s);
 size_t plan_ws_bytes(int T, int E);
 hipError_t launch_plan(const int32_t* idx, int T, int k, int E, const PlanDev& p, void* ws, hipStream_t s);
 hipError_t launch_combine(const void* o, int o_bf16, const float* topk_w, const int32_t* slot_row, int T, int k,

@@ -343,23 +343,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // 8 < T <= 64 with bf16 tokens: the same exact-product MFMA logits, shaped
-// for few tokens: a workgroup of 16 wavefronts takes 16 experts and 16 tokens
-// (one fragment each way), wavefront w the w-th sixteenth of K, with all of
-// its chunks in flight at once; the sixteen partial sums are added in
-// wavefront order through LDS.
-constexpr int kRsWaves = 16;
-constexpr int kRsMaxChunks = 8;  // K / 16 <= 256
+// for few tokens and split along K so that the launch fills the chip: a
+// workgroup takes 16 experts and one of KS slices of K (at most kRsMaxChunks
+// chunks of 32), and its wavefront w the tokens 16w .. 16w + 15 with all of
+// its chunks in flight at once.  Slice s of the sum goes to
+// partials[s][t][e]; the top-k launch adds the slices in slice order (then the
+// bias), so the result does not depend on scheduling.
+constexpr int kRsMaxChunks = 12;
+constexpr int kRsMaxSlices = 16;  // d <= 4096, a multiple of 512: 16 slices always fit
 
-__global__ __launch_bounds__(64 * kRsWaves) void k_router_mfma_small(const float* __restrict__ W,
-                                                                    const float* __restrict__ bias,
-                                                                    const uint16_t* __restrict__ x, int T, int E,
-                                                                    int d, float* __restrict__ logits) {
-  __shared__ f32x4 red[kRsWaves][64];
+// Slices of K for this router, or 0 when the shape takes another kernel.
+int router_ksplit(int T, int d, int x_dtype) {
+  if (x_dtype != MOE_BF16 || T <= 8 || T > 64 || d % 512 != 0 || d > 4096) return 0;
+  const int nch = d / 32;
+  for (int ks = 1; ks <= kRsMaxSlices; ++ks)
+    if (nch % ks == 0 && nch / ks <= kRsMaxChunks) return ks;
+  return 0;
+}
+
+__global__ __launch_bounds__(256) void k_router_mfma_split(const float* __restrict__ W, const uint16_t* __restrict__ x,
+                                                           int T, int E, int d, int kslice,
+                                                           float* __restrict__ partials) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int n = lane & 15, G = lane >> 4;
-  const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
-  const int kw = d / kRsWaves, kb = wid * kw;
-  const int nc = kw / 32;
+  const int e0 = blockIdx.x * 16, t0 = wid * 16;
+  if (t0 >= T) return;
+  const int kb = blockIdx.y * kslice, nc = kslice / 32;
   const uint16_t* xr = x + (long)min(t0 + n, T - 1) * d + kb + 8 * G;
   const float* wr = W + (long)min(e0 + n, E - 1) * d + kb + 8 * G;
   u32x4 xa[kRsMaxChunks];
@@ -383,30 +392,20 @@ __global__ __launch_bounds__(64 * kRsWaves) void k_router_mfma_small(const float
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, p3, acc, 0, 0, 0);
     }
   }
-  red[wid][lane] = acc;
-  __syncthreads();
-  // thread o < 256: lane o / 4 of the fragment, row v = o % 4, i.e. token
-  // t0 + 4G + v and expert e0 + n (D layout of the MFMA)
-  const int o = threadIdx.x;
-  if (o < 256) {
-    const int ol = o >> 2, v = o & 3;
-    const int t = t0 + 4 * (ol >> 4) + v, e = e0 + (ol & 15);
-    if (t < T && e < E) {
-      float sum = 0.0f;
+  // D layout: lane (n, G) holds token t0 + 4G + v, expert e0 + n
+  const int e = e0 + n;
+  float* out = partials + (long)blockIdx.y * T * E;
 #pragma unroll
-      for (int w = 0; w < kRsWaves; ++w) sum += red[w][ol][v];
-      logits[(long)t * E + e] = sum + (bias ? bias[e] : 0.0f);
-    }
+  for (int v = 0; v < 4; ++v) {
+    const int t = t0 + 4 * G + v;
+    if (t < T && e < E) out[(long)t * E + e] = acc[v];
   }
 }
 
 hipError_t launch_router_logits(const float* W, const float* b, const void* x, int x_dtype, int T, int E, int d,
                                 float* logits, hipStream_t s) {
   const int xb = x_dtype == MOE_BF16 ? 1 : 0;
-  if (xb && T > 8 && T <= 64 && d % (32 * kRsWaves) == 0 && d / kRsWaves <= 32 * kRsMaxChunks) {
-    hipLaunchKernelGGL(k_router_mfma_small, dim3((E + 15) / 16, (T + 15) / 16), dim3(64 * kRsWaves), 0, s, W, b,
-                       (const uint16_t*)x, T, E, d, logits);
-  } else if (T <= 64) {
+  if (T <= 64) {
     if (xb)
       hipLaunchKernelGGL(k_router_gemv_f64<true>, dim3(E), dim3(256), 0, s, W, b, x, T, E, d, logits);
     else
@@ -449,6 +448,49 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   }
 }
 
+// The same after the K-split router: logits[t][e] = (slice 0 + slice 1 + ...
+// in slice order) + bias[e], written out, then the top-k of those values.
+template <int NPL>
+__global__ __launch_bounds__(256) void k_topk_slices(const float* __restrict__ partials, int ks,
+                                                     const float* __restrict__ bias, int T, int E, int k,
+                                                     float* __restrict__ logits, int32_t* __restrict__ idx,
+                                                     float* __restrict__ w) {
+  __shared__ uint32_t sk[4][64];
+  __shared__ int32_t si[4][64];
+  __shared__ int32_t oi[4][64];
+  __shared__ float ov[4][64];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wid;
+  if (t >= T) return;
+  // every slice's loads are issued before the (ordered) sums
+  float lv[NPL], sl[NPL][kRsMaxSlices];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = min(lane + 64 * i, E - 1);
+#pragma unroll
+    for (int p = 0; p < kRsMaxSlices; ++p) sl[i][p] = p < ks ? partials[((long)p * T + t) * E + e] : 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = min(lane + 64 * i, E - 1);
+    float sum = sl[i][0];
+#pragma unroll
+    for (int p = 1; p < kRsMaxSlices; ++p)
+      if (p < ks) sum += sl[i][p];
+    lv[i] = sum + (bias ? bias[e] : 0.0f);
+    if (lane + 64 * i < E) logits[(long)t * E + e] = lv[i];
+  }
+  wave_topk_vals<NPL>(lv, E, k, lane, sk[wid], si[wid], oi[wid], ov[wid]);
+  const float v = lane < k ? ov[wid][lane] : 0.0f;
+  const float vmax = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 0));
+  const float ex = lane < k ? expf(v - vmax) : 0.0f;
+  const float sum = wave_sum(ex);
+  if (lane < k) {
+    idx[(long)t * k + lane] = oi[wid][lane];
+    w[(long)t * k + lane] = ex / sum;
+  }
+}
+
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w, hipStream_t s) {
   const dim3 g((T + 3) / 4), b(256);
   if (E <= 64)
@@ -459,6 +501,34 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, f
     hipLaunchKernelGGL(k_topk<8>, g, b, 0, s, logits, T, E, k, idx, w);
   else
     hipLaunchKernelGGL(k_topk<16>, g, b, 0, s, logits, T, E, k, idx, w);
+  return hipGetLastError();
+}
+
+size_t router_partials_bytes(int T, int E, int d, int x_dtype) {
+  return (size_t)router_ksplit(T, d, x_dtype) * T * E * 4;
+}
+
+hipError_t launch_route(const float* W, const float* b, const void* x, int x_dtype, int T, int E, int d, int k,
+                        float* logits, float* partials, int32_t* idx, float* w, hipStream_t s) {
+  const int ks = router_ksplit(T, d, x_dtype);
+  if (ks == 0) {
+    const hipError_t e = launch_router_logits(W, b, x, x_dtype, T, E, d, logits, s);
+    if (e != hipSuccess) return e;
+    return launch_topk(logits, T, E, k, idx, w, s);
+  }
+  hipLaunchKernelGGL(k_router_mfma_split, dim3((E + 15) / 16, ks), dim3(256), 0, s, W, (const uint16_t*)x, T, E, d,
+                     d / ks, partials);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 g((T + 3) / 4), bl(256);
+  if (E <= 64)
+    hipLaunchKernelGGL(k_topk_slices<1>, g, bl, 0, s, partials, ks, b, T, E, k, logits, idx, w);
+  else if (E <= 256)
+    hipLaunchKernelGGL(k_topk_slices<4>, g, bl, 0, s, partials, ks, b, T, E, k, logits, idx, w);
+  else if (E <= 512)
+    hipLaunchKernelGGL(k_topk_slices<8>, g, bl, 0, s, partials, ks, b, T, E, k, logits, idx, w);
+  else
+    hipLaunchKernelGGL(k_topk_slices<16>, g, bl, 0, s, partials, ks, b, T, E, k, logits, idx, w);
   return hipGetLastError();
 }
 

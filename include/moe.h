@@ -195,7 +195,9 @@ moe_status moe_dequantize(const moe_qmatrix* m, int32_t expert, int32_t out_dtyp
  * joins the MoE layers; this is the plain pre-norm residual chain):
  *   if y != NULL:  h[t][i] += y[t][i]            (fp32 residual, y of y_dtype)
  *   x[t][i] = bf16( h[t][i] / sqrt(mean_i h[t][i]^2 + eps) )
- * h: device fp32 [T][d] (updated in place); x_out: device bf16 [T][d]. */
+ * h: device fp32 [T][d] (updated in place, 16-byte aligned); x_out: device
+ * bf16 [T][d] (8-byte aligned); y: 8-byte (bf16) or 16-byte (fp32) aligned.
+ * d must be a multiple of 4 (MOE_ERR_UNSUPPORTED otherwise). */
 moe_status moe_residual_rmsnorm(float* h, const void* y, int32_t y_dtype, int32_t T, int32_t d,
                                 float eps, void* x_out, void* stream);
 

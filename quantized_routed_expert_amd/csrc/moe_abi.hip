@@ -261,6 +261,9 @@ moe_status moe_decode_stack(const moe_layer* layers, int32_t n_layers, float* h,
 moe_status moe_residual_rmsnorm(float* h, const void* y, int32_t y_dtype, int32_t T, int32_t d, float eps,
                                 void* x_out, void* stream) {
   if (!h || !x_out || T < 1 || d < 1 || !valid_dtype(y_dtype) || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
+  if (d % 4 != 0) return MOE_ERR_UNSUPPORTED;  // the kernel moves 4 columns at a time
+  if (!aligned(h, 16) || !aligned(x_out, 8) || (y && !aligned(y, y_dtype == MOE_BF16 ? 8 : 16)))
+    return MOE_ERR_ALIGNMENT;
   return hip_status(launch_residual_rmsnorm(h, y, y_dtype, T, d, eps, x_out, (hipStream_t)stream));
 }
 

@@ -708,45 +708,73 @@ hipError_t launch_plan(const int32_t* idx, int T, int k, int E, const PlanDev& p
 // 0..T*k-1, then the shared expert's rows T*k + t.
 // ============================================================================
 
+// y[t] = (shared row) + sum_j topk_w[t][j] * o[slot_row[t][j]], the terms
+// added in slot order j (fp32 FMAs).  Each thread takes 8 consecutive columns;
+// the rows of up to kCombineBatch slots are loaded before they are added, so
+// that the loads of a token are in flight together.
+constexpr int kCombineBatch = 8;
+
 __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ o, int o_bf16,
                                                  const float* __restrict__ topk_w, const int32_t* __restrict__ slot_row,
                                                  int T, int k, int d, int has_shared, void* __restrict__ y,
                                                  int y_bf16) {
   const int t = blockIdx.y;
-  const int i = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  const int i = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (i >= d) return;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  auto row4 = [&](long r) -> f32x4 {
+  auto row8 = [&](long r, float (&f)[8]) {
     if (o_bf16) {
-      const u32x2 v = *(const u32x2*)((const uint16_t*)o + r * d + i);
-      f32x4 f = {bf16_bits_to_f32(v.x & 0xffffu), bf16_bits_to_f32(v.x >> 16), bf16_bits_to_f32(v.y & 0xffffu),
-                 bf16_bits_to_f32(v.y >> 16)};
-      return f;
+      const u32x4 v = *(const u32x4*)((const uint16_t*)o + r * d + i);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f[2 * q] = bf16_bits_to_f32(v[q] & 0xffffu);
+        f[2 * q + 1] = bf16_bits_to_f32(v[q] >> 16);
+      }
+    } else {
+      const f32x4 u = *(const f32x4*)((const float*)o + r * d + i);
+      const f32x4 w = *(const f32x4*)((const float*)o + r * d + i + 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f[q] = u[q];
+        f[4 + q] = w[q];
+      }
     }
-    return *(const f32x4*)((const float*)o + r * d + i);
   };
-  if (has_shared) acc = row4((long)T * k + t);
-  for (int j = 0; j < k; ++j) {
-    const int r = slot_row[(long)t * k + j];
-    if (r < 0) continue;
-    const float wj = topk_w[(long)t * k + j];
-    const f32x4 v = row4(r);
-    acc.x = fmaf(wj, v.x, acc.x);
-    acc.y = fmaf(wj, v.y, acc.y);
-    acc.z = fmaf(wj, v.z, acc.z);
-    acc.w = fmaf(wj, v.w, acc.w);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (has_shared) row8((long)T * k + t, acc);
+  for (int j0 = 0; j0 < k; j0 += kCombineBatch) {
+    float v[kCombineBatch][8];
+    float wj[kCombineBatch];
+    int rj[kCombineBatch];
+#pragma unroll
+    for (int b = 0; b < kCombineBatch; ++b) {
+      const int j = j0 + b;
+      rj[b] = j < k ? slot_row[(long)t * k + j] : -1;
+      wj[b] = j < k ? topk_w[(long)t * k + j] : 0.0f;
+    }
+#pragma unroll
+    for (int b = 0; b < kCombineBatch; ++b) {
+      if (rj[b] >= 0) row8(rj[b], v[b]);
+    }
+#pragma unroll
+    for (int b = 0; b < kCombineBatch; ++b) {
+      if (rj[b] < 0) continue;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = fmaf(wj[b], v[b][q], acc[q]);
+    }
   }
   if (y_bf16) {
-    u32x2 r = {pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w)};
-    *(u32x2*)((uint16_t*)y + (long)t * d + i) = r;
+    u32x4 r = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+               pack_bf16x2(acc[6], acc[7])};
+    *(u32x4*)((uint16_t*)y + (long)t * d + i) = r;
   } else {
-    *(f32x4*)((float*)y + (long)t * d + i) = acc;
+    *(f32x4*)((float*)y + (long)t * d + i) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *(f32x4*)((float*)y + (long)t * d + i + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
   }
 }
 
 hipError_t launch_combine(const void* o, int o_bf16, const float* topk_w, const int32_t* slot_row, int T, int k,
                           int d, int has_shared, void* y, int y_dtype, hipStream_t s) {
-  const int per_blk = 256 * 4;
+  const int per_blk = 256 * 8;
   hipLaunchKernelGGL(k_combine, dim3((d + per_blk - 1) / per_blk, T), dim3(256), 0, s, o, o_bf16, topk_w, slot_row,
                      T, k, d, has_shared, y, y_dtype == MOE_BF16 ? 1 : 0);
   return hipGetLastError();
@@ -757,24 +785,67 @@ hipError_t launch_combine(const void* o, int o_bf16, const float* topk_w, const 
 // token.
 // ============================================================================
 
+// Each thread takes groups of 4 consecutive columns; the first kGlueVec
+// groups per thread stay in registers between the two passes (d <= 4096 at 256
+// threads), any further ones are read back.
+constexpr int kGlueVec = 4;
+
 __global__ __launch_bounds__(256) void k_residual_rmsnorm(float* __restrict__ h, const void* __restrict__ y, int y_bf16,
                                                           int d, float eps, uint16_t* __restrict__ x_out) {
   const int t = blockIdx.x;
   float* hr = h + (long)t * d;
   __shared__ float red[4];
+  auto add_y = [&](int i, f32x4 v) -> f32x4 {
+    if (!y) return v;
+    if (y_bf16) {
+      const u32x2 u = *(const u32x2*)((const uint16_t*)y + (long)t * d + i);
+      v[0] += bf16_bits_to_f32(u.x & 0xffffu);
+      v[1] += bf16_bits_to_f32(u.x >> 16);
+      v[2] += bf16_bits_to_f32(u.y & 0xffffu);
+      v[3] += bf16_bits_to_f32(u.y >> 16);
+    } else {
+      const f32x4 u = *(const f32x4*)((const float*)y + (long)t * d + i);
+      v[0] += u[0];
+      v[1] += u[1];
+      v[2] += u[2];
+      v[3] += u[3];
+    }
+    return v;
+  };
+  f32x4 keep[kGlueVec];
   float ss = 0.0f;
-  for (int i = threadIdx.x; i < d; i += blockDim.x) {
-    float v = hr[i];
-    if (y) v += y_bf16 ? bf16_bits_to_f32(((const uint16_t*)y)[(long)t * d + i]) : ((const float*)y)[(long)t * d + i];
-    hr[i] = v;
-    ss = fmaf(v, v, ss);
+#pragma unroll
+  for (int q = 0; q < kGlueVec; ++q) {
+    const int i = (threadIdx.x + 256 * q) * 4;
+    if (i < d) {
+      const f32x4 v = add_y(i, *(const f32x4*)(hr + i));
+      *(f32x4*)(hr + i) = v;
+      keep[q] = v;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ss = fmaf(v[c], v[c], ss);
+    }
+  }
+  for (int i = (threadIdx.x + 256 * kGlueVec) * 4; i < d; i += 256 * 4) {
+    const f32x4 v = add_y(i, *(const f32x4*)(hr + i));
+    *(f32x4*)(hr + i) = v;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ss = fmaf(v[c], v[c], ss);
   }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
   const float tot = red[0] + red[1] + red[2] + red[3];
   const float inv = 1.0f / sqrtf(tot / (float)d + eps);
-  for (int i = threadIdx.x; i < d; i += blockDim.x) x_out[(long)t * d + i] = (uint16_t)f32_to_bf16_bits(hr[i] * inv);
+  auto put = [&](int i, f32x4 v) {
+    const u32x2 r = {pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv)};
+    *(u32x2*)(x_out + (long)t * d + i) = r;
+  };
+#pragma unroll
+  for (int q = 0; q < kGlueVec; ++q) {
+    const int i = (threadIdx.x + 256 * q) * 4;
+    if (i < d) put(i, keep[q]);
+  }
+  for (int i = (threadIdx.x + 256 * kGlueVec) * 4; i < d; i += 256 * 4) put(i, *(const f32x4*)(hr + i));
 }
 
 hipError_t launch_residual_rmsnorm(float* h, const void* y, int y_dtype, int T, int d, float eps, void* x_out,

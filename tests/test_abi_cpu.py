@@ -159,6 +159,10 @@ def test_dequant_and_glue_validation():
         lib.MOE_ERR_INVALID_ARG
     assert so.moe_residual_rmsnorm(1 << 20, None, 0, 0, 8, ctypes.c_float(1e-6), 1 << 21, None) == \
         lib.MOE_ERR_INVALID_ARG
+    assert so.moe_residual_rmsnorm(1 << 20, None, 0, 1, 6, ctypes.c_float(1e-6), 1 << 21, None) == \
+        lib.MOE_ERR_UNSUPPORTED
+    assert so.moe_residual_rmsnorm((1 << 20) + 8, None, 0, 1, 8, ctypes.c_float(1e-6), 1 << 21, None) == \
+        lib.MOE_ERR_ALIGNMENT
 
 
 def test_workspace_size_monotone_and_covers_paths():

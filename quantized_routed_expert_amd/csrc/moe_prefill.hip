@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void k_pf_prepare(const void* __restrict__ x, 
                                                     const int32_t* __restrict__ n_active, int has_shared,
                                                     int32_t* __restrict__ mstart, PfTile* __restrict__ tiles,
                                                     int32_t* __restrict__ n_mtiles, int k) {
-  __shared__ int32_t part[256];
+  __shared__ int32_t part[256 / 64 + 1];  // scan scratch
   __shared__ float red[4];
   const int tid = threadIdx.x;
   if ((int)blockIdx.x < T) {
@@ -105,20 +105,12 @@ __global__ __launch_bounds__(256) void k_pf_prepare(const void* __restrict__ x, 
     const int cnt = (s < *n_active) ? offsets[active[s] + 1] - offsets[active[s]] : T;
     sum += (cnt + kBM - 1) / kBM;
   }
-  part[tid] = sum;
-  __syncthreads();
+  int total;
+  int run = block_exclusive_scan<256>(sum, part, total);
   if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < 256; ++i) {
-      const int v = part[i];
-      part[i] = run;
-      run += v;
-    }
-    mstart[n_slots] = run;
-    *n_mtiles = run;
+    mstart[n_slots] = total;
+    *n_mtiles = total;
   }
-  __syncthreads();
-  int run = part[tid];
   for (int s = s0; s < s1; ++s) {
     mstart[s] = run;
     const bool routed = s < *n_active;

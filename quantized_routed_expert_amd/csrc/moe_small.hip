@@ -632,10 +632,22 @@ __global__ __launch_bounds__(1024) void k_plan_scan(int T, int k, int E, int nb,
   __shared__ int32_t scratch[2][17];
   __shared__ int32_t err_s;
   const int e = threadIdx.x;
-  constexpr int kB = 16;  // block counts per batch, all loads of a batch in flight together
+  // The counts of the first kR blocks (T <= 4096) stay in registers between the
+  // two passes, all loaded together; the blocks beyond are handled in batches
+  // of kB, their prefixes written in the first pass and read back.
+  constexpr int kR = 64, kB = 16;
+  int cr[kR];
   int cnt = 0;
   if (e < E) {
-    for (int b0 = 0; b0 < nb; b0 += kB) {  // per-block exclusive prefix, in place
+#pragma unroll
+    for (int u = 0; u < kR; ++u) cr[u] = u < nb ? hist[(long)u * E + e] : 0;
+#pragma unroll
+    for (int u = 0; u < kR; ++u) {
+      const int c = cr[u];
+      cr[u] = cnt;  // exclusive prefix within the expert
+      cnt += c;
+    }
+    for (int b0 = kR; b0 < nb; b0 += kB) {
       int c[kB];
 #pragma unroll
       for (int u = 0; u < kB; ++u) c[u] = b0 + u < nb ? hist[(long)(b0 + u) * E + e] : 0;
@@ -654,7 +666,10 @@ __global__ __launch_bounds__(1024) void k_plan_scan(int T, int k, int E, int nb,
     p.offsets[e] = off;
     if (cnt > 0) p.active[aoff] = e;
     if (e >= n_act) p.active[e] = -1;
-    for (int b0 = 0; b0 < nb; b0 += kB) {
+#pragma unroll
+    for (int u = 0; u < kR; ++u)
+      if (u < nb) hist[(long)u * E + e] = cr[u] + off;
+    for (int b0 = kR; b0 < nb; b0 += kB) {
       int c[kB];
 #pragma unroll
       for (int u = 0; u < kB; ++u) c[u] = b0 + u < nb ? hist[(long)(b0 + u) * E + e] : 0;

@@ -150,7 +150,7 @@ def test_topk_heavy_ties(E, k):
 
 @pytest.mark.parametrize("T,k,E,bad", [(1, 8, 512, False), (8, 8, 512, False), (64, 8, 512, False),
                                        (65, 4, 16, False), (300, 8, 512, False), (4096, 8, 512, False),
-                                       (33, 3, 7, True)])
+                                       (5000, 6, 300, False), (33, 3, 7, True)])
 def test_plan_bit_exact(T, k, E, bad):
     _say(f"[plan] T={T} k={k} E={E} bad={bad}")
     g = np.random.default_rng(T * 31 + k)

@@ -68,20 +68,39 @@ __global__ __launch_bounds__(256) void k_pf_prepare(const void* __restrict__ x, 
   const int tid = threadIdx.x;
   if ((int)blockIdx.x < T) {
     const long t = blockIdx.x;
-    auto ld = [&](int i) -> float {
-      return XB ? bf16_bits_to_f32(((const uint16_t*)x)[t * d + i]) : ((const float*)x)[t * d + i];
+    // groups of 4 consecutive elements (one 8- or 16-byte load); the IQ4_NL
+    // layout moves whole groups: group g of a block (elements 4g .. 4g + 3) lands
+    // at positions 8g .. 8g + 3 (g < 4) or 8(g - 4) + 4 .. 8(g - 4) + 7
+    auto ld4 = [&](int i) -> f32x4 {
+      if constexpr (XB) {
+        const u32x2 u = *(const u32x2*)((const uint16_t*)x + t * d + i);
+        return f32x4{bf16_bits_to_f32(u.x & 0xffffu), bf16_bits_to_f32(u.x >> 16), bf16_bits_to_f32(u.y & 0xffffu),
+                     bf16_bits_to_f32(u.y >> 16)};
+      } else {
+        return *(const f32x4*)((const float*)x + t * d + i);
+      }
     };
-    // the token is read once: d <= 16 * 256 elements stay in registers
-    constexpr int kPerThread = 16;
-    float v[kPerThread];
+    auto st4 = [&](int i, f32x4 v, float down) {
+      const int pos = gate_fmt == MOE_IQ4_NL ? (i & ~31) + iq4_pos(i & 31) : i;  // i and pos: multiples of 4
+      const f16x2 lo = {(f16)(v[0] * down), (f16)(v[1] * down)}, hi = {(f16)(v[2] * down), (f16)(v[3] * down)};
+      *(u32x2*)(x16 + t * d + pos) = u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    };
+    // the token is read once: d <= 4 * 4 * 256 elements stay in registers
+    constexpr int kGroups = 4;
+    f32x4 v[kGroups];
     float mx = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      const int i = tid + j * 256;
-      v[j] = i < d ? ld(i) : 0.0f;
-      mx = fmaxf(mx, fabsf(v[j]));
+    for (int j = 0; j < kGroups; ++j) {
+      const int i = (tid + j * 256) * 4;
+      v[j] = i < d ? ld4(i) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mx = fmaxf(mx, fabsf(v[j][c]));
     }
-    for (int i = tid + kPerThread * 256; i < d; i += 256) mx = fmaxf(mx, fabsf(ld(i)));
+    for (int i = (tid + kGroups * 256) * 4; i < d; i += 256 * 4) {
+      const f32x4 u = ld4(i);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mx = fmaxf(mx, fabsf(u[c]));
+    }
     mx = wave_max(mx);
     if ((tid & 63) == 0) red[tid >> 6] = mx;
     __syncthreads();
@@ -89,11 +108,11 @@ __global__ __launch_bounds__(256) void k_pf_prepare(const void* __restrict__ x, 
     const int ex = x16_exponent(mx);
     const float down = ldexpf(1.0f, -ex);
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      const int i = tid + j * 256;
-      if (i < d) x16[t * d + act_pos(gate_fmt, i)] = (f16)(v[j] * down);
+    for (int j = 0; j < kGroups; ++j) {
+      const int i = (tid + j * 256) * 4;
+      if (i < d) st4(i, v[j], down);
     }
-    for (int i = tid + kPerThread * 256; i < d; i += 256) x16[t * d + act_pos(gate_fmt, i)] = (f16)(ld(i) * down);
+    for (int i = (tid + kGroups * 256) * 4; i < d; i += 256 * 4) st4(i, ld4(i), down);
     if (tid == 0) xs[t] = ldexpf(1.0f, ex);
     return;
   }

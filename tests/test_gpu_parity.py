@@ -120,13 +120,14 @@ def test_router_topk_exact(T, d):
 
 
 @pytest.mark.parametrize("E,k", [(16, 2), (64, 8), (512, 8), (1000, 32)])
-def test_topk_heavy_ties(E, k):
-    """All-equal logits (a zero router) and a few equal maxima: lower ids first."""
-    _say(f"[ties] E={E} k={k}")
-    wl, layer = _small_layer(40 + E, E=E, k=k)
+@pytest.mark.parametrize("T,d", [(3, 256), (40, 512)])
+def test_topk_heavy_ties(E, k, T, d):
+    """All-equal logits (a zero router) and a few equal maxima: lower ids first
+    (T = 40, d = 512: the K-split router and its slice-summing top-k)."""
+    _say(f"[ties] E={E} k={k} T={T} d={d}")
+    wl, layer = _small_layer(40 + E, d=d, E=E, k=k)
     layer["router_w"].zero_()
     layer["router_b"].zero_()
-    T = 3
     layer["router_b"][E // 2] = 1.0   # token-independent: one clear winner ...
     layer["router_b"][E - 1] = 0.5    # ... then two equal runners-up
     layer["router_b"][1] = 0.5

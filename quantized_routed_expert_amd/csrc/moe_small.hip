@@ -738,7 +738,7 @@ __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ o, int
   if (i >= d) return;
   auto row8 = [&](long r, float (&f)[8]) {
     if (o_bf16) {
-      const u32x4 v = *(const u32x4*)((const uint16_t*)o + r * d + i);
+      const u32x4 v = __builtin_nontemporal_load((const u32x4*)((const uint16_t*)o + r * d + i));
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         f[2 * q] = bf16_bits_to_f32(v[q] & 0xffffu);

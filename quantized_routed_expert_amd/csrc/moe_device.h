@@ -78,7 +78,9 @@ constexpr uint32_t kIq4U3 = 0xF1D9C5B5u;  // 181, 197, 217, 241
 __device__ __forceinline__ uint32_t iq4_lookup4(uint32_t q) {
   const uint32_t lo = __builtin_amdgcn_perm(kIq4U1, kIq4U0, q);
   const uint32_t hi = __builtin_amdgcn_perm(kIq4U3, kIq4U2, q ^ 0x08080808u);
-  const uint32_t sel = ((q >> 1) & 0x04040404u) | 0x03020100u;
+  // ((q >> 1) & 0x04040404) | 0x03020100 in one v_bitop3 (truth table 0xEA =
+  // (A & B) | C over the inputs 0xF0, 0xCC, 0xAA)
+  const uint32_t sel = __builtin_amdgcn_bitop3_b32(q >> 1, 0x04040404u, 0x03020100u, 0xEA);
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 

@@ -112,9 +112,28 @@ def bf16_bits_to_float(bits):
 
 
 def round_to_bf16(x):
-    """float64 -> nearest bfloat16 value, via float32 (the precision the
-    hardware path rounds from), returned as float64."""
-    return bf16_bits_to_float(f32_to_bf16_bits(np.asarray(x, dtype=np.float64).astype(np.float32)))
+    """float64 -> nearest bfloat16 value (round to nearest, ties to even),
+    rounded once from the float64 value, returned as float64.
+
+    bfloat16 keeps 8 significant bits and float32's exponent range: normal
+    values in [2^-126, 2^128) have a spacing of 2^(e - 7) in the binade
+    [2^e, 2^(e+1)); below 2^-126 the spacing is 2^-133 (subnormals).  x is
+    divided by its spacing (a power of two, exact), rounded to an integer
+    with ties to even, and scaled back; a result at or beyond 2^128 is an
+    overflow to infinity.  Pinned against an exact rational rounding,
+    including inputs that a float32 intermediate would round twice.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.array(x, dtype=np.float64, copy=True)
+    fin = np.isfinite(x) & (x != 0)
+    xf = x[fin]
+    _, e2 = np.frexp(xf)                     # |x| = m * 2^e2, m in [0.5, 1)
+    ex = np.maximum(e2 - 1, -126)            # binade exponent, clamped at the subnormal range
+    sp = np.ldexp(1.0, (ex - 7).astype(np.int64))
+    r = np.rint(xf / sp) * sp                # rint rounds ties to even
+    r = np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, xf), r)
+    out[fin] = r
+    return out
 
 
 def dequant_q8_0(codes, scales):

@@ -17,7 +17,8 @@ step, with no blocking, fusion or reordering:
 5. experts        h = silu(W_g x) * (W_u x),  o = W_d h   (per routed pair)
 6. shared expert  s = the same FFN with the shared weights, weight 1
 7. combine        y_t = s_t + sum_j w[t, j] * o[(t, j)]
-8. stack glue     x_l = bf16(rmsnorm(h_l)), h_{l+1} = h_l + y_l (layer chaining)
+8. stack glue     x_l = bf16(rmsnorm(h_l)), h_{l+1} = h_l + y_l: the helpers
+                  that join stacked layers (rmsnorm_to_bf16, residual_add)
 
 Routing picks only selected experts per token ("RAM and VRAM Hold Different
 Parts of the Expert Weights", setup-guide page).  The rest of the layer (router,
@@ -109,12 +110,21 @@ def plan(idx, E):
     n_active       number of active experts
 
     Pairs whose expert id is outside [0, E) are dropped (they get no row; their
-    slot_row entry is -1) and reported through ``error`` = 1.
+    slot_row entry is -1) and reported through bit 1 of ``error``.  A top-k
+    selection never names an expert twice for one token, so a plan built from
+    one has distinct ids per token; for an index array that repeats an id
+    within a token, the pair with the lowest slot j is kept and every later
+    repeat is dropped the same way and reported through bit 4.
     """
     idx = np.asarray(idx, dtype=np.int64)
     T, k = idx.shape
-    valid = (idx >= 0) & (idx < E)
-    error = 0 if valid.all() else 1
+    in_range = (idx >= 0) & (idx < E)
+    valid = in_range.copy()
+    for t in range(T):
+        for j in range(k):
+            if in_range[t, j] and idx[t, j] in idx[t, :j][in_range[t, :j]]:
+                valid[t, j] = False
+    error = (0 if in_range.all() else 1) | (0 if (valid == in_range).all() else 4)
     counts = np.zeros(E, dtype=np.int64)
     for t in range(T):
         for j in range(k):
@@ -311,16 +321,3 @@ def rmsnorm_to_bf16(h):
 def residual_add(h, y):
     """h_{l+1} = h_l + y_l, carried in float32 like the residual stream."""
     return (np.asarray(h, dtype=np.float32) + np.asarray(y, dtype=np.float32)).astype(np.float64)
-
-
-def stack(layers, h0, out_dtype="f32"):
-    """Run the pre-norm residual chain over ``layers`` from the float32 residual
-    h0 [T, d].  Returns the final residual and every layer's bf16 input."""
-    h = np.asarray(h0, dtype=np.float32).astype(np.float64)
-    xs = []
-    for layer in layers:
-        x = rmsnorm_to_bf16(h)
-        xs.append(x)
-        y = moe_layer(layer, x, out_dtype)
-        h = residual_add(h, y)
-    return h, xs

@@ -88,6 +88,65 @@ def test_bf16_rounding_against_torch():
     assert np.array_equal(ref, got)
 
 
+def test_bf16_round_once_against_exact_rationals():
+    """round_to_bf16 rounds the float64 value once (ties to even), checked
+    against exact rational rounding on random values over the whole range,
+    every exact midpoint kind, subnormals, overflow, and values just off a
+    midpoint that a float32 intermediate would first round onto it."""
+    import math
+    from fractions import Fraction
+
+    import exact_round as ER
+
+    rng = np.random.default_rng(8)
+    vals = list(rng.normal(size=400) * np.exp2(rng.uniform(-140, 130, size=400)))
+    vals += [0.0, -0.0, 1.0, -3.0, 2.0 ** -133, 2.0 ** -134, 3 * 2.0 ** -135, 2.0 ** -126, 2.0 ** -127 * 1.5]
+    # largest finite bf16, just below and at the overflow midpoint
+    mx = (2 - 2.0 ** -7) * 2.0 ** 127
+    vals += [mx, mx + 2.0 ** 119 - 2.0 ** 90, mx + 2.0 ** 119, -(mx + 2.0 ** 119)]
+    for e in (-130, -126, -60, -1, 0, 7, 100, 127):
+        for m in range(128, 256, 9):
+            b = m * 2.0 ** (e - 7)             # a bf16 value with significand m
+            mid = b + 2.0 ** (e - 8)           # the midpoint above it
+            vals += [mid, -mid, mid + mid * 2.0 ** -40, mid - mid * 2.0 ** -40]
+    x = np.array(vals, dtype=np.float64)
+    got = F.round_to_bf16(x)
+    for v, g in zip(x, got):
+        want = ER.rne(Fraction(float(v)), ER.BF16)
+        if isinstance(want, float) and math.isinf(want):
+            assert math.isinf(g) and (g > 0) == (want > 0), v
+        else:
+            assert math.isfinite(g) and Fraction(float(g)) == want, (v, g, float(want))
+    assert np.isnan(F.round_to_bf16(np.array([np.nan]))[0])
+    assert np.array_equal(F.round_to_bf16(np.array([np.inf, -np.inf])), np.array([np.inf, -np.inf]))
+
+
+def test_numpy_float16_conversion_rounds_once():
+    """numpy's float64 -> float16 conversion (the GPU tests' reference for the
+    prefill fp16 weight tile) is one round-to-nearest-even, overflow to inf,
+    checked against exact rational rounding."""
+    import math
+    from fractions import Fraction
+
+    import exact_round as ER
+
+    rng = np.random.default_rng(12)
+    vals = list(rng.normal(size=300) * np.exp2(rng.uniform(-28, 17, size=300)))
+    for m in range(1024, 2048, 37):
+        for e in (-24, -15, -14, 0, 15):
+            b = m * 2.0 ** (e - 10)
+            mid = b + 2.0 ** (e - 11)
+            vals += [mid, mid + mid * 2.0 ** -30, mid - mid * 2.0 ** -30]
+    vals += [65504.0, 65519.99, 65520.0, -65520.0, 2.0 ** -25, 3 * 2.0 ** -26]
+    for v in vals:
+        g = float(np.float16(v))
+        want = ER.rne(Fraction(v), ER.F16)
+        if isinstance(want, float):
+            assert math.isinf(g) and (g > 0) == (want > 0), v
+        else:
+            assert math.isfinite(g) and Fraction(g) == want, (v, g, float(want))
+
+
 # ---------------------------------------------------------------- block formats
 
 def test_block_sizes_match_golden():

@@ -15,6 +15,8 @@ import pytest
 from oracle import formats as F
 from oracle import moe as M
 
+import exact_round as ER
+from test_oracle_formats import test_bf16_round_once_against_exact_rationals as _pin_bf16
 from test_oracle_formats import test_fp16_exhaustive_against_numpy as _pin_fp16
 from test_oracle_formats import test_iq4_nl_nibble_order_and_exact_values as _pin_iq4_order
 
@@ -194,6 +196,29 @@ def test_plan_drops_out_of_range_ids_and_flags_error():
     assert p["offsets"][3] == 4
 
 
+def test_plan_keeps_first_of_repeated_ids():
+    """A repeated id within a token: the lowest slot keeps its row, later
+    repeats are dropped exactly as an out-of-range id is, with bit 4 set."""
+    rng = np.random.default_rng(21)
+    T, k, E = 9, 4, 6
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    idx[2, 3] = idx[2, 0]
+    idx[5, 1] = idx[5, 2] = idx[5, 3] = idx[5, 0]
+    idx[7, 2] = idx[7, 1]
+    idx[8, 0] = -3       # out of range first ...
+    idx[8, 3] = -3       # ... a repeated out-of-range id is only out of range
+    p = M.plan(idx, E)
+    assert p["error"] == 1 | 4
+    ref = idx.copy()
+    ref[2, 3] = ref[5, 1] = ref[5, 2] = ref[5, 3] = ref[7, 2] = -1
+    q = M.plan(ref, E)
+    assert q["error"] == 1
+    for n in ("counts", "offsets", "row_token", "row_slot", "slot_row", "active"):
+        assert np.array_equal(p[n], q[n]), n
+    assert p["slot_row"][2 * k + 0] >= 0 and p["slot_row"][2 * k + 3] == -1
+    assert p["n_rows"] == T * k - 5 - 2
+
+
 # ---------------------------------------------------------------- experts / layer
 
 def _silu_exact_ref(z):
@@ -337,18 +362,46 @@ def test_output_rounding_once():
 
 # ---------------------------------------------------------------- stack glue
 
-def test_rmsnorm_unit_rms_and_residual():
-    rng = np.random.default_rng(19)
-    h = rng.normal(0, 5, size=(4, 256))
-    x = M.rmsnorm_to_bf16(h)
-    rms = np.sqrt(np.mean(x * x, axis=1))
-    assert np.allclose(rms, 1.0, atol=4e-3)
-    assert np.array_equal(np.sign(x), np.sign(h))
-    assert np.array_equal(x, F.round_to_bf16(x))
-    z = M.rmsnorm_to_bf16(np.zeros((1, 8)))
-    assert np.all(z == 0)
-    y = rng.normal(size=(4, 256))
-    assert np.array_equal(M.residual_add(h, y), (h.astype(np.float32) + y.astype(np.float32)).astype(np.float64))
+def _glue_rows(seed=19, d=16):
+    """Residual rows in float32: unit scale (eps negligible), 1e-3 scale (mean
+    square about eps, so eps matters), a zero row, a row with one nonzero entry
+    and a row of a constant value."""
+    rng = np.random.default_rng(seed)
+    rows = [rng.normal(0, 1, size=d), rng.normal(0, 5, size=d), rng.normal(0, 1e-3, size=d),
+            rng.normal(0, 7e-4, size=d), np.zeros(d), np.eye(1, d, 3)[0] * 2.5e-3, np.full(d, -0.75)]
+    return np.stack(rows).astype(np.float32)
+
+
+def test_rmsnorm_matches_exact_rational_rounding():
+    """x_i = RNE_bf16(h_i / sqrt(sum_j h_j^2 / d + 1e-6)), decided exactly with
+    rationals (no square root is taken: v >= c <=> h^2 >= c^2 S)."""
+    h = _glue_rows()
+    d = h.shape[1]
+    x = M.rmsnorm_to_bf16(h.astype(np.float64))
+    eps = Fraction(1e-6)  # the float64 value of 1e-6, as the oracle uses it
+    n_checked = 0
+    for t in range(h.shape[0]):
+        S = sum(Fraction(float(v)) ** 2 for v in h[t]) / d + eps
+        for i in range(d):
+            want, dist = ER.rne_sqrt_ratio(Fraction(float(h[t, i])), S, ER.BF16)
+            if dist < 1e-9:
+                continue  # within float64 rounding of a midpoint: either neighbour is correct
+            assert Fraction(float(x[t, i])) == want, (t, i, x[t, i], float(want))
+            n_checked += 1
+    assert n_checked >= h.size - 2
+    assert np.all(x[4] == 0)
+
+
+def test_residual_add_is_float32_rounded_sum():
+    """h + y rounded once to float32, against exact rationals and torch."""
+    import torch
+    rng = np.random.default_rng(20)
+    h = rng.normal(0, 3, size=(3, 64)).astype(np.float32)
+    y = (rng.normal(0, 1, size=(3, 64)) * np.exp(rng.uniform(-20, 5, size=(3, 64)))).astype(np.float32)
+    got = M.residual_add(h, y)
+    for a, b, g in zip(h.ravel(), y.ravel(), got.ravel()):
+        assert Fraction(float(g)) == ER.rne(Fraction(float(a)) + Fraction(float(b)), ER.F32)
+    assert np.array_equal(got, (torch.from_numpy(h) + torch.from_numpy(y)).numpy().astype(np.float64))
 
 
 # ---------------------------------------------------------------- planted mistakes
@@ -421,3 +474,40 @@ def test_planted_mistakes_are_caught(monkeypatch):
             p["row_slot"][lo:hi] = p["row_slot"][lo:hi][::-1].copy()
         return p
     _expect_pin_failure(monkeypatch, M, "plan", bad_plan, test_plan_matches_library_routines, 3)
+
+    # (9) plan keeps the last of repeated ids instead of the first
+    def bad_plan_dup(idx, E):
+        return _plan_keep_last(orig_plan, idx, E)
+    _expect_pin_failure(monkeypatch, M, "plan", bad_plan_dup, test_plan_keeps_first_of_repeated_ids)
+
+    # (10) RMSNorm with the wrong eps, the wrong denominator, eps outside the root
+    orig_round = F.round_to_bf16
+    for bad in (lambda H: orig_round(H / np.sqrt(np.mean(H * H, -1, keepdims=True) + 1e-5)),
+                lambda H: orig_round(H / np.sqrt(np.mean(H * H, -1, keepdims=True))),
+                lambda H: orig_round(H / np.sqrt(np.sum(H * H, -1, keepdims=True) / (H.shape[-1] - 1) + 1e-6)),
+                lambda H: orig_round(H / (np.sqrt(np.mean(H * H, -1, keepdims=True)) + 1e-6))):
+        _expect_pin_failure(monkeypatch, M, "rmsnorm_to_bf16", lambda h, bad=bad: bad(np.asarray(h, np.float64)),
+                            test_rmsnorm_matches_exact_rational_rounding)
+
+    # (11) bf16 rounding through a float32 intermediate (two roundings)
+    def bad_round(x):
+        f = np.asarray(x, np.float64).astype(np.float32)
+        return F.bf16_bits_to_float(F.f32_to_bf16_bits(f))
+    _expect_pin_failure(monkeypatch, F, "round_to_bf16", bad_round, _pin_bf16)
+
+    # (12) residual sum left in float64
+    _expect_pin_failure(monkeypatch, M, "residual_add",
+                        lambda h, y: np.asarray(h, np.float32).astype(np.float64) + np.asarray(y, np.float32),
+                        test_residual_add_is_float32_rounded_sum)
+
+
+def _plan_keep_last(orig_plan, idx, E):
+    """The plan with, among repeated ids of a token, the LAST slot kept."""
+    idx = np.asarray(idx, dtype=np.int32).copy()
+    T, k = idx.shape
+    for t in range(T):
+        for j in range(k):
+            if 0 <= idx[t, j] < E and idx[t, j] in idx[t, j + 1:]:
+                idx[t, j] = -1
+    p = orig_plan(idx, E)
+    return p

@@ -53,7 +53,9 @@ typedef enum {
   MOE_ERR_HIP = -5          /* a HIP launch or runtime call failed */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+/* Activation / output element types.  MOE_F16 is accepted by moe_dequantize
+ * only (the prefill path's fp16 weight tile). */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_F16 = 2 } moe_dtype;
 
 /* Block formats; all blocks run along a row's reduction dimension (cols).
  *  MOE_Q8_0   32-element blocks; codes int8 [n][rows][cols]; scales IEEE
@@ -97,7 +99,7 @@ typedef struct {
 } moe_layer;
 
 /* The expert plan for T tokens with k slots each (all device int32):
- *  counts[E]        pairs routed to each expert
+ *  counts[E]        pairs routed to each expert (pairs kept, see error)
  *  offsets[E+1]     exclusive prefix sum of counts; offsets[E] = valid pairs
  *  row_token[T*k]   token of plan row r; rows of expert e are
  *                   [offsets[e], offsets[e+1]) in ascending token order
@@ -105,9 +107,19 @@ typedef struct {
  *  slot_row[T*k]    plan row of pair (t, j) at index t*k + j (-1 if dropped)
  *  active[E]        ids with counts > 0, ascending, padded with -1
  *  n_active[1]      number of active experts
- *  error[1]         0, or a bit set: 1 = an expert id outside [0, E) was
- *                   dropped; 2 = an SwiGLU activation exceeded the fp16 range
- *                   (moe_ffn_forward, moe_decode_stack)
+ *  error[1]         0, or bits set:
+ *                     1 = an expert id outside [0, E) was dropped;
+ *                     2 = an SwiGLU activation exceeded the fp16 range
+ *                         (moe_ffn_forward, moe_decode_stack);
+ *                     4 = an id repeated within a token was dropped (a top-k
+ *                         selection names each expert once; of repeats the
+ *                         lowest slot j keeps its row);
+ *                     8 = the prefill path (T > 64) met a Q8_0 / IQ4_NL block
+ *                         scale whose product with the format's largest code
+ *                         magnitude (128 / 127) is not finite in fp16, i.e.
+ *                         |scale| >= 512 (Q8_0) or >= 516 (IQ4_NL), or a
+ *                         non-finite scale: such weights may be infinite.
+ *                   A dropped pair gets slot_row -1 and no plan row.
  * Rows past offsets[E] in row_token / row_slot are set to -1. */
 typedef struct {
   int32_t* counts;
@@ -154,10 +166,14 @@ moe_status moe_plan(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
  * carried as fp16 hi/lo pairs, intermediate SwiGLU values must stay below
  * 65504 in magnitude; error bit 2 reports otherwise).  For T > 64 the prefill
  * path runs: weights are rounded to fp16 (code times block scale, rounded
- * once; NVFP4-style weights are exact and their tensor scale is applied in
- * fp32), tokens are scaled by a power of two per token into fp16 (exact for
- * bf16 tokens), SwiGLU activations are rounded to fp16 (error bit 2 if one
- * exceeds 65504 in magnitude), fp16 MFMA with fp32 accumulation.
+ * once: relative error at most 2^-11, never a lossy subnormal, since a
+ * product below 2^-14 has a subnormal scale and is then an exact multiple of
+ * 2^-24; error bit 8 flags scales at which a weight can overflow;
+ * NVFP4-style weights are exact and their tensor scale is applied in fp32),
+ * tokens are scaled by a power of two per token into fp16 (exact for bf16
+ * tokens), SwiGLU activations are rounded to fp16 (error bit 2 if one
+ * exceeds 65504 in magnitude; values below 2^-14 keep an absolute precision
+ * of 2^-25), fp16 MFMA with fp32 accumulation.
  * The combine never uses atomics: results are bitwise reproducible. */
 moe_status moe_ffn_forward(const moe_layer* layer, const void* x, int32_t x_dtype, int32_t T,
                            const float* topk_w, const moe_plan_buf* plan,
@@ -186,8 +202,17 @@ moe_status moe_ffn_combine(const moe_layer* layer, int32_t x_dtype, int32_t T, c
                            const moe_plan_buf* plan, void* y, int32_t y_dtype, void* ws, size_t ws_bytes,
                            void* stream);
 
-/* Test hook: dequantise expert `expert` of `m` into dst device [rows][cols] as
- * fp32 (exact) or bf16 (round-to-nearest-even of the exact value). */
+/* Test hook: dequantise expert `expert` of `m` into dst device [rows][cols]:
+ *  MOE_F32   exact values (NVFP4-style: fp32(e2m1 * e4m3 * tensor_scale));
+ *  MOE_BF16  round-to-nearest-even of those values;
+ *  MOE_F16   the fp16 weight tile the prefill GEMM multiplies, produced by the
+ *            GEMM's own decode routine: Q8_0 / IQ4_NL the code times the
+ *            block scale in fp16 arithmetic (one rounding to nearest even of
+ *            the exact product; subnormal below 2^-14, infinite when the
+ *            product reaches 65520 -- see error bit 8); NVFP4-style
+ *            e2m1 * e4m3 (exact), without the tensor scale, which the GEMM
+ *            applies to its fp32 result.
+ * dst must be 4-byte aligned. */
 moe_status moe_dequantize(const moe_qmatrix* m, int32_t expert, int32_t out_dtype, void* dst,
                           void* stream);
 

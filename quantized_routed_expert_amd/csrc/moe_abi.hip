@@ -206,13 +206,14 @@ moe_status moe_ffn_combine(const moe_layer* layer, int32_t x_dtype, int32_t T, c
 }
 
 moe_status moe_dequantize(const moe_qmatrix* m, int32_t expert, int32_t out_dtype, void* dst, void* stream) {
-  if (!m || !dst || !valid_dtype(out_dtype)) return MOE_ERR_INVALID_ARG;
+  if (!m || !dst || !(valid_dtype(out_dtype) || out_dtype == MOE_F16)) return MOE_ERR_INVALID_ARG;
   if (!valid_qtype(m->type)) return MOE_ERR_UNSUPPORTED;
   if (m->rows <= 0 || m->cols <= 0 || m->n_expert <= 0 || expert < 0 || expert >= m->n_expert)
     return MOE_ERR_INVALID_ARG;
   if (m->cols % 32 != 0) return MOE_ERR_UNSUPPORTED;
   if (!m->codes || !m->scales || (m->type == MOE_NVFP4 && !m->tensor_scale)) return MOE_ERR_INVALID_ARG;
   if (!aligned(m->codes, 16) || !aligned(m->scales, 16) || !aligned(dst, 4)) return MOE_ERR_ALIGNMENT;
+  if (out_dtype == MOE_F16) return hip_status(launch_dequant_pf(qmat_dev(*m), expert, dst, (hipStream_t)stream));
   return hip_status(launch_dequant(qmat_dev(*m), expert, out_dtype, dst, (hipStream_t)stream));
 }
 

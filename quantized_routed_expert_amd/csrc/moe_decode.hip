@@ -197,15 +197,17 @@ __global__ __launch_bounds__(256) void k_prep_x(const void* __restrict__ x, int 
       hi[q] = (f16)sv;
       lo[q] = (f16)(sv - (float)hi[q]);
     }
+    // (a pair the plan dropped -- an invalid or repeated id -- has no row)
     for (int j = 0; j <= k; ++j) {
       const long r = rows[j];
+      if (r < 0) continue;
       *(f16x8*)&x16[(r * P) * d + 8 * c] = hi;
       if (P == 2) *(f16x8*)&x16[(r * P + 1) * d + 8 * c] = lo;
     }
   }
   if ((int)threadIdx.x < (k + 1) * P) {
     const int j = threadIdx.x / P, part = threadIdx.x - j * P;
-    xs[(long)rows[j] * P + part] = ldexpf(1.0f, ex);
+    if (rows[j] >= 0) xs[(long)rows[j] * P + part] = ldexpf(1.0f, ex);
   }
 }
 

@@ -216,6 +216,59 @@ __device__ __forceinline__ f16x8 pf_decode(const PfCodes<FMT>& pc, int i) {
   }
 }
 
+// The prefill weights are fp16 (code times block scale, rounded once).  A
+// block scale of magnitude at or above kPfScaleMax<FMT> makes the product with
+// the format's largest code magnitude (Q8_0: 128, IQ4_NL: 127) overflow fp16
+// (it reaches 65520 and rounds to infinity); such scales, and non-finite ones,
+// are reported through error bit 8.  NVFP4-style products (at most 6 * 448)
+// are always finite.
+template <int FMT>
+constexpr uint32_t kPfScaleMax = FMT == MOE_Q8_0 ? 0x6000u /* 512.0 */ : 0x6008u /* 516.0 */;
+
+template <int FMT>
+__device__ __forceinline__ bool pf_scale_out_of_range(const PfCodes<FMT>& pc) {
+  if constexpr (FMT == MOE_NVFP4) return false;
+  return (pc.sc & 0x7fffu) >= kPfScaleMax<FMT>;
+}
+
+// Test hook: one expert's weights exactly as the prefill GEMM feeds them to
+// the MFMA (pf_load_codes + pf_decode), one thread per 32-element chunk, in
+// element order; NVFP4-style: e2m1 * e4m3 without the tensor scale.
+template <int FMT>
+__global__ void k_dequant_pf(QMatDev m, int expert, f16* __restrict__ dst) {
+  const int rows = m.rows, cols = m.cols;
+  const int nb = cols / 32;
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long)rows * nb) return;
+  const int r = (int)(i / nb), b = (int)(i % nb);
+  const long rw = (long)expert * rows + r;
+  PfCodes<FMT> pc;
+  pf_load_codes<FMT>(m.codes + rw * code_row_bytes(FMT, cols), m.scales + rw * scale_row_bytes(FMT, cols), b * 32,
+                     pc);
+  f16* o = dst + (long)r * cols + b * 32;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f16x8 v = pf_decode<FMT>(pc, q);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      // IQ4_NL decodes elements 4q..4q+3 and 16+4q..16+4q+3; the others 8q..8q+7
+      const int el = FMT == MOE_IQ4_NL ? (u < 4 ? 4 * q + u : 16 + 4 * q + (u - 4)) : 8 * q + u;
+      o[el] = v[u];
+    }
+  }
+}
+
+hipError_t launch_dequant_pf(const QMatDev& m, int expert, void* dst, hipStream_t s) {
+  const long total = (long)m.rows * (m.cols / 32);
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  switch (m.type) {
+    case MOE_Q8_0: hipLaunchKernelGGL(k_dequant_pf<MOE_Q8_0>, grid, block, 0, s, m, expert, (f16*)dst); break;
+    case MOE_IQ4_NL: hipLaunchKernelGGL(k_dequant_pf<MOE_IQ4_NL>, grid, block, 0, s, m, expert, (f16*)dst); break;
+    default: hipLaunchKernelGGL(k_dequant_pf<MOE_NVFP4>, grid, block, 0, s, m, expert, (f16*)dst); break;
+  }
+  return hipGetLastError();
+}
+
 // One work item (M-tile x N-tile) over its first NMF M fragments.
 template <int FMT, bool GATEUP, int NF, int NMF>
 __device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sAbuf, float* s_rsx, const PfTile tl,
@@ -295,6 +348,7 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sAbuf, fl
     for (int f = 0; f < NF; ++f) acc[mi][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   PfCodes<FMT> pc[NF], pn[NF];
+  bool wbad = false;  // a block scale beyond the fp16 weight range
   copy_a(0, 0);
   load_b(0, pc);
   // gate/up: the token scale of tile row tid, kept for the epilogue
@@ -314,6 +368,8 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sAbuf, fl
       load_b(s + 1, pn);
     }
     const uint8_t* sa = sAbuf + (s & 1) * kPfBuf;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) wbad |= pf_scale_out_of_range<FMT>(pc[f]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint8_t* p = sa + aoff[i];
@@ -365,6 +421,7 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sAbuf, fl
     }
   }
   if (GATEUP && bad) atomicOr(a.error, 2);
+  if (__any(wbad) && lane == 0) atomicOr(a.error, 8);
 }
 
 template <int FMT, bool GATEUP, int NF>

@@ -551,38 +551,56 @@ size_t plan_ws_bytes(int T, int E) {
   return align_up((size_t)nb * E * 4 + (size_t)nb * 4, 256);
 }
 
-// Token masks of one block of <= 64 tokens into LDS mask[E]; returns 1 if an
-// id was out of range.
-__device__ __forceinline__ int block_token_masks(const int32_t* __restrict__ idx, int t0, int t1, int k, int E,
-                                                 unsigned long long* mask) {
-  for (int e = threadIdx.x; e < E; e += blockDim.x) mask[e] = 0ull;
-  __syncthreads();
-  int err = 0;
-  for (int p = t0 * k + threadIdx.x; p < t1 * k; p += blockDim.x) {
-    const int e = idx[p];
-    if (e >= 0 && e < E)
-      atomicOr(&mask[e], 1ull << (p / k - t0));
-    else
-      err = 1;
-  }
-  return __syncthreads_or(err);
+// Status of pair q (local index) of a block whose ids are staged in LDS
+// sidx: its expert id if the pair is kept, -1 for an id outside [0, E), -2
+// for an id already named at an earlier slot of the same token (a top-k
+// selection names each expert once; of repeats the lowest slot is kept).
+__device__ __forceinline__ int pair_status(const int32_t* sidx, int q, int k, int E) {
+  const int e = sidx[q];
+  if (e < 0 || e >= E) return -1;
+  const int j = q % k, q0 = q - j;
+  for (int jj = 0; jj < j; ++jj)
+    if (sidx[q0 + jj] == e) return -2;
+  return e;
 }
 
-__device__ __forceinline__ void plan_scatter_block(const int32_t* __restrict__ idx, int t0, int t1, int k, int E,
+// Ids of one block of <= 64 tokens into LDS sidx, then token masks into LDS
+// mask[E]; returns the error bits of the block (1: an id out of range, 4: a
+// repeated id).
+__device__ __forceinline__ int block_token_masks(const int32_t* __restrict__ idx, int t0, int t1, int k, int E,
+                                                 int32_t* sidx, unsigned long long* mask) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) mask[e] = 0ull;
+  for (int q = threadIdx.x; q < (t1 - t0) * k; q += blockDim.x) sidx[q] = idx[t0 * k + q];
+  __syncthreads();
+  int err = 0;
+  for (int q = threadIdx.x; q < (t1 - t0) * k; q += blockDim.x) {
+    const int e = pair_status(sidx, q, k, E);
+    if (e >= 0)
+      atomicOr(&mask[e], 1ull << (q / k));
+    else
+      err |= e == -1 ? 1 : 4;
+  }
+  const int e1 = __syncthreads_or(err & 1);
+  const int e4 = __syncthreads_or(err & 4);
+  return (e1 ? 1 : 0) | (e4 ? 4 : 0);
+}
+
+__device__ __forceinline__ void plan_scatter_block(int t0, int t1, int k, int E, const int32_t* sidx,
                                                    const unsigned long long* mask, const int32_t* base,
                                                    const PlanDev& p) {
-  for (int q = t0 * k + threadIdx.x; q < t1 * k; q += blockDim.x) {
-    const int e = idx[q];
-    if (e < 0 || e >= E) {
-      p.slot_row[q] = -1;
+  for (int q = threadIdx.x; q < (t1 - t0) * k; q += blockDim.x) {
+    const int e = pair_status(sidx, q, k, E);
+    const int qg = t0 * k + q;
+    if (e < 0) {
+      p.slot_row[qg] = -1;
       continue;
     }
-    const int tl = q / k - t0;
+    const int tl = q / k;
     const int rank = __popcll(mask[e] & ((1ull << tl) - 1ull));
     const int r = base[e] + rank;
     p.row_token[r] = t0 + tl;
     p.row_slot[r] = q % k;
-    p.slot_row[q] = r;
+    p.slot_row[qg] = r;
   }
 }
 
@@ -590,8 +608,9 @@ __device__ __forceinline__ void plan_scatter_block(const int32_t* __restrict__ i
 __global__ __launch_bounds__(1024) void k_plan_small(const int32_t* __restrict__ idx, int T, int k, int E, PlanDev p) {
   __shared__ unsigned long long mask[1024];
   __shared__ int32_t base[1024];
+  __shared__ int32_t sidx[kPlanTB * 32];
   __shared__ int32_t scratch[2][17];
-  const int err = block_token_masks(idx, 0, T, k, E, mask);
+  const int err = block_token_masks(idx, 0, T, k, E, sidx, mask);
   const int e = threadIdx.x;
   const int cnt = e < E ? __popcll(mask[e]) : 0;
   int n_valid, n_act;
@@ -614,15 +633,16 @@ __global__ __launch_bounds__(1024) void k_plan_small(const int32_t* __restrict__
     p.row_slot[r] = -1;
   }
   __syncthreads();
-  plan_scatter_block(idx, 0, T, k, E, mask, base, p);
+  plan_scatter_block(0, T, k, E, sidx, mask, base, p);
 }
 
 __global__ __launch_bounds__(256) void k_plan_count(const int32_t* __restrict__ idx, int T, int k, int E,
                                                     int32_t* __restrict__ hist, int32_t* __restrict__ blk_err) {
   __shared__ unsigned long long mask[1024];
+  __shared__ int32_t sidx[kPlanTB * 32];
   const int b = blockIdx.x;
   const int t0 = b * kPlanTB, t1 = min(T, t0 + kPlanTB);
-  const int err = block_token_masks(idx, t0, t1, k, E, mask);
+  const int err = block_token_masks(idx, t0, t1, k, E, sidx, mask);
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(long)b * E + e] = __popcll(mask[e]);
   if (threadIdx.x == 0) blk_err[b] = err;
 }
@@ -681,7 +701,7 @@ __global__ __launch_bounds__(1024) void k_plan_scan(int T, int k, int E, int nb,
   if (threadIdx.x == 0) err_s = 0;
   __syncthreads();
   for (int b = threadIdx.x; b < nb; b += blockDim.x)
-    if (blk_err[b]) atomicOr(&err_s, 1);
+    if (blk_err[b]) atomicOr(&err_s, blk_err[b]);
   __syncthreads();
   if (e == 0) {
     p.offsets[E] = n_valid;
@@ -697,10 +717,11 @@ __global__ __launch_bounds__(1024) void k_plan_scan(int T, int k, int E, int nb,
 __global__ __launch_bounds__(256) void k_plan_scatter(const int32_t* __restrict__ idx, int T, int k, int E,
                                                       const int32_t* __restrict__ base, PlanDev p) {
   __shared__ unsigned long long mask[1024];
+  __shared__ int32_t sidx[kPlanTB * 32];
   const int b = blockIdx.x;
   const int t0 = b * kPlanTB, t1 = min(T, t0 + kPlanTB);
-  block_token_masks(idx, t0, t1, k, E, mask);
-  plan_scatter_block(idx, t0, t1, k, E, mask, base + (long)b * E, p);
+  block_token_masks(idx, t0, t1, k, E, sidx, mask);
+  plan_scatter_block(t0, t1, k, E, sidx, mask, base + (long)b * E, p);
 }
 
 hipError_t launch_plan(const int32_t* idx, int T, int k, int E, const PlanDev& p, void* ws, hipStream_t s) {

@@ -24,6 +24,7 @@ MOE_ERR_HIP = -5
 
 MOE_F32 = 0
 MOE_BF16 = 1
+MOE_F16 = 2
 
 MOE_Q8_0 = 1
 MOE_IQ4_NL = 2

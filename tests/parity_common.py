@@ -23,6 +23,31 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / (den if den > 0 else 1.0))
 
 
+def bf16_ulp(v):
+    """Spacing of bfloat16 values at |v| (2^(e - 7) in the binade [2^e, 2^(e+1)),
+    2^-133 below 2^-126)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a >= 2.0 ** -126, np.exp2(e - 7), 2.0 ** -133)
+
+
+def check_bf16_glue(xg, x_ref, what, max_frac=1e-3):
+    """A bf16 layer input formed in fp32 on the GPU against the oracle's
+    (rounded once from float64): every element equal, or one bf16 step away
+    (the fp32 normalisation landed on the other side of a rounding midpoint),
+    and such elements rare.  Returns the number of one-step differences."""
+    xg = np.asarray(xg, dtype=np.float64)
+    x_ref = np.asarray(x_ref, dtype=np.float64)
+    diff = xg != x_ref
+    n = int(diff.sum())
+    if n:
+        step = np.maximum(bf16_ulp(xg[diff]), bf16_ulp(x_ref[diff]))
+        far = np.abs(xg[diff] - x_ref[diff]) > step
+        assert not far.any(), f"{what}: {int(far.sum())} elements differ by more than one bf16 step"
+    assert n <= max_frac * xg.size, f"{what}: {n} of {xg.size} elements differ by one bf16 step"
+    return n
+
+
 def to_np(t):
     if t.dtype == torch.bfloat16:
         return t.float().cpu().numpy().astype(np.float64)

@@ -15,7 +15,7 @@ from oracle import moe as M
 from quantized_routed_expert_amd import lib, synth
 from quantized_routed_expert_amd.stack import Stack
 
-from parity_common import check_layer, check_selection, rel_l2, to_np
+from parity_common import check_bf16_glue, check_layer, check_selection, rel_l2, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -76,6 +76,17 @@ def test_dequantize_bit_exact(qtype):
         lib.moe_dequantize(q, e, lib.MOE_BF16, outb)
         gotb = outb.float().cpu().numpy().astype(np.float64)
         assert np.array_equal(gotb, F.round_to_bf16(want)), f"{qtype} bf16 expert {e}"
+        # the prefill GEMM's fp16 weight tile, through its own decode routine:
+        # fp16 round-to-nearest-even of the exact product (NVFP4-style: without
+        # the tensor scale), infinities included
+        want16 = want if ts is None else F.dequant(qtype, host["codes"][e], host["scales"][e], 1.0)
+        outh = torch.empty((m["rows"], m["cols"]), dtype=torch.float16, device=DEV)
+        lib.moe_dequantize(q, e, lib.MOE_F16, outh)
+        goth = outh.cpu().numpy()
+        assert np.array_equal(goth, want16.astype(np.float16)), \
+            f"{qtype} fp16 tile expert {e}: {np.sum(goth != want16.astype(np.float16))} mismatches"
+        if qtype != "nvfp4":
+            assert np.isinf(goth).any() and (goth[np.isfinite(goth)] != 0).any()
 
 
 # ---------------------------------------------------------------- routing
@@ -151,7 +162,8 @@ def test_topk_heavy_ties(E, k, T, d):
 
 @pytest.mark.parametrize("T,k,E,bad", [(1, 8, 512, False), (8, 8, 512, False), (64, 8, 512, False),
                                        (65, 4, 16, False), (300, 8, 512, False), (4096, 8, 512, False),
-                                       (5000, 6, 300, False), (33, 3, 7, True)])
+                                       (5000, 6, 300, False), (33, 3, 7, True), (40, 6, 50, "dup"),
+                                       (200, 8, 64, "dup")])
 def test_plan_bit_exact(T, k, E, bad):
     _say(f"[plan] T={T} k={k} E={E} bad={bad}")
     g = np.random.default_rng(T * 31 + k)
@@ -163,6 +175,12 @@ def test_plan_bit_exact(T, k, E, bad):
         idx[3, 1] = -1
         idx[10, 0] = E
         idx[T - 1, k - 1] = E + 100
+    if bad == "dup":
+        # repeated ids within a token: the lowest slot keeps its row (bit 4)
+        idx[5, k - 1] = idx[5, 0]
+        idx[7, 1:] = idx[7, 0]
+        idx[T - 2, 2] = idx[T - 2, 1]
+        idx[T - 1, 0] = idx[T - 1, k - 1]  # (slot k-1 is out of range here: no repeat)
     plan = lib.Plan(T, k, E, DEV)
     wsb = 1 << 24
     ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
@@ -300,6 +318,75 @@ def test_swiglu_overflow_is_flagged():
     assert int(st.bufs[0].plan.error.item()) & 2
 
 
+@pytest.mark.parametrize("T", [5, 40, 100])
+def test_ffn_forward_with_dropped_pairs(T):
+    """A plan that dropped pairs (ids out of range, ids repeated within a
+    token) through moe_ffn_forward: the dropped pairs contribute nothing, the
+    others match the oracle, and nothing is written outside the buffers (the
+    workspace is bracketed by guard regions that must stay untouched)."""
+    _say(f"[dropped pairs] T={T}")
+    wl, layer = _small_layer(600 + T, d=256, f=128, E=16, k=4, types=("iq4_nl", "iq4_nl", "q8_0"))
+    g = np.random.default_rng(T)
+    idx = np.stack([g.permutation(16)[:4] for _ in range(T)]).astype(np.int32)
+    idx[0, 1] = -1
+    idx[1, 3] = 16
+    idx[2, 2] = idx[2, 0]
+    idx[T - 1, 1:] = idx[T - 1, 0]
+    w = g.uniform(0.1, 1.0, size=(T, 4))
+    w /= w.sum(1, keepdims=True)
+    x = torch.randn((T, wl.d), generator=torch.Generator().manual_seed(T)).to(torch.bfloat16)
+    L = lib.layer_struct(layer)
+    plan = lib.Plan(T, 4, 16, DEV)
+    wsb = lib.moe_workspace_size(L, T)
+    guard = 1 << 16
+    buf = torch.full((wsb + 2 * guard,), 0x5A, dtype=torch.uint8, device=DEV)
+    ws = buf[guard:guard + wsb]
+    xd = x.to(DEV)
+    idx_d = torch.from_numpy(idx).to(DEV)
+    w_d = torch.from_numpy(w.astype(np.float32)).to(DEV)
+    y = torch.empty((T, wl.d), dtype=torch.float32, device=DEV)
+    lib.moe_plan(idx_d, T, 4, 16, plan, ws, wsb)
+    lib.moe_ffn_forward(L, xd, lib.MOE_BF16, T, w_d, plan, y, lib.MOE_F32, ws, wsb)
+    torch.cuda.synchronize()
+    assert int(plan.error.item()) == 1 | 4
+    assert torch.all(buf[:guard] == 0x5A) and torch.all(buf[guard + wsb:] == 0x5A), "write outside the workspace"
+    lnp = synth.layer_to_numpy(layer)
+    xn = x.float().numpy().astype(np.float64)
+    p_ref = M.plan(idx, 16)
+    assert p_ref["error"] == 1 | 4
+    got = plan.host()
+    for n in ("counts", "offsets", "row_token", "row_slot", "slot_row", "active"):
+        assert np.array_equal(got[n], p_ref[n]), n
+    y_ref = M.layer_from_selection(lnp, xn, idx, w.astype(np.float32).astype(np.float64), p_ref, out_dtype="f64")
+    err = rel_l2(y.cpu().numpy(), y_ref)
+    assert err <= (TOL_DECODE if T <= 64 else TOL_PREFILL), err
+
+
+@pytest.mark.parametrize("types", [("q8_0", "q8_0", "q8_0"), ("iq4_nl", "iq4_nl", "iq4_nl")],
+                         ids=lambda t: "-".join(t))
+def test_prefill_extreme_scales(types):
+    """Prefill at the edges of the fp16 weight range.  Subnormal block scales
+    (0x0001 .. 0x03FF) give exact or 2^-11-accurate fp16 weights: parity
+    holds.  A block scale of 0x7BFF (65504) can overflow fp16: error bit 8."""
+    T = 100
+    _say(f"[prefill extreme] {types}")
+    wl, layer = _small_layer(700, d=256, f=128, E=8, k=2, types=types, shared=False)
+    g = torch.Generator(device=DEV).manual_seed(3)
+    sc = layer["routed"]["down"]["scales"]
+    bits = torch.randint(1, 0x400, sc.shape, generator=g, device=DEV, dtype=torch.int32)
+    sc.copy_(bits.to(torch.int16).view(torch.float16))
+    x = torch.randn((T, wl.d), generator=torch.Generator().manual_seed(9)).to(torch.bfloat16)
+    st, gpu = _run_single(layer, x, "bf16", "f32")
+    assert int(st.bufs[0].plan.error.item()) == 0
+    lnp = synth.layer_to_numpy(layer)
+    stats = check_layer(lnp, x.float().numpy().astype(np.float64), gpu, "f64", TOL_PREFILL)
+    _say(f"[prefill extreme] subnormal down scales: {stats}")
+    # one block scale of every routed gate matrix at the fp16 maximum
+    layer["routed"]["gate"]["scales"][:, 5, 2] = 65504.0
+    st, gpu = _run_single(layer, x, "bf16", "f32")
+    assert int(st.bufs[0].plan.error.item()) & 8
+
+
 # ---------------------------------------------------------------- full-size shapes
 
 def _full_stack(name, n_layers, T=None):
@@ -341,7 +428,7 @@ def test_full_size_decode_workloads(name):
     y0 = to_np(st.bufs[0].y)
     x1 = M.rmsnorm_to_bf16(M.residual_add(h0, y0))
     x1g = to_np(st.xs[1])
-    assert np.mean(x1g == x1) > 0.999 and rel_l2(x1g, x1) < 4e-3
+    check_bf16_glue(x1g, x1, "layer 1 input")
 
 
 def test_full_size_prefill_sampled_tokens():

@@ -270,6 +270,26 @@ moe_status moe_decode_stack(const moe_layer* layers, int32_t n_layers, float* h,
  * tokens (0 on invalid or unsupported arguments). */
 size_t moe_decode_stack_workspace_size(const moe_layer* layer, int32_t T_max);
 
+/* moe_decode_stack for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation, kernels and records, with the workspace taken from a
+ * library-owned device array of moe_decode_stack_scratch_bytes() bytes
+ * (8 MiB; one per GPU, held until the process ends) instead of a caller
+ * workspace.  The caller still passes h and the records.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); its first
+ * call on a device looks up that device's array address once.
+ *   Errors: as moe_decode_stack; MOE_ERR_WORKSPACE when the shape needs more
+ *   than the array holds (moe_decode_stack_workspace_size > 8 MiB), before
+ *   any launch; MOE_ERR_HIP if the array's address cannot be obtained.
+ *   Every call on one GPU shares that GPU's array and leaves its contents
+ *   behind: calls that overlap in time on one GPU (different streams, or
+ *   host threads) race and must be serialised by the caller. */
+moe_status moe_decode_stack_noalloc(const moe_layer* layers, int32_t n_layers, float* h, int32_t T, float eps,
+                                    const moe_stack_record* rec, void* stream);
+
+/* Size in bytes of the array moe_decode_stack_noalloc uses on each GPU. */
+size_t moe_decode_stack_scratch_bytes(void);
+
 /* Workspace bytes needed by moe_route / moe_plan / moe_ffn_forward for up to
  * T_max tokens on this layer shape (0 on invalid arguments). */
 size_t moe_workspace_size(const moe_layer* layer, int32_t T_max);

@@ -5,6 +5,8 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 #include "moe.h"
 #include "moe_launch.h"
 
@@ -257,6 +259,55 @@ moe_status moe_decode_stack(const moe_layer* layers, int32_t n_layers, float* h,
   if (!ws || ws_bytes < fused_ws_bytes(T, L0.d, L0.f, L0.k, L0.E)) return MOE_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
   return hip_status(launch_fused_step(layers, n_layers, h, T, r, ws, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant of moe_decode_stack: its workspace is a file-scope
+// device array, one per GPU the library runs on (each device holds its own
+// copy at its own address).  The array's name is a host-side stand-in: host
+// code uses only the device address hipGetSymbolAddress returns, taken once
+// per device on the first call with that device current.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, or null on failure.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_decode_stack_scratch_bytes(void) { return kScratchBytes; }
+
+moe_status moe_decode_stack_noalloc(const moe_layer* layers, int32_t n_layers, float* h, int32_t T, float eps,
+                                    const moe_stack_record* rec, void* stream) {
+  if (!layers || n_layers < 1 || T < 1) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe_decode_stack_workspace_size(&layers[0], T);
+  // an invalid or unsupported shape: moe_decode_stack's own validation names it
+  if (need == 0) return moe_decode_stack(layers, n_layers, h, T, eps, rec, nullptr, 0, stream);
+  if (need > kScratchBytes) return MOE_ERR_WORKSPACE;
+  void* ws = scratch_address();
+  if (!ws) return MOE_ERR_HIP;
+  return moe_decode_stack(layers, n_layers, h, T, eps, rec, ws, kScratchBytes, stream);
 }
 
 moe_status moe_residual_rmsnorm(float* h, const void* y, int32_t y_dtype, int32_t T, int32_t d, float eps,

@@ -35,7 +35,8 @@ DTYPE = {"f32": MOE_F32, "bf16": MOE_BF16}
 
 EXPORTED = ["moe_route", "moe_plan", "moe_ffn_forward", "moe_ffn_prepare", "moe_ffn_gateup", "moe_ffn_down",
             "moe_ffn_combine", "moe_dequantize", "moe_residual_rmsnorm", "moe_decode_stack",
-            "moe_decode_stack_workspace_size", "moe_workspace_size", "moe_status_string", "moe_version"]
+            "moe_decode_stack_workspace_size", "moe_decode_stack_noalloc", "moe_decode_stack_scratch_bytes",
+            "moe_workspace_size", "moe_status_string", "moe_version"]
 
 
 class MoeError(RuntimeError):
@@ -86,6 +87,8 @@ def _load():
         "moe_residual_rmsnorm": (i32, [vp, vp, i32, i32, i32, ctypes.c_float, vp, vp]),
         "moe_decode_stack": (i32, [LP, i32, vp, i32, ctypes.c_float, ctypes.POINTER(StackRecord), vp, sz, vp]),
         "moe_decode_stack_workspace_size": (sz, [LP, i32]),
+        "moe_decode_stack_noalloc": (i32, [LP, i32, vp, i32, ctypes.c_float, ctypes.POINTER(StackRecord), vp]),
+        "moe_decode_stack_scratch_bytes": (sz, []),
         "moe_workspace_size": (sz, [LP, i32]),
         "moe_status_string": (ctypes.c_char_p, [i32]),
         "moe_version": (ctypes.c_char_p, []),
@@ -270,6 +273,17 @@ def stack_record(logits=None, topk_idx=None, topk_w=None, x=None, y=None, error=
                     ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None)
     r._keep = ev  # the handle array must outlive the struct
     return r
+
+
+def moe_decode_stack_noalloc(layers, n_layers, h, T, eps, rec, stream=None):
+    """moe_decode_stack with the library's own per-GPU scratch array as workspace."""
+    st = _lib.moe_decode_stack_noalloc(layers, int(n_layers), _ptr(h), int(T), float(eps),
+                                       ctypes.byref(rec) if rec is not None else None, _stream(stream))
+    _check(st, "moe_decode_stack_noalloc")
+
+
+def moe_decode_stack_scratch_bytes():
+    return int(_lib.moe_decode_stack_scratch_bytes())
 
 
 def moe_decode_stack(layers, n_layers, h, T, eps, rec, ws, ws_bytes, stream=None):

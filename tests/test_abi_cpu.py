@@ -219,3 +219,18 @@ def test_decode_stack_validation():
     rec = lib.StackRecord(None, None, None, (1 << 32) + 2, None, None, None)
     assert so.moe_decode_stack(arr, 2, 1 << 30, 4, ctypes.c_float(1e-6), ctypes.byref(rec), 1 << 31, wsb,
                                None) == lib.MOE_ERR_ALIGNMENT
+
+
+def test_decode_stack_noalloc_validates_on_the_host():
+    """The allocation-free decode step rejects bad arguments, unsupported
+    shapes and shapes beyond its scratch array before touching any GPU."""
+    so = lib.library()
+    assert so.moe_decode_stack_scratch_bytes() == 8 << 20
+    arr = lib.layer_array([_fake_layer(d=1024, f=256, E=64, k=4, qtype=lib.MOE_IQ4_NL, down=lib.MOE_IQ4_NL)])
+    h = 1 << 30
+    assert so.moe_decode_stack_noalloc(arr, 0, h, 1, ctypes.c_float(1e-6), None, None) == lib.MOE_ERR_INVALID_ARG
+    assert so.moe_decode_stack_noalloc(arr, 1, h, 9, ctypes.c_float(1e-6), None, None) == lib.MOE_ERR_UNSUPPORTED
+    big = lib.layer_array([_fake_layer(d=4096, f=16384, E=1024, k=32, qtype=lib.MOE_IQ4_NL,
+                                       down=lib.MOE_IQ4_NL)])
+    assert so.moe_decode_stack_workspace_size(ctypes.byref(big[0]), 8) > 8 << 20
+    assert so.moe_decode_stack_noalloc(big, 1, h, 8, ctypes.c_float(1e-6), None, None) == lib.MOE_ERR_WORKSPACE

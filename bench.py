@@ -58,6 +58,10 @@ def source_digest(paths):
 
 DOMINANT = {
     # workload -> (kernel, pattern of its symbol in rocprofv3 output, sources it is built from)
+    "decode_persistent": ("k_ps_decode (the whole 48-layer single-token step, one launch)", r"qre::k_ps_decode<",
+                          ["quantized_routed_expert_amd/csrc/moe_persist.hip",
+                           "quantized_routed_expert_amd/csrc/moe_dq.h",
+                           "quantized_routed_expert_amd/csrc/moe_device.h"]),
     "decode": ("k_fz_gateup (top-k + plan + gate/up + SwiGLU, IQ4_NL)", r"qre::k_fz_gateup<",
                ["quantized_routed_expert_amd/csrc/moe_fused.hip", "quantized_routed_expert_amd/csrc/moe_dq.h",
                 "quantized_routed_expert_amd/csrc/moe_device.h"]),
@@ -196,11 +200,19 @@ def main():
     launch_bytes = []
     launch_flops = []
     xd = lib.MOE_BF16
+    persistent = fused and lib.moe_decode_stack_persistent(st.arr, wl.n_layers, T)
     for _ in range(args.kernel_passes if fused else 0):
         evs_k = [torch.cuda.Event(enable_timing=True) for _ in range(2 * wl.n_layers)]
         for e in evs_k:
             e.record(stream)  # creates the underlying HIP events
         st.step(st.timed_record(evs_k))
+        if persistent:
+            # one launch runs the whole step: its events bracket it, and its
+            # algorithmic bytes are the step's
+            durations.append((evs_k[0], evs_k[1]))
+            launch_bytes.append(stack_bytes)
+            launch_flops.append(stack_flops)
+            continue
         for i in range(wl.n_layers):
             durations.append((evs_k[2 * i], evs_k[2 * i + 1]))
             u = U[i]
@@ -228,7 +240,7 @@ def main():
     torch.cuda.synchronize()
     dur_ms = np.array([a.elapsed_time(b) for a, b in durations])
     avg_ms = float(dur_ms.mean())
-    kname, _, ksrc = DOMINANT[args.workload]
+    kname, _, ksrc = DOMINANT["decode_persistent" if persistent else args.workload]
     digest = source_digest(ksrc)
     if args.workload == "prefill":
         achieved = float(np.mean(launch_flops)) / (avg_ms / 1e3) / 1e12

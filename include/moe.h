@@ -237,7 +237,9 @@ typedef struct moe_stack_record {
   int32_t* error;     /* [n_layers] plan / overflow flags of each layer (bits as moe_plan_buf.error) */
   void** events;      /* [n_layers][2] hipEvent_t handles (created by the caller), attached to each
                          layer's gate/up launch so that they carry that kernel's start and end; for
-                         timing the kernel in eager (not graph-captured) calls */
+                         timing the kernel in eager (not graph-captured) calls.  When the step is the
+                         persistent launch (moe_decode_stack_persistent), entries 0 and 1 carry that
+                         launch's start and end and the others are unused. */
 } moe_stack_record;
 
 /* Fused decode step through a stack of routed-expert layers for T <= 8
@@ -265,6 +267,18 @@ typedef struct moe_stack_record {
  * flags are reported only through rec->error.  Asynchronous on `stream`. */
 moe_status moe_decode_stack(const moe_layer* layers, int32_t n_layers, float* h, int32_t T, float eps,
                             const moe_stack_record* rec, void* ws, size_t ws_bytes, void* stream);
+
+/* 1 if moe_decode_stack runs this stack (layers[0]'s shape, n_layers, T) as
+ * one persistent launch, 0 if as per-layer launches.  The persistent step
+ * takes T = 1, d a multiple of 1024 up to 4096, f up to 1024, E up to 1024,
+ * at most 128 layers, and rows short enough that every step's weight codes
+ * are issued up front (gate/up: d <= 3072 for IQ4_NL / NVFP4-style, 1536 for
+ * Q8_0; down: f <= 768); unless the environment sets QRE_DECODE_LAUNCHES=1.
+ * It computes the same layer: its SwiGLU rows h are kept in fp32 and scaled
+ * by a power of two per row into fp16 hi / lo parts for the down products,
+ * and a wait between its workgroups that does not end within its poll bound
+ * sets error bit 16 in every layer's record still to run. */
+int32_t moe_decode_stack_persistent(const moe_layer* layers, int32_t n_layers, int32_t T);
 
 /* Workspace bytes for moe_decode_stack on this layer shape with up to T_max
  * tokens (0 on invalid or unsupported arguments). */

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqre_moe.so")
 
-SOURCES = ["moe_abi.hip", "moe_small.hip", "moe_decode.hip", "moe_fused.hip", "moe_prefill.hip"]
+SOURCES = ["moe_abi.hip", "moe_small.hip", "moe_decode.hip", "moe_fused.hip", "moe_prefill.hip", "moe_persist.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

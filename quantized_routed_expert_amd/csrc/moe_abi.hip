@@ -310,6 +310,11 @@ moe_status moe_decode_stack_noalloc(const moe_layer* layers, int32_t n_layers, f
   return moe_decode_stack(layers, n_layers, h, T, eps, rec, ws, kScratchBytes, stream);
 }
 
+int32_t moe_decode_stack_persistent(const moe_layer* layers, int32_t n_layers, int32_t T) {
+  if (!layers || n_layers < 1 || T < 1 || check_dims(&layers[0]) != MOE_OK) return 0;
+  return fused_step_persistent(layers[0], n_layers, T) ? 1 : 0;
+}
+
 moe_status moe_residual_rmsnorm(float* h, const void* y, int32_t y_dtype, int32_t T, int32_t d, float eps,
                                 void* x_out, void* stream) {
   if (!h || !x_out || T < 1 || d < 1 || !valid_dtype(y_dtype) || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;

@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 
 #include "moe_dq.h"
 
@@ -292,95 +293,6 @@ __global__ __launch_bounds__(256) void k_fz_route(const FzRouteArgs a) {
     const double b = (double)bias_e;
     for (int t = 0; t < T; ++t) a.logits[(long)t * a.E + e] = (float)(r[t] + b);
   }
-}
-
-// Top-k of one token's logits L[0..E) by a whole workgroup of 256 threads
-// (E <= 64 * NPL, 1 <= k <= 32), with the result of wave_topk: slot j < k in
-// out_idx[j] / out_val[j], descending logit, the lower expert id first on
-// ties.  Thread t holds entries t + 256 i.  The threshold tau is the smallest
-// of ng >= k group maxima (groups of 256 / ng consecutive threads, never
-// spanning two wavefronts), so every selected entry is >= tau.  Each wavefront
-// packs its entries >= tau into its own list, and each list entry counts the
-// entries of all lists above it (64-bit keys: the order-preserving logit key,
-// then the complement of the expert id, so that no two keys are equal and the
-// count is the slot).  If a list would exceed 64 entries (heavy ties),
-// wavefront 0 runs wave_topk instead.  Ends with a barrier, after which the
-// result is visible to every wavefront.
-template <int NPL>
-__device__ __forceinline__ void wg_topk1(const float* __restrict__ L, int E, int k, uint32_t* smax,
-                                         uint64_t (*ck)[64], int32_t* cnt, uint32_t* tk_key, int32_t* tk_idx,
-                                         int32_t* out_idx, float* out_val) {
-  constexpr int PT = NPL / 4;  // entries per thread
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  uint32_t key[PT];
-#pragma unroll
-  for (int i = 0; i < PT; ++i) {
-    const int e = tid + 256 * i;
-    key[i] = topk_key32(L[min(e, E - 1)]) & (e < E ? 0xffffffffu : 0u);
-  }
-  int ng = 4;
-  while (ng < k) ng <<= 1;
-  const int gs = 256 / ng;  // 64 .. 8 threads per group
-  uint32_t gm = key[0];
-#pragma unroll
-  for (int i = 1; i < PT; ++i) gm = max(gm, key[i]);
-  if (gs >= 2) gm = max(gm, dpp_u32<kDppShr1, 0xf>(gm));
-  if (gs >= 4) gm = max(gm, dpp_u32<kDppShr2, 0xf>(gm));
-  if (gs >= 8) gm = max(gm, dpp_u32<kDppShr4, 0xf>(gm));
-  if (gs >= 16) gm = max(gm, dpp_u32<kDppShr8, 0xf>(gm));
-  if (gs >= 32) gm = max(gm, dpp_u32<kDppBcast15, 0xa>(gm));
-  if (gs >= 64) gm = max(gm, dpp_u32<kDppBcast31, 0xc>(gm));
-  if ((lane & (gs - 1)) == gs - 1) smax[tid / gs] = gm;  // the group's last thread holds its maximum
-  __syncthreads();
-  uint32_t tau = 0xffffffffu;
-  for (int j0 = 0; j0 < ng; j0 += 4) {
-    const u32x4 q = *(const u32x4*)&smax[j0];
-    tau = min(tau, min(min(q.x, q.y), min(q.z, q.w)));
-  }
-  // ---- this wavefront's entries >= tau, in index order
-  int c = 0;
-#pragma unroll
-  for (int i = 0; i < PT; ++i) {
-    const bool in = key[i] != 0u && key[i] >= tau;
-    const uint64_t mk = __ballot(in);
-    const int pos = c + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
-    if (in && pos < 64) ck[wid][pos] = ((uint64_t)key[i] << 32) | (uint32_t)~(uint32_t)(tid + 256 * i);
-    c += __popcll(mk);
-  }
-  // zero keys pad the list to a multiple of 8 (they count for nothing)
-  if (c <= 64 && lane >= c && lane < ((c + 7) & ~7)) ck[wid][lane] = 0ull;
-  if (lane == 0) cnt[wid] = c;
-  __syncthreads();
-  const int c0 = cnt[0], c1 = cnt[1], c2 = cnt[2], c3 = cnt[3];
-  const int cmax = max(max(c0, c1), max(c2, c3));
-  if (cmax <= 64) {
-    const int cw = cnt[wid];
-    const uint64_t kl = lane < cw ? ck[wid][lane] : 0ull;
-    int rank = 0;
-    for (int j0 = 0; j0 < cmax; j0 += 8) {
-      u32x4 q[4][4];
-#pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2)
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          q[w2][u] = j0 < cnt[w2] ? *(const u32x4*)&ck[w2][j0 + 2 * u] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const uint64_t x0 = ((uint64_t)q[w2][u].y << 32) | q[w2][u].x;
-          const uint64_t x1 = ((uint64_t)q[w2][u].w << 32) | q[w2][u].z;
-          rank += (x0 > kl ? 1 : 0) + (x1 > kl ? 1 : 0);
-        }
-    }
-    if (lane < cw && rank < k) {
-      out_idx[rank] = (int32_t)~(uint32_t)kl;
-      out_val[rank] = topk_key32_value((uint32_t)(kl >> 32));
-    }
-  } else if (wid == 0) {
-    wave_topk<NPL>(L, E, k, lane, tk_key, tk_idx, out_idx, out_val);
-  }
-  __syncthreads();
 }
 
 // (2) Top-k + plan (in LDS, recomputed by every workgroup that needs it) +
@@ -678,15 +590,31 @@ FusedWs carve_fused(void* ws, int T, int d, int f, int k, int E) {
 
 size_t fused_ws_bytes(int T, int d, int f, int k, int E) {
   const size_t TK = (size_t)T * k;
-  return 2 * align_up((size_t)T * d * 4, 256) + align_up((size_t)T * d * 2, 256) +
-         decode_ws_bytes(T, d, f, k, MOE_BF16) + align_up((size_t)T * E * 4, 256) + 256 +
-         3 * align_up(TK * 4, 256) + align_up((TK + 1) * sizeof(SlotEnt), 256) +
-         align_up((size_t)T * (d / 64) * 4, 256) + align_up((size_t)(d / 64) * 4, 256);
+  const size_t launches = 2 * align_up((size_t)T * d * 4, 256) + align_up((size_t)T * d * 2, 256) +
+                          decode_ws_bytes(T, d, f, k, MOE_BF16) + align_up((size_t)T * E * 4, 256) + 256 +
+                          3 * align_up(TK * 4, 256) + align_up((TK + 1) * sizeof(SlotEnt), 256) +
+                          align_up((size_t)T * (d / 64) * 4, 256) + align_up((size_t)(d / 64) * 4, 256);
+  // a single-token call may take the persistent step, whose layout starts at offset 0 too
+  const size_t ps = persist_ws_bytes(d, f, E);
+  return launches > ps ? launches : ps;
+}
+
+// The persistent single-token step is taken where it covers the shape, unless
+// the environment sets QRE_DECODE_LAUNCHES=1 (the per-layer launches, for
+// comparison; read at every call).
+static bool persist_enabled() {
+  const char* v = getenv("QRE_DECODE_LAUNCHES");
+  return !(v && v[0] == '1');
+}
+
+bool fused_step_persistent(const moe_layer& L0, int n_layers, int T) {
+  return persist_enabled() && persist_covers(L0, n_layers, T);
 }
 
 hipError_t launch_fused_step(const moe_layer* layers, int n_layers, float* h, int T, const FusedRecord& rec,
                              void* ws, hipStream_t s) {
   const moe_layer& L0 = layers[0];
+  if (fused_step_persistent(L0, n_layers, T)) return launch_persist_step(layers, n_layers, h, rec, ws, s);
   const int d = L0.d, f = L0.f, k = L0.k, E = L0.E;
   FusedWs F = carve_fused(ws, T, d, f, k, E);
   const int max_slots = (T * k < E ? T * k : E) + (L0.has_shared ? 1 : 0);

@@ -103,6 +103,16 @@ size_t fused_ws_bytes(int T, int d, int f, int k, int E);
 hipError_t launch_fused_step(const moe_layer* layers, int n_layers, float* h, int T, const FusedRecord& rec,
                              void* ws, hipStream_t s);
 
+// Persistent single-token decode step (moe_persist.hip): the whole stack in
+// one launch after a set-up launch per 16 layers.  persist_covers says whether
+// a stack shape takes it; its workspace is persist_ws_bytes from offset 0.
+constexpr int kPsMaxLayers = 128;
+bool fused_step_persistent(const moe_layer& L0, int n_layers, int T);
+bool persist_covers(const moe_layer& L, int n_layers, int T);
+size_t persist_ws_bytes(int d, int f, int E);
+hipError_t launch_persist_step(const moe_layer* layers, int n_layers, float* h, const FusedRecord& rec, void* ws,
+                               hipStream_t s);
+
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 }  // namespace qre

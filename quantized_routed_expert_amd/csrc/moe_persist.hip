@@ -1,0 +1,845 @@
+// Persistent decode step for one token (moe_decode_stack at T = 1): every
+// layer of the stack in one launch, the analogue of the pages' fused
+// "device-planned MoE tail" with its "grouped kernels" (UD-IQ2_XS (L4 fix)
+// page, "What was changed"), re-planned for one MI355X.
+//
+// Each workgroup runs the layer loop.  Per layer its phases are:
+//   glue    the layer input x = bf16(r / sqrt(mean(r^2) + eps)) from the
+//           residual r (complete once every 64-column tile of the previous
+//           layer's combine has landed), kept in LDS as scaled fp16;
+//   router  the logit of expert w (workgroup w), from a router row issued
+//           before the wait for r;
+//   gate/up the shared expert's 16-row tiles (no routing needed), then the
+//           top-k over all logits (recomputed in LDS by each workgroup that
+//           needs it) and the routed experts' tiles; h = silu(g) * u in fp32;
+//   down    64 output rows of one slot (shared or routed pair j), once that
+//           slot's h row is complete; h is scaled by a power of two per row
+//           into fp16 hi/lo parts for the MFMA;
+//   combine the last workgroup of each 64-column tile forms
+//           y = o_shared + sum_j w_j o_j (slot order), the next residual and
+//           its sum of squares.
+// Dependencies between workgroups are monotonic counters in the workspace
+// (zeroed by the set-up launch before the step): logits written, gate/up
+// tiles per slot, down items per column tile, combined tiles.  Increments to
+// one address serialise in the memory system (measured: about 40 ns each), so
+// each event that many workgroups signal is counted on several sub-counters,
+// one 256-byte line each, and a waiting wavefront polls all of them in one
+// load instruction.  Waits poll with a bounded count; a wait that runs out
+// sets error bit 16 and an abort word that ends every other wait, so the grid
+// always drains.  The grid is at most the number of workgroups that fit on
+// the device at once, so every workgroup a wait depends on is running.
+//
+// Data passed between workgroups (logits, h rows, o rows, residual tiles and
+// their sums of squares) is written with agent-scope atomic stores and read
+// with loads carrying the same cache-coherence bits as agent-scope atomic
+// loads (sc1: they bypass the XCDs' private L2 caches; 16-byte buffer loads
+// where the data is contiguous); a producer waits for its stores to complete
+// (s_waitcnt) before its counter increment, and a consumer issues its loads
+// after observing the counter.  Weight codes that do not depend on a wait
+// (the next layer's router row and shared-expert tile, a down tile's codes)
+// are issued before it.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include "moe_dq.h"
+
+namespace qre {
+
+namespace {
+
+// Matrices of one layer in PsLayer::m
+enum { kGate = 0, kUp = 1, kDown = 2, kSGate = 3, kSUp = 4, kSDown = 5 };
+
+constexpr int kPsPD = 6;  // steps of weight codes issued up front per matrix (gate/up; down IQ4_NL / NVFP4)
+
+// Counters, one per 256-byte line.  Events signalled by many workgroups are
+// spread over sub-counters: arriver i of an event increments sub-counter
+// i % (that event's sub-counter count).
+constexpr int kLine = 64;  // int32 per line
+constexpr int kMaxSlots = 33;             // k <= 32 routed + shared
+constexpr int kSubLogit = 32;             // router workgroups, by index
+constexpr int kSubTiles = 8;              // combined column tiles, by tile
+constexpr int kSubSlot = 4;               // gate/up tiles of a slot, by tile
+constexpr int kLnLogit = 0;
+constexpr int kLnTiles = kLnLogit + kSubLogit;
+constexpr int kLnAbort = kLnTiles + kSubTiles;
+constexpr int kLnSlot = kLnAbort + 1;                   // kSubSlot lines per slot
+constexpr int kLnTileCnt = kLnSlot + kMaxSlots * kSubSlot;  // one line per column tile (d / 64 <= 64)
+constexpr int kNumCnt = kLnTileCnt + 64;
+
+constexpr uint32_t kSpinMax = 1u << 20;  // polls of one wait before it gives up
+constexpr int kSc1 = 16;                 // cache-policy bits of an agent-scope load (sc1)
+
+}  // namespace
+
+struct PsMat {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* ts;
+};
+
+struct PsLayer {
+  const float* router_w;
+  const float* bias;
+  PsMat m[6];
+};
+
+constexpr int kPsChunk = 16;  // layer descriptors per set-up launch
+
+struct PsArgs {
+  const PsLayer* layers;
+  int n_layers, d, f, E, k, hs;
+  float eps;
+  float* h;            // residual entering the stack, and leaving it
+  float* rbuf[2];      // residuals between layers (by parity)
+  float* ss[2];        // [d / 64] tile sums of squares of a residual (by parity)
+  float* logits[2];    // [E] router logits (by parity)
+  float* hrow;         // [k + hs][f] SwiGLU rows by slot (slot 0 = shared when present)
+  float* orow;         // [k + 1][d] down outputs: pair j at row j, shared at row k
+  int32_t* sync;       // kNumCnt lines of counters
+  float* rec_logits;   // optional records (see moe_stack_record)
+  int32_t* rec_idx;
+  float* rec_w;
+  uint16_t* rec_x;
+  float* rec_y;
+  int32_t* rec_err;
+  int32_t* err_ws;     // the error word when there are no per-layer records
+};
+
+__device__ __forceinline__ float ld_ag(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_ag(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// 16 bytes at byte offset `off` from the wavefront-uniform `base`, with the
+// cache-coherence bits of an agent-scope atomic load (a raw buffer load).
+__device__ __forceinline__ f32x4 ld_ag4(const float* base, int off) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7fffffff, 0x00020000);
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
+}
+
+// Every store of the workgroup has completed; then one increment of counter c
+// (no value returned, so the workgroup does not wait for it).
+__device__ __forceinline__ void ps_arrive(int32_t* c) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// As ps_arrive, returning the counter's value before the increment.
+__device__ __forceinline__ int ps_arrive_old(int32_t* c) {
+  __shared__ int s_old;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) s_old = atomicAdd(c, 1);
+  __syncthreads();
+  return s_old;
+}
+
+// Wait until an event with narr arrivers per epoch, counted on nsub
+// sub-counters (c + i * kLine, arriver j on sub-counter j % nsub), has reached
+// `epoch` full rounds.  Wavefront 0 polls every sub-counter in one load
+// instruction per round; the others wait at the barrier.  Returns false if the
+// wait ran out (error bit 16, abort word set) or another workgroup's did.
+__device__ __forceinline__ bool ps_wait(const int32_t* c, int nsub, int narr, int epoch, int32_t* abort_w,
+                                        int32_t* err) {
+  __shared__ int s_ok;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int per = lane < nsub ? max(0, (narr - lane + nsub - 1) / nsub) : 0;
+    const int need = per * epoch;
+    const int32_t* cl = c + min(lane, nsub - 1) * kLine;
+    int ok = 1;
+    uint32_t n = 0;
+    while (true) {
+      const int v = __hip_atomic_load(cl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__all(lane >= nsub || v >= need)) break;
+      if ((n & 15u) == 15u && __hip_atomic_load(abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+        ok = 0;
+        break;
+      }
+      if (++n > kSpinMax) {
+        if (lane == 0) {
+          atomicOr(err, 16);
+          __hip_atomic_store(abort_w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (lane == 0) s_ok = ok;
+  }
+  __syncthreads();
+  return s_ok != 0;
+}
+
+// Workgroup LDS of the persistent kernel.
+constexpr int kPsMaxD = 4096, kPsMaxF = 1024, kPsMaxE = 1024;
+struct PsLds {
+  f16 x16[kPsMaxD];                 // layer input, scaled fp16, in the gate/up weights' decode order
+  f16 hh[2][kPsMaxF];               // down: h of the slot as scaled fp16 hi / lo parts
+  f16 zero[kPsMaxF];                // A-operand rows that hold no column
+  uint8_t sc[2 * 16 * kPsMaxD / 16];  // scale rows of the current item
+  f32x4 red[4][2][64];              // K-split partial sums
+  float logit[kPsMaxE];
+  uint64_t tk_list[4][64];
+  uint32_t tk_max[32];
+  int32_t tk_cnt[4];
+  uint32_t tk_key[64];
+  int32_t tk_idx[64];
+  int32_t idx[32];                  // this layer's top-k, slot order
+  float wv[32];                     // ... their logits, then their gate weights
+  double pr[4];
+  float red1[8];
+  float xs;
+  int ex;
+};
+
+// One 16-row tile of the gate and up projections of one expert for the
+// single token (x16 in LDS): four wavefronts split K, each lane row n of the
+// tile and K slice G of every step; block-diagonal A operand (Q8_0, IQ4_NL)
+// or a dense one (NVFP4-style), as in the per-layer decode tile.
+// ps_gu_issue puts the tile's weight codes and scale rows in flight (they
+// need no activation); ps_gu_compute writes h[tile * 16 + n] =
+// silu(g) * u (fp32) of the rows.
+template <int FMT>
+struct GuCodes {
+  u32x4 c[2][kPsPD];  // codes of every step, gate and up
+  u32x4 s[2];         // 16-byte chunks of the tile's scale rows, this thread's
+  float ts[2];        // NVFP4-style tensor scales
+};
+
+template <int FMT>
+__device__ __forceinline__ void ps_gu_issue(const PsMat& Wg, const PsMat& Wu, int e, int tile, int K, int rows,
+                                            GuCodes<FMT>& g) {
+  constexpr int EPS = dq_eps(FMT);
+  constexpr int STEP_B = FMT == MOE_Q8_0 ? 4 * EPS : 2 * EPS;  // code bytes per step and row
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int n = lane & 15, G = lane >> 4;
+  const int kw = K / 4;
+  const int nsteps = kw / (4 * EPS);
+  const int crb = code_row_bytes(FMT, K), srb = scale_row_bytes(FMT, K);
+  const int kbase = wid * kw + G * EPS;
+  const long rw = (long)e * rows + tile * 16 + n;
+  const PsMat* W[2] = {&Wg, &Wu};
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const uint8_t* cl = W[m]->codes + rw * crb + (FMT == MOE_Q8_0 ? kbase : (kbase >> 1));
+#pragma unroll
+    for (int u = 0; u < kPsPD; ++u)
+      g.c[m][u] = __builtin_nontemporal_load((const u32x4*)(cl + min(u, nsteps - 1) * STEP_B));
+    g.ts[m] = FMT == MOE_NVFP4 ? W[m]->ts[e] : 1.0f;
+  }
+  // scale rows: 16 * srb bytes per matrix, contiguous; at most two chunks a thread
+  const int sch = srb;  // 16-byte chunks per matrix
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int ch = min(tid + 256 * b, 2 * sch - 1);
+    const int m = ch >= sch ? 1 : 0;
+    g.s[b] = __builtin_nontemporal_load(
+        (const u32x4*)(W[m]->scales + ((long)e * rows + tile * 16) * srb + (ch - m * sch) * 16));
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void ps_gu_compute(PsLds& S, const GuCodes<FMT>& g, int tile, int K, float* hout,
+                                              int32_t* err) {
+  constexpr int EPS = dq_eps(FMT);
+  constexpr int NMF = EPS / 8;
+  constexpr bool BD = FMT != MOE_NVFP4;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int n = lane & 15, G = lane >> 4;
+  const int kw = K / 4;
+  const int nsteps = kw / (4 * EPS);
+  const int srb = scale_row_bytes(FMT, K);
+  const int kbase = wid * kw + G * EPS;
+  const int sch = srb;
+  __syncthreads();  // the previous item is done with S.sc and S.red
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+    if (tid + 256 * b < 2 * sch) *(u32x4*)(S.sc + (tid + 256 * b) * 16) = g.s[b];
+  __syncthreads();
+  const bool valid = BD ? (n == 4 * G) : (n == 0);  // A rows holding the token's column
+  const f16* ap = valid ? S.x16 + kbase : S.zero;
+  const uint16_t* ssl[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) ssl[m] = (const uint16_t*)(S.sc + m * sch * 16 + n * srb) + (kbase >> 5);
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int s = 0; s < kPsPD; ++s) {
+    if (s < nsteps) {
+      f16x8 ac[NMF];
+#pragma unroll
+      for (int i = 0; i < NMF; ++i) ac[i] = *(const f16x8*)(ap + s * 4 * EPS + 8 * i);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const uint32_t ss = ssl[m][s * (4 * EPS / 32)];
+        f32x4 D = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NMF; ++i)
+          D = __builtin_amdgcn_mfma_f32_16x16x32_f16(ac[i], decode_b<FMT>(g.c[m][s], i, ss), D, 0, 0, 0);
+        if constexpr (FMT == MOE_NVFP4) {
+          acc[m] += D;
+        } else {
+          const float sc = f16_bits_to_f32(ss);
+          acc[m].x = fmaf(sc, D.x, acc[m].x);
+          acc[m].y = fmaf(sc, D.y, acc[m].y);
+          acc[m].z = fmaf(sc, D.z, acc[m].z);
+          acc[m].w = fmaf(sc, D.w, acc[m].w);
+        }
+      }
+    }
+    // one step's decoded weights at a time (the codes of every step are
+    // already in registers; decoding ahead would only hold more registers)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (BD) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      acc[m].x += __shfl_xor(acc[m].x, 16, 64);
+      acc[m].x += __shfl_xor(acc[m].x, 32, 64);
+    }
+  }
+  // the token's column is D row 0: element x of lanes n (group 0)
+  S.red[wid][0][lane] = acc[0];
+  S.red[wid][1][lane] = acc[1];
+  __syncthreads();
+  if (wid == 0 && G == 0) {
+    float gs = 0.f, us = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      gs += S.red[q][0][lane].x;
+      us += S.red[q][1][lane].x;
+    }
+    const float xs = S.xs;
+    gs = gs * g.ts[0] * xs;
+    us = us * g.ts[1] * xs;
+    const float hv = silu_f(gs) * us;
+    if (!(fabsf(hv) <= 3.0e38f)) atomicOr(err, 2);
+    st_ag(hout + tile * 16 + n, hv);
+  }
+}
+
+// 64 output rows [ct * 64, ct * 64 + 64) of the down projection of one
+// expert for the single token: h (staged in S.hh as hi / lo fp16 parts of
+// h * 2^-ex) is the A operand's two columns; each wavefront 16 rows over all
+// of K = f.  ps_dn_issue puts the codes and scale rows in flight;
+// ps_dn_compute writes o = (hi + lo) * 2^ex of the rows.
+template <int FMT>
+struct DnCodes {
+  u32x4 c[FMT == MOE_Q8_0 ? 2 * kPsPD : kPsPD];
+  u32x4 s;
+  float ts;
+};
+
+template <int FMT>
+__device__ __forceinline__ void ps_dn_issue(const PsMat& Wd, int e, int ct, int K, int rows, DnCodes<FMT>& g) {
+  constexpr int EPS = dq_eps(FMT);
+  constexpr int PD = FMT == MOE_Q8_0 ? 2 * kPsPD : kPsPD;
+  constexpr int STEP_B = FMT == MOE_Q8_0 ? 4 * EPS : 2 * EPS;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int n = lane & 15, G = lane >> 4;
+  const int nsteps = K / (4 * EPS);
+  const int crb = code_row_bytes(FMT, K), srb = scale_row_bytes(FMT, K);
+  const int kbase = G * EPS;
+  const int row = ct * 64 + wid * 16 + n;
+  const uint8_t* cl = Wd.codes + ((long)e * rows + row) * crb + (FMT == MOE_Q8_0 ? kbase : (kbase >> 1));
+#pragma unroll
+  for (int u = 0; u < PD; ++u) g.c[u] = __builtin_nontemporal_load((const u32x4*)(cl + min(u, nsteps - 1) * STEP_B));
+  const int sch = 64 * srb / 16;  // at most 256: one chunk a thread
+  g.s = __builtin_nontemporal_load(
+      (const u32x4*)(Wd.scales + ((long)e * rows + ct * 64) * srb + min(tid, sch - 1) * 16));
+  g.ts = FMT == MOE_NVFP4 ? Wd.ts[e] : 1.0f;
+}
+
+template <int FMT>
+__device__ __forceinline__ void ps_dn_compute(PsLds& S, const DnCodes<FMT>& g, int ct, int K, float hscale,
+                                              float* oout) {
+  constexpr int EPS = dq_eps(FMT);
+  constexpr int NMF = EPS / 8;
+  constexpr bool BD = FMT != MOE_NVFP4;
+  constexpr int PD = FMT == MOE_Q8_0 ? 2 * kPsPD : kPsPD;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int n = lane & 15, G = lane >> 4;
+  const int nsteps = K / (4 * EPS);
+  const int srb = scale_row_bytes(FMT, K);
+  const int kbase = G * EPS;
+  const int row = ct * 64 + wid * 16 + n;
+  const int sch = 64 * srb / 16;
+  if (tid < sch) *(u32x4*)(S.sc + tid * 16) = g.s;  // (S.sc is free: the caller's barrier after staging h)
+  __syncthreads();
+  // columns: hi (0) and lo (1)
+  int c;
+  bool valid;
+  if constexpr (BD) {
+    valid = (n >> 2) == G && (n & 3) < 2;
+    c = n & 3;
+  } else {
+    valid = n < 2;
+    c = n;
+  }
+  const f16* ap = valid ? S.hh[c] + kbase : S.zero;
+  const uint16_t* ssl = (const uint16_t*)(S.sc + (wid * 16 + n) * srb) + (kbase >> 5);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < PD; ++s) {
+    if (s < nsteps) {
+      const uint32_t ss = ssl[s * (4 * EPS / 32)];
+      f32x4 D = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < NMF; ++i) {
+        const f16x8 a8 = *(const f16x8*)(ap + s * 4 * EPS + 8 * i);
+        D = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, decode_b<FMT>(g.c[s], i, ss), D, 0, 0, 0);
+      }
+      if constexpr (FMT == MOE_NVFP4) {
+        acc += D;
+      } else {
+        const float sc = f16_bits_to_f32(ss);
+        acc.x = fmaf(sc, D.x, acc.x);
+        acc.y = fmaf(sc, D.y, acc.y);
+        acc.z = fmaf(sc, D.z, acc.z);
+        acc.w = fmaf(sc, D.w, acc.w);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (BD) {
+    acc.x += __shfl_xor(acc.x, 16, 64);
+    acc.y += __shfl_xor(acc.y, 16, 64);
+    acc.x += __shfl_xor(acc.x, 32, 64);
+    acc.y += __shfl_xor(acc.y, 32, 64);
+  }
+  // D rows 0 and 1 (the hi and lo columns) of lanes n in group 0
+  if (G == 0) st_ag(oout + row, (acc.x * g.ts + acc.y * g.ts) * hscale);
+}
+
+// Glue of one token: x = bf16(r / sqrt(sum(r^2) / d + eps)), with the sum of
+// squares from the previous layer's tile sums (or from r itself for the first
+// layer).  Thread tid holds elements (q * 256 + tid) * 4 .. + 3 for q < d /
+// 1024 (as floats of the bf16 values, for the router); writes the scaled fp16
+// copy (gate weights' decode order) and its scale to LDS, and the bf16 record.
+__device__ __forceinline__ void ps_glue(PsLds& S, const float* r, const float* ssp, int d, float eps, int gate_fmt,
+                                        uint16_t* rec_x, f32x4 (&xv)[4]) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nq = d / 1024;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (q < nq) xv[q] = ld_ag4(r, (q * 256 + tid) * 16);
+  float tot;
+  if (ssp) {
+    const float v = lane < d / 64 ? ld_ag(ssp + lane) : 0.0f;
+    tot = wave_sum(v);  // every wavefront sums the tiles in the same order
+  } else {
+    float ss = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (q < nq) ss += xv[q].x * xv[q].x + xv[q].y * xv[q].y + xv[q].z * xv[q].z + xv[q].w * xv[q].w;
+    ss = wave_sum(ss);
+    if (lane == 0) S.red1[wid] = ss;
+    __syncthreads();
+    tot = S.red1[0] + S.red1[1] + S.red1[2] + S.red1[3];
+  }
+  const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+  float mx = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (q < nq) {
+      const uint32_t p0 = pack_bf16x2(xv[q].x * inv, xv[q].y * inv);
+      const uint32_t p1 = pack_bf16x2(xv[q].z * inv, xv[q].w * inv);
+      xv[q] = f32x4{bf16_bits_to_f32(p0 & 0xffffu), bf16_bits_to_f32(p0 >> 16), bf16_bits_to_f32(p1 & 0xffffu),
+                    bf16_bits_to_f32(p1 >> 16)};
+      if (rec_x) *(u32x2*)(rec_x + (q * 256 + tid) * 4) = u32x2{p0, p1};
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xv[q].x), fabsf(xv[q].y)), fmaxf(fabsf(xv[q].z), fabsf(xv[q].w))));
+    }
+  }
+  mx = wave_max(mx);
+  if (lane == 0) S.red1[4 + wid] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(S.red1[4], S.red1[5]), fmaxf(S.red1[6], S.red1[7]));
+  const int ex = x16_exponent(mx);
+  const float down = ldexpf(1.0f, -ex);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (q < nq) {
+      const int i = (q * 256 + tid) * 4;
+      S.x16[act_pos(gate_fmt, i + 0)] = (f16)(xv[q].x * down);
+      S.x16[act_pos(gate_fmt, i + 1)] = (f16)(xv[q].y * down);
+      S.x16[act_pos(gate_fmt, i + 2)] = (f16)(xv[q].z * down);
+      S.x16[act_pos(gate_fmt, i + 3)] = (f16)(xv[q].w * down);
+    }
+  }
+  if (tid == 0) S.xs = ldexpf(1.0f, ex);
+  __syncthreads();
+}
+
+// Router row of expert e, the part this thread multiplies: elements
+// (q * 256 + tid) * 4 .. + 3 (the glue's), one 16-byte load per q.
+__device__ __forceinline__ void ps_router_load(const float* Wr, int e, int d, f32x4 (&wv)[4]) {
+  const int nq = d / 1024;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (q < nq) wv[q] = __builtin_nontemporal_load((const f32x4*)(Wr + (long)e * d + (q * 256 + threadIdx.x) * 4));
+}
+
+// logit = fp32(sum_i W[e][i] x[i] + b[e]) with fp64 sums of the exact products.
+__device__ __forceinline__ float ps_router_dot(PsLds& S, const f32x4 (&wv)[4], const f32x4 (&xv)[4], int d,
+                                               float bias) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int nq = d / 1024;
+  double acc = 0.0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (q < nq)
+      acc += (double)wv[q].x * (double)xv[q].x + (double)wv[q].y * (double)xv[q].y +
+             (double)wv[q].z * (double)xv[q].z + (double)wv[q].w * (double)xv[q].w;
+  acc = wave_sum_f64(acc);
+  if (lane == 0) S.pr[wid] = acc;
+  __syncthreads();
+  const double r = ((S.pr[0] + S.pr[1]) + S.pr[2]) + S.pr[3];
+  __syncthreads();  // S.pr may be reused
+  return (float)(r + (double)bias);
+}
+
+template <int GF, int DF>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_ps_decode(const PsArgs a) {
+  __shared__ PsLds S;
+  pin_arg(a.layers);
+  pin_arg(a.h);
+  pin_arg(a.hrow);
+  pin_arg(a.orow);
+  pin_arg(a.sync);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int G = gridDim.x, w = blockIdx.x;
+  const int d = a.d, f = a.f, E = a.E, k = a.k, hs = a.hs, L = a.n_layers;
+  const int nS = k + hs;
+  const int gu_per = f / 16, dn_per = d / 64;
+  const int gu_total = nS * gu_per, dn_total = nS * dn_per;
+  const int n_router = min(G, E);
+  const bool has_x = w < E || w < gu_total;
+  const bool has_routed_gu = [&] {
+    for (int it = w; it < gu_total; it += G)
+      if (it / gu_per >= hs) return true;
+    return false;
+  }();
+  const bool needs_topk = w == 0 || has_routed_gu || w < dn_total;
+  // this workgroup's first gate/up item is a shared-expert tile (tile w): its
+  // codes are issued before the wait for each layer's input
+  const bool pre_sh = hs && w < gu_per;
+  int32_t* sync = a.sync;
+  int32_t* abort_w = sync + kLnAbort * kLine;
+
+  for (int i = tid; i < kPsMaxF; i += 256) S.zero[i] = (f16)0.0f;
+
+  f32x4 wv[4];
+  if (w < E) ps_router_load(a.layers[0].router_w, w, d, wv);
+  GuCodes<GF> gsh;
+  if (pre_sh) ps_gu_issue<GF>(a.layers[0].m[kSGate], a.layers[0].m[kSUp], 0, w, d, f, gsh);
+
+  for (int l = 0; l < L; ++l) {
+    const PsLayer& P = a.layers[l];
+    int32_t* err = a.rec_err ? a.rec_err + l : a.err_ws;
+    const float* r_in = l == 0 ? a.h : a.rbuf[l & 1];
+    float* r_out = l == L - 1 ? a.h : a.rbuf[(l + 1) & 1];
+    float* lg = a.logits[l & 1];
+
+    // ---- glue and router
+    if (has_x) {
+      if (l > 0 && !ps_wait(sync + kLnTiles * kLine, kSubTiles, dn_per, l, abort_w, err)) return;
+      f32x4 xv[4];
+      ps_glue(S, r_in, l == 0 ? nullptr : a.ss[l & 1], d, a.eps, GF,
+              (w == 0 && a.rec_x) ? a.rec_x + (long)l * d : nullptr, xv);
+      for (int e = w; e < E; e += G) {
+        if (e != w) ps_router_load(P.router_w, e, d, wv);
+        const float bias = P.bias ? P.bias[e] : 0.0f;
+        const float v = ps_router_dot(S, wv, xv, d, bias);
+        if (tid == 0) {
+          st_ag(lg + e, v);
+          if (a.rec_logits) a.rec_logits[(long)l * E + e] = v;
+        }
+      }
+      if (w < E) ps_arrive(sync + (kLnLogit + w % kSubLogit) * kLine);
+    }
+
+    // ---- gate/up of the shared expert (slot 0), which needs no routing
+    for (int it = w; it < gu_total && it / gu_per < hs; it += G) {
+      if (!(it == w && pre_sh)) ps_gu_issue<GF>(P.m[kSGate], P.m[kSUp], 0, it % gu_per, d, f, gsh);
+      ps_gu_compute<GF>(S, gsh, it % gu_per, d, a.hrow, err);
+      ps_arrive(sync + (kLnSlot + (it % gu_per) % kSubSlot) * kLine);
+    }
+
+    // ---- top-k and gate weights (every workgroup that needs them)
+    if (needs_topk) {
+      if (!ps_wait(sync + kLnLogit * kLine, kSubLogit, n_router, l + 1, abort_w, err)) return;
+      for (int i4 = tid; i4 * 4 < E; i4 += 256) {
+        const f32x4 v = ld_ag4(lg, i4 * 16);  // (the buffer is padded past E)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (i4 * 4 + c < E) S.logit[i4 * 4 + c] = v[c];
+      }
+      __syncthreads();
+      wg_topk1<16>(S.logit, E, k, S.tk_max, S.tk_list, S.tk_cnt, S.tk_key, S.tk_idx, S.idx, S.wv);
+      if (wid == 0) {
+        const float v = lane < k ? S.wv[lane] : 0.0f;
+        const float vmax = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 0));
+        const float ex = lane < k ? expf(v - vmax) : 0.0f;
+        const float sum = wave_sum(ex);
+        if (lane < k) {
+          S.wv[lane] = ex / sum;
+          if (w == 0 && a.rec_idx) a.rec_idx[(long)l * k + lane] = S.idx[lane];
+          if (w == 0 && a.rec_w) a.rec_w[(long)l * k + lane] = ex / sum;
+        }
+      }
+      __syncthreads();
+    }
+
+    // ---- gate/up of the routed experts: slot hs + j holds pair j
+    for (int it = w; it < gu_total; it += G) {
+      const int slot = it / gu_per;
+      if (slot < hs) continue;
+      GuCodes<GF> g;
+      ps_gu_issue<GF>(P.m[kGate], P.m[kUp], S.idx[slot - hs], it % gu_per, d, f, g);
+      ps_gu_compute<GF>(S, g, it % gu_per, d, a.hrow + (long)slot * f, err);
+      ps_arrive(sync + (kLnSlot + slot * kSubSlot + (it % gu_per) % kSubSlot) * kLine);
+    }
+
+    // ---- down, and the combine of each finished 64-column tile
+    for (int it = w; it < dn_total; it += G) {
+      const int slot = it / dn_per, ct = it % dn_per;
+      const bool sh = slot < hs;
+      DnCodes<DF> g;
+      ps_dn_issue<DF>(sh ? P.m[kSDown] : P.m[kDown], sh ? 0 : S.idx[slot - hs], ct, f, d, g);
+      if (!ps_wait(sync + (kLnSlot + slot * kSubSlot) * kLine, kSubSlot, gu_per, l + 1, abort_w, err)) return;
+      // the slot's h row, scaled by a power of two into fp16 hi / lo parts
+      const float* hr = a.hrow + (long)slot * f;
+      const f32x4 hv = tid * 4 < f ? ld_ag4(hr, tid * 16) : f32x4{0.f, 0.f, 0.f, 0.f};
+      float mx = fmaxf(fmaxf(fabsf(hv.x), fabsf(hv.y)), fmaxf(fabsf(hv.z), fabsf(hv.w)));
+      mx = wave_max(mx);
+      __syncthreads();  // the previous item is done with S.hh, S.sc and S.red1
+      if (lane == 0) S.red1[wid] = mx;
+      __syncthreads();
+      mx = fmaxf(fmaxf(S.red1[0], S.red1[1]), fmaxf(S.red1[2], S.red1[3]));
+      const int ex = x16_exponent(mx);
+      const float down = ldexpf(1.0f, -ex);
+      if (tid * 4 < f) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float sv = hv[c] * down;
+          const f16 hi = (f16)sv;
+          const int pos = act_pos(DF, tid * 4 + c);
+          S.hh[0][pos] = hi;
+          S.hh[1][pos] = (f16)(sv - (float)hi);
+        }
+      }
+      const int pair = sh ? k : slot - hs;
+      ps_dn_compute<DF>(S, g, ct, f, ldexpf(1.0f, ex), a.orow + (long)pair * d);
+      const int old = ps_arrive_old(sync + (kLnTileCnt + ct) * kLine);
+      if (old == nS * (l + 1) - 1) {
+        // the last of the tile's nS down items: combine the tile
+        if (wid == 0) {
+          const int col = ct * 64 + lane;
+          float y = hs ? ld_ag(a.orow + (long)k * d + col) : 0.0f;
+          float oj[32];
+#pragma unroll
+          for (int j = 0; j < 32; ++j)
+            if (j < k) oj[j] = ld_ag(a.orow + (long)j * d + col);
+#pragma unroll
+          for (int j = 0; j < 32; ++j)
+            if (j < k) y = fmaf(S.wv[j], oj[j], y);
+          const float rn = ld_ag(r_in + col) + y;
+          st_ag(r_out + col, rn);
+          if (a.rec_y) a.rec_y[(long)l * d + col] = y;
+          const float ss = wave_sum(rn * rn);
+          if (lane == 0) st_ag(a.ss[(l + 1) & 1] + ct, ss);
+        }
+        ps_arrive(sync + (kLnTiles + ct % kSubTiles) * kLine);
+      }
+    }
+
+    // ---- the next layer's router row and shared-expert tile, in flight
+    // while the residual forms
+    if (l + 1 < L) {
+      if (w < E) ps_router_load(a.layers[l + 1].router_w, w, d, wv);
+      if (pre_sh) ps_gu_issue<GF>(a.layers[l + 1].m[kSGate], a.layers[l + 1].m[kSUp], 0, w, d, f, gsh);
+    }
+  }
+}
+
+// Set-up launch: the layer descriptors of one chunk into the workspace table;
+// the first chunk also clears the counters and the error words.
+struct PsSetupArgs {
+  PsLayer L[kPsChunk];
+  int l0, count;
+  PsLayer* table;
+  int32_t* sync;
+  int32_t* rec_err;
+  int n_layers;
+  int32_t* err_ws;
+};
+
+__global__ __launch_bounds__(256) void k_ps_setup(const PsSetupArgs s) {
+  const int tid = threadIdx.x;
+  if (tid < s.count) s.table[s.l0 + tid] = s.L[tid];
+  if (s.l0 == 0) {
+    for (int i = tid; i < kNumCnt * kLine; i += 256) s.sync[i] = 0;  // (all counter lines)
+    if (s.rec_err)
+      for (int i = tid; i < s.n_layers; i += 256) s.rec_err[i] = 0;
+    if (tid == 0) *s.err_ws = 0;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// host side
+// ----------------------------------------------------------------------------
+
+namespace {
+
+struct PsWs {
+  PsLayer* table;
+  int32_t* sync;
+  int32_t* err_ws;
+  float* rbuf[2];
+  float* ss[2];
+  float* logits[2];
+  float* hrow;
+  float* orow;
+};
+
+PsWs carve_ps(void* ws, int d, int f, int E) {
+  char* p = (char*)ws;
+  PsWs W;
+  W.table = (PsLayer*)p;
+  p += align_up((size_t)kPsMaxLayers * sizeof(PsLayer), 256);
+  W.sync = (int32_t*)p;
+  p += align_up((size_t)kNumCnt * kLine * 4, 256);
+  W.err_ws = (int32_t*)p;
+  p += 256;
+  for (int i = 0; i < 2; ++i) {
+    W.rbuf[i] = (float*)p;
+    p += align_up((size_t)d * 4, 256);
+    W.ss[i] = (float*)p;
+    p += align_up((size_t)(d / 64) * 4, 256);
+    W.logits[i] = (float*)p;
+    p += align_up((size_t)E * 4, 256);
+  }
+  W.hrow = (float*)p;
+  p += align_up((size_t)kMaxSlots * f * 4, 256);
+  W.orow = (float*)p;
+  return W;
+}
+
+PsMat ps_mat(const moe_qmatrix& m) { return PsMat{(const uint8_t*)m.codes, (const uint8_t*)m.scales, m.tensor_scale}; }
+
+// The grid is at most the workgroups resident at once, so that every
+// workgroup a wait depends on is running.  With timing events, the launch
+// carries them (its own start and end).
+template <int GF, int DF>
+hipError_t launch_ps(const PsArgs& a, int need, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  auto kern = k_ps_decode<GF, DF>;
+  const int res = resident_wgs(kern, 0);
+  if (res <= 0) return hipErrorInvalidConfiguration;
+  const int grid = need < res ? need : res;
+  if (e0)
+    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, e0, e1, 0, a);
+  else
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int GF>
+hipError_t launch_ps_d(int df, const PsArgs& a, int need, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  switch (df) {
+    case MOE_Q8_0: return launch_ps<GF, MOE_Q8_0>(a, need, s, e0, e1);
+    case MOE_IQ4_NL: return launch_ps<GF, MOE_IQ4_NL>(a, need, s, e0, e1);
+    default: return launch_ps<GF, MOE_NVFP4>(a, need, s, e0, e1);
+  }
+}
+
+}  // namespace
+
+size_t persist_ws_bytes(int d, int f, int E) {
+  return align_up((size_t)kPsMaxLayers * sizeof(PsLayer), 256) + align_up((size_t)kNumCnt * kLine * 4, 256) + 256 +
+         2 * (align_up((size_t)d * 4, 256) + align_up((size_t)(d / 64) * 4, 256) + align_up((size_t)E * 4, 256)) +
+         align_up((size_t)kMaxSlots * f * 4, 256) + align_up((size_t)kMaxSlots * d * 4, 256);
+}
+
+bool persist_covers(const moe_layer& L, int n_layers, int T) {
+  if (T != 1 || n_layers > kPsMaxLayers) return false;
+  if (L.d % 1024 != 0 || L.d > kPsMaxD || L.E > kPsMaxE || L.k > 32) return false;
+  if (L.f % 128 != 0 || L.f > kPsMaxF) return false;
+  // every step's codes issued up front: gate/up K / 4, down K = f
+  const int eg = dq_eps(L.gate.type), ed = dq_eps(L.down.type);
+  if (L.d / 4 / (4 * eg) > kPsPD) return false;
+  if (L.f / (4 * ed) > (L.down.type == MOE_Q8_0 ? 2 * kPsPD : kPsPD)) return false;
+  return true;
+}
+
+hipError_t launch_persist_step(const moe_layer* layers, int n_layers, float* h, const FusedRecord& rec, void* ws,
+                               hipStream_t s) {
+  const moe_layer& L0 = layers[0];
+  PsWs W = carve_ps(ws, L0.d, L0.f, L0.E);
+  for (int l0 = 0; l0 < n_layers; l0 += kPsChunk) {
+    PsSetupArgs sa{};
+    sa.l0 = l0;
+    sa.count = n_layers - l0 < kPsChunk ? n_layers - l0 : kPsChunk;
+    for (int i = 0; i < sa.count; ++i) {
+      const moe_layer& L = layers[l0 + i];
+      PsLayer& P = sa.L[i];
+      P.router_w = L.router_w;
+      P.bias = L.router_bias;
+      P.m[kGate] = ps_mat(L.gate);
+      P.m[kUp] = ps_mat(L.up);
+      P.m[kDown] = ps_mat(L.down);
+      if (L.has_shared) {
+        P.m[kSGate] = ps_mat(L.shared_gate);
+        P.m[kSUp] = ps_mat(L.shared_up);
+        P.m[kSDown] = ps_mat(L.shared_down);
+      }
+    }
+    sa.table = W.table;
+    sa.sync = W.sync;
+    sa.rec_err = rec.error;
+    sa.n_layers = n_layers;
+    sa.err_ws = W.err_ws;
+    hipLaunchKernelGGL(k_ps_setup, dim3(1), dim3(256), 0, s, sa);
+  }
+  PsArgs a{};
+  a.layers = W.table;
+  a.n_layers = n_layers;
+  a.d = L0.d;
+  a.f = L0.f;
+  a.E = L0.E;
+  a.k = L0.k;
+  a.hs = L0.has_shared ? 1 : 0;
+  a.eps = rec.eps;
+  a.h = h;
+  for (int i = 0; i < 2; ++i) {
+    a.rbuf[i] = W.rbuf[i];
+    a.ss[i] = W.ss[i];
+    a.logits[i] = W.logits[i];
+  }
+  a.hrow = W.hrow;
+  a.orow = W.orow;
+  a.sync = W.sync;
+  a.rec_logits = rec.logits;
+  a.rec_idx = rec.topk_idx;
+  a.rec_w = rec.topk_w;
+  a.rec_x = rec.x;
+  a.rec_y = rec.y;
+  a.rec_err = rec.error;
+  a.err_ws = W.err_ws;
+  const int nS = L0.k + a.hs;
+  int need = L0.E;
+  need = need > nS * (L0.f / 16) ? need : nS * (L0.f / 16);
+  need = need > nS * (L0.d / 64) ? need : nS * (L0.d / 64);
+  hipEvent_t e0 = rec.events ? rec.events[0] : nullptr, e1 = rec.events ? rec.events[1] : nullptr;
+  switch (L0.gate.type) {
+    case MOE_Q8_0: return launch_ps_d<MOE_Q8_0>(L0.down.type, a, need, s, e0, e1);
+    case MOE_IQ4_NL: return launch_ps_d<MOE_IQ4_NL>(L0.down.type, a, need, s, e0, e1);
+    default: return launch_ps_d<MOE_NVFP4>(L0.down.type, a, need, s, e0, e1);
+  }
+}
+
+}  // namespace qre

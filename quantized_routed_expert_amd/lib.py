@@ -36,6 +36,7 @@ DTYPE = {"f32": MOE_F32, "bf16": MOE_BF16}
 EXPORTED = ["moe_route", "moe_plan", "moe_ffn_forward", "moe_ffn_prepare", "moe_ffn_gateup", "moe_ffn_down",
             "moe_ffn_combine", "moe_dequantize", "moe_residual_rmsnorm", "moe_decode_stack",
             "moe_decode_stack_workspace_size", "moe_decode_stack_noalloc", "moe_decode_stack_scratch_bytes",
+            "moe_decode_stack_persistent",
             "moe_workspace_size", "moe_status_string", "moe_version"]
 
 
@@ -89,6 +90,7 @@ def _load():
         "moe_decode_stack_workspace_size": (sz, [LP, i32]),
         "moe_decode_stack_noalloc": (i32, [LP, i32, vp, i32, ctypes.c_float, ctypes.POINTER(StackRecord), vp]),
         "moe_decode_stack_scratch_bytes": (sz, []),
+        "moe_decode_stack_persistent": (i32, [LP, i32, i32]),
         "moe_workspace_size": (sz, [LP, i32]),
         "moe_status_string": (ctypes.c_char_p, [i32]),
         "moe_version": (ctypes.c_char_p, []),
@@ -280,6 +282,11 @@ def moe_decode_stack_noalloc(layers, n_layers, h, T, eps, rec, stream=None):
     st = _lib.moe_decode_stack_noalloc(layers, int(n_layers), _ptr(h), int(T), float(eps),
                                        ctypes.byref(rec) if rec is not None else None, _stream(stream))
     _check(st, "moe_decode_stack_noalloc")
+
+
+def moe_decode_stack_persistent(layers, n_layers, T):
+    """True if moe_decode_stack runs this stack as one persistent launch."""
+    return bool(_lib.moe_decode_stack_persistent(layers, int(n_layers), int(T)))
 
 
 def moe_decode_stack_scratch_bytes():

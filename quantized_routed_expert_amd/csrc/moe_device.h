@@ -19,6 +19,7 @@ typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __attribute__((ext_vector_type(4))) int32_t i32x4;
@@ -110,6 +111,21 @@ __device__ __forceinline__ f16x8 iq4_dword_to_f16x8(uint32_t w) {
   return __builtin_bit_cast(f16x8, r);
 }
 
+// The same eight values plus 1152, exactly (the fp16 numbers 1024 + u for the
+// biased bytes u = value + 128): two operations fewer per pair.  A product sum
+// over these weights exceeds the true one by 1152 times the sum of the
+// activations it covers, which the caller subtracts once.
+__device__ __forceinline__ f16x8 iq4_dword_to_f16x8_p1152(uint32_t w) {
+  const uint32_t ulo = iq4_lookup4(w & 0x0F0F0F0Fu);
+  const uint32_t uhi = iq4_lookup4((w >> 4) & 0x0F0F0F0Fu);
+  u32x4 r;
+  r.x = __builtin_amdgcn_perm(0x64646464u, ulo, 0x04010400u);
+  r.y = __builtin_amdgcn_perm(0x64646464u, ulo, 0x04030402u);
+  r.z = __builtin_amdgcn_perm(0x64646464u, uhi, 0x04010400u);
+  r.w = __builtin_amdgcn_perm(0x64646464u, uhi, 0x04030402u);
+  return __builtin_bit_cast(f16x8, r);
+}
+
 // Position of block element e (0..31) in the IQ4_NL activation layout that
 // matches iq4_dword_to_f16x8: code dword i covers positions 8i..8i+7.
 __device__ __forceinline__ int iq4_pos(int e) {
@@ -147,6 +163,14 @@ __device__ __forceinline__ u32x2 q8_dword_to_f16x4(uint32_t w) {
 __device__ __forceinline__ f16x8 q8_dwords_to_f16x8(uint32_t a, uint32_t b) {
   const u32x2 x = q8_dword_to_f16x4(a), y = q8_dword_to_f16x4(b);
   u32x4 r = {x.x, x.y, y.x, y.y};
+  return __builtin_bit_cast(f16x8, r);
+}
+
+// Eight int8 codes plus 1152, exactly (as iq4_dword_to_f16x8_p1152).
+__device__ __forceinline__ f16x8 q8_dwords_to_f16x8_p1152(uint32_t a, uint32_t b) {
+  const uint32_t ua = a ^ 0x80808080u, ub = b ^ 0x80808080u;
+  u32x4 r = {__builtin_amdgcn_perm(0x64646464u, ua, 0x04010400u), __builtin_amdgcn_perm(0x64646464u, ua, 0x04030402u),
+             __builtin_amdgcn_perm(0x64646464u, ub, 0x04010400u), __builtin_amdgcn_perm(0x64646464u, ub, 0x04030402u)};
   return __builtin_bit_cast(f16x8, r);
 }
 
@@ -462,6 +486,85 @@ __device__ __forceinline__ void wg_topk1(const float* __restrict__ L, int E, int
     }
   } else if (wid == 0) {
     wave_topk<NPL>(L, E, k, lane, tk_key, tk_idx, out_idx, out_val);
+  }
+  __syncthreads();
+}
+
+// Top-k of one token's logits L[0..E) by a whole workgroup of 256 threads
+// (E <= 256 * PT, 1 <= k <= 32), with the result of wave_topk: slot j < k in
+// out_idx[j] / out_val[j], descending logit, the lower expert id first on
+// ties.  Thread t holds entries t + 256 i.  The threshold tau is the k-th
+// largest of 32 group maxima (groups of 8 threads), found by k rounds of a
+// wavefront maximum that each remove one copy; the k group maxima at or
+// above tau are k entries, so every selected entry is >= tau.  The entries >=
+// tau (typically a few more than k) are compacted into one LDS list of
+// 64-bit keys (the order-preserving logit key, then the complement of the
+// expert id: no two keys are equal), and wavefront 0 ranks them.  If more
+// than 64 entries pass (heavy ties), wavefront 0 runs wave_topk instead.
+// Ends with a barrier, after which the result is visible to every wavefront.
+template <int PT>
+__device__ __forceinline__ void wg_topk_tau(const float* __restrict__ L, int E, int k, uint32_t* smax /*[32]*/,
+                                           uint64_t* list /*[64]*/, int32_t* cnt /*[4]*/, uint32_t* tk_key,
+                                           int32_t* tk_idx, int32_t* out_idx, float* out_val) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  uint32_t key[PT];
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    const int e = tid + 256 * i;
+    key[i] = topk_key32(L[min(e, E - 1)]) & (e < E ? 0xffffffffu : 0u);
+  }
+  uint32_t gm = key[0];
+#pragma unroll
+  for (int i = 1; i < PT; ++i) gm = max(gm, key[i]);
+  gm = max(gm, dpp_u32<kDppShr1, 0xf>(gm));
+  gm = max(gm, dpp_u32<kDppShr2, 0xf>(gm));
+  gm = max(gm, dpp_u32<kDppShr4, 0xf>(gm));
+  if ((lane & 7) == 7) smax[tid >> 3] = gm;  // the group's last thread holds its maximum
+  __syncthreads();
+  // every wavefront finds tau itself (no further barrier)
+  uint32_t v = lane < 32 ? smax[lane] : 0u;
+  uint32_t tau = 0u;
+  for (int r = 0; r < k; ++r) {
+    tau = wave_max_u32(v);
+    const uint64_t hm = __ballot(v == tau);
+    if (lane == (int)__builtin_ctzll(hm)) v = 0u;
+  }
+  int c = 0;
+  uint64_t mk[PT];
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    mk[i] = __ballot(key[i] != 0u && key[i] >= tau);
+    c += __popcll(mk[i]);
+  }
+  if (lane == 0) cnt[wid] = c;
+  __syncthreads();
+  const int c0 = cnt[0], c1 = cnt[1], c2 = cnt[2], c3 = cnt[3];
+  const int C = c0 + c1 + c2 + c3;
+  if (C <= 64) {
+    int pos = wid == 0 ? 0 : (wid == 1 ? c0 : (wid == 2 ? c0 + c1 : c0 + c1 + c2));
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int p = pos + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mk[i] >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mk[i], 0u));
+      if ((mk[i] >> lane) & 1ull) list[p] = ((uint64_t)key[i] << 32) | (uint32_t)~(uint32_t)(tid + 256 * i);
+      pos += __popcll(mk[i]);
+    }
+    __syncthreads();
+    if (wid == 0) {
+      const uint64_t kl = lane < C ? list[lane] : 0ull;
+      int rank = 0;
+      for (int j = 0; j < C; ++j) {
+        const uint64_t kj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(kl >> 32), j) << 32) |
+                            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)kl, j);
+        rank += kj > kl ? 1 : 0;
+      }
+      if (lane < C && rank < k) {
+        out_idx[rank] = (int32_t)~(uint32_t)kl;
+        out_val[rank] = topk_key32_value((uint32_t)(kl >> 32));
+      }
+    }
+  } else if (wid == 0) {
+    wave_topk<PT * 4>(L, E, k, lane, tk_key, tk_idx, out_idx, out_val);
   }
   __syncthreads();
 }

@@ -176,6 +176,15 @@ __device__ __forceinline__ bool ps_wait(const int32_t* c, int nsub, int narr, in
   return s_ok != 0;
 }
 
+// threadIdx.x, recomputed where it is used: values derived from it are then
+// formed inside the layer loop instead of being hoisted out of it and held
+// in registers for the whole kernel.
+__device__ __forceinline__ int ps_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // Workgroup LDS of the persistent kernel.
 constexpr int kPsMaxD = 4096, kPsMaxF = 1024, kPsMaxE = 1024;
 struct PsLds {
@@ -183,7 +192,9 @@ struct PsLds {
   f16 hh[2][kPsMaxF];               // down: h of the slot as scaled fp16 hi / lo parts
   f16 zero[kPsMaxF];                // A-operand rows that hold no column
   uint8_t sc[2 * 16 * kPsMaxD / 16];  // scale rows of the current item
-  f32x4 red[4][2][64];              // K-split partial sums
+  float red[4][2][64];              // K-split partial sums (the token's column)
+  float xsum[kPsMaxD / 16];         // sums of x16 over each EPS-element chunk (decode order)
+  float hsum[2][kPsMaxF / 16];      // the same for the hi / lo parts of h
   float logit[kPsMaxE];
   uint64_t tk_list[4][64];
   uint32_t tk_max[32];
@@ -217,7 +228,7 @@ __device__ __forceinline__ void ps_gu_issue(const PsMat& Wg, const PsMat& Wu, in
                                             GuCodes<FMT>& g) {
   constexpr int EPS = dq_eps(FMT);
   constexpr int STEP_B = FMT == MOE_Q8_0 ? 4 * EPS : 2 * EPS;  // code bytes per step and row
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = ps_tid(), lane = tid & 63, wid = tid >> 6;
   const int n = lane & 15, G = lane >> 4;
   const int kw = K / 4;
   const int nsteps = kw / (4 * EPS);
@@ -225,15 +236,9 @@ __device__ __forceinline__ void ps_gu_issue(const PsMat& Wg, const PsMat& Wu, in
   const int kbase = wid * kw + G * EPS;
   const long rw = (long)e * rows + tile * 16 + n;
   const PsMat* W[2] = {&Wg, &Wu};
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const uint8_t* cl = W[m]->codes + rw * crb + (FMT == MOE_Q8_0 ? kbase : (kbase >> 1));
-#pragma unroll
-    for (int u = 0; u < kPsPD; ++u)
-      g.c[m][u] = __builtin_nontemporal_load((const u32x4*)(cl + min(u, nsteps - 1) * STEP_B));
-    g.ts[m] = FMT == MOE_NVFP4 ? W[m]->ts[e] : 1.0f;
-  }
-  // scale rows: 16 * srb bytes per matrix, contiguous; at most two chunks a thread
+  // scale rows first (16 * srb bytes per matrix, contiguous; at most two
+  // chunks a thread), then the codes step by step, so that the compute can
+  // start on the first steps while the later ones stream in
   const int sch = srb;  // 16-byte chunks per matrix
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
@@ -242,6 +247,25 @@ __device__ __forceinline__ void ps_gu_issue(const PsMat& Wg, const PsMat& Wu, in
     g.s[b] = __builtin_nontemporal_load(
         (const u32x4*)(W[m]->scales + ((long)e * rows + tile * 16) * srb + (ch - m * sch) * 16));
   }
+  const uint8_t* cl[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    cl[m] = W[m]->codes + rw * crb + (FMT == MOE_Q8_0 ? kbase : (kbase >> 1));
+    g.ts[m] = FMT == MOE_NVFP4 ? W[m]->ts[e] : 1.0f;
+  }
+#pragma unroll
+  for (int u = 0; u < kPsPD; ++u)
+#pragma unroll
+    for (int m = 0; m < 2; ++m) g.c[m][u] = __builtin_nontemporal_load((const u32x4*)(cl[m] + min(u, nsteps - 1) * STEP_B));
+}
+
+// Weights of MFMA i of a step: exact values (NVFP4-style), or exact values
+// plus 1152 (Q8_0, IQ4_NL; the caller subtracts 1152 times the activation sum).
+template <int FMT>
+__device__ __forceinline__ f16x8 ps_decode(const u32x4& c, int i, uint32_t sraw) {
+  if constexpr (FMT == MOE_IQ4_NL) return iq4_dword_to_f16x8_p1152(c[i]);
+  else if constexpr (FMT == MOE_Q8_0) return q8_dwords_to_f16x8_p1152(c[2 * i], c[2 * i + 1]);
+  else return decode_b<FMT>(c, i, sraw);
 }
 
 template <int FMT>
@@ -250,7 +274,7 @@ __device__ __forceinline__ void ps_gu_compute(PsLds& S, const GuCodes<FMT>& g, i
   constexpr int EPS = dq_eps(FMT);
   constexpr int NMF = EPS / 8;
   constexpr bool BD = FMT != MOE_NVFP4;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = ps_tid(), lane = tid & 63, wid = tid >> 6;
   const int n = lane & 15, G = lane >> 4;
   const int kw = K / 4;
   const int nsteps = kw / (4 * EPS);
@@ -267,28 +291,28 @@ __device__ __forceinline__ void ps_gu_compute(PsLds& S, const GuCodes<FMT>& g, i
   const uint16_t* ssl[2];
 #pragma unroll
   for (int m = 0; m < 2; ++m) ssl[m] = (const uint16_t*)(S.sc + m * sch * 16 + n * srb) + (kbase >> 5);
-  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  // the token's column is D row 0 (element x): with the block-diagonal
+  // operand, lane (n, G) holds row n's partial sum over the step's chunk of
+  // lane group G
+  float acc[2] = {0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < kPsPD; ++s) {
     if (s < nsteps) {
       f16x8 ac[NMF];
 #pragma unroll
       for (int i = 0; i < NMF; ++i) ac[i] = *(const f16x8*)(ap + s * 4 * EPS + 8 * i);
+      const float csum = BD ? 1152.0f * S.xsum[(kbase >> (EPS == 32 ? 5 : 4)) + 4 * s] : 0.0f;
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const uint32_t ss = ssl[m][s * (4 * EPS / 32)];
         f32x4 D = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < NMF; ++i)
-          D = __builtin_amdgcn_mfma_f32_16x16x32_f16(ac[i], decode_b<FMT>(g.c[m][s], i, ss), D, 0, 0, 0);
+          D = __builtin_amdgcn_mfma_f32_16x16x32_f16(ac[i], ps_decode<FMT>(g.c[m][s], i, ss), D, 0, 0, 0);
         if constexpr (FMT == MOE_NVFP4) {
-          acc[m] += D;
+          acc[m] += D.x;
         } else {
-          const float sc = f16_bits_to_f32(ss);
-          acc[m].x = fmaf(sc, D.x, acc[m].x);
-          acc[m].y = fmaf(sc, D.y, acc[m].y);
-          acc[m].z = fmaf(sc, D.z, acc[m].z);
-          acc[m].w = fmaf(sc, D.w, acc[m].w);
+          acc[m] = fmaf(f16_bits_to_f32(ss), D.x - csum, acc[m]);
         }
       }
     }
@@ -299,11 +323,10 @@ __device__ __forceinline__ void ps_gu_compute(PsLds& S, const GuCodes<FMT>& g, i
   if constexpr (BD) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      acc[m].x += __shfl_xor(acc[m].x, 16, 64);
-      acc[m].x += __shfl_xor(acc[m].x, 32, 64);
+      acc[m] += __shfl_xor(acc[m], 16, 64);
+      acc[m] += __shfl_xor(acc[m], 32, 64);
     }
   }
-  // the token's column is D row 0: element x of lanes n (group 0)
   S.red[wid][0][lane] = acc[0];
   S.red[wid][1][lane] = acc[1];
   __syncthreads();
@@ -311,8 +334,8 @@ __device__ __forceinline__ void ps_gu_compute(PsLds& S, const GuCodes<FMT>& g, i
     float gs = 0.f, us = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      gs += S.red[q][0][lane].x;
-      us += S.red[q][1][lane].x;
+      gs += S.red[q][0][lane];
+      us += S.red[q][1][lane];
     }
     const float xs = S.xs;
     gs = gs * g.ts[0] * xs;
@@ -340,18 +363,18 @@ __device__ __forceinline__ void ps_dn_issue(const PsMat& Wd, int e, int ct, int 
   constexpr int EPS = dq_eps(FMT);
   constexpr int PD = FMT == MOE_Q8_0 ? 2 * kPsPD : kPsPD;
   constexpr int STEP_B = FMT == MOE_Q8_0 ? 4 * EPS : 2 * EPS;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = ps_tid(), lane = tid & 63, wid = tid >> 6;
   const int n = lane & 15, G = lane >> 4;
   const int nsteps = K / (4 * EPS);
   const int crb = code_row_bytes(FMT, K), srb = scale_row_bytes(FMT, K);
   const int kbase = G * EPS;
   const int row = ct * 64 + wid * 16 + n;
   const uint8_t* cl = Wd.codes + ((long)e * rows + row) * crb + (FMT == MOE_Q8_0 ? kbase : (kbase >> 1));
-#pragma unroll
-  for (int u = 0; u < PD; ++u) g.c[u] = __builtin_nontemporal_load((const u32x4*)(cl + min(u, nsteps - 1) * STEP_B));
-  const int sch = 64 * srb / 16;  // at most 256: one chunk a thread
+  const int sch = 64 * srb / 16;  // at most 256: one chunk a thread (issued first)
   g.s = __builtin_nontemporal_load(
       (const u32x4*)(Wd.scales + ((long)e * rows + ct * 64) * srb + min(tid, sch - 1) * 16));
+#pragma unroll
+  for (int u = 0; u < PD; ++u) g.c[u] = __builtin_nontemporal_load((const u32x4*)(cl + min(u, nsteps - 1) * STEP_B));
   g.ts = FMT == MOE_NVFP4 ? Wd.ts[e] : 1.0f;
 }
 
@@ -362,7 +385,7 @@ __device__ __forceinline__ void ps_dn_compute(PsLds& S, const DnCodes<FMT>& g, i
   constexpr int NMF = EPS / 8;
   constexpr bool BD = FMT != MOE_NVFP4;
   constexpr int PD = FMT == MOE_Q8_0 ? 2 * kPsPD : kPsPD;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = ps_tid(), lane = tid & 63, wid = tid >> 6;
   const int n = lane & 15, G = lane >> 4;
   const int nsteps = K / (4 * EPS);
   const int srb = scale_row_bytes(FMT, K);
@@ -383,7 +406,8 @@ __device__ __forceinline__ void ps_dn_compute(PsLds& S, const DnCodes<FMT>& g, i
   }
   const f16* ap = valid ? S.hh[c] + kbase : S.zero;
   const uint16_t* ssl = (const uint16_t*)(S.sc + (wid * 16 + n) * srb) + (kbase >> 5);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // D rows 0 and 1 hold the hi and lo columns (elements x and y)
+  f32x2 acc = {0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < PD; ++s) {
     if (s < nsteps) {
@@ -392,16 +416,16 @@ __device__ __forceinline__ void ps_dn_compute(PsLds& S, const DnCodes<FMT>& g, i
 #pragma unroll
       for (int i = 0; i < NMF; ++i) {
         const f16x8 a8 = *(const f16x8*)(ap + s * 4 * EPS + 8 * i);
-        D = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, decode_b<FMT>(g.c[s], i, ss), D, 0, 0, 0);
+        D = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, ps_decode<FMT>(g.c[s], i, ss), D, 0, 0, 0);
       }
       if constexpr (FMT == MOE_NVFP4) {
-        acc += D;
+        acc.x += D.x;
+        acc.y += D.y;
       } else {
+        const int chunk = (kbase >> (EPS == 32 ? 5 : 4)) + 4 * s;
         const float sc = f16_bits_to_f32(ss);
-        acc.x = fmaf(sc, D.x, acc.x);
-        acc.y = fmaf(sc, D.y, acc.y);
-        acc.z = fmaf(sc, D.z, acc.z);
-        acc.w = fmaf(sc, D.w, acc.w);
+        acc.x = fmaf(sc, fmaf(-1152.0f, S.hsum[0][chunk], D.x), acc.x);
+        acc.y = fmaf(sc, fmaf(-1152.0f, S.hsum[1][chunk], D.y), acc.y);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -421,9 +445,20 @@ __device__ __forceinline__ void ps_dn_compute(PsLds& S, const DnCodes<FMT>& g, i
 // layer).  Thread tid holds elements (q * 256 + tid) * 4 .. + 3 for q < d /
 // 1024 (as floats of the bf16 values, for the router); writes the scaled fp16
 // copy (gate weights' decode order) and its scale to LDS, and the bf16 record.
-__device__ __forceinline__ void ps_glue(PsLds& S, const float* r, const float* ssp, int d, float eps, int gate_fmt,
+// Sum of v over aligned groups of LPC (4 or 8) consecutive lanes, in the
+// group's last lane (row shifts within rows of 16 lanes).
+template <int LPC>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp_f32<kDppShr1, 0xf>(v);
+  v += dpp_f32<kDppShr2, 0xf>(v);
+  if constexpr (LPC == 8) v += dpp_f32<kDppShr4, 0xf>(v);
+  return v;
+}
+
+template <int GF>
+__device__ __forceinline__ void ps_glue(PsLds& S, const float* r, const float* ssp, int d, float eps,
                                         uint16_t* rec_x, f32x4 (&xv)[4]) {
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = ps_tid(), lane = tid & 63, wid = tid >> 6;
   const int nq = d / 1024;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
@@ -465,10 +500,19 @@ __device__ __forceinline__ void ps_glue(PsLds& S, const float* r, const float* s
   for (int q = 0; q < 4; ++q) {
     if (q < nq) {
       const int i = (q * 256 + tid) * 4;
-      S.x16[act_pos(gate_fmt, i + 0)] = (f16)(xv[q].x * down);
-      S.x16[act_pos(gate_fmt, i + 1)] = (f16)(xv[q].y * down);
-      S.x16[act_pos(gate_fmt, i + 2)] = (f16)(xv[q].z * down);
-      S.x16[act_pos(gate_fmt, i + 3)] = (f16)(xv[q].w * down);
+      f16 hv[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        hv[c] = (f16)(xv[q][c] * down);
+        S.x16[act_pos(GF, i + c)] = hv[c];
+      }
+      if constexpr (GF != MOE_NVFP4) {
+        // sum over each EPS-element chunk of the stored values (the weights
+        // carry +1152, see ps_decode)
+        constexpr int EPS = dq_eps(GF);
+        const float cs = group_sum<EPS / 4>(((float)hv[0] + (float)hv[1]) + ((float)hv[2] + (float)hv[3]));
+        if ((lane & (EPS / 4 - 1)) == EPS / 4 - 1) S.xsum[i / EPS] = cs;
+      }
     }
   }
   if (tid == 0) S.xs = ldexpf(1.0f, ex);
@@ -481,13 +525,13 @@ __device__ __forceinline__ void ps_router_load(const float* Wr, int e, int d, f3
   const int nq = d / 1024;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    if (q < nq) wv[q] = __builtin_nontemporal_load((const f32x4*)(Wr + (long)e * d + (q * 256 + threadIdx.x) * 4));
+    if (q < nq) wv[q] = __builtin_nontemporal_load((const f32x4*)(Wr + (long)e * d + (q * 256 + ps_tid()) * 4));
 }
 
 // logit = fp32(sum_i W[e][i] x[i] + b[e]) with fp64 sums of the exact products.
 __device__ __forceinline__ float ps_router_dot(PsLds& S, const f32x4 (&wv)[4], const f32x4 (&xv)[4], int d,
                                                float bias) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = ps_tid() & 63, wid = ps_tid() >> 6;
   const int nq = d / 1024;
   double acc = 0.0;
 #pragma unroll
@@ -503,7 +547,7 @@ __device__ __forceinline__ float ps_router_dot(PsLds& S, const f32x4 (&wv)[4], c
   return (float)(r + (double)bias);
 }
 
-template <int GF, int DF>
+template <int GF, int DF, int PT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_ps_decode(const PsArgs a) {
   __shared__ PsLds S;
   pin_arg(a.layers);
@@ -511,7 +555,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   pin_arg(a.hrow);
   pin_arg(a.orow);
   pin_arg(a.sync);
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int G = gridDim.x, w = blockIdx.x;
   const int d = a.d, f = a.f, E = a.E, k = a.k, hs = a.hs, L = a.n_layers;
   const int nS = k + hs;
@@ -531,7 +574,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   int32_t* sync = a.sync;
   int32_t* abort_w = sync + kLnAbort * kLine;
 
-  for (int i = tid; i < kPsMaxF; i += 256) S.zero[i] = (f16)0.0f;
+  for (int i = ps_tid(); i < kPsMaxF; i += 256) S.zero[i] = (f16)0.0f;
 
   f32x4 wv[4];
   if (w < E) ps_router_load(a.layers[0].router_w, w, d, wv);
@@ -539,6 +582,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   if (pre_sh) ps_gu_issue<GF>(a.layers[0].m[kSGate], a.layers[0].m[kSUp], 0, w, d, f, gsh);
 
   for (int l = 0; l < L; ++l) {
+    const int tid = ps_tid(), lane = tid & 63, wid = tid >> 6;
     const PsLayer& P = a.layers[l];
     int32_t* err = a.rec_err ? a.rec_err + l : a.err_ws;
     const float* r_in = l == 0 ? a.h : a.rbuf[l & 1];
@@ -549,10 +593,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     if (has_x) {
       if (l > 0 && !ps_wait(sync + kLnTiles * kLine, kSubTiles, dn_per, l, abort_w, err)) return;
       f32x4 xv[4];
-      ps_glue(S, r_in, l == 0 ? nullptr : a.ss[l & 1], d, a.eps, GF,
-              (w == 0 && a.rec_x) ? a.rec_x + (long)l * d : nullptr, xv);
+      ps_glue<GF>(S, r_in, l == 0 ? nullptr : a.ss[l & 1], d, a.eps,
+                  (w == 0 && a.rec_x) ? a.rec_x + (long)l * d : nullptr, xv);
       for (int e = w; e < E; e += G) {
-        if (e != w) ps_router_load(P.router_w, e, d, wv);
+        if (e != w) ps_router_load(P.router_w, e, d, wv);  // (the first row is already in flight)
         const float bias = P.bias ? P.bias[e] : 0.0f;
         const float v = ps_router_dot(S, wv, xv, d, bias);
         if (tid == 0) {
@@ -580,7 +624,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
           if (i4 * 4 + c < E) S.logit[i4 * 4 + c] = v[c];
       }
       __syncthreads();
-      wg_topk1<16>(S.logit, E, k, S.tk_max, S.tk_list, S.tk_cnt, S.tk_key, S.tk_idx, S.idx, S.wv);
+      wg_topk_tau<PT>(S.logit, E, k, S.tk_max, &S.tk_list[0][0], S.tk_cnt, S.tk_key, S.tk_idx, S.idx, S.wv);
       if (wid == 0) {
         const float v = lane < k ? S.wv[lane] : 0.0f;
         const float vmax = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 0));
@@ -605,6 +649,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       ps_arrive(sync + (kLnSlot + slot * kSubSlot + (it % gu_per) % kSubSlot) * kLine);
     }
 
+    // the next layer's router row, in flight from here on (a workgroup that
+    // issued it after its down work would wait for it at the next router)
+    if (l + 1 < L && w < E) ps_router_load(a.layers[l + 1].router_w, w, d, wv);
+
     // ---- down, and the combine of each finished 64-column tile
     for (int it = w; it < dn_total; it += G) {
       const int slot = it / dn_per, ct = it % dn_per;
@@ -624,13 +672,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       const int ex = x16_exponent(mx);
       const float down = ldexpf(1.0f, -ex);
       if (tid * 4 < f) {
+        float shi = 0.f, slo = 0.f;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const float sv = hv[c] * down;
           const f16 hi = (f16)sv;
+          const f16 lo = (f16)(sv - (float)hi);
           const int pos = act_pos(DF, tid * 4 + c);
           S.hh[0][pos] = hi;
-          S.hh[1][pos] = (f16)(sv - (float)hi);
+          S.hh[1][pos] = lo;
+          shi += (float)hi;
+          slo += (float)lo;
+        }
+        if constexpr (DF != MOE_NVFP4) {
+          // chunk sums of the stored parts (the weights carry +1152)
+          constexpr int EPS = dq_eps(DF);
+          shi = group_sum<EPS / 4>(shi);
+          slo = group_sum<EPS / 4>(slo);
+          if ((lane & (EPS / 4 - 1)) == EPS / 4 - 1) {
+            S.hsum[0][tid * 4 / EPS] = shi;
+            S.hsum[1][tid * 4 / EPS] = slo;
+          }
         }
       }
       const int pair = sh ? k : slot - hs;
@@ -658,12 +720,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       }
     }
 
-    // ---- the next layer's router row and shared-expert tile, in flight
-    // while the residual forms
-    if (l + 1 < L) {
-      if (w < E) ps_router_load(a.layers[l + 1].router_w, w, d, wv);
-      if (pre_sh) ps_gu_issue<GF>(a.layers[l + 1].m[kSGate], a.layers[l + 1].m[kSUp], 0, w, d, f, gsh);
-    }
+    // ---- the next layer's shared-expert tile, in flight while the residual forms
+    if (l + 1 < L && pre_sh) ps_gu_issue<GF>(a.layers[l + 1].m[kSGate], a.layers[l + 1].m[kSUp], 0, w, d, f, gsh);
   }
 }
 
@@ -735,9 +793,9 @@ PsMat ps_mat(const moe_qmatrix& m) { return PsMat{(const uint8_t*)m.codes, (cons
 // The grid is at most the workgroups resident at once, so that every
 // workgroup a wait depends on is running.  With timing events, the launch
 // carries them (its own start and end).
-template <int GF, int DF>
-hipError_t launch_ps(const PsArgs& a, int need, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  auto kern = k_ps_decode<GF, DF>;
+template <int GF, int DF, int PT>
+hipError_t launch_ps_pt(const PsArgs& a, int need, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  auto kern = k_ps_decode<GF, DF, PT>;
   const int res = resident_wgs(kern, 0);
   if (res <= 0) return hipErrorInvalidConfiguration;
   const int grid = need < res ? need : res;
@@ -746,6 +804,12 @@ hipError_t launch_ps(const PsArgs& a, int need, hipStream_t s, hipEvent_t e0, hi
   else
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+// logits per top-k thread: E <= 512 takes two, E <= 1024 four
+template <int GF, int DF>
+hipError_t launch_ps(const PsArgs& a, int need, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  return a.E <= 512 ? launch_ps_pt<GF, DF, 2>(a, need, s, e0, e1) : launch_ps_pt<GF, DF, 4>(a, need, s, e0, e1);
 }
 
 template <int GF>

@@ -82,6 +82,12 @@ WORKLOADS = {
                         gate_type="iq4_nl", up_type="iq4_nl", down_type="iq4_nl", shared=True,
                         x_dtype="bf16", y_dtype="bf16", zipf_s=1.1, tokens="iid", seed=4,
                         note="4096-token prefill chunk"),
+    # the prefill chunk with NVIDIA's NVFP4 routed-expert format (the pages'
+    # seven-engine benchmark runs NVFP4 routed experts bit-exact)
+    "prefill_nvfp4": Workload("prefill_nvfp4", d=3072, f=768, E=512, k=8, T=4096, n_layers=48,
+                              gate_type="nvfp4", up_type="nvfp4", down_type="nvfp4", shared=True,
+                              x_dtype="bf16", y_dtype="bf16", zipf_s=1.1, tokens="iid", seed=5,
+                              note="4096-token prefill chunk, NVFP4-style experts"),
 }
 
 

@@ -88,15 +88,6 @@ def test_fused_stack_small(case):
     _say(f"[fused] {stats}")
 
 
-@pytest.mark.parametrize("name", ["decode", "verify"])
-def test_fused_full_size(name):
-    wl = synth.scaled(synth.WORKLOADS[name], n_layers=2)
-    _say(f"[fused {name}] generating 2 layers")
-    layers, st = _make(wl, 2)
-    stats = _check_fused(wl, layers, st, TOL_DECODE)
-    _say(f"[fused {name}] {stats}")
-
-
 @pytest.mark.parametrize("T", [1, 3])
 def test_fused_heavy_ties(T):
     """A zero router: every logit equal, so each token takes experts 0..k-1."""

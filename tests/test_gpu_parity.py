@@ -389,61 +389,7 @@ def test_prefill_extreme_scales(types):
 
 # ---------------------------------------------------------------- full-size shapes
 
-def _full_stack(name, n_layers, T=None):
-    wl = synth.WORKLOADS[name]
-    wl = synth.scaled(wl, n_layers=n_layers, T=T or wl.T)
-    _say(f"[{name}] generating {n_layers} layers at d={wl.d} f={wl.f} E={wl.E}")
-    layers = [synth.make_layer(wl, l, DEV) for l in range(n_layers)]
-    h0 = synth.make_tokens(wl, DEV)
-    st = Stack(layers, wl.T, y_dtype=wl.y_dtype, x_dtype="bf16", chain=True)
-    st.set_tokens(h0)
-    st.step()
-    torch.cuda.synchronize()
-    return wl, layers, st
-
-
-def _check_stack_layer(wl, layers, st, l, tol, tokens=None):
-    b = st.bufs[l]
-    idx = b.topk_idx.cpu().numpy()
-    sel = np.arange(wl.T) if tokens is None else np.asarray(tokens)
-    experts = set(idx[sel].ravel().tolist())
-    lnp = synth.layer_to_numpy(layers[l], experts)
-    x_np = to_np(st.xs[l])[sel]
-    gpu = {"logits": b.logits.cpu().numpy()[sel], "idx": idx[sel], "w": b.topk_w.cpu().numpy()[sel],
-           "y": to_np(b.y)[sel]}
-    stats = check_layer(lnp, x_np, gpu, "f64", tol)
-    stats["U"] = int(b.plan.n_active.item())
-    return stats
-
-
-@pytest.mark.parametrize("name", ["decode", "verify", "slots"])
-def test_full_size_decode_workloads(name):
-    wl, layers, st = _full_stack(name, 2)
-    for l in range(2):
-        stats = _check_stack_layer(wl, layers, st, l, TOL_DECODE)
-        _say(f"[{name}] layer {l}: {stats}")
-        assert int(st.bufs[l].plan.error.item()) == 0
-    # glue: x_1 = bf16(rmsnorm(h_0 + y_0)) on the GPU's own h_0 (layer-0 residual)
-    h0 = st.h0.cpu().numpy().astype(np.float64)
-    y0 = to_np(st.bufs[0].y)
-    x1 = M.rmsnorm_to_bf16(M.residual_add(h0, y0))
-    x1g = to_np(st.xs[1])
-    check_bf16_glue(x1g, x1, "layer 1 input")
-
-
-def test_full_size_prefill_sampled_tokens():
-    wl, layers, st = _full_stack("prefill", 1)
-    g = np.random.default_rng(5)
-    tokens = np.sort(g.choice(wl.T, size=12, replace=False))
-    tokens[0] = 0
-    tokens[-1] = wl.T - 1
-    stats = _check_stack_layer(wl, layers, st, 0, TOL_PREFILL, tokens)
-    _say(f"[prefill] layer 0 sampled: {stats}")
-    # plan of the full batch, bit exact against the oracle from the GPU's indices
-    want = M.plan(st.bufs[0].topk_idx.cpu().numpy(), wl.E)
-    got = st.bufs[0].plan.host()
-    for n in ("counts", "offsets", "row_token", "row_slot", "slot_row", "active"):
-        assert np.array_equal(got[n], want[n]), n
+# (full-size stacks: tests/test_gpu_full.py)
 
 
 # ---------------------------------------------------------------- determinism / graphs

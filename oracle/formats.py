@@ -18,6 +18,13 @@ GGUF files):
   of byte i), one FP8 E4M3 block scale, one fp32 scale per (expert, matrix).  The
   pages' benchmark ("Benchmark: seven engines on one RTX 5090", "Engine
   provenance") runs NVIDIA's NVFP4 routed experts bit-exact.
+* Q5_1: 32-element blocks of 5-bit unsigned codes with a binary16 step d and a
+  binary16 offset m, w = d * q + m, from ggml's public Q5_1 definition (a
+  covered down format in "What was changed").  The low 4 bits of the codes use
+  the IQ4_NL nibble order (16 bytes); the fifth bit of element e is bit e of a
+  32-bit word.  Structure of arrays: the 16 code bytes per block, and one
+  8-byte record per block holding d, m and that word (little-endian), 24 bytes
+  per 32 weights = 6 bits per weight.
 
 Every value is computed from its closed form with exact float64 arithmetic.
 """
@@ -209,14 +216,51 @@ def dequant_nvfp4(codes, scales, tensor_scale):
     return (a * ts).astype(np.float32).astype(np.float64)
 
 
+Q5_1_BLOCK = 32
+
+
+def q5_1_unpack(codes, records):
+    """Q5_1 code bytes [..., rows, cols/2] and 8-byte block records
+    [..., rows, cols/32 * 8] -> (q [..., rows, cols] in 0..31, d and m
+    [..., rows, cols/32] as float64).
+
+    Record bytes 0-1: binary16 d; 2-3: binary16 m; 4-7: the high-bit word,
+    little-endian; bit e of that word is the fifth bit of block element e.
+    """
+    low = iq4_nl_unpack(codes).astype(np.int64)  # the same 4-bit packing
+    rec = np.asarray(records).astype(np.int64)
+    rows_shape = rec.shape[:-1]
+    nb = rec.shape[-1] // 8
+    rec = rec.reshape(rows_shape + (nb, 8))
+    d = fp16_bits_to_float(rec[..., 0] | (rec[..., 1] << 8))
+    m = fp16_bits_to_float(rec[..., 2] | (rec[..., 3] << 8))
+    word = rec[..., 4] | (rec[..., 5] << 8) | (rec[..., 6] << 16) | (rec[..., 7] << 24)
+    high = (word[..., None] >> np.arange(Q5_1_BLOCK)) & 1       # [..., nb, 32]
+    q = low.reshape(rows_shape + (nb, Q5_1_BLOCK)) + 16 * high
+    return q.reshape(rows_shape + (nb * Q5_1_BLOCK,)), d, m
+
+
+def dequant_q5_1(codes, records):
+    """Q5_1 block dequantisation: w = d * q + m, exact in float64 (d * q has at
+    most 16 significant bits, and the sum of two values of the binary16 range
+    needs at most 45)."""
+    q, d, m = q5_1_unpack(codes, records)
+    rows_shape = q.shape[:-1]
+    nb = q.shape[-1] // Q5_1_BLOCK
+    q = q.reshape(rows_shape + (nb, Q5_1_BLOCK)).astype(np.float64)
+    return (q * d[..., None] + m[..., None]).reshape(rows_shape + (nb * Q5_1_BLOCK,))
+
+
 def dequant(qtype, codes, scales, tensor_scale=None):
-    """Dispatch on the format name ('q8_0', 'iq4_nl', 'nvfp4') for one expert matrix."""
+    """Dispatch on the format name ('q8_0', 'iq4_nl', 'nvfp4', 'q5_1') for one expert matrix."""
     if qtype == "q8_0":
         return dequant_q8_0(codes, scales)
     if qtype == "iq4_nl":
         return dequant_iq4_nl(codes, scales)
     if qtype == "nvfp4":
         return dequant_nvfp4(codes, scales, tensor_scale)
+    if qtype == "q5_1":
+        return dequant_q5_1(codes, scales)
     raise ValueError(f"unknown format {qtype!r}")
 
 
@@ -230,4 +274,6 @@ def bytes_per_matrix(qtype, rows, cols):
         return n // 32 * 18
     if qtype == "nvfp4":
         return n // 16 * 9 + 4
+    if qtype == "q5_1":
+        return n // 32 * 24
     raise ValueError(qtype)

@@ -271,3 +271,97 @@ def test_zero_scale_blocks_decode_to_zero():
     codes4 = np.random.default_rng(5).integers(0, 256, size=(2, 32)).astype(np.uint8)
     assert np.all(F.dequant_iq4_nl(codes4, z) == 0)
     assert np.all(F.dequant_nvfp4(codes4, np.zeros((2, 4), np.uint8), np.float32(0.5)) == 0)
+
+
+# ---------------------------------------------------------------- Q5_1
+
+def _q5_1_record(d_bits, m_bits, word):
+    return np.array([d_bits & 0xFF, d_bits >> 8, m_bits & 0xFF, m_bits >> 8,
+                     word & 0xFF, (word >> 8) & 0xFF, (word >> 16) & 0xFF, word >> 24], dtype=np.uint8)
+
+
+def _q5_1_block(q):
+    """Pack 32 five-bit codes into (16 code bytes, high-bit word) by the layout:
+    low nibble of byte j = element j, high nibble = element j + 16, bit e of the
+    word = the fifth bit of element e."""
+    q = np.asarray(q, dtype=np.int64)
+    codes = ((q[:16] & 15) | ((q[16:] & 15) << 4)).astype(np.uint8)
+    word = int(sum(int((q[e] >> 4) & 1) << e for e in range(32)))
+    return codes, word
+
+
+def test_q5_1_every_code_at_every_position_exact():
+    """Every code 0..31 at every block position, with d and m over signs,
+    subnormals, zero and the largest binary16 values, against exact rationals."""
+    scales = [0x3C00, 0xBC00, 0x0001, 0x03FF, 0x0400, 0x7BFF, 0xFBFF, 0x0000, 0x2E66, 0xB123]
+    rng = np.random.default_rng(13)
+    codes, recs, want = [], [], []
+    for shift in range(32):
+        q = (np.arange(32) + shift) % 32
+        c, word = _q5_1_block(q)
+        d_bits = scales[shift % len(scales)]
+        m_bits = scales[(3 * shift + 1) % len(scales)] if shift % 4 else int(rng.integers(0, 0x7C00))
+        codes.append(c)
+        recs.append(_q5_1_record(d_bits, m_bits, word))
+        d = Fraction(float(np.uint16(d_bits).view(np.float16)))
+        m = Fraction(float(np.uint16(m_bits).view(np.float16)))
+        want.append([d * int(v) + m for v in q])
+    codes = np.stack(codes)[None]            # [1 row, 32 blocks * 16]
+    codes = codes.reshape(1, -1)
+    recs = np.stack(recs).reshape(1, -1)
+    got = F.dequant_q5_1(codes, recs)
+    flat = [x for blk in want for x in blk]
+    assert len(flat) == got.shape[1]
+    for g, w in zip(got[0], flat):
+        assert Fraction(float(g)) == w
+
+
+def test_q5_1_high_bit_and_nibble_order():
+    """One set bit of the high-bit word raises exactly its element by 16 d; a
+    nibble in byte j lands at element j (low) or j + 16 (high)."""
+    d_bits, m_bits = 0x3800, 0x3400  # 0.5, 0.25
+    base_codes = np.zeros((1, 16), np.uint8)
+    base = F.dequant_q5_1(base_codes, _q5_1_record(d_bits, m_bits, 0)[None])[0]
+    assert np.all(base == 0.25)
+    for e in (0, 1, 7, 15, 16, 17, 30, 31):
+        w = F.dequant_q5_1(base_codes, _q5_1_record(d_bits, m_bits, 1 << e)[None])[0]
+        diff = w - base
+        assert diff[e] == 8.0 and np.count_nonzero(diff) == 1
+    for j in (0, 5, 15):
+        c = np.zeros((1, 16), np.uint8)
+        c[0, j] = 0x93  # low nibble 3, high nibble 9
+        w = F.dequant_q5_1(c, _q5_1_record(d_bits, m_bits, 0)[None])[0]
+        assert w[j] == 0.5 * 3 + 0.25 and w[j + 16] == 0.5 * 9 + 0.25
+        assert np.count_nonzero(w - base) == 2
+
+
+def test_q5_1_zero_step_and_offset_decode_to_zero():
+    rng = np.random.default_rng(14)
+    c = rng.integers(0, 256, size=(3, 64)).astype(np.uint8)
+    recs = np.concatenate([_q5_1_record(0, 0x8000, int(rng.integers(0, 2 ** 32)))
+                           for _ in range(12)]).reshape(3, 32)
+    assert np.all(F.dequant_q5_1(c, recs) == 0)
+
+
+def test_q5_1_planted_mistakes_are_caught(monkeypatch):
+    # the high bit of element j + 16 taken from bit j
+    def bad_unpack(codes, records):
+        q, d, m = orig(codes, records)
+        rows_shape = q.shape[:-1]
+        nb = q.shape[-1] // 32
+        q = q.reshape(rows_shape + (nb, 32)).copy()
+        q[..., 16:] = (q[..., 16:] & 15) | (q[..., :16] & 16)
+        return q.reshape(rows_shape + (nb * 32,)), d, m
+    orig = F.q5_1_unpack
+    monkeypatch.setattr(F, "q5_1_unpack", bad_unpack)
+    with pytest.raises(AssertionError):
+        test_q5_1_high_bit_and_nibble_order()
+    monkeypatch.undo()
+    # step and offset swapped
+    def bad_unpack2(codes, records):
+        q, d, m = orig(codes, records)
+        return q, m, d
+    monkeypatch.setattr(F, "q5_1_unpack", bad_unpack2)
+    with pytest.raises(AssertionError):
+        test_q5_1_every_code_at_every_position_exact()
+    monkeypatch.undo()

@@ -38,6 +38,15 @@ def _rand_matrix(rng, qtype, n, rows, cols, scale_lo=0.002, scale_hi=0.02):
         sc = rng.integers(0x20, 0x50, size=(n, rows, cols // 16)).astype(np.uint8)
         ts = rng.uniform(1e-3, 1e-2, size=n).astype(np.float32)
         return {"type": qtype, "codes": codes, "scales": sc, "tensor_scale": ts}
+    if qtype == "q5_1":
+        codes = rng.integers(0, 256, size=(n, rows, cols // 2)).astype(np.uint8)
+        nb = cols // 32
+        d = np.float16(rng.uniform(scale_lo, scale_hi, size=(n, rows, nb)) / 31 * 4).view(np.uint16)
+        m = np.float16(-rng.uniform(scale_lo, scale_hi, size=(n, rows, nb)) * 2).view(np.uint16)
+        word = rng.integers(0, 2 ** 32, size=(n, rows, nb), dtype=np.uint64).astype(np.uint32)
+        rec = np.stack([d & 0xFF, d >> 8, m & 0xFF, m >> 8, word & 0xFF, (word >> 8) & 0xFF,
+                        (word >> 16) & 0xFF, word >> 24], axis=-1).astype(np.uint8)
+        return {"type": qtype, "codes": codes, "scales": rec.reshape(n, rows, nb * 8), "tensor_scale": None}
     raise ValueError(qtype)
 
 
@@ -234,7 +243,8 @@ def test_silu_against_plain_formula_and_extremes():
 
 
 @pytest.mark.parametrize("qtypes", [("q8_0", "q8_0", "q8_0"), ("iq4_nl", "iq4_nl", "iq4_nl"),
-                                    ("nvfp4", "nvfp4", "nvfp4"), ("iq4_nl", "iq4_nl", "q8_0")])
+                                    ("nvfp4", "nvfp4", "nvfp4"), ("iq4_nl", "iq4_nl", "q8_0"),
+                                    ("iq4_nl", "iq4_nl", "q5_1")])
 def test_layer_matches_bruteforce_loops(qtypes):
     d, f, E, k, T = 32, 32, 5, 2, 3
     layer = tiny_layer(11, d=d, f=f, E=E, k=k, qtypes=qtypes)

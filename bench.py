@@ -82,9 +82,10 @@ DOMINANT = {
 
 def matrix_bytes(qtype, rows, cols):
     """Algorithmic bytes of one expert matrix: codes + block scales (+ the fp32
-    tensor scale of the NVFP4-style format).  IQ4_NL: 18 B per 32 weights."""
+    tensor scale of the NVFP4-style format).  IQ4_NL: 18 B per 32 weights; Q5_1:
+    24 B per 32 (16 of codes, an 8-byte record)."""
     n = rows * cols
-    return {"q8_0": n // 32 * 34, "iq4_nl": n // 32 * 18, "nvfp4": n // 16 * 9 + 4}[qtype]
+    return {"q8_0": n // 32 * 34, "iq4_nl": n // 32 * 18, "nvfp4": n // 16 * 9 + 4, "q5_1": n // 32 * 24}[qtype]
 
 
 def traffic_from_profile(key, digest):

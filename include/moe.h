@@ -69,8 +69,14 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_F16 = 2 } moe_dtype;
  *             element 2i in the low nibble of byte i; scales FP8 E4M3 (OCP)
  *             [n][rows][cols/16]; tensor_scale fp32 [n];
  *             w = fp32(e2m1 * e4m3 * tensor_scale).
+ *  MOE_Q5_1   32-element blocks of 5-bit codes q (ggml's Q5_1, a covered down
+ *             format); codes uint8 [n][rows][cols/2] hold the low 4 bits in
+ *             the IQ4_NL byte order; scales [n][rows][cols/32] 8-byte records:
+ *             binary16 d, binary16 m, then a little-endian uint32 whose bit e
+ *             is the fifth bit of block element e; w = d * q + m.  Down
+ *             projections only (MOE_ERR_UNSUPPORTED for gate / up).
  */
-typedef enum { MOE_Q8_0 = 1, MOE_IQ4_NL = 2, MOE_NVFP4 = 3 } moe_qtype;
+typedef enum { MOE_Q8_0 = 1, MOE_IQ4_NL = 2, MOE_NVFP4 = 3, MOE_Q5_1 = 4 } moe_qtype;
 
 /* One projection for n_expert experts, structure of arrays (codes and scales
  * in separate device arrays).  rows = outputs, cols = reduction dimension.
@@ -86,9 +92,10 @@ typedef struct {
 } moe_qmatrix;
 
 /* One MoE layer.  gate/up: rows = f, cols = d; down: rows = d, cols = f.
- * gate and up share one format; the shared expert (if any) uses the routed
- * experts' format for each role and has n_expert = 1.  Kernel coverage:
- * d and f multiples of 128, 1 <= k <= E <= 1024, k <= 32. */
+ * gate and up share one format (Q8_0, IQ4_NL or NVFP4-style); down takes any
+ * of the four; the shared expert (if any) uses the routed experts' format for
+ * each role and has n_expert = 1.  Kernel coverage: d and f multiples of 128,
+ * 1 <= k <= E <= 1024, k <= 32. */
 typedef struct {
   int32_t d, f, E, k;
   const float* router_w;     /* device fp32 [E][d] */
@@ -118,7 +125,9 @@ typedef struct {
  *                         scale whose product with the format's largest code
  *                         magnitude (128 / 127) is not finite in fp16, i.e.
  *                         |scale| >= 512 (Q8_0) or >= 516 (IQ4_NL), or a
- *                         non-finite scale: such weights may be infinite.
+ *                         non-finite scale, or a Q5_1 block whose
+ *                         max(|m|, |31 d + m|) reaches 65520: such weights
+ *                         may be infinite.
  *                   A dropped pair gets slot_row -1 and no plan row.
  * Rows past offsets[E] in row_token / row_slot are set to -1. */
 typedef struct {
@@ -203,13 +212,15 @@ moe_status moe_ffn_combine(const moe_layer* layer, int32_t x_dtype, int32_t T, c
                            void* stream);
 
 /* Test hook: dequantise expert `expert` of `m` into dst device [rows][cols]:
- *  MOE_F32   exact values (NVFP4-style: fp32(e2m1 * e4m3 * tensor_scale));
+ *  MOE_F32   exact values (NVFP4-style: fp32(e2m1 * e4m3 * tensor_scale);
+ *            Q5_1: fp32(d * q + m), one rounding of the exact value);
  *  MOE_BF16  round-to-nearest-even of those values;
  *  MOE_F16   the fp16 weight tile the prefill GEMM multiplies, produced by the
  *            GEMM's own decode routine: Q8_0 / IQ4_NL the code times the
  *            block scale in fp16 arithmetic (one rounding to nearest even of
  *            the exact product; subnormal below 2^-14, infinite when the
- *            product reaches 65520 -- see error bit 8); NVFP4-style
+ *            product reaches 65520 -- see error bit 8); Q5_1 d * q + m in fp16
+ *            arithmetic (one fused rounding); NVFP4-style
  *            e2m1 * e4m3 (exact), without the tensor scale, which the GEMM
  *            applies to its fp32 result.
  * dst must be 4-byte aligned. */

@@ -21,7 +21,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-bool valid_qtype(int t) { return t == MOE_Q8_0 || t == MOE_IQ4_NL || t == MOE_NVFP4; }
+bool valid_qtype(int t) { return t == MOE_Q8_0 || t == MOE_IQ4_NL || t == MOE_NVFP4 || t == MOE_Q5_1; }
 bool valid_dtype(int t) { return t == MOE_F32 || t == MOE_BF16; }
 
 moe_status check_qmatrix(const moe_qmatrix& m, int n_expert, int rows, int cols) {
@@ -57,6 +57,7 @@ moe_status check_layer(const moe_layer* L) {
   if ((st = check_qmatrix(L->up, L->E, L->f, L->d)) != MOE_OK) return st;
   if ((st = check_qmatrix(L->down, L->E, L->d, L->f)) != MOE_OK) return st;
   if (L->gate.type != L->up.type) return MOE_ERR_UNSUPPORTED;
+  if (L->gate.type == MOE_Q5_1) return MOE_ERR_UNSUPPORTED;  // a down format only
   if (L->has_shared != 0 && L->has_shared != 1) return MOE_ERR_INVALID_ARG;
   if (L->has_shared) {
     if ((st = check_qmatrix(L->shared_gate, 1, L->f, L->d)) != MOE_OK) return st;

@@ -239,7 +239,7 @@ hipError_t launch_fmt(const DecodeArgs& a, int ncols_max, int items, hipStream_t
   constexpr int CPT = cols_per_tile<FMT>();
   const int K = a.mat[0].cols;
   const int nt = pick_nt(CPT, ncols_max, K);
-  const size_t lds = dq_lds_bytes(CPT, nt, K, a.ksplit, GATEUP ? 2 : 1);
+  const size_t lds = dq_lds_bytes(FMT, CPT, nt, K, a.ksplit, GATEUP ? 2 : 1);
   if (dq_nsteps(FMT, K, a.ksplit) > dq_pd(FMT, GATEUP)) return launch_fmt_roll<FMT, GATEUP, true>(a, nt, lds, items, s);
   return launch_fmt_roll<FMT, GATEUP, false>(a, nt, lds, items, s);
 }
@@ -249,6 +249,9 @@ hipError_t launch_pass(int fmt, const DecodeArgs& a, int ncols_max, int items, h
   switch (fmt) {
     case MOE_Q8_0: return launch_fmt<MOE_Q8_0, GATEUP>(a, ncols_max, items, s);
     case MOE_IQ4_NL: return launch_fmt<MOE_IQ4_NL, GATEUP>(a, ncols_max, items, s);
+    case MOE_Q5_1:
+      if constexpr (!GATEUP) return launch_fmt<MOE_Q5_1, false>(a, ncols_max, items, s);
+      return hipErrorInvalidValue;  // a down format only
     default: return launch_fmt<MOE_NVFP4, GATEUP>(a, ncols_max, items, s);
   }
 }
@@ -279,7 +282,7 @@ static hipError_t launch_fz_down_fmt(const DecodeArgs& a, int items, hipStream_t
   constexpr int CPT = cols_per_tile<FMT>();
   const int K = a.mat[0].cols;
   const int nt = pick_nt(CPT, a.T * 2, K);
-  const size_t lds = dq_lds_bytes(CPT, nt, K, a.ksplit, 1);
+  const size_t lds = dq_lds_bytes(FMT, CPT, nt, K, a.ksplit, 1);
   if (dq_nsteps(FMT, K, a.ksplit) > dq_pd(FMT, false)) return launch_fz_down_roll<FMT, true>(a, nt, lds, items, s);
   return launch_fz_down_roll<FMT, false>(a, nt, lds, items, s);
 }
@@ -288,6 +291,7 @@ hipError_t launch_dq_down_table(const DecodeArgs& a, int fmt, int items, hipStre
   switch (fmt) {
     case MOE_Q8_0: return launch_fz_down_fmt<MOE_Q8_0>(a, items, s);
     case MOE_IQ4_NL: return launch_fz_down_fmt<MOE_IQ4_NL>(a, items, s);
+    case MOE_Q5_1: return launch_fz_down_fmt<MOE_Q5_1>(a, items, s);
     default: return launch_fz_down_fmt<MOE_NVFP4>(a, items, s);
   }
 }

@@ -133,9 +133,35 @@ __device__ __forceinline__ int iq4_pos(int e) {
 }
 
 // Position of element i of a row in the activation layout matching the
-// weight decode of format `fmt` (IQ4_NL reorders elements inside each block).
+// weight decode of format `fmt` (IQ4_NL and Q5_1, whose 4-bit codes share the
+// byte order, reorder elements inside each block).
 __device__ __forceinline__ int act_pos(int fmt, int i) {
-  return fmt == MOE_IQ4_NL ? ((i & ~31) + iq4_pos(i & 31)) : i;
+  return (fmt == MOE_IQ4_NL || fmt == MOE_Q5_1) ? ((i & ~31) + iq4_pos(i & 31)) : i;
+}
+
+// ---------------------------------------------------------------- Q5_1
+
+// Four bits (bit b of x, x < 16) moved to bit 4 of byte b: the fifth bits of
+// four Q5_1 codes.  The four shifted copies of x occupy disjoint bit ranges,
+// so the product has no carries.
+__device__ __forceinline__ uint32_t q5_high4(uint32_t x) { return (x * 0x02040810u) & 0x10101010u; }
+
+// One dword of Q5_1 low nibbles (bytes 4i..4i+3 of a block) and the block's
+// high-bit word -> the eight codes q (0..31) as the exact fp16 values 1024 + q
+// (the pattern 0x64qq), in the IQ4_NL element order 4i..4i+3, 16+4i..16+4i+3.
+__device__ __forceinline__ f16x8 q5_1_dword_to_f16x8_p1024(uint32_t w, uint32_t qh, int i) {
+  const uint32_t lo = (w & 0x0F0F0F0Fu) | q5_high4((qh >> (4 * i)) & 0xFu);
+  const uint32_t hi = ((w >> 4) & 0x0F0F0F0Fu) | q5_high4((qh >> (16 + 4 * i)) & 0xFu);
+  u32x4 r = {__builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u), __builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u),
+             __builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u), __builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u)};
+  return __builtin_bit_cast(f16x8, r);
+}
+
+// The same codes as the exact fp16 values q (subtracting 1024 is exact).
+__device__ __forceinline__ f16x8 q5_1_dword_to_f16x8(uint32_t w, uint32_t qh, int i) {
+  const f16x8 off = {(f16)-1024.0f, (f16)-1024.0f, (f16)-1024.0f, (f16)-1024.0f,
+                     (f16)-1024.0f, (f16)-1024.0f, (f16)-1024.0f, (f16)-1024.0f};
+  return q5_1_dword_to_f16x8_p1024(w, qh, i) + off;
 }
 
 // Exponent e such that max|x| * 2^-e lies in [2^14, 2^15) (0 for an all-zero row).
@@ -603,8 +629,10 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int& to
 __host__ __device__ constexpr int code_row_bytes(int type, int cols) {
   return type == MOE_Q8_0 ? cols : cols / 2;
 }
+// Q8_0 / IQ4_NL: one binary16 scale per 32; NVFP4: one E4M3 per 16; Q5_1: an
+// 8-byte record (d, m, high-bit word) per 32
 __host__ __device__ constexpr int scale_row_bytes(int type, int cols) {
-  return type == MOE_NVFP4 ? cols / 16 : (cols / 32) * 2;
+  return type == MOE_NVFP4 ? cols / 16 : (type == MOE_Q5_1 ? (cols / 32) * 8 : (cols / 32) * 2);
 }
 
 }  // namespace qre

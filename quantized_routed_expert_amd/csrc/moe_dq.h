@@ -102,12 +102,17 @@ __device__ __forceinline__ void dq_pin_args(const DecodeArgs& a) {
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
+// Weights of MFMA i of a step (code dword i of the lane's chunk): exact fp16
+// values; for NVFP4-style with the block scale folded in (exact); for Q5_1
+// the codes q (the block's d and m apply after the MFMA; qh: its high-bit word).
 template <int FMT>
-__device__ __forceinline__ f16x8 decode_b(const u32x4& c, int i, uint32_t sraw) {
+__device__ __forceinline__ f16x8 decode_b(const u32x4& c, int i, uint32_t sraw, uint32_t qh = 0u) {
   if constexpr (FMT == MOE_IQ4_NL) {
     return iq4_dword_to_f16x8(c[i]);
   } else if constexpr (FMT == MOE_Q8_0) {
     return q8_dwords_to_f16x8(c[2 * i], c[2 * i + 1]);
+  } else if constexpr (FMT == MOE_Q5_1) {
+    return q5_1_dword_to_f16x8(c[i], qh, i);
   } else {
     // dwords 0,1 hold the chunk's first 16-element block, 2,3 the second
     const float sc = i < 2 ? e4m3_byte_to_f32<0>(sraw) : e4m3_byte_to_f32<1>(sraw);
@@ -237,11 +242,13 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
   for (int b = 0; b < SB; ++b) sv[b] = __builtin_nontemporal_load(s_src(min(tid + b * 256, s_chunks - 1)));
   // A rows that hold no column read zeros from kw halves after the scales
   const int zoff = (int)(sS + s_chunks * 16 - (uint8_t*)sA) / 2;
-  // this lane's scale words in LDS: row (wid / ksplit) * 16 + n, the step-0 block
+  // this lane's scale words in LDS: row (wid / ksplit) * 16 + n, the step-0
+  // block (Q5_1: 8-byte records, four 16-bit words each)
+  constexpr int SW = FMT == MOE_Q5_1 ? 4 : 1;
   const uint16_t* ssl[NMAT];
 #pragma unroll
   for (int m = 0; m < NMAT; ++m)
-    ssl[m] = (const uint16_t*)(sS + m * s_chunks_m * 16 + ((wid / ksplit) * 16 + n) * srb) + (kbase >> 5);
+    ssl[m] = (const uint16_t*)(sS + m * s_chunks_m * 16 + ((wid / ksplit) * 16 + n) * srb) + (kbase >> 5) * SW;
   // REUSE (without ROLL): the codes of every step, loaded in the first pass,
   // stay in registers for the later passes instead of being read again.
   u32x4 cb_keep[NMAT][PD];
@@ -359,10 +366,20 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
       for (int jt = 0; jt < NT; ++jt) acc[m][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto compute_step = [&](const u32x4 (&cc)[NMAT], int s) {
-      // Q8_0 / IQ4_NL: the block's fp16 scale; NVFP4: the chunk's two E4M3 scales
-      uint32_t ss[NMAT];
+      // Q8_0 / IQ4_NL: the block's fp16 scale; NVFP4: the chunk's two E4M3
+      // scales; Q5_1: d and m (ss), the high-bit word (sh)
+      uint32_t ss[NMAT], sh[NMAT];
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) ss[m] = ssl[m][s * (4 * EPS / 32)];
+      for (int m = 0; m < NMAT; ++m) {
+        if constexpr (FMT == MOE_Q5_1) {
+          const u32x2 rec = *(const u32x2*)(ssl[m] + s * (4 * EPS / 32) * SW);
+          ss[m] = rec.x;
+          sh[m] = rec.y;
+        } else {
+          ss[m] = ssl[m][s * (4 * EPS / 32)];
+          sh[m] = 0u;
+        }
+      }
       f16x8 ac[NT][NMF];
 #pragma unroll
       for (int jt = 0; jt < NT; ++jt)
@@ -370,6 +387,18 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
         for (int i = 0; i < NMF; ++i) {
           ac[jt][i] = *(const f16x8*)&sA[abase[jt] + s * 4 * EPS + 8 * i];
         }
+      // Q5_1: the activation sum of each column over the lane group's chunk
+      // (an MFMA against ones), which the block offset m multiplies
+      f32x4 Dsum[NT];
+      if constexpr (FMT == MOE_Q5_1) {
+        const f16x8 ones = {(f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f};
+#pragma unroll
+        for (int jt = 0; jt < NT; ++jt) {
+          Dsum[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int i = 0; i < NMF; ++i) Dsum[jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ac[jt][i], ones, Dsum[jt], 0, 0, 0);
+        }
+      }
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
         f32x4 D[NT];
@@ -377,11 +406,20 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
         for (int jt = 0; jt < NT; ++jt) D[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < NMF; ++i) {
-          const f16x8 bf = decode_b<FMT>(cc[m], i, ss[m]);
+          const f16x8 bf = decode_b<FMT>(cc[m], i, ss[m], sh[m]);
 #pragma unroll
           for (int jt = 0; jt < NT; ++jt) D[jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ac[jt][i], bf, D[jt], 0, 0, 0);
         }
-        if constexpr (FMT == MOE_NVFP4) {
+        if constexpr (FMT == MOE_Q5_1) {
+          const float dd = f16_bits_to_f32(ss[m] & 0xffffu), mm = f16_bits_to_f32(ss[m] >> 16);
+#pragma unroll
+          for (int jt = 0; jt < NT; ++jt) {
+            acc[m][jt].x = fmaf(dd, D[jt].x, fmaf(mm, Dsum[jt].x, acc[m][jt].x));
+            acc[m][jt].y = fmaf(dd, D[jt].y, fmaf(mm, Dsum[jt].y, acc[m][jt].y));
+            acc[m][jt].z = fmaf(dd, D[jt].z, fmaf(mm, Dsum[jt].z, acc[m][jt].z));
+            acc[m][jt].w = fmaf(dd, D[jt].w, fmaf(mm, Dsum[jt].w, acc[m][jt].w));
+          }
+        } else if constexpr (FMT == MOE_NVFP4) {
 #pragma unroll
           for (int jt = 0; jt < NT; ++jt) acc[m][jt] += D[jt];
         } else {
@@ -558,9 +596,9 @@ inline DecodeWs carve(void* ws, int T, int d, int f, int k, int P) {
 // Dynamic LDS of a decode pass: nt N-tiles of staged activations (or the K
 // reduction's partial sums), the scale rows of the workgroup's tiles for each
 // of nmat matrices, and K / ksplit zero halves.
-inline size_t dq_lds_bytes(int cpt, int nt, int K, int ksplit, int nmat) {
+inline size_t dq_lds_bytes(int fmt, int cpt, int nt, int K, int ksplit, int nmat) {
   const size_t act = (size_t)nt * cpt * K * 2, red = (size_t)4 * nmat * nt * 64 * 16;
-  return (act > red ? act : red) + (size_t)nmat * (64 / ksplit) * (K / 16) + (size_t)(K / ksplit) * 2;
+  return (act > red ? act : red) + (size_t)nmat * (64 / ksplit) * scale_row_bytes(fmt, K) + (size_t)(K / ksplit) * 2;
 }
 
 // Waves along K per 16-row tile: as many as divide the lane-group step count.

@@ -532,7 +532,7 @@ hipError_t launch_fz_gate_fmt(const FzGateArgs& g, int items, int E, hipStream_t
   const int K = g.a.mat[0].cols;
   const int nt = pick_nt(CPT, g.a.T, K);
   // the activation buffer also holds the logits while the plan is built
-  const size_t lds = std::max(dq_lds_bytes(CPT, nt, K, g.a.ksplit, 2), (size_t)g.a.T * E * 4);
+  const size_t lds = std::max(dq_lds_bytes(FMT, CPT, nt, K, g.a.ksplit, 2), (size_t)g.a.T * E * 4);
   if (dq_nsteps(FMT, K, g.a.ksplit) > dq_pd(FMT, true))
     return launch_fz_gate_nt<FMT, true>(g, nt, items, lds, E, s, e0, e1);
   return launch_fz_gate_nt<FMT, false>(g, nt, items, lds, E, s, e0, e1);

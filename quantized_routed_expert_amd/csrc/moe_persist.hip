@@ -187,11 +187,15 @@ __device__ __forceinline__ int ps_tid() {
 
 // Workgroup LDS of the persistent kernel.
 constexpr int kPsMaxD = 4096, kPsMaxF = 1024, kPsMaxE = 1024;
+// scale rows of one item: a gate/up tile (16 rows of two matrices, K = d) or
+// a down item (64 rows, K = f; Q5_1 records are the largest)
+constexpr int kPsScGu = 2 * 16 * scale_row_bytes(MOE_Q8_0, kPsMaxD), kPsScDn = 64 * scale_row_bytes(MOE_Q5_1, kPsMaxF);
+constexpr int kPsScBytes = kPsScGu > kPsScDn ? kPsScGu : kPsScDn;
 struct PsLds {
   f16 x16[kPsMaxD];                 // layer input, scaled fp16, in the gate/up weights' decode order
   f16 hh[2][kPsMaxF];               // down: h of the slot as scaled fp16 hi / lo parts
   f16 zero[kPsMaxF];                // A-operand rows that hold no column
-  uint8_t sc[2 * 16 * kPsMaxD / 16];  // scale rows of the current item
+  uint8_t sc[kPsScBytes];           // scale rows of the current item
   float red[4][2][64];              // K-split partial sums (the token's column)
   float xsum[kPsMaxD / 16];         // sums of x16 over each EPS-element chunk (decode order)
   float hsum[2][kPsMaxF / 16];      // the same for the hi / lo parts of h
@@ -259,13 +263,14 @@ __device__ __forceinline__ void ps_gu_issue(const PsMat& Wg, const PsMat& Wu, in
     for (int m = 0; m < 2; ++m) g.c[m][u] = __builtin_nontemporal_load((const u32x4*)(cl[m] + min(u, nsteps - 1) * STEP_B));
 }
 
-// Weights of MFMA i of a step: exact values (NVFP4-style), or exact values
-// plus 1152 (Q8_0, IQ4_NL; the caller subtracts 1152 times the activation sum).
+// Weights of MFMA i of a step: exact values (NVFP4-style), exact values plus
+// 1152 (Q8_0, IQ4_NL; the caller subtracts 1152 times the activation sum), or
+// the codes q (Q5_1, whose d and m the caller applies; qh: the high-bit word).
 template <int FMT>
-__device__ __forceinline__ f16x8 ps_decode(const u32x4& c, int i, uint32_t sraw) {
+__device__ __forceinline__ f16x8 ps_decode(const u32x4& c, int i, uint32_t sraw, uint32_t qh = 0u) {
   if constexpr (FMT == MOE_IQ4_NL) return iq4_dword_to_f16x8_p1152(c[i]);
   else if constexpr (FMT == MOE_Q8_0) return q8_dwords_to_f16x8_p1152(c[2 * i], c[2 * i + 1]);
-  else return decode_b<FMT>(c, i, sraw);
+  else return decode_b<FMT>(c, i, sraw, qh);
 }
 
 template <int FMT>
@@ -351,10 +356,14 @@ __device__ __forceinline__ void ps_gu_compute(PsLds& S, const GuCodes<FMT>& g, i
 // h * 2^-ex) is the A operand's two columns; each wavefront 16 rows over all
 // of K = f.  ps_dn_issue puts the codes and scale rows in flight;
 // ps_dn_compute writes o = (hi + lo) * 2^ex of the rows.
+// 16-byte chunks of the item's scale rows per thread (Q5_1: up to 64 rows x
+// f / 32 records of 8 bytes)
+constexpr int ps_dn_sch(int fmt) { return fmt == MOE_Q5_1 ? 4 : 1; }
+
 template <int FMT>
 struct DnCodes {
   u32x4 c[FMT == MOE_Q8_0 ? 2 * kPsPD : kPsPD];
-  u32x4 s;
+  u32x4 s[ps_dn_sch(FMT)];
   float ts;
 };
 
@@ -370,9 +379,11 @@ __device__ __forceinline__ void ps_dn_issue(const PsMat& Wd, int e, int ct, int 
   const int kbase = G * EPS;
   const int row = ct * 64 + wid * 16 + n;
   const uint8_t* cl = Wd.codes + ((long)e * rows + row) * crb + (FMT == MOE_Q8_0 ? kbase : (kbase >> 1));
-  const int sch = 64 * srb / 16;  // at most 256: one chunk a thread (issued first)
-  g.s = __builtin_nontemporal_load(
-      (const u32x4*)(Wd.scales + ((long)e * rows + ct * 64) * srb + min(tid, sch - 1) * 16));
+  const int sch = 64 * srb / 16;  // at most 256 * ps_dn_sch (issued first)
+  const uint8_t* sbase = Wd.scales + ((long)e * rows + ct * 64) * srb;
+#pragma unroll
+  for (int j = 0; j < ps_dn_sch(FMT); ++j)
+    g.s[j] = __builtin_nontemporal_load((const u32x4*)(sbase + min(tid + 256 * j, sch - 1) * 16));
 #pragma unroll
   for (int u = 0; u < PD; ++u) g.c[u] = __builtin_nontemporal_load((const u32x4*)(cl + min(u, nsteps - 1) * STEP_B));
   g.ts = FMT == MOE_NVFP4 ? Wd.ts[e] : 1.0f;
@@ -392,7 +403,10 @@ __device__ __forceinline__ void ps_dn_compute(PsLds& S, const DnCodes<FMT>& g, i
   const int kbase = G * EPS;
   const int row = ct * 64 + wid * 16 + n;
   const int sch = 64 * srb / 16;
-  if (tid < sch) *(u32x4*)(S.sc + tid * 16) = g.s;  // (S.sc is free: the caller's barrier after staging h)
+  // (S.sc is free: the caller's barrier after staging h)
+#pragma unroll
+  for (int j = 0; j < ps_dn_sch(FMT); ++j)
+    if (tid + 256 * j < sch) *(u32x4*)(S.sc + (tid + 256 * j) * 16) = g.s[j];
   __syncthreads();
   // columns: hi (0) and lo (1)
   int c;
@@ -405,22 +419,36 @@ __device__ __forceinline__ void ps_dn_compute(PsLds& S, const DnCodes<FMT>& g, i
     c = n;
   }
   const f16* ap = valid ? S.hh[c] + kbase : S.zero;
-  const uint16_t* ssl = (const uint16_t*)(S.sc + (wid * 16 + n) * srb) + (kbase >> 5);
+  constexpr int SW = FMT == MOE_Q5_1 ? 4 : 1;  // 16-bit words per scale record
+  const uint16_t* ssl = (const uint16_t*)(S.sc + (wid * 16 + n) * srb) + (kbase >> 5) * SW;
   // D rows 0 and 1 hold the hi and lo columns (elements x and y)
   f32x2 acc = {0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < PD; ++s) {
     if (s < nsteps) {
-      const uint32_t ss = ssl[s * (4 * EPS / 32)];
+      uint32_t ss, qh = 0u;
+      if constexpr (FMT == MOE_Q5_1) {
+        const u32x2 rec = *(const u32x2*)(ssl + s * (4 * EPS / 32) * SW);
+        ss = rec.x;
+        qh = rec.y;
+      } else {
+        ss = ssl[s * (4 * EPS / 32)];
+      }
       f32x4 D = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < NMF; ++i) {
         const f16x8 a8 = *(const f16x8*)(ap + s * 4 * EPS + 8 * i);
-        D = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, ps_decode<FMT>(g.c[s], i, ss), D, 0, 0, 0);
+        D = __builtin_amdgcn_mfma_f32_16x16x32_f16(a8, ps_decode<FMT>(g.c[s], i, ss, qh), D, 0, 0, 0);
       }
       if constexpr (FMT == MOE_NVFP4) {
         acc.x += D.x;
         acc.y += D.y;
+      } else if constexpr (FMT == MOE_Q5_1) {
+        // w = d q + m: d times the code product plus m times the chunk's activation sum
+        const int chunk = (kbase >> 5) + 4 * s;
+        const float dd = f16_bits_to_f32(ss & 0xffffu), mm = f16_bits_to_f32(ss >> 16);
+        acc.x = fmaf(dd, D.x, fmaf(mm, S.hsum[0][chunk], acc.x));
+        acc.y = fmaf(dd, D.y, fmaf(mm, S.hsum[1][chunk], acc.y));
       } else {
         const int chunk = (kbase >> (EPS == 32 ? 5 : 4)) + 4 * s;
         const float sc = f16_bits_to_f32(ss);
@@ -685,7 +713,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
           slo += (float)lo;
         }
         if constexpr (DF != MOE_NVFP4) {
-          // chunk sums of the stored parts (the weights carry +1152)
+          // chunk sums of the stored parts (Q8_0 / IQ4_NL: the weights carry
+          // +1152; Q5_1: the block offset m multiplies them)
           constexpr int EPS = dq_eps(DF);
           shi = group_sum<EPS / 4>(shi);
           slo = group_sum<EPS / 4>(slo);
@@ -817,6 +846,7 @@ hipError_t launch_ps_d(int df, const PsArgs& a, int need, hipStream_t s, hipEven
   switch (df) {
     case MOE_Q8_0: return launch_ps<GF, MOE_Q8_0>(a, need, s, e0, e1);
     case MOE_IQ4_NL: return launch_ps<GF, MOE_IQ4_NL>(a, need, s, e0, e1);
+    case MOE_Q5_1: return launch_ps<GF, MOE_Q5_1>(a, need, s, e0, e1);
     default: return launch_ps<GF, MOE_NVFP4>(a, need, s, e0, e1);
   }
 }

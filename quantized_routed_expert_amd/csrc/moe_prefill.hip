@@ -180,12 +180,13 @@ constexpr int kPfThreads = 64 * kPfWaves;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Code bytes of one lane's block-sized chunk per stage: IQ4_NL / NVFP4 16 (32
-// elements), Q8_0 32.
+// Code bytes of one lane's block-sized chunk per stage: IQ4_NL / NVFP4 / Q5_1
+// 16 (32 elements), Q8_0 32.
 template <int FMT>
 struct PfCodes {
   u32x4 c[FMT == MOE_Q8_0 ? 2 : 1];
-  uint32_t sc;  // fp16 block scale, or two E4M3 scales (NVFP4)
+  uint32_t sc;  // fp16 block scale, two E4M3 scales (NVFP4), or Q5_1's d | m << 16
+  uint32_t qh;  // Q5_1: the block's high-bit word
 };
 
 template <int FMT>
@@ -196,18 +197,30 @@ __device__ __forceinline__ void pf_load_codes(const uint8_t* crow, const uint8_t
   } else {
     pc.c[0] = *(const u32x4*)(crow + (kel >> 1));
   }
-  pc.sc = ((const uint16_t*)srow)[kel >> 5];
+  if constexpr (FMT == MOE_Q5_1) {
+    const u32x2 rec = *(const u32x2*)(srow + (kel >> 5) * 8);
+    pc.sc = rec.x;
+    pc.qh = rec.y;
+  } else {
+    pc.sc = ((const uint16_t*)srow)[kel >> 5];
+    pc.qh = 0u;
+  }
 }
 
 // fp16 weights of MFMA i (code dword i of the lane's block-sized chunk):
 // Q8_0 / IQ4_NL: the exact code values (fp16 integers) times the fp16 block
 // scale, rounded once; NVFP4: e2m1 * e4m3, exact in fp16 (the tensor scale is
-// applied to the fp32 result).
+// applied to the fp32 result); Q5_1: d * q + m in fp16, one fused rounding.
 template <int FMT>
 __device__ __forceinline__ f16x8 pf_decode(const PfCodes<FMT>& pc, int i) {
   if constexpr (FMT == MOE_NVFP4) {
     const float sc = i < 2 ? e4m3_byte_to_f32<0>(pc.sc) : e4m3_byte_to_f32<1>(pc.sc);
     return fp4_dword_to_f16x8(pc.c[0][i], (f16)sc);
+  } else if constexpr (FMT == MOE_Q5_1) {
+    const f16 d = __builtin_bit_cast(f16, (uint16_t)(pc.sc & 0xffffu));
+    const f16 m = __builtin_bit_cast(f16, (uint16_t)(pc.sc >> 16));
+    const f16x8 dd = {d, d, d, d, d, d, d, d}, mm = {m, m, m, m, m, m, m, m};
+    return __builtin_elementwise_fma(q5_1_dword_to_f16x8(pc.c[0][i], pc.qh, i), dd, mm);
   } else {
     const f16 d = __builtin_bit_cast(f16, (uint16_t)pc.sc);
     const f16x8 dd = {d, d, d, d, d, d, d, d};
@@ -221,14 +234,23 @@ __device__ __forceinline__ f16x8 pf_decode(const PfCodes<FMT>& pc, int i) {
 // the format's largest code magnitude (Q8_0: 128, IQ4_NL: 127) overflow fp16
 // (it reaches 65520 and rounds to infinity); such scales, and non-finite ones,
 // are reported through error bit 8.  NVFP4-style products (at most 6 * 448)
-// are always finite.
+// are always finite.  A Q5_1 block's values d q + m lie between m (q = 0) and
+// 31 d + m (q = 31); they overflow when either end reaches 65520 in
+// magnitude (computed in fp32: exact, as 31 d and m are fp16 values whose sum
+// near 65520 needs far fewer than 24 bits), or when d or m is not finite.
 template <int FMT>
 constexpr uint32_t kPfScaleMax = FMT == MOE_Q8_0 ? 0x6000u /* 512.0 */ : 0x6008u /* 516.0 */;
 
 template <int FMT>
 __device__ __forceinline__ bool pf_scale_out_of_range(const PfCodes<FMT>& pc) {
-  if constexpr (FMT == MOE_NVFP4) return false;
-  return (pc.sc & 0x7fffu) >= kPfScaleMax<FMT>;
+  if constexpr (FMT == MOE_NVFP4) {
+    return false;
+  } else if constexpr (FMT == MOE_Q5_1) {
+    const float d = f16_bits_to_f32(pc.sc & 0xffffu), m = f16_bits_to_f32(pc.sc >> 16);
+    return !(fmaxf(fabsf(m), fabsf(fmaf(31.0f, d, m))) < 65520.0f);
+  } else {
+    return (pc.sc & 0x7fffu) >= kPfScaleMax<FMT>;
+  }
 }
 
 // Test hook: one expert's weights exactly as the prefill GEMM feeds them to
@@ -251,8 +273,8 @@ __global__ void k_dequant_pf(QMatDev m, int expert, f16* __restrict__ dst) {
     const f16x8 v = pf_decode<FMT>(pc, q);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      // IQ4_NL decodes elements 4q..4q+3 and 16+4q..16+4q+3; the others 8q..8q+7
-      const int el = FMT == MOE_IQ4_NL ? (u < 4 ? 4 * q + u : 16 + 4 * q + (u - 4)) : 8 * q + u;
+      // IQ4_NL and Q5_1 decode elements 4q..4q+3 and 16+4q..16+4q+3; the others 8q..8q+7
+      const int el = (FMT == MOE_IQ4_NL || FMT == MOE_Q5_1) ? (u < 4 ? 4 * q + u : 16 + 4 * q + (u - 4)) : 8 * q + u;
       o[el] = v[u];
     }
   }
@@ -264,6 +286,7 @@ hipError_t launch_dequant_pf(const QMatDev& m, int expert, void* dst, hipStream_
   switch (m.type) {
     case MOE_Q8_0: hipLaunchKernelGGL(k_dequant_pf<MOE_Q8_0>, grid, block, 0, s, m, expert, (f16*)dst); break;
     case MOE_IQ4_NL: hipLaunchKernelGGL(k_dequant_pf<MOE_IQ4_NL>, grid, block, 0, s, m, expert, (f16*)dst); break;
+    case MOE_Q5_1: hipLaunchKernelGGL(k_dequant_pf<MOE_Q5_1>, grid, block, 0, s, m, expert, (f16*)dst); break;
     default: hipLaunchKernelGGL(k_dequant_pf<MOE_NVFP4>, grid, block, 0, s, m, expert, (f16*)dst); break;
   }
   return hipGetLastError();
@@ -503,6 +526,9 @@ hipError_t launch_gemm(int fmt, int nf, const PrefillArgs& a, int grid, hipStrea
   switch (fmt) {
     case MOE_Q8_0: return launch_gemm_fmt<MOE_Q8_0, GATEUP>(nf, a, grid, s);
     case MOE_IQ4_NL: return launch_gemm_fmt<MOE_IQ4_NL, GATEUP>(nf, a, grid, s);
+    case MOE_Q5_1:
+      if constexpr (!GATEUP) return launch_gemm_fmt<MOE_Q5_1, false>(nf, a, grid, s);
+      return hipErrorInvalidValue;  // a down format only
     default: return launch_gemm_fmt<MOE_NVFP4, GATEUP>(nf, a, grid, s);
   }
 }

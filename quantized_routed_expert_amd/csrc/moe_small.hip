@@ -39,6 +39,18 @@ __global__ void k_dequant(QMatDev m, int expert, int out_bf16, void* dst) {
         v[16 + 4 * i4 + t] = (float)q[4 + t] * d;
       }
     }
+  } else if (m.type == MOE_Q5_1) {
+    // record: d, m, high-bit word; value fp32(d q + m), one rounding (fma)
+    const u32x2 rec = *(const u32x2*)(srow + b * 8);
+    const float d = f16_bits_to_f32(rec.x & 0xffffu), mo = f16_bits_to_f32(rec.x >> 16);
+    const u32x4 c = *(const u32x4*)(crow + b * 16);
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f16x8 q = q5_1_dword_to_f16x8(c[i4], rec.y, i4);
+      for (int t = 0; t < 4; ++t) {
+        v[4 * i4 + t] = fmaf((float)q[t], d, mo);
+        v[16 + 4 * i4 + t] = fmaf((float)q[4 + t], d, mo);
+      }
+    }
   } else {  // NVFP4: two 16-element blocks
     const float ts = m.ts[expert];
     const u32x4 c = *(const u32x4*)(crow + b * 16);

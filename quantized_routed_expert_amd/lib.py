@@ -29,8 +29,9 @@ MOE_F16 = 2
 MOE_Q8_0 = 1
 MOE_IQ4_NL = 2
 MOE_NVFP4 = 3
+MOE_Q5_1 = 4
 
-QTYPE = {"q8_0": MOE_Q8_0, "iq4_nl": MOE_IQ4_NL, "nvfp4": MOE_NVFP4}
+QTYPE = {"q8_0": MOE_Q8_0, "iq4_nl": MOE_IQ4_NL, "nvfp4": MOE_NVFP4, "q5_1": MOE_Q5_1}
 DTYPE = {"f32": MOE_F32, "bf16": MOE_BF16}
 
 EXPORTED = ["moe_route", "moe_plan", "moe_ffn_forward", "moe_ffn_prepare", "moe_ffn_gateup", "moe_ffn_down",

@@ -36,7 +36,7 @@ import torch
 # Encoder tables (the encode direction only).
 _IQ4_NL_VALUES = [-127, -104, -83, -65, -49, -35, -22, -10, 1, 13, 25, 38, 53, 69, 89, 113]
 
-QTYPE_ID = {"q8_0": 1, "iq4_nl": 2, "nvfp4": 3}
+QTYPE_ID = {"q8_0": 1, "iq4_nl": 2, "nvfp4": 3, "q5_1": 4}
 
 
 @dataclass(frozen=True)
@@ -154,6 +154,37 @@ def encode_iq4_nl(w):
     return codes, d16.squeeze(-1)
 
 
+def encode_q5_1(w):
+    """fp32 [..., rows, cols] -> (uint8 codes [..., rows, cols/2], uint8 block records
+    [..., rows, cols/32 * 8]).
+
+    Per 32-element block: d = fp16((max - min) / 31), m = fp16(min), q = the
+    nearest of 0..31 to (x - m) / d (halves up).  Codes hold the low four bits
+    in the IQ4_NL byte order (element j low nibble, j + 16 high nibble of byte
+    j); a record is d, m (binary16, little-endian) and a little-endian uint32
+    whose bit e is the fifth bit of element e."""
+    shp = w.shape
+    b = w.reshape(*shp[:-1], shp[-1] // 32, 32)
+    mn = b.amin(dim=-1)
+    mx = b.amax(dim=-1)
+    d16 = ((mx - mn) / 31.0).to(torch.float16)
+    m16 = mn.to(torch.float16)
+    dq = d16.float().unsqueeze(-1)
+    nz = dq > 0
+    r = (b - m16.float().unsqueeze(-1)) / torch.where(nz, dq, torch.ones_like(dq))
+    q = torch.where(nz, torch.floor(r + 0.5), torch.zeros_like(r)).clamp(0, 31).to(torch.int64)
+    low = q & 15
+    codes = (low[..., :16] | (low[..., 16:] << 4)).to(torch.uint8).reshape(*shp[:-1], shp[-1] // 2)
+    bit = torch.arange(32, device=w.device, dtype=torch.int64)
+    word = ((q >> 4) << bit).sum(dim=-1)
+    dbits = d16.view(torch.int16).to(torch.int64) & 0xFFFF
+    mbits = m16.view(torch.int16).to(torch.int64) & 0xFFFF
+    rec = torch.stack([dbits & 0xFF, dbits >> 8, mbits & 0xFF, mbits >> 8,
+                       word & 0xFF, (word >> 8) & 0xFF, (word >> 16) & 0xFF, (word >> 24) & 0xFF], dim=-1)
+    records = rec.to(torch.uint8).reshape(*shp[:-1], (shp[-1] // 32) * 8)
+    return codes.contiguous(), records.contiguous()
+
+
 def _e2m1_rne(r):
     """float -> E2M1 nibble, round to nearest, ties to even mantissa, saturating at 6."""
     a = r.abs()
@@ -205,6 +236,8 @@ def make_matrix(qtype, n, rows, cols, seed, device="cpu", chunk_elems=1 << 27):
         elif qtype == "nvfp4":
             c, s, t = encode_nvfp4(w)
             ts_l.append(t)
+        elif qtype == "q5_1":
+            c, s = encode_q5_1(w)
         else:
             raise ValueError(qtype)
         codes_l.append(c)

@@ -73,6 +73,10 @@ CASES = [
     # one token whose gate/up pass has more steps than are issued up front
     # (the separate gate/up and down launches)
     (("q8_0", "q8_0", "q8_0"), 1, 4096, 256, 600, 6, False),
+    # Q5_1 down projections: several tokens, and one token (the persistent step)
+    (("iq4_nl", "iq4_nl", "q5_1"), 4, 2048, 512, 128, 8, True),
+    (("q8_0", "q8_0", "q5_1"), 8, 1024, 256, 64, 4, False),
+    (("iq4_nl", "iq4_nl", "q5_1"), 1, 3072, 768, 512, 8, True),
 ]
 
 

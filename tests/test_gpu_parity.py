@@ -48,6 +48,30 @@ def _edge_matrix(qtype, n=2, rows=32, cols=256, seed=0):
         sc.reshape(-1)[:6] = [0x0000, 0x8000, 0x0001, 0x03FF, 0x7BFF, 0xFBFF]
         return {"type": qtype, "n": n, "rows": rows, "cols": cols, "codes": torch.from_numpy(codes),
                 "scales": torch.from_numpy(sc.view(np.int16)).view(torch.float16), "tensor_scale": None}
+    if qtype == "q5_1":
+        # every code byte; d and m of either sign over the finite binary16 range
+        # (subnormals, zeros, the maximum: 31 d + m then overflows fp16); random
+        # high-bit words with the all-zero and all-one words among them
+        codes = g.integers(0, 256, size=(n, rows, cols // 2)).astype(np.uint8)
+        codes.reshape(-1)[:256] = np.arange(256)
+        nb = cols // 32
+        d = g.integers(0, 0x7C00, size=(n, rows, nb)).astype(np.uint16)
+        d |= (g.integers(0, 2, size=d.shape) << 15).astype(np.uint16)
+        m = g.integers(0, 0x7C00, size=(n, rows, nb)).astype(np.uint16)
+        m |= (g.integers(0, 2, size=m.shape) << 15).astype(np.uint16)
+        d.reshape(-1)[:6] = [0x0000, 0x8000, 0x0001, 0x03FF, 0x7BFF, 0xFBFF]
+        m.reshape(-1)[:6] = [0x8000, 0x0000, 0x8001, 0x0400, 0x7BFF, 0x7BFF]
+        # ordinary blocks: m about -16 d, as an encoder produces
+        d.reshape(-1)[6:40] = 0x1C00
+        m.reshape(-1)[6:40] = 0xA800
+        qh = g.integers(0, 1 << 32, size=(n, rows, nb), dtype=np.uint64).astype(np.uint32)
+        qh.reshape(-1)[:2] = [0, 0xFFFFFFFF]
+        rec = np.zeros((n, rows, nb, 8), dtype=np.uint8)
+        rec[..., 0:2] = d.view(np.uint8).reshape(n, rows, nb, 2)
+        rec[..., 2:4] = m.view(np.uint8).reshape(n, rows, nb, 2)
+        rec[..., 4:8] = qh.astype("<u4").view(np.uint8).reshape(n, rows, nb, 4)
+        return {"type": qtype, "n": n, "rows": rows, "cols": cols, "codes": torch.from_numpy(codes),
+                "scales": torch.from_numpy(rec.reshape(n, rows, nb * 8).copy()), "tensor_scale": None}
     codes = g.integers(0, 256, size=(n, rows, cols // 2)).astype(np.uint8)
     codes.reshape(-1)[:256] = np.arange(256)
     finite = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], dtype=np.uint8)
@@ -58,7 +82,7 @@ def _edge_matrix(qtype, n=2, rows=32, cols=256, seed=0):
             "scales": torch.from_numpy(sc), "tensor_scale": torch.from_numpy(ts)}
 
 
-@pytest.mark.parametrize("qtype", ["q8_0", "iq4_nl", "nvfp4"])
+@pytest.mark.parametrize("qtype", ["q8_0", "iq4_nl", "nvfp4", "q5_1"])
 def test_dequantize_bit_exact(qtype):
     _say(f"[dequant] {qtype}")
     m = _edge_matrix(qtype)
@@ -71,14 +95,17 @@ def test_dequantize_bit_exact(qtype):
         out = torch.empty((m["rows"], m["cols"]), dtype=torch.float32, device=DEV)
         lib.moe_dequantize(q, e, lib.MOE_F32, out)
         got = out.cpu().numpy().astype(np.float64)
-        assert np.array_equal(got, want), f"{qtype} expert {e}: {np.sum(got != want)} mismatches"
+        # Q5_1: d q + m need not be an fp32 value; the fp32 output is its
+        # round-to-nearest-even (numpy's float64 -> float32 conversion rounds once)
+        want32 = want.astype(np.float32).astype(np.float64) if qtype == "q5_1" else want
+        assert np.array_equal(got, want32), f"{qtype} expert {e}: {np.sum(got != want32)} mismatches"
         outb = torch.empty((m["rows"], m["cols"]), dtype=torch.bfloat16, device=DEV)
         lib.moe_dequantize(q, e, lib.MOE_BF16, outb)
         gotb = outb.float().cpu().numpy().astype(np.float64)
-        assert np.array_equal(gotb, F.round_to_bf16(want)), f"{qtype} bf16 expert {e}"
+        assert np.array_equal(gotb, F.round_to_bf16(want32)), f"{qtype} bf16 expert {e}"
         # the prefill GEMM's fp16 weight tile, through its own decode routine:
-        # fp16 round-to-nearest-even of the exact product (NVFP4-style: without
-        # the tensor scale), infinities included
+        # fp16 round-to-nearest-even of the exact value (NVFP4-style: without
+        # the tensor scale; Q5_1: of d q + m), infinities included
         want16 = want if ts is None else F.dequant(qtype, host["codes"][e], host["scales"][e], 1.0)
         outh = torch.empty((m["rows"], m["cols"]), dtype=torch.float16, device=DEV)
         lib.moe_dequantize(q, e, lib.MOE_F16, outh)
@@ -226,7 +253,7 @@ def test_tiny_workload_full():
 
 
 FORMATS = [("iq4_nl", "iq4_nl", "iq4_nl"), ("iq4_nl", "iq4_nl", "q8_0"), ("nvfp4", "nvfp4", "nvfp4"),
-           ("q8_0", "q8_0", "q8_0")]
+           ("q8_0", "q8_0", "q8_0"), ("iq4_nl", "iq4_nl", "q5_1"), ("nvfp4", "nvfp4", "q5_1")]
 
 
 @pytest.mark.parametrize("types", FORMATS, ids=lambda t: "-".join(t))
@@ -385,6 +412,82 @@ def test_prefill_extreme_scales(types):
     layer["routed"]["gate"]["scales"][:, 5, 2] = 65504.0
     st, gpu = _run_single(layer, x, "bf16", "f32")
     assert int(st.bufs[0].plan.error.item()) & 8
+
+
+def _set_q5_1_records(mat, d_bits, m_bits):
+    """Overwrite d and m of every block record of a Q5_1 matrix (device tensors
+    of int32 binary16 bit patterns, one per block)."""
+    rec = mat["scales"].view(*mat["scales"].shape[:-1], -1, 8)
+    rec[..., 0] = (d_bits & 0xFF).to(torch.uint8)
+    rec[..., 1] = ((d_bits >> 8) & 0xFF).to(torch.uint8)
+    rec[..., 2] = (m_bits & 0xFF).to(torch.uint8)
+    rec[..., 3] = ((m_bits >> 8) & 0xFF).to(torch.uint8)
+
+
+def test_prefill_q5_1_extreme_records():
+    """Prefill with Q5_1 down projections at the edges of the fp16 weight
+    range: subnormal d and m (weights exact or 2^-11-accurate in fp16) keep
+    parity; a block whose 31 d + m reaches 65520 sets error bit 8, and so does
+    one whose m alone does."""
+    T = 100
+    _say("[prefill q5_1 extreme]")
+    wl, layer = _small_layer(710, d=256, f=128, E=8, k=2, types=("iq4_nl", "iq4_nl", "q5_1"), shared=False)
+    dn = layer["routed"]["down"]
+    nb = dn["scales"].shape[-1] // 8
+    g = torch.Generator(device=DEV).manual_seed(4)
+    shp = dn["scales"].shape[:-1] + (nb,)
+    d_bits = torch.randint(1, 0x400, shp, generator=g, device=DEV, dtype=torch.int32)
+    m_bits = torch.randint(1, 0x400, shp, generator=g, device=DEV, dtype=torch.int32) | 0x8000
+    _set_q5_1_records(dn, d_bits, m_bits)
+    x = torch.randn((T, wl.d), generator=torch.Generator().manual_seed(9)).to(torch.bfloat16)
+    st, gpu = _run_single(layer, x, "bf16", "f32")
+    assert int(st.bufs[0].plan.error.item()) == 0
+    lnp = synth.layer_to_numpy(layer)
+    stats = check_layer(lnp, x.float().numpy().astype(np.float64), gpu, "f64", TOL_PREFILL)
+    _say(f"[prefill q5_1 extreme] subnormal records: {stats}")
+    # d = 2114, m = -14: 31 d + m = 65520 exactly, the first value that rounds to infinity
+    rec = dn["scales"].view(*shp, 8)
+    for e in range(wl.E):
+        rec[e, 7, 1, 0:4] = torch.tensor([0x21, 0x68, 0x00, 0xCB], dtype=torch.uint8)
+    st, _ = _run_single(layer, x, "bf16", "f32")
+    assert int(st.bufs[0].plan.error.item()) & 8
+    # one below (m = -14 - 2^-7: 65519.99): in range
+    _set_q5_1_records(dn, d_bits, m_bits)
+    for e in range(wl.E):
+        rec[e, 7, 1, 0:4] = torch.tensor([0x21, 0x68, 0x01, 0xCB], dtype=torch.uint8)
+    st, _ = _run_single(layer, x, "bf16", "f32")
+    assert int(st.bufs[0].plan.error.item()) == 0
+    # m alone at the binary16 maximum's neighbourhood, d = 0: in range (65504)
+    # then an infinite m: out of range
+    for e in range(wl.E):
+        rec[e, 3, 2, 0:4] = torch.tensor([0x00, 0x00, 0xFF, 0x7B], dtype=torch.uint8)
+    st, _ = _run_single(layer, x, "bf16", "f32")
+    assert int(st.bufs[0].plan.error.item()) == 0
+    for e in range(wl.E):
+        rec[e, 3, 2, 0:4] = torch.tensor([0x00, 0x00, 0x00, 0x7C], dtype=torch.uint8)
+    st, _ = _run_single(layer, x, "bf16", "f32")
+    assert int(st.bufs[0].plan.error.item()) & 8
+
+
+def test_q5_1_gate_up_rejected():
+    """Q5_1 is a down format: a layer with Q5_1 gate / up projections is
+    rejected before any launch."""
+    _say("[q5_1 gate rejected]")
+    wl, layer = _small_layer(720, d=256, f=128, E=8, k=2, types=("q5_1", "q5_1", "q8_0"), shared=False)
+    L = lib.layer_struct(layer)
+    T = 4
+    plan = lib.Plan(T, 2, 8, DEV)
+    wsb = lib.moe_workspace_size(L, T)
+    ws = torch.empty((wsb,), dtype=torch.uint8, device=DEV)
+    x = torch.zeros((T, wl.d), dtype=torch.bfloat16, device=DEV)
+    idx = torch.zeros((T, 2), dtype=torch.int32, device=DEV)
+    idx[:, 1] = 1
+    w = torch.full((T, 2), 0.5, dtype=torch.float32, device=DEV)
+    y = torch.empty((T, wl.d), dtype=torch.float32, device=DEV)
+    lib.moe_plan(idx, T, 2, 8, plan, ws, wsb)
+    with pytest.raises(lib.MoeError) as ei:
+        lib.moe_ffn_forward(L, x, lib.MOE_BF16, T, w, plan, y, lib.MOE_F32, ws, wsb)
+    assert ei.value.status == lib.MOE_ERR_UNSUPPORTED
 
 
 # ---------------------------------------------------------------- full-size shapes

@@ -55,6 +55,9 @@ CASES = [
     (("q8_0", "q8_0", "nvfp4"), 1024, 384, 128, 3, False),
     (("nvfp4", "nvfp4", "iq4_nl"), 3072, 256, 1024, 8, False),
     (("q8_0", "q8_0", "q8_0"), 1024, 128, 16, 16, True),
+    # Q5_1 down projections (8-byte block records, several scale chunks a thread)
+    (("iq4_nl", "iq4_nl", "q5_1"), 3072, 768, 512, 8, True),
+    (("nvfp4", "nvfp4", "q5_1"), 1024, 256, 64, 4, False),
 ]
 
 

@@ -36,6 +36,26 @@ def test_iq4_nl_picks_nearest_codebook_entry():
                 assert idx[a, b, 32 * c + blocks[a, b, c]] == 0
 
 
+def test_q5_1_round_trip_within_half_step():
+    """The Q5_1 encoder's codes decode (through the oracle) to within half a
+    step d of the drawn weights, plus the rounding of the block minimum to m;
+    every code 0..31 is used and each block reaches both ends."""
+    w = torch.randn(2, 8, 128, generator=torch.Generator().manual_seed(2)) * 0.02
+    codes, rec = synth.encode_q5_1(w)
+    assert codes.shape == (2, 8, 64) and rec.shape == (2, 8, 32)
+    q, d, m = F.q5_1_unpack(codes.numpy(), rec.numpy())
+    wn = w.numpy().astype(np.float64).reshape(2, 8, 4, 32)
+    dq = F.dequant_q5_1(codes.numpy(), rec.numpy()).reshape(2, 8, 4, 32)
+    # slack: half a step, the rounding of the minimum to m, and at the top of
+    # the block the rounding of the step to binary16 (31 steps of it)
+    mn, mx = wn.min(-1), wn.max(-1)
+    slack = 0.5 * d + np.abs(m - mn) + 31.0 * np.abs(d - (mx - mn) / 31.0) + 1e-12
+    assert np.all(np.abs(dq - wn).max(-1) <= slack)
+    qb = q.reshape(2, 8, 4, 32)
+    assert set(np.unique(q)) == set(range(32))
+    assert np.all(qb.min(-1) == 0) and np.all(qb.max(-1) == 31)
+
+
 def test_nvfp4_codes_nearest_and_saturating():
     w = torch.randn(2, 4, 64, generator=torch.Generator().manual_seed(2)) * 0.02
     codes, sc, ts = synth.encode_nvfp4(w)

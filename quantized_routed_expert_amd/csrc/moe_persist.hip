@@ -19,8 +19,11 @@
 //           y = o_shared + sum_j w_j o_j (slot order), the next residual and
 //           its sum of squares.
 // Dependencies between workgroups are monotonic counters in the workspace
-// (zeroed by the set-up launch before the step): logits written, gate/up
-// tiles per slot, down items per column tile, combined tiles.  Increments to
+// (zeroed by the set-up launch before the step): gate/up tiles per slot, down
+// items per column tile, combined tiles.  The router logits carry their own
+// readiness: each is stored as one 64-bit word holding the value and the
+// layer's tag, and a workgroup that needs them polls the words themselves, so
+// the poll that finds the last one present has also read them all.  Increments to
 // one address serialise in the memory system (measured: about 40 ns each), so
 // each event that many workgroups signal is counted on several sub-counters,
 // one 256-byte line each, and a waiting wavefront polls all of them in one
@@ -57,11 +60,9 @@ constexpr int kPsPD = 6;  // steps of weight codes issued up front per matrix (g
 // i % (that event's sub-counter count).
 constexpr int kLine = 64;  // int32 per line
 constexpr int kMaxSlots = 33;             // k <= 32 routed + shared
-constexpr int kSubLogit = 32;             // router workgroups, by index
 constexpr int kSubTiles = 8;              // combined column tiles, by tile
 constexpr int kSubSlot = 4;               // gate/up tiles of a slot, by tile
-constexpr int kLnLogit = 0;
-constexpr int kLnTiles = kLnLogit + kSubLogit;
+constexpr int kLnTiles = 0;
 constexpr int kLnAbort = kLnTiles + kSubTiles;
 constexpr int kLnSlot = kLnAbort + 1;                   // kSubSlot lines per slot
 constexpr int kLnTileCnt = kLnSlot + kMaxSlots * kSubSlot;  // one line per column tile (d / 64 <= 64)
@@ -93,7 +94,7 @@ struct PsArgs {
   float* h;            // residual entering the stack, and leaving it
   float* rbuf[2];      // residuals between layers (by parity)
   float* ss[2];        // [d / 64] tile sums of squares of a residual (by parity)
-  float* logits[2];    // [E] router logits (by parity)
+  uint64_t* lgt[2];    // [E] router logits tagged with layer + 1 (by parity; zeroed by the set-up)
   float* hrow;         // [k + hs][f] SwiGLU rows by slot (slot 0 = shared when present)
   float* orow;         // [k + 1][d] down outputs: pair j at row j, shared at row k
   int32_t* sync;       // kNumCnt lines of counters
@@ -174,6 +175,50 @@ __device__ __forceinline__ bool ps_wait(const int32_t* c, int nsub, int narr, in
   }
   __syncthreads();
   return s_ok != 0;
+}
+
+// Poll the E tagged logits of one layer until every one carries `tag`; thread
+// t reads entries t + 256 i (i < PT) and, as each turns up, writes its value
+// to slog.  Entries already seen are not read again.  Bounded like ps_wait;
+// returns false if the poll ran out or another workgroup's wait did.  Ends
+// with a barrier (slog complete and visible) on success.
+template <int PT>
+__device__ __forceinline__ bool ps_poll_logits(const uint64_t* lg, int E, uint32_t tag, float* slog,
+                                               int32_t* abort_w, int32_t* err) {
+  __shared__ int s_stop[2];
+  const int tid = threadIdx.x;
+  uint32_t pend = 0u;
+#pragma unroll
+  for (int i = 0; i < PT; ++i)
+    if (tid + 256 * i < E) pend |= 1u << i;
+  for (uint32_t n = 1;; ++n) {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      if ((pend >> i) & 1u) {
+        const uint64_t v = __hip_atomic_load(lg + tid + 256 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((uint32_t)(v >> 32) == tag) {
+          slog[tid + 256 * i] = __uint_as_float((uint32_t)v);
+          pend &= ~(1u << i);
+        }
+      }
+    }
+    // (two stop words, by round parity: a word is rewritten only after every
+    // thread has passed the barrier that follows the reads of its last value)
+    if (tid == 0) {
+      int stop = 0;
+      if ((n & 15u) == 0u && __hip_atomic_load(abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) stop = 1;
+      if (n > kSpinMax) {
+        atomicOr(err, 16);
+        __hip_atomic_store(abort_w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        stop = 1;
+      }
+      s_stop[n & 1u] = stop;
+    }
+    const int np = __syncthreads_count(pend != 0u);
+    if (np == 0) return true;
+    if (s_stop[n & 1u]) return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
 }
 
 // threadIdx.x, recomputed where it is used: values derived from it are then
@@ -483,9 +528,8 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-template <int GF>
-__device__ __forceinline__ void ps_glue(PsLds& S, const float* r, const float* ssp, int d, float eps,
-                                        uint16_t* rec_x, f32x4 (&xv)[4]) {
+__device__ __forceinline__ void ps_glue_x(PsLds& S, const float* r, const float* ssp, int d, float eps,
+                                          uint16_t* rec_x, f32x4 (&xv)[4]) {
   const int tid = ps_tid(), lane = tid & 63, wid = tid >> 6;
   const int nq = d / 1024;
 #pragma unroll
@@ -506,7 +550,6 @@ __device__ __forceinline__ void ps_glue(PsLds& S, const float* r, const float* s
     tot = S.red1[0] + S.red1[1] + S.red1[2] + S.red1[3];
   }
   const float inv = 1.0f / sqrtf(tot / (float)d + eps);
-  float mx = 0.0f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     if (q < nq) {
@@ -515,9 +558,20 @@ __device__ __forceinline__ void ps_glue(PsLds& S, const float* r, const float* s
       xv[q] = f32x4{bf16_bits_to_f32(p0 & 0xffffu), bf16_bits_to_f32(p0 >> 16), bf16_bits_to_f32(p1 & 0xffffu),
                     bf16_bits_to_f32(p1 >> 16)};
       if (rec_x) *(u32x2*)(rec_x + (q * 256 + tid) * 4) = u32x2{p0, p1};
-      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xv[q].x), fabsf(xv[q].y)), fmaxf(fabsf(xv[q].z), fabsf(xv[q].w))));
     }
   }
+}
+
+// The second half of the glue: x (as produced by ps_glue_x) as scaled fp16 in
+// LDS, in the gate weights' decode order, with its scale and chunk sums.
+template <int GF>
+__device__ __forceinline__ void ps_glue_stage(PsLds& S, const f32x4 (&xv)[4], int d) {
+  const int tid = ps_tid(), lane = tid & 63, wid = tid >> 6;
+  const int nq = d / 1024;
+  float mx = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (q < nq) mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xv[q].x), fabsf(xv[q].y)), fmaxf(fabsf(xv[q].z), fabsf(xv[q].w))));
   mx = wave_max(mx);
   if (lane == 0) S.red1[4 + wid] = mx;
   __syncthreads();
@@ -588,8 +642,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int nS = k + hs;
   const int gu_per = f / 16, dn_per = d / 64;
   const int gu_total = nS * gu_per, dn_total = nS * dn_per;
-  const int n_router = min(G, E);
-  const bool has_x = w < E || w < gu_total;
+  const bool has_gu = w < gu_total;
+  const bool has_x = w < E || has_gu;
   const bool has_routed_gu = [&] {
     for (int it = w; it < gu_total; it += G)
       if (it / gu_per >= hs) return true;
@@ -615,24 +669,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     int32_t* err = a.rec_err ? a.rec_err + l : a.err_ws;
     const float* r_in = l == 0 ? a.h : a.rbuf[l & 1];
     float* r_out = l == L - 1 ? a.h : a.rbuf[(l + 1) & 1];
-    float* lg = a.logits[l & 1];
+    uint64_t* lg = a.lgt[l & 1];
+    const uint32_t ltag = (uint32_t)(l + 1);
 
-    // ---- glue and router
+    // ---- glue and router (the logits first: they gate every routed item)
     if (has_x) {
       if (l > 0 && !ps_wait(sync + kLnTiles * kLine, kSubTiles, dn_per, l, abort_w, err)) return;
       f32x4 xv[4];
-      ps_glue<GF>(S, r_in, l == 0 ? nullptr : a.ss[l & 1], d, a.eps,
-                  (w == 0 && a.rec_x) ? a.rec_x + (long)l * d : nullptr, xv);
+      ps_glue_x(S, r_in, l == 0 ? nullptr : a.ss[l & 1], d, a.eps,
+                (w == 0 && a.rec_x) ? a.rec_x + (long)l * d : nullptr, xv);
       for (int e = w; e < E; e += G) {
         if (e != w) ps_router_load(P.router_w, e, d, wv);  // (the first row is already in flight)
         const float bias = P.bias ? P.bias[e] : 0.0f;
         const float v = ps_router_dot(S, wv, xv, d, bias);
         if (tid == 0) {
-          st_ag(lg + e, v);
+          __hip_atomic_store(lg + e, ((uint64_t)ltag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
           if (a.rec_logits) a.rec_logits[(long)l * E + e] = v;
         }
       }
-      if (w < E) ps_arrive(sync + (kLnLogit + w % kSubLogit) * kLine);
+      if (has_gu) ps_glue_stage<GF>(S, xv, d);
     }
 
     // ---- gate/up of the shared expert (slot 0), which needs no routing
@@ -644,14 +700,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
     // ---- top-k and gate weights (every workgroup that needs them)
     if (needs_topk) {
-      if (!ps_wait(sync + kLnLogit * kLine, kSubLogit, n_router, l + 1, abort_w, err)) return;
-      for (int i4 = tid; i4 * 4 < E; i4 += 256) {
-        const f32x4 v = ld_ag4(lg, i4 * 16);  // (the buffer is padded past E)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (i4 * 4 + c < E) S.logit[i4 * 4 + c] = v[c];
-      }
-      __syncthreads();
+      if (!ps_poll_logits<PT>(lg, E, ltag, S.logit, abort_w, err)) return;
       wg_topk_tau<PT>(S.logit, E, k, S.tk_max, &S.tk_list[0][0], S.tk_cnt, S.tk_key, S.tk_idx, S.idx, S.wv);
       if (wid == 0) {
         const float v = lane < k ? S.wv[lane] : 0.0f;
@@ -764,6 +813,8 @@ struct PsSetupArgs {
   int32_t* rec_err;
   int n_layers;
   int32_t* err_ws;
+  uint64_t* lgt;  // both tagged logit arrays
+  int n_lgt;
 };
 
 __global__ __launch_bounds__(256) void k_ps_setup(const PsSetupArgs s) {
@@ -771,6 +822,7 @@ __global__ __launch_bounds__(256) void k_ps_setup(const PsSetupArgs s) {
   if (tid < s.count) s.table[s.l0 + tid] = s.L[tid];
   if (s.l0 == 0) {
     for (int i = tid; i < kNumCnt * kLine; i += 256) s.sync[i] = 0;  // (all counter lines)
+    for (int i = tid; i < s.n_lgt; i += 256) s.lgt[i] = 0ull;         // (no tag is 0)
     if (s.rec_err)
       for (int i = tid; i < s.n_layers; i += 256) s.rec_err[i] = 0;
     if (tid == 0) *s.err_ws = 0;
@@ -789,7 +841,7 @@ struct PsWs {
   int32_t* err_ws;
   float* rbuf[2];
   float* ss[2];
-  float* logits[2];
+  uint64_t* lgt[2];
   float* hrow;
   float* orow;
 };
@@ -808,9 +860,11 @@ PsWs carve_ps(void* ws, int d, int f, int E) {
     p += align_up((size_t)d * 4, 256);
     W.ss[i] = (float*)p;
     p += align_up((size_t)(d / 64) * 4, 256);
-    W.logits[i] = (float*)p;
-    p += align_up((size_t)E * 4, 256);
   }
+  // the two tagged logit arrays, contiguous (the set-up zeroes both)
+  W.lgt[0] = (uint64_t*)p;
+  W.lgt[1] = W.lgt[0] + E;
+  p += align_up((size_t)2 * E * 8, 256);
   W.hrow = (float*)p;
   p += align_up((size_t)kMaxSlots * f * 4, 256);
   W.orow = (float*)p;
@@ -855,7 +909,7 @@ hipError_t launch_ps_d(int df, const PsArgs& a, int need, hipStream_t s, hipEven
 
 size_t persist_ws_bytes(int d, int f, int E) {
   return align_up((size_t)kPsMaxLayers * sizeof(PsLayer), 256) + align_up((size_t)kNumCnt * kLine * 4, 256) + 256 +
-         2 * (align_up((size_t)d * 4, 256) + align_up((size_t)(d / 64) * 4, 256) + align_up((size_t)E * 4, 256)) +
+         2 * (align_up((size_t)d * 4, 256) + align_up((size_t)(d / 64) * 4, 256)) + align_up((size_t)2 * E * 8, 256) +
          align_up((size_t)kMaxSlots * f * 4, 256) + align_up((size_t)kMaxSlots * d * 4, 256);
 }
 
@@ -897,6 +951,8 @@ hipError_t launch_persist_step(const moe_layer* layers, int n_layers, float* h, 
     sa.rec_err = rec.error;
     sa.n_layers = n_layers;
     sa.err_ws = W.err_ws;
+    sa.lgt = W.lgt[0];
+    sa.n_lgt = 2 * L0.E;
     hipLaunchKernelGGL(k_ps_setup, dim3(1), dim3(256), 0, s, sa);
   }
   PsArgs a{};
@@ -912,7 +968,7 @@ hipError_t launch_persist_step(const moe_layer* layers, int n_layers, float* h, 
   for (int i = 0; i < 2; ++i) {
     a.rbuf[i] = W.rbuf[i];
     a.ss[i] = W.ss[i];
-    a.logits[i] = W.logits[i];
+    a.lgt[i] = W.lgt[i];
   }
   a.hrow = W.hrow;
   a.orow = W.orow;

@@ -245,10 +245,7 @@ struct PsLds {
   float xsum[kPsMaxD / 16];         // sums of x16 over each EPS-element chunk (decode order)
   float hsum[2][kPsMaxF / 16];      // the same for the hi / lo parts of h
   float logit[kPsMaxE];
-  uint64_t tk_list[4][64];
-  uint32_t tk_max[32];
-  int32_t tk_cnt[4];
-  uint32_t tk_key[64];
+  uint32_t tk_key[64];              // top-k candidates
   int32_t tk_idx[64];
   int32_t idx[32];                  // this layer's top-k, slot order
   float wv[32];                     // ... their logits, then their gate weights
@@ -701,8 +698,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     // ---- top-k and gate weights (every workgroup that needs them)
     if (needs_topk) {
       if (!ps_poll_logits<PT>(lg, E, ltag, S.logit, abort_w, err)) return;
-      wg_topk_tau<PT>(S.logit, E, k, S.tk_max, &S.tk_list[0][0], S.tk_cnt, S.tk_key, S.tk_idx, S.idx, S.wv);
+      // one wavefront selects (no barrier until the result is published)
       if (wid == 0) {
+        wave_topk<PT * 4>(S.logit, E, k, lane, S.tk_key, S.tk_idx, S.idx, S.wv);
         const float v = lane < k ? S.wv[lane] : 0.0f;
         const float vmax = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 0));
         const float ex = lane < k ? expf(v - vmax) : 0.0f;

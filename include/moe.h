@@ -116,7 +116,9 @@ typedef struct {
  *  n_active[1]      number of active experts
  *  error[1]         0, or bits set:
  *                     1 = an expert id outside [0, E) was dropped;
- *                     2 = an SwiGLU activation exceeded the fp16 range
+ *                     2 = an SwiGLU activation was not finite (T <= 64,
+ *                         where h is kept in fp32) or exceeded the fp16
+ *                         range (the prefill path, T > 64)
  *                         (moe_ffn_forward, moe_decode_stack);
  *                     4 = an id repeated within a token was dropped (a top-k
  *                         selection names each expert once; of repeats the
@@ -171,9 +173,10 @@ moe_status moe_plan(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
  *   s_t = the same with the shared expert (weight 1), if present
  *   y_t = s_t + sum_j topk_w[t][j] * o_{slot_row[t*k+j]}   (slots in order j)
  * x: device [T][d] of x_dtype; y: device [T][d] of y_dtype.  For T <= 64 the
- * decode path runs: exact dequantisation, fp32 accumulation (activations are
- * carried as fp16 hi/lo pairs, intermediate SwiGLU values must stay below
- * 65504 in magnitude; error bit 2 reports otherwise).  For T > 64 the prefill
+ * decode path runs: exact dequantisation, fp32 accumulation; tokens enter the
+ * products as fp16 with a power-of-two scale per token (fp32 tokens as hi/lo
+ * pairs), and each SwiGLU row h, formed in fp32, as fp16 hi/lo parts scaled by
+ * a power of two per row (error bit 2 if an h is not finite).  For T > 64 the prefill
  * path runs: weights are rounded to fp16 (code times block scale, rounded
  * once: relative error at most 2^-11, never a lossy subnormal, since a
  * product below 2^-14 has a subnormal scale and is then an exact multiple of
@@ -285,10 +288,9 @@ moe_status moe_decode_stack(const moe_layer* layers, int32_t n_layers, float* h,
  * at most 128 layers, and rows short enough that every step's weight codes
  * are issued up front (gate/up: d <= 3072 for IQ4_NL / NVFP4-style, 1536 for
  * Q8_0; down: f <= 768); unless the environment sets QRE_DECODE_LAUNCHES=1.
- * It computes the same layer: its SwiGLU rows h are kept in fp32 and scaled
- * by a power of two per row into fp16 hi / lo parts for the down products,
- * and a wait between its workgroups that does not end within its poll bound
- * sets error bit 16 in every layer's record still to run. */
+ * It computes the same layer with the same numerics, and a wait between its
+ * workgroups that does not end within its poll bound sets error bit 16 in
+ * every layer's record still to run. */
 int32_t moe_decode_stack_persistent(const moe_layer* layers, int32_t n_layers, int32_t T);
 
 /* Workspace bytes for moe_decode_stack on this layer shape with up to T_max

@@ -299,7 +299,7 @@ hipError_t launch_dq_down_table(const DecodeArgs& a, int fmt, int items, hipStre
 size_t decode_ws_bytes(int T, int d, int f, int k, int x_dtype) {
   const int P = x_dtype == MOE_F32 ? 2 : 1;
   const size_t R = (size_t)T * k + T;
-  return align_up(R * P * d * 2, 256) + align_up(R * P * 4, 256) + align_up(R * 2 * f * 2, 256) +
+  return align_up(R * P * d * 2, 256) + align_up(R * P * 4, 256) + align_up(R * f * 4, 256) + align_up(R * (f / 16) * 4, 256) +
          align_up(R * d * 4, 256) + align_up(((size_t)T * k + 2) * sizeof(SlotEnt), 256) + 256;
 }
 

@@ -164,6 +164,16 @@ __device__ __forceinline__ f16x8 q5_1_dword_to_f16x8(uint32_t w, uint32_t qh, in
   return q5_1_dword_to_f16x8_p1024(w, qh, i) + off;
 }
 
+// 16 bytes at byte offset `off` from the wavefront-uniform `base`, with the
+// cache-coherence bits of an agent-scope atomic load (sc1: a raw buffer load
+// that bypasses the XCDs' private L2 caches), for data another workgroup of
+// the same launch stored with agent-scope atomic stores.
+__device__ __forceinline__ f32x4 ld_ag4(const float* base, int off) {
+  constexpr int kSc1 = 16;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7fffffff, 0x00020000);
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
+}
+
 // Exponent e such that max|x| * 2^-e lies in [2^14, 2^15) (0 for an all-zero row).
 __device__ __forceinline__ int x16_exponent(float mx) {
   int ex = 0;

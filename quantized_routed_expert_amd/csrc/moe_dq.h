@@ -48,10 +48,16 @@ struct DecodeArgs {
   int T, k;
   int P;                   // fp16 parts per column: 1 (bf16 tokens), 2 (fp32 tokens, or h hi/lo)
   int ksplit;              // waves along K per 16-row tile (1, 2, 4)
-  const f16* in16;         // gate/up: X16 [T*P][d]; down: H16 [(T*k+T)*2][f]
+  const f16* in16;         // gate/up: X16 [T*P][d]
   const float* in_scale;   // gate/up: scale of each X16 row (a power of two)
-  f16* h16;                // gate/up output H16 [(T*k+T)*2][f]
-  int down_type;           // gate/up: layout of H16 rows (IQ4_NL: block-permuted)
+  // SwiGLU rows: the gate/up pass writes h in fp32 (positions in the down
+  // weights' decode order) and the largest |h| of each row over each of its
+  // 16-feature tiles (float bits); the down pass stages h scaled by a power
+  // of two per row as fp16 hi / lo parts and applies the power of two to its
+  // result
+  float* hf;               // [(T*k+T)][f]
+  uint32_t* hmax;          // [(T*k+T)][f / 16]
+  int down_type;           // gate/up: layout of the h rows (IQ4_NL, Q5_1: block-permuted)
   float* o;                // down output O [(T*k+T)][d]
   const int32_t* pair_of_row;  // fused down pass: O row of each plan row (t*k + j); null: the plan row
   // fused down pass: the combine, formed by the last workgroup of each
@@ -94,7 +100,8 @@ __device__ __forceinline__ void dq_pin_args(const DecodeArgs& a) {
   pin_arg(a.down_type);
   pin_arg(a.in16);
   pin_arg(a.in_scale);
-  pin_arg(a.h16);
+  pin_arg(a.hf);
+  pin_arg(a.hmax);
   pin_arg(a.o);
   pin_arg(a.pair_of_row);
   pin_arg(a.error);
@@ -155,6 +162,9 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
   // one word per column of a pass for the epilogue: the token's activation
   // scale (gate/up) or the output row (PAIRS)
   __shared__ uint32_t s_colw[4 * 8];
+  __shared__ uint32_t s_colx[4 * 8];  // down pass: the power of two of each column's row
+  __shared__ float s_tdown[4 * 4];    // ... and its inverse, by row of the pass (at most CPP / 2 = 16)
+  constexpr int AST = GATEUP ? 1 : 2;  // down pass: hi / lo parts interleaved in 8-element runs
   constexpr int EPS = dq_eps(FMT);                   // elements per lane per step (one 16-byte load)
   constexpr int NMF = EPS / 8;                       // MFMAs per step
   constexpr bool BD = FMT != MOE_NVFP4;              // block-diagonal activations
@@ -193,19 +203,15 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
   // contiguous across the lane groups (64 bytes per row per step).
   const int kbase = kpart * kw + G * EPS;
 
-  // input row of column `col` (a token, or one fp16 part of it).  GATHER
-  // (per-layer path): the preparation wrote the gate/up input in plan-row
-  // order (rows T*k + t: the shared expert's), so a slot's rows are
+  // gate/up input row of column `col` (a token, or one fp16 part of it).
+  // GATHER (per-layer path): the preparation wrote the gate/up input in
+  // plan-row order (rows T*k + t: the shared expert's), so a slot's rows are
   // consecutive; fused path: one row per token, found through the plan.
   auto in_row_of = [&](int col) -> long {
-    if constexpr (GATEUP) {
-      const int tc = col / P, part = col - tc * P;
-      if constexpr (GATHER) return (long)(si.row0 + tc) * P + part;
-      const int t = si.is_sh ? tc : row_token[si.row0 + tc];
-      return (long)t * P + part;
-    } else {
-      return (long)(si.row0 + col / 2) * 2 + (col & 1);
-    }
+    const int tc = col / P, part = col - tc * P;
+    if constexpr (GATHER) return (long)(si.row0 + tc) * P + part;
+    const int t = si.is_sh ? tc : row_token[si.row0 + tc];
+    return (long)t * P + part;
   };
 
   const int chunks_per_col = K / 8;  // 16-byte activation chunks per column
@@ -258,14 +264,40 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
     // ---- the first batch of this pass's activation chunks, issued before the
     // weight codes so that waiting for them does not wait for the codes
     // (REUSE: the chunks go straight to LDS below instead)
+    // 16-byte staging chunk ch lands at LDS byte 16 ch.  Gate/up: chunk kk / 8
+    // of column c (column-major fp16).  Down: the pass's h rows, consecutive
+    // fp32 rows of the workspace, copied as they are (row t of the pass at
+    // bytes [4Kt, 4K(t+1)); converted in place below).
+    const float* hsrc = GATEUP ? nullptr : a.hf + (long)(si.row0 + c0 / 2) * K;
+    // down: the tile maxima of the pass's rows (wavefront w: rows w, w + 4,
+    // ... of the pass), loaded first so that they land before everything else
+    constexpr int QH = (CPP / 2 + 3) / 4;
+    uint32_t hmb[QH];
+#pragma unroll
+    for (int q = 0; q < QH; ++q) hmb[q] = 0u;
+    if constexpr (!GATEUP) {
+      const int nt16 = K / 16;
+#pragma unroll
+      for (int q = 0; q < QH; ++q) {
+        const int t = wid + 4 * q;
+        if (t * 2 < ncp) {
+          const uint32_t* hm = a.hmax + (long)(si.row0 + c0 / 2 + t) * nt16;
+          for (int i = lane; i < nt16; i += 64) hmb[q] = max(hmb[q], hm[i]);
+        }
+      }
+    }
+    auto chunk_src = [&](int ch) -> const u32x4* {
+      if constexpr (GATEUP) {
+        const int c = ch / chunks_per_col, kk = (ch - c * chunks_per_col) * 8;
+        return (const u32x4*)(a.in16 + in_row_of(c0 + c) * K + kk);
+      } else {
+        return (const u32x4*)hsrc + ch;
+      }
+    };
     u32x4 av[REUSE ? 1 : AB];
     if constexpr (!REUSE) {
 #pragma unroll
-      for (int b = 0; b < AB; ++b) {
-        const int ch = min(tid + b * 256, nch - 1);
-        const int c = ch / chunks_per_col, kk = (ch - c * chunks_per_col) * 8;
-        av[b] = *(const u32x4*)(a.in16 + in_row_of(c0 + c) * K + kk);
-      }
+      for (int b = 0; b < AB; ++b) av[b] = *chunk_src(min(tid + b * 256, nch - 1));
     }
     uint32_t cw = 0;
     {
@@ -296,51 +328,71 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
       typedef __attribute__((address_space(3))) void lds_void_t;
       for (int q = wid; q * 64 < nch; q += 4) {
         const int ch = q * 64 + lane;
-        if (ch < nch) {
-          const int c = ch / chunks_per_col, kk = (ch - c * chunks_per_col) * 8;
-          __builtin_amdgcn_global_load_lds((const void*)(a.in16 + in_row_of(c0 + c) * K + kk),
-                                           (lds_void_t*)(sA + q * 512), 16, 0, 0);
-        }
+        if (ch < nch) __builtin_amdgcn_global_load_lds((const void*)chunk_src(ch), (lds_void_t*)(sA + q * 512), 16, 0, 0);
       }
     } else {
 #pragma unroll
       for (int b = 0; b < AB; ++b) {
         const int ch = tid + b * 256;
-        if (ch < nch) {
-          const int c = ch / chunks_per_col, kk = (ch - c * chunks_per_col) * 8;
-          *(u32x4*)&sA[c * K + kk] = av[b];
-        }
+        if (ch < nch) *(u32x4*)&sA[ch * 8] = av[b];
       }
     }
     if (tid < ncp) s_colw[tid] = cw;
+    if constexpr (!GATEUP) {
+      // the power of two of each row of the pass: its largest |h| into
+      // [2^14, 2^15)
+#pragma unroll
+      for (int q = 0; q < QH; ++q) {
+        const int t = wid + 4 * q;
+        const int ex = x16_exponent(__uint_as_float(wave_max_u32(hmb[q])));
+        if (t * 2 < ncp) {
+          if (lane < 2) s_colx[2 * t + lane] = __float_as_uint(ldexpf(1.0f, ex));
+          if (lane == 0) s_tdown[t] = ldexpf(1.0f, -ex);
+        }
+      }
+    }
     if (c0 == 0) {
       // the item's scales (the first chunks were loaded with the activations)
 #pragma unroll
       for (int b = 0; b < SB; ++b)
         if (tid + b * 256 < s_chunks) *(u32x4*)(sS + (tid + b * 256) * 16) = sv[b];
       for (int ch = tid + SB * 256; ch < s_chunks; ch += 256) *(u32x4*)(sS + ch * 16) = *s_src(ch);
-      for (int z = tid; z < kw / 8; z += 256) *(u32x4*)&sA[zoff + z * 8] = u32x4{0u, 0u, 0u, 0u};
+      for (int z = tid; z < AST * kw / 8; z += 256) *(u32x4*)&sA[zoff + z * 8] = u32x4{0u, 0u, 0u, 0u};
     }
     // the rest in batches of RB loads in flight per thread
     if constexpr (REUSE) __builtin_amdgcn_s_waitcnt(0);  // the DMA chunks (and the codes) have landed
     for (int ch0 = tid + AB * 256; !REUSE && ch0 < nch; ch0 += RB * 256) {
       u32x4 bv[RB];
 #pragma unroll
-      for (int b = 0; b < RB; ++b) {
-        const int ch = min(ch0 + b * 256, nch - 1);
-        const int c = ch / chunks_per_col, kk = (ch - c * chunks_per_col) * 8;
-        bv[b] = *(const u32x4*)(a.in16 + in_row_of(c0 + c) * K + kk);
-      }
+      for (int b = 0; b < RB; ++b) bv[b] = *chunk_src(min(ch0 + b * 256, nch - 1));
 #pragma unroll
       for (int b = 0; b < RB; ++b) {
         const int ch = ch0 + b * 256;
-        if (ch < nch) {
-          const int c = ch / chunks_per_col, kk = (ch - c * chunks_per_col) * 8;
-          *(u32x4*)&sA[c * K + kk] = bv[b];
-        }
+        if (ch < nch) *(u32x4*)&sA[ch * 8] = bv[b];
       }
     }
     __syncthreads();
+    if constexpr (!GATEUP) {
+      // h rows in place: each 32-byte run of eight fp32 values becomes the
+      // eight scaled fp16 hi parts, then the eight lo parts (one thread reads
+      // and rewrites its own run, so no run is read after another's write)
+      uint8_t* sb = (uint8_t*)sA;
+      const int runs = nch / 2, runs_per_row = K / 8;
+      for (int j = tid; j < runs; j += 256) {
+        const float dn = s_tdown[j / runs_per_row];
+        const f32x4 v0 = *(const f32x4*)(sb + j * 32), v1 = *(const f32x4*)(sb + j * 32 + 16);
+        f16x8 hi, lo;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float sv = (c < 4 ? v0[c] : v1[c - 4]) * dn;
+          hi[c] = (f16)sv;
+          lo[c] = (f16)(sv - (float)hi[c]);
+        }
+        *(f16x8*)(sb + j * 32) = hi;
+        *(f16x8*)(sb + j * 32 + 16) = lo;
+      }
+      __syncthreads();
+    }
 
     // A-operand LDS position for each N-tile (this lane is A row m = n, K
     // slice G); lanes without a column read the zero region instead
@@ -356,7 +408,8 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
         valid = n < CPT;
         c = jt * CPT + n;
       }
-      abase[jt] = (valid && c < ncp) ? c * K + kbase : zoff;
+      // (down: column c is part c & 1 of the pass's row c / 2)
+      abase[jt] = (valid && c < ncp) ? (GATEUP ? c * K + kbase : (c >> 1) * 2 * K + (c & 1) * 8 + 2 * kbase) : zoff;
     }
 
     f32x4 acc[NMAT][NT];
@@ -385,7 +438,7 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
       for (int jt = 0; jt < NT; ++jt)
 #pragma unroll
         for (int i = 0; i < NMF; ++i) {
-          ac[jt][i] = *(const f16x8*)&sA[abase[jt] + s * 4 * EPS + 8 * i];
+          ac[jt][i] = *(const f16x8*)&sA[abase[jt] + AST * (s * 4 * EPS + 8 * i)];
         }
       // Q5_1: the activation sum of each column over the lane group's chunk
       // (an MFMA against ones), which the block offset m multiplies
@@ -516,34 +569,41 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
         }
 #pragma unroll
         for (int v = 0; v < 4; v += 1) {
+          // column of this lane group (uniform across its 16 lanes, n = 0..15)
           int cl;
+          bool ok;
           if constexpr (BD) {
-            if (P == 1 ? (v != G) : (v != 2 * G)) continue;
+            ok = P == 1 ? (v == G) : (v == 2 * G);
             cl = jt * CPT + v;
           } else {
-            if (P == 2 && (v & 1)) continue;
+            ok = !(P == 2 && (v & 1)) && 4 * G + v < CPT;
             cl = jt * CPT + 4 * G + v;
-            if (4 * G + v >= CPT) continue;
           }
-          if (cl >= ncp) continue;
+          ok = ok && cl < ncp;
           const int tc = (c0 + cl) / P;
           float val[NMAT];
 #pragma unroll
-          for (int m = 0; m < NMAT; ++m) val[m] = (P == 2) ? vals[m][v] + vals[m][v + 1] : vals[m][v];
+          for (int m = 0; m < NMAT; ++m) val[m] = (P == 2 && v < 3) ? vals[m][v] + vals[m][v + 1] : vals[m][v];
           const int out_row = si.row0 + tc;
           if constexpr (GATEUP) {
-            const int t = si.is_sh ? tc : row_token[si.row0 + tc];
-            const float xs = __uint_as_float(s_colw[cl]);
-            const float g = val[0] * xs, u = val[1] * xs;
-            const float h = silu_f(g) * u;
-            if (!(fabsf(h) < 65504.0f)) atomicOr(a.error, 2);
-            const f16 hi = (f16)h;
-            const f16 lo = (f16)(h - (float)hi);
-            const int f = rows;
-            const int pos = act_pos(a.down_type, frow);
-            a.h16[((long)out_row * 2 + 0) * f + pos] = hi;
-            a.h16[((long)out_row * 2 + 1) * f + pos] = lo;
-          } else {
+            float h = 0.0f;
+            if (ok) {
+              const float xs = __uint_as_float(s_colw[cl]);
+              const float g = val[0] * xs, u = val[1] * xs;
+              h = silu_f(g) * u;
+              if (!(fabsf(h) <= 3.4028235e38f)) atomicOr(a.error, 2);
+              a.hf[(long)out_row * rows + act_pos(a.down_type, frow)] = h;
+            }
+            // the row's largest |h| over the tile's 16 features (a row of 16
+            // lanes)
+            uint32_t hb = __float_as_uint(fabsf(h));
+            hb = max(hb, dpp_u32<kDppShr1, 0xf>(hb));
+            hb = max(hb, dpp_u32<kDppShr2, 0xf>(hb));
+            hb = max(hb, dpp_u32<kDppShr4, 0xf>(hb));
+            hb = max(hb, dpp_u32<kDppShr8, 0xf>(hb));
+            if (ok && n == 15) a.hmax[(long)out_row * (rows / 16) + tile] = hb;
+          } else if (ok) {
+            val[0] *= __uint_as_float(s_colx[cl]);  // the row's power of two (exact)
             // fused path: routed rows go to their (token, slot) pair's row
             const int orow = (PAIRS && !si.is_sh) ? (int)s_colw[cl] : out_row;
             if constexpr (PAIRS) {
@@ -567,7 +627,8 @@ __device__ __forceinline__ void dq_item(const DecodeArgs& a, const SlotInfo& si,
 struct DecodeWs {
   f16* x16;
   float* xs;
-  f16* h16;
+  float* hf;
+  uint32_t* hmax;
   float* o;
   SlotEnt* slots;    // per-layer slot table (see DecodeArgs::slots), T*k + 2 entries
   int32_t* n_slots;
@@ -583,8 +644,10 @@ inline DecodeWs carve(void* ws, int T, int d, int f, int k, int P) {
   p += align_up(R * P * d * 2, 256);
   w.xs = (float*)p;
   p += align_up(R * P * 4, 256);
-  w.h16 = (f16*)p;
-  p += align_up(R * 2 * f * 2, 256);
+  w.hf = (float*)p;
+  p += align_up(R * f * 4, 256);
+  w.hmax = (uint32_t*)p;
+  p += align_up(R * (f / 16) * 4, 256);
   w.o = (float*)p;
   p += align_up(R * d * 4, 256);
   w.slots = (SlotEnt*)p;
@@ -595,10 +658,10 @@ inline DecodeWs carve(void* ws, int T, int d, int f, int k, int P) {
 
 // Dynamic LDS of a decode pass: nt N-tiles of staged activations (or the K
 // reduction's partial sums), the scale rows of the workgroup's tiles for each
-// of nmat matrices, and K / ksplit zero halves.
+// of nmat matrices, and 2 K / ksplit zero halves.
 inline size_t dq_lds_bytes(int fmt, int cpt, int nt, int K, int ksplit, int nmat) {
   const size_t act = (size_t)nt * cpt * K * 2, red = (size_t)4 * nmat * nt * 64 * 16;
-  return (act > red ? act : red) + (size_t)nmat * (64 / ksplit) * scale_row_bytes(fmt, K) + (size_t)(K / ksplit) * 2;
+  return (act > red ? act : red) + (size_t)nmat * (64 / ksplit) * scale_row_bytes(fmt, K) + (size_t)(K / ksplit) * 4;
 }
 
 // Waves along K per 16-row tile: as many as divide the lane-group step count.
@@ -634,7 +697,8 @@ inline DecodeArgs gateup_args(const moe_layer& L, int T, int P, const DecodeWs& 
   a.ksplit = pick_ksplit(L.d, eps);
   a.in16 = w.x16;
   a.in_scale = w.xs;
-  a.h16 = w.h16;
+  a.hf = w.hf;
+  a.hmax = w.hmax;
   a.down_type = L.down.type;
   return a;
 }
@@ -648,7 +712,8 @@ inline DecodeArgs down_args(const moe_layer& L, int T, const DecodeWs& w) {
   if (L.has_shared) a.smat[0] = qmat_dev(L.shared_down);
   a.P = 2;
   a.ksplit = 1;
-  a.in16 = w.h16;
+  a.hf = w.hf;
+  a.hmax = w.hmax;
   a.o = w.o;
   return a;
 }

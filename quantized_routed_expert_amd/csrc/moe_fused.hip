@@ -301,7 +301,7 @@ __global__ __launch_bounds__(256) void k_fz_route(const FzRouteArgs a) {
 // ascending id order.  Workgroup 0 publishes the plan for the down pass and
 // the next layer's combine.
 struct FzGateArgs {
-  DecodeArgs a;  // gate/up pass arguments (in16 = x16, in_scale = xs, h16, error)
+  DecodeArgs a;  // gate/up pass arguments (in16 = x16, in_scale = xs, hf, hmax, error)
   const float* logits;
   int E;
   FusedPlan plan;

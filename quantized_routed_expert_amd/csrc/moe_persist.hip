@@ -69,7 +69,6 @@ constexpr int kLnTileCnt = kLnSlot + kMaxSlots * kSubSlot;  // one line per colu
 constexpr int kNumCnt = kLnTileCnt + 64;
 
 constexpr uint32_t kSpinMax = 1u << 20;  // polls of one wait before it gives up
-constexpr int kSc1 = 16;                 // cache-policy bits of an agent-scope load (sc1)
 
 }  // namespace
 
@@ -112,13 +111,6 @@ __device__ __forceinline__ float ld_ag(const float* p) {
 }
 __device__ __forceinline__ void st_ag(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// 16 bytes at byte offset `off` from the wavefront-uniform `base`, with the
-// cache-coherence bits of an agent-scope atomic load (a raw buffer load).
-__device__ __forceinline__ f32x4 ld_ag4(const float* base, int off) {
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7fffffff, 0x00020000);
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
 }
 
 // Every store of the workgroup has completed; then one increment of counter c

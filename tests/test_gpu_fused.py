@@ -131,3 +131,28 @@ def test_fused_repeatable_and_graph_replay(T):
     st.step()
     torch.cuda.synchronize()
     assert torch.equal(st.h, ref)
+
+
+@pytest.mark.parametrize("T", [2, 8])
+def test_fused_small_activations(T):
+    """SwiGLU outputs about 1e-5 (gate and up scales divided by 2^7) through
+    the per-layer launches of the fused step: h rows are scaled by a power of
+    two before the fp16 split, so the 1e-4 bar holds."""
+    wl = synth.Workload("t", d=1024, f=256, E=64, k=4, T=T, n_layers=2, gate_type="iq4_nl", up_type="iq4_nl",
+                        down_type="q8_0", shared=True, x_dtype="bf16", y_dtype="f32", zipf_s=1.1,
+                        tokens="walk", seed=950 + T, stack=True)
+    layers = [synth.make_layer(wl, l, DEV) for l in range(2)]
+    for L in layers:
+        for grp in ("routed", "shared"):
+            for n in ("gate", "up"):
+                L[grp][n]["scales"].mul_(2.0 ** -7)
+    st = FusedStack(layers, T, record=True, device=DEV)
+    st.set_tokens(synth.make_tokens(wl, DEV))
+    st.step()
+    torch.cuda.synchronize()
+    stats = _check_fused(wl, layers, st, TOL_DECODE)
+    lnp = synth.layer_to_numpy(layers[0])
+    _, parts = M.moe_layer(lnp, to_np(st.xs[0])[:1], "f64", return_parts=True)
+    hmax = max(np.abs(parts["h_rows"]).max(), np.abs(parts["h_shared"]).max())
+    _say(f"[fused small h] T={T} max |h| {hmax:.2e}; {stats}")
+    assert hmax < 1e-4

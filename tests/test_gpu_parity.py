@@ -334,15 +334,58 @@ def test_prefill_narrow_shapes_fp32_tokens(types):
     _say(f"[prefill narrow] {stats}")
 
 
-def test_swiglu_overflow_is_flagged():
-    _say("[overflow]")
+@pytest.mark.parametrize("T", [2, 80])
+def test_swiglu_overflow_is_flagged(T):
+    """Error bit 2: the decode path (T <= 64) keeps h in fp32 and scales each
+    row into fp16 parts, so it flags only an h that is not finite (here:
+    tokens of 1e25 against gate / up scales of 30000); the prefill path flags
+    an h beyond the fp16 range (scales of 30000 suffice)."""
+    _say(f"[overflow] T={T}")
     wl, layer = _small_layer(7, d=256, f=128, E=8, k=2, types=("q8_0", "q8_0", "q8_0"))
     for n in ("gate", "up"):
         layer["routed"][n]["scales"].fill_(30000.0)
         layer["shared"][n]["scales"].fill_(30000.0)
-    x = torch.randn((2, wl.d)).to(torch.bfloat16)
-    st, _ = _run_single(layer, x, "bf16", "f32")
+    x = torch.randn((T, wl.d)) * (1e25 if T <= 64 else 1.0)
+    st, _ = _run_single(layer, x.to(torch.bfloat16), "bf16", "f32")
     assert int(st.bufs[0].plan.error.item()) & 2
+    if T <= 64:
+        # the same weights on ordinary tokens: h up to about 1e13, finite, no flag
+        st, _ = _run_single(layer, torch.randn((T, wl.d)).to(torch.bfloat16), "bf16", "f32")
+        assert int(st.bufs[0].plan.error.item()) == 0
+
+
+def _shrink_gate_up(layer, factor):
+    for grp in ("routed", "shared"):
+        if layer.get(grp) is None:
+            continue
+        for n in ("gate", "up"):
+            m = layer[grp][n]
+            if m["type"] == "nvfp4":
+                m["tensor_scale"].mul_(factor)
+            else:
+                m["scales"].mul_(factor)
+
+
+@pytest.mark.parametrize("types", [("iq4_nl", "iq4_nl", "iq4_nl"), ("q8_0", "q8_0", "q5_1"),
+                                   ("nvfp4", "nvfp4", "nvfp4")], ids=lambda t: "-".join(t))
+@pytest.mark.parametrize("T", [1, 8, 37, 64])
+def test_decode_path_small_activations(types, T):
+    """SwiGLU outputs about 1e-5 (gate and up scales divided by 2^7): each h
+    row is scaled by a power of two before it is split into fp16 parts, so
+    the decode path keeps its 1e-4 bar."""
+    _say(f"[decode small h] {types} T={T}")
+    wl, layer = _small_layer(900 + T, d=512, f=256, E=16, k=4, types=types)
+    _shrink_gate_up(layer, 2.0 ** -7)
+    x = torch.randn((T, wl.d), generator=torch.Generator().manual_seed(T)).to(torch.bfloat16)
+    st, gpu = _run_single(layer, x, "bf16", "f32")
+    assert int(st.bufs[0].plan.error.item()) == 0
+    lnp = synth.layer_to_numpy(layer)
+    xn = x.float().numpy().astype(np.float64)
+    stats = check_layer(lnp, xn, gpu, "f32", TOL_DECODE)
+    _, parts = M.moe_layer(lnp, xn[:1], "f64", return_parts=True)
+    hmax = max(np.abs(parts["h_rows"]).max(), np.abs(parts["h_shared"]).max())
+    _say(f"[decode small h] max |h| (token 0) {hmax:.2e}; {stats}")
+    assert hmax < 1e-4
 
 
 @pytest.mark.parametrize("T", [5, 40, 100])

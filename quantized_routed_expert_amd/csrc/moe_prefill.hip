@@ -161,9 +161,9 @@ __global__ __launch_bounds__(256) void k_pf_prepare(const void* __restrict__ x, 
 //
 // Four wavefronts each hold all M rows of the tile and NF = 4 weight-row
 // fragments, so a decoded weight fragment feeds up to eight MFMAs and an A
-// fragment read from LDS feeds four; two workgroups share a CU (IQ4_NL: at
-// most 256 registers per lane), so that one wavefront's MFMAs overlap the
-// other's LDS reads and weight decode on each SIMD.  A tile is computed over
+// fragment read from LDS feeds four; where the registers allow (see
+// pf_min_blocks) two workgroups share a CU, so that one wavefront's MFMAs
+// overlap the other's LDS reads and weight decode on each SIMD.  A tile is computed over
 // its first NMF = 2, 4 or 8 M fragments only (enough for its rows): rows past
 // the slot's end in the last fragments are copied from its first row and
 // never stored.
@@ -406,6 +406,9 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sAbuf, fl
         for (int f = 0; f < NF; ++f)
           acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bw[f], acc[mi][f], 0, 0, 0);
       }
+      // NVFP4-style, Q8_0: one sub-step's decoded weights at a time (decoding
+      // ahead holds more registers than two workgroups a CU leave)
+      if constexpr (FMT != MOE_IQ4_NL) __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int f = 0; f < NF; ++f) pc[f] = pn[f];
@@ -447,8 +450,17 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sAbuf, fl
   if (__any(wbad) && lane == 0) atomicOr(a.error, 8);
 }
 
+// Workgroups per CU the register budget is cut for: two where the kernel fits
+// 256 registers a lane without spilling (IQ4_NL; the NVFP4-style down pass,
+// measured 6% faster per step than at one), else one (its accumulators then
+// live in AGPRs).
+template <int FMT, bool GATEUP>
+constexpr int pf_min_blocks() {
+  return (FMT == MOE_IQ4_NL || (FMT == MOE_NVFP4 && !GATEUP)) ? 2 : 1;
+}
+
 template <int FMT, bool GATEUP, int NF>
-__global__ __launch_bounds__(kPfThreads, FMT == MOE_IQ4_NL ? 2 : 1) void k_pf_gemm(const PrefillArgs a) {
+__global__ __launch_bounds__(kPfThreads, (pf_min_blocks<FMT, GATEUP>())) void k_pf_gemm(const PrefillArgs a) {
   __shared__ __align__(16) uint8_t sAbuf[2 * kPfBuf];  // [2][kBM][16 chunks][16 B]
   __shared__ float s_rsx[kBM];                         // gate/up: token scale of each tile row
   const QMatDev& M0 = a.mat[0];

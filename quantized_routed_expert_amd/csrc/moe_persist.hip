@@ -15,15 +15,16 @@
 //   down    64 output rows of one slot (shared or routed pair j), once that
 //           slot's h row is complete; h is scaled by a power of two per row
 //           into fp16 hi/lo parts for the MFMA;
-//   combine the last workgroup of each 64-column tile forms
+//   combine the workgroup with a tile's last-slot down item forms
 //           y = o_shared + sum_j w_j o_j (slot order), the next residual and
-//           its sum of squares.
+//           its sum of squares, once the tile's down outputs are present.
 // Dependencies between workgroups are monotonic counters in the workspace
-// (zeroed by the set-up launch before the step): gate/up tiles per slot, down
-// items per column tile, combined tiles.  The router logits carry their own
+// (zeroed by the set-up launch before the step): gate/up tiles per slot and
+// combined tiles.  The router logits and the o rows carry their own
 // readiness: each is stored as one 64-bit word holding the value and the
 // layer's tag, and a workgroup that needs them polls the words themselves, so
-// the poll that finds the last one present has also read them all.  Increments to
+// the poll that finds the last one present has also read them all (few
+// workgroups poll each, so the polls cost little bandwidth).  Increments to
 // one address serialise in the memory system (measured: about 40 ns each), so
 // each event that many workgroups signal is counted on several sub-counters,
 // one 256-byte line each, and a waiting wavefront polls all of them in one
@@ -32,8 +33,8 @@
 // always drains.  The grid is at most the number of workgroups that fit on
 // the device at once, so every workgroup a wait depends on is running.
 //
-// Data passed between workgroups (logits, h rows, o rows, residual tiles and
-// their sums of squares) is written with agent-scope atomic stores and read
+// Other data passed between workgroups (h rows, residual tiles and their
+// sums of squares) is written with agent-scope atomic stores and read
 // with loads carrying the same cache-coherence bits as agent-scope atomic
 // loads (sc1: they bypass the XCDs' private L2 caches; 16-byte buffer loads
 // where the data is contiguous); a producer waits for its stores to complete
@@ -41,6 +42,8 @@
 // after observing the counter.  Weight codes that do not depend on a wait
 // (the next layer's router row and shared-expert tile, a down tile's codes)
 // are issued before it.
+#include <algorithm>
+
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -65,8 +68,7 @@ constexpr int kSubSlot = 4;               // gate/up tiles of a slot, by tile
 constexpr int kLnTiles = 0;
 constexpr int kLnAbort = kLnTiles + kSubTiles;
 constexpr int kLnSlot = kLnAbort + 1;                   // kSubSlot lines per slot
-constexpr int kLnTileCnt = kLnSlot + kMaxSlots * kSubSlot;  // one line per column tile (d / 64 <= 64)
-constexpr int kNumCnt = kLnTileCnt + 64;
+constexpr int kNumCnt = kLnSlot + kMaxSlots * kSubSlot;
 
 constexpr uint32_t kSpinMax = 1u << 20;  // polls of one wait before it gives up
 
@@ -95,7 +97,7 @@ struct PsArgs {
   float* ss[2];        // [d / 64] tile sums of squares of a residual (by parity)
   uint64_t* lgt[2];    // [E] router logits tagged with layer + 1 (by parity; zeroed by the set-up)
   float* hrow;         // [k + hs][f] SwiGLU rows by slot (slot 0 = shared when present)
-  float* orow;         // [k + 1][d] down outputs: pair j at row j, shared at row k
+  uint64_t* otg;       // [k + 1][d] down outputs, tagged (layer + 1): pair j at row j, shared at row k
   int32_t* sync;       // kNumCnt lines of counters
   float* rec_logits;   // optional records (see moe_stack_record)
   int32_t* rec_idx;
@@ -121,14 +123,50 @@ __device__ __forceinline__ void ps_arrive(int32_t* c) {
   if (threadIdx.x == 0) __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// As ps_arrive, returning the counter's value before the increment.
-__device__ __forceinline__ int ps_arrive_old(int32_t* c) {
-  __shared__ int s_old;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) s_old = atomicAdd(c, 1);
-  __syncthreads();
-  return s_old;
+// A value with its readiness: one 64-bit word, the tag in the high half (no
+// tag is 0, so a zeroed word is never ready), stored in one access.
+__device__ __forceinline__ void st_tag(uint64_t* p, uint32_t tag, float v) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workgroup-wide poll of tagged words: thread t waits for the words
+// p0[i * step] (i < NE, bit i of `pend` set) to carry `tag` and returns their
+// values in v; a word already seen is not read again.  Bounded as ps_wait
+// (error bit 16 and the abort word when it runs out; gives up when the abort
+// word is set).  Returns false when it gave up.  Ends with a barrier.
+template <int NE>
+__device__ __forceinline__ bool ps_poll(const uint64_t* p0, int step, uint32_t pend, uint32_t tag, float (&v)[NE],
+                                        int32_t* abort_w, int32_t* err) {
+  __shared__ int s_stop[2];
+  const int tid = threadIdx.x;
+  for (uint32_t n = 1;; ++n) {
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      if ((pend >> i) & 1u) {
+        const uint64_t w = __hip_atomic_load(p0 + i * step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((uint32_t)(w >> 32) == tag) {
+          v[i] = __uint_as_float((uint32_t)w);
+          pend &= ~(1u << i);
+        }
+      }
+    }
+    // (two stop words, by round parity: a word is rewritten only after every
+    // thread has passed the barrier that follows the reads of its last value)
+    if (tid == 0) {
+      int stop = 0;
+      if ((n & 15u) == 0u && __hip_atomic_load(abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) stop = 1;
+      if (n > kSpinMax) {
+        atomicOr(err, 16);
+        __hip_atomic_store(abort_w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        stop = 1;
+      }
+      s_stop[n & 1u] = stop;
+    }
+    const int np = __syncthreads_count(pend != 0u);
+    if (np == 0) return true;
+    if (s_stop[n & 1u]) return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
 }
 
 // Wait until an event with narr arrivers per epoch, counted on nsub
@@ -237,6 +275,7 @@ struct PsLds {
   float xsum[kPsMaxD / 16];         // sums of x16 over each EPS-element chunk (decode order)
   float hsum[2][kPsMaxF / 16];      // the same for the hi / lo parts of h
   float logit[kPsMaxE];
+  float comb[kMaxSlots][64];        // the combine: the tile's down outputs, by o row
   uint32_t tk_key[64];              // top-k candidates
   int32_t tk_idx[64];
   int32_t idx[32];                  // this layer's top-k, slot order
@@ -425,7 +464,7 @@ __device__ __forceinline__ void ps_dn_issue(const PsMat& Wd, int e, int ct, int 
 
 template <int FMT>
 __device__ __forceinline__ void ps_dn_compute(PsLds& S, const DnCodes<FMT>& g, int ct, int K, float hscale,
-                                              float* oout) {
+                                              uint64_t* oout, uint32_t tag) {
   constexpr int EPS = dq_eps(FMT);
   constexpr int NMF = EPS / 8;
   constexpr bool BD = FMT != MOE_NVFP4;
@@ -499,7 +538,7 @@ __device__ __forceinline__ void ps_dn_compute(PsLds& S, const DnCodes<FMT>& g, i
     acc.y += __shfl_xor(acc.y, 32, 64);
   }
   // D rows 0 and 1 (the hi and lo columns) of lanes n in group 0
-  if (G == 0) st_ag(oout + row, (acc.x * g.ts + acc.y * g.ts) * hscale);
+  if (G == 0) st_tag(oout + row, tag, (acc.x * g.ts + acc.y * g.ts) * hscale);
 }
 
 // Glue of one token: x = bf16(r / sqrt(sum(r^2) / d + eps)), with the sum of
@@ -618,13 +657,45 @@ __device__ __forceinline__ float ps_router_dot(PsLds& S, const f32x4 (&wv)[4], c
   return (float)(r + (double)bias);
 }
 
+// The combine of column tile ct (64 columns) of layer l: the nR = k + hs down
+// outputs of every column (thread (q, c) polls o rows q, q + 4, ... of column
+// c), then y = o_shared + sum_j w_j o_j (slot order), the new residual and
+// the tile's sum of squares.  Returns false if the poll gave up.
+__device__ __forceinline__ bool ps_combine(PsLds& S, const PsArgs& a, int l, int ct, const float* r_in, float* r_out,
+                                           int32_t* abort_w, int32_t* err) {
+  const int tid = ps_tid(), c = tid & 63, q = tid >> 6;
+  const int d = a.d, k = a.k, nR = a.k + a.hs;
+  constexpr int NE = (kMaxSlots + 3) / 4;
+  uint32_t pend = 0u;
+#pragma unroll
+  for (int i = 0; i < NE; ++i)
+    if (q + 4 * i < nR) pend |= 1u << i;
+  float v[NE];
+  if (!ps_poll<NE>(a.otg + (long)q * d + ct * 64 + c, 4 * d, pend, (uint32_t)(l + 1), v, abort_w, err)) return false;
+#pragma unroll
+  for (int i = 0; i < NE; ++i)
+    if (q + 4 * i < nR) S.comb[q + 4 * i][c] = v[i];
+  __syncthreads();
+  if (q == 0) {
+    const int col = ct * 64 + c;
+    float y = a.hs ? S.comb[k][c] : 0.0f;
+    for (int j = 0; j < k; ++j) y = fmaf(S.wv[j], S.comb[j][c], y);
+    const float rn = ld_ag(r_in + col) + y;
+    st_ag(r_out + col, rn);
+    if (a.rec_y) a.rec_y[(long)l * d + col] = y;
+    const float ss = wave_sum(rn * rn);
+    if (c == 0) st_ag(a.ss[(l + 1) & 1] + ct, ss);
+  }
+  return true;
+}
+
 template <int GF, int DF, int PT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_ps_decode(const PsArgs a) {
   __shared__ PsLds S;
   pin_arg(a.layers);
   pin_arg(a.h);
   pin_arg(a.hrow);
-  pin_arg(a.orow);
+  pin_arg(a.otg);
   pin_arg(a.sync);
   const int G = gridDim.x, w = blockIdx.x;
   const int d = a.d, f = a.f, E = a.E, k = a.k, hs = a.hs, L = a.n_layers;
@@ -764,26 +835,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         }
       }
       const int pair = sh ? k : slot - hs;
-      ps_dn_compute<DF>(S, g, ct, f, ldexpf(1.0f, ex), a.orow + (long)pair * d);
-      const int old = ps_arrive_old(sync + (kLnTileCnt + ct) * kLine);
-      if (old == nS * (l + 1) - 1) {
-        // the last of the tile's nS down items: combine the tile
-        if (wid == 0) {
-          const int col = ct * 64 + lane;
-          float y = hs ? ld_ag(a.orow + (long)k * d + col) : 0.0f;
-          float oj[32];
-#pragma unroll
-          for (int j = 0; j < 32; ++j)
-            if (j < k) oj[j] = ld_ag(a.orow + (long)j * d + col);
-#pragma unroll
-          for (int j = 0; j < 32; ++j)
-            if (j < k) y = fmaf(S.wv[j], oj[j], y);
-          const float rn = ld_ag(r_in + col) + y;
-          st_ag(r_out + col, rn);
-          if (a.rec_y) a.rec_y[(long)l * d + col] = y;
-          const float ss = wave_sum(rn * rn);
-          if (lane == 0) st_ag(a.ss[(l + 1) & 1] + ct, ss);
-        }
+      ps_dn_compute<DF>(S, g, ct, f, ldexpf(1.0f, ex), a.otg + (long)pair * d, (uint32_t)(l + 1));
+      // the workgroup with the tile's last-slot item combines the tile once
+      // the tile's nS down outputs are present
+      if (slot == nS - 1) {
+        if (!ps_combine(S, a, l, ct, r_in, r_out, abort_w, err)) return;
         ps_arrive(sync + (kLnTiles + ct % kSubTiles) * kLine);
       }
     }
@@ -803,16 +859,20 @@ struct PsSetupArgs {
   int32_t* rec_err;
   int n_layers;
   int32_t* err_ws;
-  uint64_t* lgt;  // both tagged logit arrays
-  int n_lgt;
+  uint64_t* tags;  // every tagged word of the step (logits, o rows), contiguous
+  int n_tags;
 };
 
+// One workgroup, or for the first chunk enough to zero the tagged words (no
+// tag is 0, so a zeroed word reads as not yet written).
 __global__ __launch_bounds__(256) void k_ps_setup(const PsSetupArgs s) {
   const int tid = threadIdx.x;
-  if (tid < s.count) s.table[s.l0 + tid] = s.L[tid];
-  if (s.l0 == 0) {
+  if (blockIdx.x == 0 && tid < s.count) s.table[s.l0 + tid] = s.L[tid];
+  if (s.l0 == 0 && blockIdx.x > 0) {
+    for (long i = (long)(blockIdx.x - 1) * 256 + tid; i < s.n_tags; i += (long)(gridDim.x - 1) * 256) s.tags[i] = 0ull;
+  }
+  if (s.l0 == 0 && blockIdx.x == 0) {
     for (int i = tid; i < kNumCnt * kLine; i += 256) s.sync[i] = 0;  // (all counter lines)
-    for (int i = tid; i < s.n_lgt; i += 256) s.lgt[i] = 0ull;         // (no tag is 0)
     if (s.rec_err)
       for (int i = tid; i < s.n_layers; i += 256) s.rec_err[i] = 0;
     if (tid == 0) *s.err_ws = 0;
@@ -833,10 +893,12 @@ struct PsWs {
   float* ss[2];
   uint64_t* lgt[2];
   float* hrow;
-  float* orow;
+  uint64_t* tags;  // lgt[0], lgt[1], otg: contiguous
+  int n_tags;
+  uint64_t* otg;
 };
 
-PsWs carve_ps(void* ws, int d, int f, int E) {
+PsWs carve_ps(void* ws, int d, int f, int E, int k) {
   char* p = (char*)ws;
   PsWs W;
   W.table = (PsLayer*)p;
@@ -851,13 +913,15 @@ PsWs carve_ps(void* ws, int d, int f, int E) {
     W.ss[i] = (float*)p;
     p += align_up((size_t)(d / 64) * 4, 256);
   }
-  // the two tagged logit arrays, contiguous (the set-up zeroes both)
-  W.lgt[0] = (uint64_t*)p;
-  W.lgt[1] = W.lgt[0] + E;
-  p += align_up((size_t)2 * E * 8, 256);
   W.hrow = (float*)p;
   p += align_up((size_t)kMaxSlots * f * 4, 256);
-  W.orow = (float*)p;
+  // the tagged words, contiguous (the set-up zeroes them): the two logit
+  // arrays, then the o rows
+  W.tags = (uint64_t*)p;
+  W.lgt[0] = W.tags;
+  W.lgt[1] = W.lgt[0] + E;
+  W.otg = W.lgt[1] + E;
+  W.n_tags = 2 * E + (k + 1) * d;
   return W;
 }
 
@@ -899,8 +963,8 @@ hipError_t launch_ps_d(int df, const PsArgs& a, int need, hipStream_t s, hipEven
 
 size_t persist_ws_bytes(int d, int f, int E) {
   return align_up((size_t)kPsMaxLayers * sizeof(PsLayer), 256) + align_up((size_t)kNumCnt * kLine * 4, 256) + 256 +
-         2 * (align_up((size_t)d * 4, 256) + align_up((size_t)(d / 64) * 4, 256)) + align_up((size_t)2 * E * 8, 256) +
-         align_up((size_t)kMaxSlots * f * 4, 256) + align_up((size_t)kMaxSlots * d * 4, 256);
+         2 * (align_up((size_t)d * 4, 256) + align_up((size_t)(d / 64) * 4, 256)) +
+         align_up((size_t)kMaxSlots * f * 4, 256) + ((size_t)2 * E + (size_t)kMaxSlots * d) * 8;
 }
 
 bool persist_covers(const moe_layer& L, int n_layers, int T) {
@@ -917,7 +981,7 @@ bool persist_covers(const moe_layer& L, int n_layers, int T) {
 hipError_t launch_persist_step(const moe_layer* layers, int n_layers, float* h, const FusedRecord& rec, void* ws,
                                hipStream_t s) {
   const moe_layer& L0 = layers[0];
-  PsWs W = carve_ps(ws, L0.d, L0.f, L0.E);
+  PsWs W = carve_ps(ws, L0.d, L0.f, L0.E, L0.k);
   for (int l0 = 0; l0 < n_layers; l0 += kPsChunk) {
     PsSetupArgs sa{};
     sa.l0 = l0;
@@ -941,9 +1005,11 @@ hipError_t launch_persist_step(const moe_layer* layers, int n_layers, float* h, 
     sa.rec_err = rec.error;
     sa.n_layers = n_layers;
     sa.err_ws = W.err_ws;
-    sa.lgt = W.lgt[0];
-    sa.n_lgt = 2 * L0.E;
-    hipLaunchKernelGGL(k_ps_setup, dim3(1), dim3(256), 0, s, sa);
+    sa.tags = W.tags;
+    sa.n_tags = W.n_tags;
+    // the first chunk: workgroup 0 and at least one more for the tagged words
+    const int blocks = l0 == 0 ? 1 + std::min(256, (W.n_tags + 1023) / 1024) : 1;
+    hipLaunchKernelGGL(k_ps_setup, dim3(blocks), dim3(256), 0, s, sa);
   }
   PsArgs a{};
   a.layers = W.table;
@@ -961,7 +1027,7 @@ hipError_t launch_persist_step(const moe_layer* layers, int n_layers, float* h, 
     a.lgt[i] = W.lgt[i];
   }
   a.hrow = W.hrow;
-  a.orow = W.orow;
+  a.otg = W.otg;
   a.sync = W.sync;
   a.rec_logits = rec.logits;
   a.rec_idx = rec.topk_idx;

@@ -283,11 +283,12 @@ moe_status moe_decode_stack(const moe_layer* layers, int32_t n_layers, float* h,
                             const moe_stack_record* rec, void* ws, size_t ws_bytes, void* stream);
 
 /* 1 if moe_decode_stack runs this stack (layers[0]'s shape, n_layers, T) as
- * one persistent launch, 0 if as per-layer launches.  The persistent step
- * takes T = 1, d a multiple of 1024 up to 4096, f up to 1024, E up to 1024,
- * at most 128 layers, and rows short enough that every step's weight codes
- * are issued up front (gate/up: d <= 3072 for IQ4_NL / NVFP4-style, 1536 for
- * Q8_0; down: f <= 768); unless the environment sets QRE_DECODE_LAUNCHES=1.
+ * one persistent launch, 0 if as per-layer launches (always 0 for a stack
+ * moe_decode_stack rejects).  The persistent step takes T = 1, at most 128
+ * layers, E up to 1024, k up to 32, and rows short enough that every step's
+ * weight codes are issued up front: f a multiple of 128 up to 768, d a
+ * multiple of 1024 up to 3072 (IQ4_NL / NVFP4-style gate/up) or 1024 (Q8_0
+ * gate/up); unless the environment sets QRE_DECODE_LAUNCHES=1.
  * It computes the same layer with the same numerics, and a wait between its
  * workgroups that does not end within its poll bound sets error bit 16 in
  * every layer's record still to run. */

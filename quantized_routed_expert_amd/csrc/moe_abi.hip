@@ -226,10 +226,9 @@ size_t moe_decode_stack_workspace_size(const moe_layer* layer, int32_t T_max) {
   return fused_ws_bytes(T_max, layer->d, layer->f, layer->k, layer->E);
 }
 
-moe_status moe_decode_stack(const moe_layer* layers, int32_t n_layers, float* h, int32_t T, float eps,
-                            const moe_stack_record* rec, void* ws, size_t ws_bytes, void* stream) {
-  if (!layers || n_layers < 1 || !h || T < 1 || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
-  if (T > kFusedMaxT) return MOE_ERR_UNSUPPORTED;
+// The layers of a fused decode stack: each valid, all of one shape and format
+// set, d within the fused step's coverage.
+static moe_status check_stack(const moe_layer* layers, int32_t n_layers) {
   const moe_layer& L0 = layers[0];
   for (int l = 0; l < n_layers; ++l) {
     const moe_layer& L = layers[l];
@@ -241,6 +240,16 @@ moe_status moe_decode_stack(const moe_layer* layers, int32_t n_layers, float* h,
       return MOE_ERR_UNSUPPORTED;
   }
   if (L0.d % 1024 != 0 || L0.d > 4096) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status moe_decode_stack(const moe_layer* layers, int32_t n_layers, float* h, int32_t T, float eps,
+                            const moe_stack_record* rec, void* ws, size_t ws_bytes, void* stream) {
+  if (!layers || n_layers < 1 || !h || T < 1 || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
+  if (T > kFusedMaxT) return MOE_ERR_UNSUPPORTED;
+  const moe_layer& L0 = layers[0];
+  moe_status st = check_stack(layers, n_layers);
+  if (st != MOE_OK) return st;
   if (!aligned(h, 16)) return MOE_ERR_ALIGNMENT;
   FusedRecord r{};
   r.eps = eps;
@@ -312,7 +321,7 @@ moe_status moe_decode_stack_noalloc(const moe_layer* layers, int32_t n_layers, f
 }
 
 int32_t moe_decode_stack_persistent(const moe_layer* layers, int32_t n_layers, int32_t T) {
-  if (!layers || n_layers < 1 || T < 1 || check_dims(&layers[0]) != MOE_OK) return 0;
+  if (!layers || n_layers < 1 || T < 1 || T > kFusedMaxT || check_stack(layers, n_layers) != MOE_OK) return 0;
   return fused_step_persistent(layers[0], n_layers, T) ? 1 : 0;
 }
 

@@ -234,3 +234,42 @@ def test_decode_stack_noalloc_validates_on_the_host():
                                        down=lib.MOE_IQ4_NL)])
     assert so.moe_decode_stack_workspace_size(ctypes.byref(big[0]), 8) > 8 << 20
     assert so.moe_decode_stack_noalloc(big, 1, h, 8, ctypes.c_float(1e-6), None, None) == lib.MOE_ERR_WORKSPACE
+
+
+def test_q5_1_gate_up_rejected():
+    """Q5_1 is covered as the down projection's format only."""
+    assert _ffn(_fake_layer(qtype=lib.MOE_Q5_1, down=lib.MOE_Q8_0)) == lib.MOE_ERR_UNSUPPORTED
+    L = _fake_layer(qtype=lib.MOE_Q8_0, down=lib.MOE_Q5_1)
+    L.router_w = 0  # any later check still fires: the format itself passed validation
+    assert _ffn(L) != lib.MOE_ERR_UNSUPPORTED
+
+
+def test_persistent_coverage_query(monkeypatch):
+    """moe_decode_stack_persistent answers 1 exactly for the stacks the
+    persistent launch covers, and 0 for any stack moe_decode_stack rejects."""
+    monkeypatch.delenv("QRE_DECODE_LAUNCHES", raising=False)
+
+    def covered(n=2, T=1, **kw):
+        args = dict(d=3072, f=768, E=512, k=8, qtype=lib.MOE_IQ4_NL, down=lib.MOE_IQ4_NL, shared=True)
+        args.update(kw)
+        L = _fake_layer(**args)
+        return lib.moe_decode_stack_persistent(lib.layer_array([L] * n), n, T)
+
+    assert covered()
+    assert not covered(T=2)
+    assert not covered(f=1024)  # down rows too long to issue up front
+    assert not covered(d=4096)  # gate/up rows too long for IQ4_NL
+    assert covered(d=1024, qtype=lib.MOE_Q8_0, down=lib.MOE_Q8_0)
+    assert not covered(d=2048, qtype=lib.MOE_Q8_0, down=lib.MOE_Q8_0)
+    assert covered(n=128)
+    assert not covered(n=129)
+    assert covered(down=lib.MOE_Q5_1)
+    assert not covered(d=512)  # outside the fused step altogether
+    # a stack moe_decode_stack would reject is never reported as persistent
+    L = _fake_layer(d=3072, f=768, E=512, k=8, qtype=lib.MOE_IQ4_NL, down=lib.MOE_IQ4_NL, shared=True)
+    bad = _fake_layer(d=3072, f=768, E=512, k=8, qtype=lib.MOE_IQ4_NL, down=lib.MOE_IQ4_NL, shared=True)
+    bad.router_w = 0
+    assert not lib.moe_decode_stack_persistent(lib.layer_array([L, bad]), 2, 1)
+    mixed = _fake_layer(d=3072, f=768, E=512, k=8, qtype=lib.MOE_IQ4_NL, down=lib.MOE_Q8_0, shared=True)
+    assert not lib.moe_decode_stack_persistent(lib.layer_array([L, mixed]), 2, 1)
+    assert not covered(qtype=lib.MOE_Q5_1, down=lib.MOE_Q5_1)

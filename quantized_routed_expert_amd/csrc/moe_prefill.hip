@@ -311,23 +311,28 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sAbuf, fl
 #pragma unroll
   for (int i = 0; i < 4; ++i) aoff[i] = (n * 16 + ((4 * G + i) ^ n)) * 16;
 
-  // ---- this lane's weight rows (one per fragment)
+  // ---- this lane's weight rows (one per fragment): a workgroup-uniform base
+  // per fragment (the expert, the N-tile, the fragment's first row) and one
+  // per-lane row offset shared by all fragments, so that the loads take the
+  // scalar base + 32-bit offset form (an expert's matrix is far below 4 GiB)
   const uint8_t* bc[NF];
   const uint8_t* bs[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
-    int mi = 0, wr;
+    int mi = 0, wr0;
     if constexpr (GATEUP) {
-      mi = f / (NF / 2);                                                       // gate, then up
-      wr = nt * (kPfWaves * 8 * NF) + wid * (8 * NF) + (f % (NF / 2)) * 16 + n;  // same f-rows for both
+      mi = f / (NF / 2);                                     // gate, then up
+      wr0 = nt * (kPfWaves * 8 * NF) + (f % (NF / 2)) * 16;  // same f-rows for both
     } else {
-      wr = nt * (kPfWaves * 16 * NF) + wid * (16 * NF) + f * 16 + n;
+      wr0 = nt * (kPfWaves * 16 * NF) + f * 16;
     }
     const QMatDev& W = is_sh ? a.smat[mi] : a.mat[mi];
-    const long rw = (long)e * rows + wr;
+    const long rw = (long)e * rows + wr0;
     bc[f] = W.codes + rw * crb;
     bs[f] = W.scales + rw * srb;
   }
+  const int lrow = wid * (GATEUP ? 8 * NF : 16 * NF) + n;
+  const uint32_t coff = (uint32_t)(lrow * crb), soff = (uint32_t)(lrow * srb);
   float tsg = 1.0f, tsu = 1.0f;  // NVFP4 tensor scales (gate, up / down)
   if constexpr (FMT == MOE_NVFP4) {
     tsg = (is_sh ? a.smat[0] : a.mat[0]).ts[e];
@@ -337,8 +342,11 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sAbuf, fl
   // ---- activation copies: copy c = 4q + w (wave w, q < NMF) fills LDS bytes
   // [1024c, 1024c + 1024), i.e. tile row 4c + lane/16, stored chunk lane%16 =
   // logical chunk ^ (row%16).
-  int asrc[NMF];  // element offset of the source row (rows past the slot's end copy its first row)
-  int acol[NMF];  // element offset of the logical chunk
+  // element offset of the source row (rows past the slot's end copy its first
+  // row) plus that of the lane's logical chunk, (lane % 16) ^ (r % 16), where
+  // r % 16 is the same for every q
+  int asrc[NMF];
+  const int acol = ((lane & 15) ^ ((wid * 4 + (lane >> 4)) & 15)) * 8;
 #pragma unroll
   for (int q = 0; q < NMF; ++q) {
     const int r = (q * kPfWaves + wid) * 4 + (lane >> 4);
@@ -346,22 +354,21 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sAbuf, fl
     const int rs = rr < cnt ? rr : 0;
     if constexpr (GATEUP) {
       const int t = is_sh ? rs : a.row_token[row0 + rs];
-      asrc[q] = t * K;
+      asrc[q] = t * K + acol;
     } else {
-      asrc[q] = (row0 + rs) * K;
+      asrc[q] = (row0 + rs) * K + acol;
     }
-    acol[q] = ((lane & 15) ^ (r & 15)) * 8;
   }
   auto copy_a = [&](int s, int buf) {
     uint8_t* base = sAbuf + buf * kPfBuf + wid * 1024;
 #pragma unroll
     for (int q = 0; q < NMF; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(act + asrc[q] + s * kPfBK + acol[q]),
+      __builtin_amdgcn_global_load_lds((const void*)(act + asrc[q] + s * kPfBK),
                                        (lds_void*)(base + q * kPfWaves * 1024), 16, 0, 0);
   };
   auto load_b = [&](int s, PfCodes<FMT> (&pc)[NF]) {
 #pragma unroll
-    for (int f = 0; f < NF; ++f) pf_load_codes<FMT>(bc[f], bs[f], s * kPfBK + 32 * G, pc[f]);
+    for (int f = 0; f < NF; ++f) pf_load_codes<FMT>(bc[f] + coff, bs[f] + soff, s * kPfBK + 32 * G, pc[f]);
   };
 
   f32x4 acc[NMF][NF];
@@ -451,12 +458,11 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sAbuf, fl
 }
 
 // Workgroups per CU the register budget is cut for: two where the kernel fits
-// 256 registers a lane without spilling (IQ4_NL; the NVFP4-style down pass,
-// measured 6% faster per step than at one), else one (its accumulators then
-// live in AGPRs).
+// 256 registers a lane without spilling (IQ4_NL and NVFP4-style), else one
+// (Q8_0, Q5_1: the wider code records; the accumulators then live in AGPRs).
 template <int FMT, bool GATEUP>
 constexpr int pf_min_blocks() {
-  return (FMT == MOE_IQ4_NL || (FMT == MOE_NVFP4 && !GATEUP)) ? 2 : 1;
+  return (FMT == MOE_IQ4_NL || FMT == MOE_NVFP4) ? 2 : 1;
 }
 
 template <int FMT, bool GATEUP, int NF>

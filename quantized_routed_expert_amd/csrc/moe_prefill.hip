@@ -189,20 +189,25 @@ struct PfCodes {
   uint32_t qh;  // Q5_1: the block's high-bit word
 };
 
+// The codes and scale of element kel's block-sized chunk of a weight row:
+// the row starts coff / soff bytes past the (workgroup-uniform) bases, and
+// every offset is a 32-bit byte count, so that the loads can take the scalar
+// base + 32-bit offset form.
 template <int FMT>
-__device__ __forceinline__ void pf_load_codes(const uint8_t* crow, const uint8_t* srow, int kel, PfCodes<FMT>& pc) {
+__device__ __forceinline__ void pf_load_codes(const uint8_t* cbase, uint32_t coff, const uint8_t* sbase, uint32_t soff,
+                                              int kel, PfCodes<FMT>& pc) {
   if constexpr (FMT == MOE_Q8_0) {
-    pc.c[0] = *(const u32x4*)(crow + kel);
-    pc.c[1] = *(const u32x4*)(crow + kel + 16);
+    pc.c[0] = *(const u32x4*)(cbase + (coff + (uint32_t)kel));
+    pc.c[1] = *(const u32x4*)(cbase + (coff + (uint32_t)kel + 16u));
   } else {
-    pc.c[0] = *(const u32x4*)(crow + (kel >> 1));
+    pc.c[0] = *(const u32x4*)(cbase + (coff + (uint32_t)(kel >> 1)));
   }
   if constexpr (FMT == MOE_Q5_1) {
-    const u32x2 rec = *(const u32x2*)(srow + (kel >> 5) * 8);
+    const u32x2 rec = *(const u32x2*)(sbase + (soff + (uint32_t)(kel >> 5) * 8u));
     pc.sc = rec.x;
     pc.qh = rec.y;
   } else {
-    pc.sc = ((const uint16_t*)srow)[kel >> 5];
+    pc.sc = *(const uint16_t*)(sbase + (soff + (uint32_t)(kel >> 5) * 2u));
     pc.qh = 0u;
   }
 }
@@ -265,8 +270,8 @@ __global__ void k_dequant_pf(QMatDev m, int expert, f16* __restrict__ dst) {
   const int r = (int)(i / nb), b = (int)(i % nb);
   const long rw = (long)expert * rows + r;
   PfCodes<FMT> pc;
-  pf_load_codes<FMT>(m.codes + rw * code_row_bytes(FMT, cols), m.scales + rw * scale_row_bytes(FMT, cols), b * 32,
-                     pc);
+  pf_load_codes<FMT>(m.codes + rw * code_row_bytes(FMT, cols), 0u, m.scales + rw * scale_row_bytes(FMT, cols), 0u,
+                     b * 32, pc);
   f16* o = dst + (long)r * cols + b * 32;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -294,8 +299,8 @@ hipError_t launch_dequant_pf(const QMatDev& m, int expert, void* dst, hipStream_
 
 // One work item (M-tile x N-tile) over its first NMF M fragments.
 template <int FMT, bool GATEUP, int NF, int NMF>
-__device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sAbuf, float* s_rsx, const PfTile tl,
-                                        int nt, int rows, int K) {
+__device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sA0, uint8_t* sA1, float* s_rsx,
+                                        const PfTile tl, int nt, int rows, int K) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int n = lane & 15, G = lane >> 4;
   const int crb = code_row_bytes(FMT, K), srb = scale_row_bytes(FMT, K);
@@ -342,11 +347,11 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sAbuf, fl
   // ---- activation copies: copy c = 4q + w (wave w, q < NMF) fills LDS bytes
   // [1024c, 1024c + 1024), i.e. tile row 4c + lane/16, stored chunk lane%16 =
   // logical chunk ^ (row%16).
-  // element offset of the source row (rows past the slot's end copy its first
+  // byte offset of the source row (rows past the slot's end copy its first
   // row) plus that of the lane's logical chunk, (lane % 16) ^ (r % 16), where
   // r % 16 is the same for every q
-  int asrc[NMF];
-  const int acol = ((lane & 15) ^ ((wid * 4 + (lane >> 4)) & 15)) * 8;
+  uint32_t asrc[NMF];
+  const uint32_t acol = (uint32_t)(((lane & 15) ^ ((wid * 4 + (lane >> 4)) & 15)) * 16);
 #pragma unroll
   for (int q = 0; q < NMF; ++q) {
     const int r = (q * kPfWaves + wid) * 4 + (lane >> 4);
@@ -354,21 +359,21 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sAbuf, fl
     const int rs = rr < cnt ? rr : 0;
     if constexpr (GATEUP) {
       const int t = is_sh ? rs : a.row_token[row0 + rs];
-      asrc[q] = t * K + acol;
+      asrc[q] = (uint32_t)t * (uint32_t)(2 * K) + acol;
     } else {
-      asrc[q] = (row0 + rs) * K + acol;
+      asrc[q] = (uint32_t)(row0 + rs) * (uint32_t)(2 * K) + acol;
     }
   }
-  auto copy_a = [&](int s, int buf) {
-    uint8_t* base = sAbuf + buf * kPfBuf + wid * 1024;
+  auto copy_a = [&](int s, uint8_t* buf) {
+    uint8_t* base = buf + wid * 1024;
 #pragma unroll
     for (int q = 0; q < NMF; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(act + asrc[q] + s * kPfBK),
+      __builtin_amdgcn_global_load_lds((const void*)((const uint8_t*)act + (asrc[q] + (uint32_t)(s * 2 * kPfBK))),
                                        (lds_void*)(base + q * kPfWaves * 1024), 16, 0, 0);
   };
   auto load_b = [&](int s, PfCodes<FMT> (&pc)[NF]) {
 #pragma unroll
-    for (int f = 0; f < NF; ++f) pf_load_codes<FMT>(bc[f] + coff, bs[f] + soff, s * kPfBK + 32 * G, pc[f]);
+    for (int f = 0; f < NF; ++f) pf_load_codes<FMT>(bc[f], coff, bs[f], soff, s * kPfBK + 32 * G, pc[f]);
   };
 
   f32x4 acc[NMF][NF];
@@ -379,7 +384,7 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sAbuf, fl
 
   PfCodes<FMT> pc[NF], pn[NF];
   bool wbad = false;  // a block scale beyond the fp16 weight range
-  copy_a(0, 0);
+  copy_a(0, sA0);
   load_b(0, pc);
   // gate/up: the token scale of tile row tid, kept for the epilogue
   float rsx = 0.0f;
@@ -390,22 +395,26 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sAbuf, fl
       rsx = a.xs[is_sh ? rs : a.row_token[row0 + rs]];
     }
   }
-  for (int s = 0; s < nstages; ++s) {
+  // One stage: its activations in `cur`, its codes in `pcur`; the next
+  // stage's copies go to `nxt` and its codes to `pnxt`.  The two buffers are
+  // distinct LDS objects and each call names them statically (the stage loop
+  // runs in pairs), so the compiler sees that the copies in flight write the
+  // other buffer and lets this stage's LDS reads run ahead of them.
+  auto stage = [&](int s, const uint8_t* cur, uint8_t* nxt, PfCodes<FMT>(&pcur)[NF], PfCodes<FMT>(&pnxt)[NF]) {
     __builtin_amdgcn_s_waitcnt(0);  // this stage's copies and codes have landed
     __syncthreads();                // ... for every wave; the other buffer is free
     if (s + 1 < nstages) {
-      copy_a(s + 1, (s + 1) & 1);
-      load_b(s + 1, pn);
+      copy_a(s + 1, nxt);
+      load_b(s + 1, pnxt);
     }
-    const uint8_t* sa = sAbuf + (s & 1) * kPfBuf;
 #pragma unroll
-    for (int f = 0; f < NF; ++f) wbad |= pf_scale_out_of_range<FMT>(pc[f]);
+    for (int f = 0; f < NF; ++f) wbad |= pf_scale_out_of_range<FMT>(pcur[f]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint8_t* p = sa + aoff[i];
+      const uint8_t* p = cur + aoff[i];
       f16x8 bw[NF];
 #pragma unroll
-      for (int f = 0; f < NF; ++f) bw[f] = pf_decode<FMT>(pc[f], i);
+      for (int f = 0; f < NF; ++f) bw[f] = pf_decode<FMT>(pcur[f], i);
 #pragma unroll
       for (int mi = 0; mi < NMF; ++mi) {
         const f16x8 af = __builtin_bit_cast(f16x8, *(const u32x4*)(p + mi * 4096));
@@ -417,8 +426,10 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sAbuf, fl
       // ahead holds more registers than two workgroups a CU leave)
       if constexpr (FMT != MOE_IQ4_NL) __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int f = 0; f < NF; ++f) pc[f] = pn[f];
+  };
+  for (int s = 0; s < nstages; s += 2) {
+    stage(s, sA0, sA1, pc, pn);
+    if (s + 1 < nstages) stage(s + 1, sA1, sA0, pn, pc);
   }
   if (GATEUP && tid < NMF * 16) s_rsx[tid] = rsx;
   __syncthreads();  // the next item's first copy must not overwrite a buffer still being read
@@ -467,7 +478,9 @@ constexpr int pf_min_blocks() {
 
 template <int FMT, bool GATEUP, int NF>
 __global__ __launch_bounds__(kPfThreads, (pf_min_blocks<FMT, GATEUP>())) void k_pf_gemm(const PrefillArgs a) {
-  __shared__ __align__(16) uint8_t sAbuf[2 * kPfBuf];  // [2][kBM][16 chunks][16 B]
+  // the two activation buffers, [kBM][16 chunks][16 B] each
+  __shared__ __align__(16) uint8_t sA0[kPfBuf];
+  __shared__ __align__(16) uint8_t sA1[kPfBuf];
   __shared__ float s_rsx[kBM];                         // gate/up: token scale of each tile row
   const QMatDev& M0 = a.mat[0];
   const int rows = M0.rows, K = M0.cols;
@@ -484,14 +497,19 @@ __global__ __launch_bounds__(kPfThreads, (pf_min_blocks<FMT, GATEUP>())) void k_
     const int item = xcd * per_xcd + it;
     if (item >= total) break;
     const int mt = item / n_ntiles, nt = item % n_ntiles;
-    const PfTile tl = a.tiles[mt];
+    PfTile tl = a.tiles[mt];
+    // (the entry is the workgroup's: keep it in scalar registers)
+    tl.e = __builtin_amdgcn_readfirstlane(tl.e);
+    tl.row0 = __builtin_amdgcn_readfirstlane(tl.row0);
+    tl.cnt = __builtin_amdgcn_readfirstlane(tl.cnt);
+    tl.m0 = __builtin_amdgcn_readfirstlane(tl.m0);
     const int nrow = min(kBM, tl.cnt - tl.m0);  // rows of this tile, 1 .. kBM
     if (nrow > 64)
-      pf_item<FMT, GATEUP, NF, 8>(a, sAbuf, s_rsx, tl, nt, rows, K);
+      pf_item<FMT, GATEUP, NF, 8>(a, sA0, sA1, s_rsx, tl, nt, rows, K);
     else if (nrow > 32)
-      pf_item<FMT, GATEUP, NF, 4>(a, sAbuf, s_rsx, tl, nt, rows, K);
+      pf_item<FMT, GATEUP, NF, 4>(a, sA0, sA1, s_rsx, tl, nt, rows, K);
     else
-      pf_item<FMT, GATEUP, NF, 2>(a, sAbuf, s_rsx, tl, nt, rows, K);
+      pf_item<FMT, GATEUP, NF, 2>(a, sA0, sA1, s_rsx, tl, nt, rows, K);
   }
 }
 

@@ -252,8 +252,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     float* __restrict__ logits) {
   // the token tile of a 128-element K group: [64 rows][16 chunks of 8], chunk
   // c of row r at c ^ (r & 15) (the 16 rows of a fragment read fall in
-  // distinct banks); two buffers, the next group's copy in flight
-  __shared__ __align__(16) uint8_t sx[2][kRmTok * 16 * 16];
+  // distinct banks); two buffers, the next group's copy in flight.  The
+  // buffers are distinct LDS objects, named statically at every use, so the
+  // compiler sees that a copy in flight writes the other buffer and does not
+  // hold this group's LDS reads until it lands.
+  __shared__ __align__(16) uint8_t sx0[kRmTok * 16 * 16];
+  __shared__ __align__(16) uint8_t sx1[kRmTok * 16 * 16];
   typedef __attribute__((address_space(3))) void lds_void_t;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int n = lane & 15, G = lane >> 4;
@@ -267,10 +271,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int slot = q * 256 + tid, r = slot >> 4, c = (slot & 15) ^ (r & 15);
     xsrc[q] = x + (long)min(t0 + r, T - 1) * d + c * 8;
   }
-  auto copy_x = [&](int kg, int buf) {
+  auto copy_x = [&](int kg, uint8_t* buf) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(xsrc[q] + kg), (lds_void_t*)(&sx[buf][(q * 256 + wid * 64) * 16]),
+      __builtin_amdgcn_global_load_lds((const void*)(xsrc[q] + kg), (lds_void_t*)(buf + (q * 256 + wid * 64) * 16),
                                        16, 0, 0);
   };
   // this lane's router rows (rows past the end repeat the last one and are not stored)
@@ -293,14 +297,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int f = 0; f < 2; ++f) acc[mi][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int buf, const f32x4 (&wb)[4][2][2]) {
+  auto compute = [&](const uint8_t* buf, const f32x4 (&wb)[4][2][2]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       u32x4 xa[4];
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
         const int r = mi * 16 + n;
-        xa[mi] = *(const u32x4*)&sx[buf][(r * 16 + ((4 * j + G) ^ n)) * 16];
+        xa[mi] = *(const u32x4*)(buf + (r * 16 + ((4 * j + G) ^ n)) * 16);
       }
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
@@ -319,24 +323,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // K in groups of 128 (d is a multiple of 128): the group's token tile and
   // router words were requested during the previous group
   f32x4 wb0[4][2][2], wb1[4][2][2];
-  copy_x(0, 0);
+  copy_x(0, sx0);
   load_w(0, wb0);
   for (int kg = 0; kg < d; kg += 256) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // group kg is in LDS for every wave; buffer 1 is free
     if (kg + 128 < d) {
-      copy_x(kg + 128, 1);
+      copy_x(kg + 128, sx1);
       load_w(kg + 128, wb1);
     }
-    compute(0, wb0);
+    compute(sx0, wb0);
     if (kg + 128 >= d) break;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // group kg + 128 is in LDS; buffer 0 is free
     if (kg + 256 < d) {
-      copy_x(kg + 256, 0);
+      copy_x(kg + 256, sx0);
       load_w(kg + 256, wb0);
     }
-    compute(1, wb1);
+    compute(sx1, wb1);
   }
   // D row 4G + v of fragment (mi, f): token t0 + mi*16 + 4G + v, expert e0 + f*16 + n
 #pragma unroll

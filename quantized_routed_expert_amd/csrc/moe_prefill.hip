@@ -422,9 +422,9 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sA0, uint
         for (int f = 0; f < NF; ++f)
           acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bw[f], acc[mi][f], 0, 0, 0);
       }
-      // NVFP4-style, Q8_0: one sub-step's decoded weights at a time (decoding
-      // ahead holds more registers than two workgroups a CU leave)
-      if constexpr (FMT != MOE_IQ4_NL) __builtin_amdgcn_sched_barrier(0);
+      // Q8_0: one sub-step's decoded weights at a time (decoding ahead holds
+      // more registers than the kernel has)
+      if constexpr (FMT == MOE_Q8_0) __builtin_amdgcn_sched_barrier(0);
     }
   };
   for (int s = 0; s < nstages; s += 2) {
@@ -469,11 +469,11 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sA0, uint
 }
 
 // Workgroups per CU the register budget is cut for: two where the kernel fits
-// 256 registers a lane without spilling (IQ4_NL and NVFP4-style), else one
-// (Q8_0, Q5_1: the wider code records; the accumulators then live in AGPRs).
+// 256 registers a lane without spilling (IQ4_NL, NVFP4-style, Q5_1), else one
+// (Q8_0: its 32-byte code records; the accumulators then live in AGPRs).
 template <int FMT, bool GATEUP>
 constexpr int pf_min_blocks() {
-  return (FMT == MOE_IQ4_NL || FMT == MOE_NVFP4) ? 2 : 1;
+  return FMT == MOE_Q8_0 ? 1 : 2;
 }
 
 template <int FMT, bool GATEUP, int NF>

@@ -432,38 +432,63 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sA0, uint
     if (s + 1 < nstages) stage(s + 1, sA1, sA0, pn, pc);
   }
   if (GATEUP && tid < NMF * 16) s_rsx[tid] = rsx;
-  __syncthreads();  // the next item's first copy must not overwrite a buffer still being read
+  __syncthreads();  // every wave is done with the activation buffers: they stage the outputs now
 
-  // ---- epilogue: D row (M) = mi*16 + 4G + v, column (N) = fragment row n
+  // ---- epilogue: D row (M) = mi*16 + 4G + v, column (N) = fragment row n.
+  // The item's outputs (tile rows x NC columns, 16-bit) are staged in the
+  // activation buffers (rows [0, RPB) in sA0, the rest in sA1), then written
+  // out as whole 16-byte pieces of rows: an output row's NC columns are
+  // contiguous (h: positions of the down weights' decode order, which permutes
+  // within blocks of 32 only; o: in order).
+  constexpr int NC = GATEUP ? kPfWaves * 8 * NF : kPfWaves * 16 * NF;
+  constexpr int RPB = kPfBuf / (NC * 2);
+  // the lane's indices, formed here: positions derived from threadIdx.x
+  // alone would otherwise be hoisted out of the item loop and held (spilled)
+  // for the whole kernel
+  int et = threadIdx.x;
+  asm volatile("" : "+v"(et));
+  const int en = et & 15, eG = (et & 63) >> 4, ewid = et >> 6;
+  auto stage_at = [&](int r, int c) -> uint16_t* {
+    uint8_t* b = r < RPB ? sA0 : sA1;
+    return (uint16_t*)(b + ((r % RPB) * NC + c) * 2);
+  };
   bool bad = false;  // an h value beyond fp16 range
 #pragma unroll
   for (int mi = 0; mi < NMF; ++mi) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int rr = m0 + mi * 16 + 4 * G + v;
-      if (rr >= cnt) continue;
-      const long orow = row0 + rr;
+      const int r = mi * 16 + 4 * eG + v;
+      const bool valid = m0 + r < cnt;
       if constexpr (GATEUP) {
-        const float sx = s_rsx[mi * 16 + 4 * G + v];
+        const float sx = s_rsx[r];
 #pragma unroll
         for (int f = 0; f < NF / 2; ++f) {
           const float g = acc[mi][f][v] * sx * tsg, u = acc[mi][f + NF / 2][v] * sx * tsu;
           // silu(g) * u with the hardware reciprocal (about 1 ulp); h is then
           // rounded to fp16
           const float hv = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
-          bad |= !(fabsf(hv) < 65504.0f);
-          const int fcol = nt * (kPfWaves * 8 * NF) + wid * (8 * NF) + f * 16 + n;
-          a.hout[orow * rows + act_pos(a.down_type, fcol)] = (f16)hv;
+          bad |= valid && !(fabsf(hv) < 65504.0f);
+          const int c = act_pos(a.down_type, ewid * (8 * NF) + f * 16 + en);
+          *stage_at(r, c) = __builtin_bit_cast(uint16_t, (f16)hv);
         }
       } else {
 #pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          const int dcol = nt * (kPfWaves * 16 * NF) + wid * (16 * NF) + f * 16 + n;
-          a.o[orow * rows + dcol] = (uint16_t)f32_to_bf16_bits(acc[mi][f][v] * tsg);
-        }
+        for (int f = 0; f < NF; ++f)
+          *stage_at(r, ewid * (16 * NF) + f * 16 + en) = (uint16_t)f32_to_bf16_bits(acc[mi][f][v] * tsg);
       }
     }
   }
+  __syncthreads();
+  {
+    constexpr int CPR = NC * 2 / 16;  // 16-byte pieces of an output row
+    const int nvalid = min(NMF * 16, cnt - m0);
+    uint16_t* out = GATEUP ? (uint16_t*)a.hout : a.o;
+    for (int i = et; i < nvalid * CPR; i += kPfThreads) {
+      const int r = i / CPR, c = i % CPR;
+      *(u32x4*)(out + (long)(row0 + m0 + r) * rows + nt * NC + c * 8) = *(const u32x4*)stage_at(r, c * 8);
+    }
+  }
+  __syncthreads();  // the next item's first copy must not overwrite a staging buffer still being read
   if (GATEUP && bad) atomicOr(a.error, 2);
   if (__any(wbad) && lane == 0) atomicOr(a.error, 8);
 }

@@ -77,7 +77,8 @@ size_t route_ws(const moe_layer* L, int T, int x_dtype) {
 }
 
 size_t ffn_ws(const moe_layer* L, int T, int x_dtype) {
-  if (T <= kDecodeMaxT) return decode_ws_bytes(T, L->d, L->f, L->k, x_dtype);
+  if (T <= kDecodeMaxT && !prefill_exact(*L, T, x_dtype)) return decode_ws_bytes(T, L->d, L->f, L->k, x_dtype);
+  if (T <= kDecodeMaxT) return prefill_exact_ws_bytes(T, L->d, L->f, L->k);
   return prefill_ws_bytes(T, L->d, L->f, L->k);
 }
 
@@ -116,6 +117,10 @@ size_t moe_workspace_size(const moe_layer* layer, int32_t T_max) {
   if (pl > need) need = pl;
   const size_t dec = decode_ws_bytes(Td, layer->d, layer->f, layer->k, MOE_F32);
   if (dec > need) need = dec;
+  if (prefill_exact(*layer, Td, MOE_BF16)) {  // (grows with T: the largest batch that takes it)
+    const size_t ex = prefill_exact_ws_bytes(Td, layer->d, layer->f, layer->k);
+    if (ex > need) need = ex;
+  }
   if (T_max > kDecodeMaxT) {
     const size_t pf = prefill_ws_bytes(T_max, layer->d, layer->f, layer->k);
     if (pf > need) need = pf;
@@ -170,7 +175,8 @@ static moe_status ffn_checked(int stage_lo, int stage_hi, const moe_layer* layer
   FfnCall c{layer, x, x_dtype, T, topk_w, plan_dev(*plan), y, y_dtype, ws};
   hipStream_t s = (hipStream_t)stream;
   for (int stage = stage_lo; stage <= stage_hi; ++stage) {
-    const hipError_t e = T <= kDecodeMaxT ? launch_decode_stage(stage, c, s) : launch_prefill_stage(stage, c, s);
+    const hipError_t e = (T <= kDecodeMaxT && !prefill_exact(*layer, T, x_dtype)) ? launch_decode_stage(stage, c, s)
+                                                                                  : launch_prefill_stage(stage, c, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   return MOE_OK;

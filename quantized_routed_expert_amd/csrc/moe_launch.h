@@ -78,6 +78,9 @@ hipError_t launch_decode_stage(int stage, const FfnCall& c, hipStream_t s);
 
 // moe_prefill.hip
 size_t prefill_ws_bytes(int T, int d, int f, int k);
+// exact mode of the prefill GEMMs for batches of the per-layer path (see moe_prefill.hip)
+bool prefill_exact(const moe_layer& L, int T, int x_dtype);
+size_t prefill_exact_ws_bytes(int T, int d, int f, int k);
 // One expert's prefill weight tile as fp16 (the GEMM's own decode), [rows][cols].
 hipError_t launch_dequant_pf(const QMatDev& m, int expert, void* dst, hipStream_t s);
 hipError_t launch_prefill_stage(int stage, const FfnCall& c, hipStream_t s);

@@ -48,6 +48,13 @@ struct PrefillArgs {
   f16* hout;               // gate/up: H
   uint16_t* o;             // down: O bf16 [(T*k+T)][d]
   int32_t* error;
+  // exact mode (batches of at most 64 tokens): gate/up writes h in fp32 and
+  // the largest |h| of each row; the down pass reads h as scaled fp16 hi / lo
+  // parts along a doubled K (hin rows of 2K: hi, then lo) and writes O in fp32
+  float* hf;               // gate/up: h fp32 [(T*k+T)][f]
+  uint32_t* hmax;          // gate/up: largest |h| of each row (float bits; zeroed by the preparation)
+  const float* hx;         // down: the power of two each hin row was scaled down by
+  float* of;               // down: O fp32 [(T*k+T)][d]
 };
 
 // Preparation, one launch: workgroups 0 .. T-1 write the scaled fp16 copy of
@@ -62,7 +69,8 @@ __global__ __launch_bounds__(256) void k_pf_prepare(const void* __restrict__ x, 
                                                     const int32_t* __restrict__ active,
                                                     const int32_t* __restrict__ n_active, int has_shared,
                                                     int32_t* __restrict__ mstart, PfTile* __restrict__ tiles,
-                                                    int32_t* __restrict__ n_mtiles, int k) {
+                                                    int32_t* __restrict__ n_mtiles, int k,
+                                                    uint32_t* __restrict__ hmax) {
   __shared__ int32_t part[256 / 64 + 1];  // scan scratch
   __shared__ float red[4];
   const int tid = threadIdx.x;
@@ -116,6 +124,8 @@ __global__ __launch_bounds__(256) void k_pf_prepare(const void* __restrict__ x, 
     if (tid == 0) xs[t] = ldexpf(1.0f, ex);
     return;
   }
+  if (hmax)  // exact mode: the row maxima of h start at zero
+    for (int i = tid; i < T * k + T; i += 256) hmax[i] = 0u;
   const int n_slots = *n_active + has_shared;
   const int per = (n_slots + 255) / 256;
   const int s0 = tid * per, s1 = min(n_slots, s0 + per);
@@ -298,13 +308,18 @@ hipError_t launch_dequant_pf(const QMatDev& m, int expert, void* dst, hipStream_
 }
 
 // One work item (M-tile x N-tile) over its first NMF M fragments.
-template <int FMT, bool GATEUP, int NF, int NMF>
+template <int FMT, bool GATEUP, int NF, int NMF, bool EXACT>
 __device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sA0, uint8_t* sA1, float* s_rsx,
                                         const PfTile tl, int nt, int rows, int K) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int n = lane & 15, G = lane >> 4;
   const int crb = code_row_bytes(FMT, K), srb = scale_row_bytes(FMT, K);
-  const int nstages = K / kPfBK;
+  // exact down pass: the activation rows are h's hi parts then its lo parts,
+  // 2K long, against the same weights (stage s reads weight columns of
+  // stage s mod K / kPfBK)
+  constexpr bool KX2 = EXACT && !GATEUP;
+  const int KA = KX2 ? 2 * K : K;
+  const int nstages = KA / kPfBK;
   const f16* act = GATEUP ? a.x16 : a.hin;  // fp16 [rows][K]
   const bool is_sh = tl.e < 0;
   const int e = is_sh ? 0 : tl.e, row0 = tl.row0, cnt = tl.cnt;
@@ -361,7 +376,7 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sA0, uint
       const int t = is_sh ? rs : a.row_token[row0 + rs];
       asrc[q] = (uint32_t)t * (uint32_t)(2 * K) + acol;
     } else {
-      asrc[q] = (uint32_t)(row0 + rs) * (uint32_t)(2 * K) + acol;
+      asrc[q] = (uint32_t)(row0 + rs) * (uint32_t)(2 * KA) + acol;
     }
   }
   auto copy_a = [&](int s, uint8_t* buf) {
@@ -373,7 +388,8 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sA0, uint
   };
   auto load_b = [&](int s, PfCodes<FMT> (&pc)[NF]) {
 #pragma unroll
-    for (int f = 0; f < NF; ++f) pf_load_codes<FMT>(bc[f], coff, bs[f], soff, s * kPfBK + 32 * G, pc[f]);
+    for (int f = 0; f < NF; ++f)
+      pf_load_codes<FMT>(bc[f], coff, bs[f], soff, (KX2 ? (s * kPfBK) % K : s * kPfBK) + 32 * G, pc[f]);
   };
 
   f32x4 acc[NMF][NF];
@@ -433,6 +449,53 @@ __device__ __forceinline__ void pf_item(const PrefillArgs& a, uint8_t* sA0, uint
   }
   if (GATEUP && tid < NMF * 16) s_rsx[tid] = rsx;
   __syncthreads();  // every wave is done with the activation buffers: they stage the outputs now
+
+  if constexpr (EXACT) {
+    // ---- exact mode (few rows): fp32 outputs stored directly.  D row (M) =
+    // mi*16 + 4G + v, column (N) = fragment row n.
+    bool bad = false;  // an h value that is not finite
+#pragma unroll
+    for (int mi = 0; mi < NMF; ++mi) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int rr = m0 + mi * 16 + 4 * G + v;
+        const bool valid = rr < cnt;
+        const long orow = row0 + (valid ? rr : 0);
+        if constexpr (GATEUP) {
+          const float sx = s_rsx[mi * 16 + 4 * G + v];
+          uint32_t mb = 0u;
+#pragma unroll
+          for (int f = 0; f < NF / 2; ++f) {
+            const float g = acc[mi][f][v] * sx * tsg, u = acc[mi][f + NF / 2][v] * sx * tsu;
+            const float hv = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+            const int fcol = nt * (kPfWaves * 8 * NF) + wid * (8 * NF) + f * 16 + n;
+            if (valid) {
+              bad |= !(fabsf(hv) <= 3.4028235e38f);
+              a.hf[orow * rows + act_pos(a.down_type, fcol)] = hv;
+              mb = max(mb, __float_as_uint(fabsf(hv)));
+            }
+          }
+          // the row's largest |h| over this wavefront's 32 features (the 16
+          // lanes of a row group), one atomic maximum per row and wavefront
+          mb = max(mb, dpp_u32<kDppShr1, 0xf>(mb));
+          mb = max(mb, dpp_u32<kDppShr2, 0xf>(mb));
+          mb = max(mb, dpp_u32<kDppShr4, 0xf>(mb));
+          mb = max(mb, dpp_u32<kDppShr8, 0xf>(mb));
+          if (n == 15 && valid) atomicMax(&a.hmax[orow], mb);
+        } else {
+          const float hx = valid ? a.hx[orow] : 0.0f;
+#pragma unroll
+          for (int f = 0; f < NF; ++f) {
+            const int dcol = nt * (kPfWaves * 16 * NF) + wid * (16 * NF) + f * 16 + n;
+            if (valid) a.of[orow * rows + dcol] = acc[mi][f][v] * tsg * hx;
+          }
+        }
+      }
+    }
+    if (GATEUP && bad) atomicOr(a.error, 2);
+    __syncthreads();  // the next item's first copy must not overwrite s_rsx still being read
+    return;
+  }
 
   // ---- epilogue: D row (M) = mi*16 + 4G + v, column (N) = fragment row n.
   // The item's outputs (tile rows x NC columns, 16-bit) are staged in the
@@ -501,7 +564,7 @@ constexpr int pf_min_blocks() {
   return FMT == MOE_Q8_0 ? 1 : 2;
 }
 
-template <int FMT, bool GATEUP, int NF>
+template <int FMT, bool GATEUP, int NF, bool EXACT>
 __global__ __launch_bounds__(kPfThreads, (pf_min_blocks<FMT, GATEUP>())) void k_pf_gemm(const PrefillArgs a) {
   // the two activation buffers, [kBM][16 chunks][16 B] each
   __shared__ __align__(16) uint8_t sA0[kPfBuf];
@@ -530,12 +593,31 @@ __global__ __launch_bounds__(kPfThreads, (pf_min_blocks<FMT, GATEUP>())) void k_
     tl.m0 = __builtin_amdgcn_readfirstlane(tl.m0);
     const int nrow = min(kBM, tl.cnt - tl.m0);  // rows of this tile, 1 .. kBM
     if (nrow > 64)
-      pf_item<FMT, GATEUP, NF, 8>(a, sA0, sA1, s_rsx, tl, nt, rows, K);
+      pf_item<FMT, GATEUP, NF, 8, EXACT>(a, sA0, sA1, s_rsx, tl, nt, rows, K);
     else if (nrow > 32)
-      pf_item<FMT, GATEUP, NF, 4>(a, sA0, sA1, s_rsx, tl, nt, rows, K);
+      pf_item<FMT, GATEUP, NF, 4, EXACT>(a, sA0, sA1, s_rsx, tl, nt, rows, K);
     else
-      pf_item<FMT, GATEUP, NF, 2>(a, sA0, sA1, s_rsx, tl, nt, rows, K);
+      pf_item<FMT, GATEUP, NF, 2, EXACT>(a, sA0, sA1, s_rsx, tl, nt, rows, K);
   }
+}
+
+// Exact mode, between the passes: each h row scaled by a power of two (its
+// largest |h| into [2^14, 2^15)) and split into fp16 hi and lo parts, hi
+// then lo along a row of 2f (the down pass's activation row), and the power
+// of two kept for the down pass's outputs.  Rows the plan left unused hold
+// stale values and are never read.
+__global__ __launch_bounds__(256) void k_pf_split_h(const float* __restrict__ hf, const uint32_t* __restrict__ hmax,
+                                                    int f, f16* __restrict__ h2, float* __restrict__ hx) {
+  const long r = blockIdx.x;
+  const int ex = x16_exponent(__uint_as_float(hmax[r]));
+  const float down = ldexpf(1.0f, -ex);
+  for (int c = threadIdx.x; c < f; c += 256) {
+    const float v = hf[r * f + c] * down;
+    const f16 hi = (f16)v;
+    h2[r * 2 * f + c] = hi;
+    h2[r * 2 * f + f + c] = (f16)(v - (float)hi);
+  }
+  if (threadIdx.x == 0) hx[r] = ldexpf(1.0f, ex);
 }
 
 namespace {
@@ -548,6 +630,11 @@ struct PrefillWs {
   uint16_t* o;
   f16* x16;   // scaled fp16 tokens
   float* xs;  // their scales
+  // exact mode
+  float* hf;       // h fp32 [R][f]
+  uint32_t* hmax;  // [R]
+  float* hx;       // [R]
+  float* of;       // O fp32 [R][d]
 };
 
 PrefillWs carve(void* ws, int T, int d, int f, int k, int E) {
@@ -567,23 +654,58 @@ PrefillWs carve(void* ws, int T, int d, int f, int k, int E) {
   w.x16 = (f16*)p;
   p += align_up((size_t)T * d * 2, 256);
   w.xs = (float*)p;
+  w.hf = nullptr;
+  w.hmax = nullptr;
+  w.hx = nullptr;
+  w.of = nullptr;
   return w;
 }
 
-template <int FMT, bool GATEUP, int NF>
+// Exact mode: the tile table, then h fp32, h as hi / lo fp16 rows of 2f (in
+// the place of the fp16 H), the row maxima and scales, O fp32 (in the place
+// of the bf16 O), the tokens.
+PrefillWs carve_exact(void* ws, int T, int d, int f, int k, int E) {
+  char* p = (char*)ws;
+  PrefillWs w;
+  w.mstart = (int32_t*)p;
+  p += align_up((size_t)(E + 2) * 4, 256);
+  w.tiles = (PfTile*)p;
+  p += align_up((size_t)pf_tile_cap(T, k, E) * sizeof(PfTile), 256);
+  w.n_mtiles = (int32_t*)p;
+  p += 256;
+  const size_t R = (size_t)T * k + T;
+  w.hf = (float*)p;
+  p += align_up(R * f * 4, 256);
+  w.h = (f16*)p;
+  p += align_up(R * f * 4, 256);
+  w.hmax = (uint32_t*)p;
+  p += align_up(R * 4, 256);
+  w.hx = (float*)p;
+  p += align_up(R * 4, 256);
+  w.of = (float*)p;
+  w.o = nullptr;
+  p += align_up(R * d * 4, 256);
+  w.x16 = (f16*)p;
+  p += align_up((size_t)T * d * 2, 256);
+  w.xs = (float*)p;
+  return w;
+}
+
+template <int FMT, bool GATEUP, int NF, bool EXACT = false>
 hipError_t launch_gemm_nf(const PrefillArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((k_pf_gemm<FMT, GATEUP, NF>), dim3(grid), dim3(kPfThreads), 0, s, a);
+  hipLaunchKernelGGL((k_pf_gemm<FMT, GATEUP, NF, EXACT>), dim3(grid), dim3(kPfThreads), 0, s, a);
   return hipGetLastError();
 }
 
-template <int FMT, bool GATEUP>
+template <int FMT, bool GATEUP, bool EXACT = false>
 hipError_t launch_gemm_fmt(int nf, const PrefillArgs& a, int grid, hipStream_t s) {
-  if constexpr (GATEUP) return launch_gemm_nf<FMT, true, 4>(a, grid, s);  // two gate and two up fragments
-  return nf == 4 ? launch_gemm_nf<FMT, false, 4>(a, grid, s) : launch_gemm_nf<FMT, false, 2>(a, grid, s);
+  if constexpr (GATEUP) return launch_gemm_nf<FMT, true, 4, EXACT>(a, grid, s);  // two gate and two up fragments
+  return nf == 4 ? launch_gemm_nf<FMT, false, 4, EXACT>(a, grid, s) : launch_gemm_nf<FMT, false, 2, EXACT>(a, grid, s);
 }
 
 template <bool GATEUP>
-hipError_t launch_gemm(int fmt, int nf, const PrefillArgs& a, int grid, hipStream_t s) {
+hipError_t launch_gemm(int fmt, int nf, const PrefillArgs& a, int grid, hipStream_t s, bool exact) {
+  if (exact) return launch_gemm_fmt<MOE_NVFP4, GATEUP, true>(nf, a, grid, s);  // (NVFP4-style only)
   switch (fmt) {
     case MOE_Q8_0: return launch_gemm_fmt<MOE_Q8_0, GATEUP>(nf, a, grid, s);
     case MOE_IQ4_NL: return launch_gemm_fmt<MOE_IQ4_NL, GATEUP>(nf, a, grid, s);
@@ -596,6 +718,27 @@ hipError_t launch_gemm(int fmt, int nf, const PrefillArgs& a, int grid, hipStrea
 
 }  // namespace
 
+// The exact mode of the prefill GEMMs serves batches of the per-layer path
+// (at most kDecodeMaxT tokens) where it is faster than the decode kernels:
+// NVFP4-style weights (exact in fp16, so the GEMMs' only roundings are the
+// ones the decode path makes too), bf16 tokens (exact as scaled fp16), and
+// more than kPfExactMinT tokens (measured crossover, 8-layer stacks of
+// d = 3072, f = 768, E = 512, top-8 + shared, µs per layer, decode kernels /
+// exact mode: 24 tokens 96.7 / 100.6, 32 tokens 107.8 / 105.9, 64 tokens
+// 154.6 / 124.6).
+constexpr int kPfExactMinT = 28;
+bool prefill_exact(const moe_layer& L, int T, int x_dtype) {
+  return T > kPfExactMinT && T <= kDecodeMaxT && x_dtype == MOE_BF16 && L.gate.type == MOE_NVFP4 &&
+         L.up.type == MOE_NVFP4 && L.down.type == MOE_NVFP4 && L.d % 128 == 0 && L.f % 128 == 0;
+}
+
+size_t prefill_exact_ws_bytes(int T, int d, int f, int k) {
+  const size_t R = (size_t)T * k + T;
+  return align_up((size_t)(4096 + 2) * 4, 256) + align_up((size_t)pf_tile_cap(T, k, 4096) * sizeof(PfTile), 256) +
+         256 + 2 * align_up(R * f * 4, 256) + 2 * align_up(R * 4, 256) + align_up(R * d * 4, 256) +
+         align_up((size_t)T * d * 2, 256) + align_up((size_t)T * 4, 256);
+}
+
 size_t prefill_ws_bytes(int T, int d, int f, int k) {
   const size_t R = (size_t)T * k + T;
   return align_up((size_t)(4096 + 2) * 4, 256) + align_up((size_t)pf_tile_cap(T, k, 4096) * sizeof(PfTile), 256) +
@@ -606,18 +749,23 @@ size_t prefill_ws_bytes(int T, int d, int f, int k) {
 hipError_t launch_prefill_stage(int stage, const FfnCall& c, hipStream_t s) {
   const moe_layer& L = *c.L;
   const int T = c.T;
-  PrefillWs w = carve(c.ws, T, L.d, L.f, L.k, 4096);
+  const bool exact = prefill_exact(L, T, c.x_dtype);
+  PrefillWs w = exact ? carve_exact(c.ws, T, L.d, L.f, L.k, 4096) : carve(c.ws, T, L.d, L.f, L.k, 4096);
   if (stage == kStagePrepare) {
     if (c.x_dtype == MOE_BF16)
       hipLaunchKernelGGL(k_pf_prepare<true>, dim3(T + 1), dim3(256), 0, s, c.x, T, L.d, L.gate.type, w.x16, w.xs,
-                         c.p.offsets, c.p.active, c.p.n_active, L.has_shared, w.mstart, w.tiles, w.n_mtiles, L.k);
+                         c.p.offsets, c.p.active, c.p.n_active, L.has_shared, w.mstart, w.tiles, w.n_mtiles, L.k,
+                         w.hmax);
     else
       hipLaunchKernelGGL(k_pf_prepare<false>, dim3(T + 1), dim3(256), 0, s, c.x, T, L.d, L.gate.type, w.x16, w.xs,
-                         c.p.offsets, c.p.active, c.p.n_active, L.has_shared, w.mstart, w.tiles, w.n_mtiles, L.k);
+                         c.p.offsets, c.p.active, c.p.n_active, L.has_shared, w.mstart, w.tiles, w.n_mtiles, L.k,
+                         w.hmax);
     return hipGetLastError();
   }
-  if (stage == kStageCombine)
+  if (stage == kStageCombine) {
+    if (exact) return launch_combine(w.of, 0, c.topk_w, c.p.slot_row, T, L.k, L.d, L.has_shared, c.y, c.y_dtype, s);
     return launch_combine(w.o, 1, c.topk_w, c.p.slot_row, T, L.k, L.d, L.has_shared, c.y, c.y_dtype, s);
+  }
   PrefillArgs a{};
   a.has_shared = L.has_shared;
   a.offsets = c.p.offsets;
@@ -643,20 +791,29 @@ hipError_t launch_prefill_stage(int stage, const FfnCall& c, hipStream_t s) {
     a.xs = w.xs;
     a.down_type = L.down.type;
     a.hout = w.h;
+    a.hf = w.hf;
+    a.hmax = w.hmax;
     // two gate and two up fragments per wavefront: a tile of 128 f-rows
     const long items = max_mtiles * (L.f / 128);
     const int grid = (int)(items < 8192 ? items : 8192) / kXcds * kXcds + kXcds;
-    return launch_gemm<true>(L.gate.type, 4, a, grid, s);
+    return launch_gemm<true>(L.gate.type, 4, a, grid, s, exact);
+  }
+  if (exact) {
+    hipLaunchKernelGGL(k_pf_split_h, dim3(T * L.k + T), dim3(256), 0, s, w.hf, w.hmax, L.f, w.h, w.hx);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   a.mat[0] = qmat_dev(L.down);
   if (L.has_shared) a.smat[0] = qmat_dev(L.shared_down);
   a.hin = w.h;
   a.o = w.o;
+  a.hx = w.hx;
+  a.of = w.of;
   // 256 d-rows per tile where d allows, else 128
   const int nf = (L.d % 256 == 0) ? 4 : 2;
   const long items = max_mtiles * (L.d / (64 * nf));
   const int grid = (int)(items < 8192 ? items : 8192) / kXcds * kXcds + kXcds;
-  return launch_gemm<false>(L.down.type, nf, a, grid, s);
+  return launch_gemm<false>(L.down.type, nf, a, grid, s, exact);
 }
 
 }  // namespace qre

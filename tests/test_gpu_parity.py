@@ -257,8 +257,12 @@ FORMATS = [("iq4_nl", "iq4_nl", "iq4_nl"), ("iq4_nl", "iq4_nl", "q8_0"), ("nvfp4
 
 
 @pytest.mark.parametrize("types", FORMATS, ids=lambda t: "-".join(t))
-@pytest.mark.parametrize("T,x_dtype", [(1, "bf16"), (3, "f32"), (8, "bf16"), (37, "bf16"), (64, "f32")])
+@pytest.mark.parametrize("T,x_dtype", [(1, "bf16"), (3, "f32"), (8, "bf16"), (37, "bf16"), (64, "f32"),
+                                       (48, "bf16"), (64, "bf16")])
 def test_decode_path_small(types, T, x_dtype):
+    """Every batch of at most 64 tokens meets the 1e-4 bar, on the decode
+    kernels or (NVFP4-style weights, bf16 tokens, more than 40 tokens) on the
+    prefill GEMMs' exact mode."""
     _say(f"[decode] {types} T={T} x={x_dtype}")
     wl, layer = _small_layer(100 + T, d=512, f=256, E=16, k=4, types=types)
     x = torch.randn((T, wl.d), generator=torch.Generator().manual_seed(T))
@@ -334,17 +338,22 @@ def test_prefill_narrow_shapes_fp32_tokens(types):
     _say(f"[prefill narrow] {stats}")
 
 
-@pytest.mark.parametrize("T", [2, 80])
-def test_swiglu_overflow_is_flagged(T):
-    """Error bit 2: the decode path (T <= 64) keeps h in fp32 and scales each
-    row into fp16 parts, so it flags only an h that is not finite (here:
-    tokens of 1e25 against gate / up scales of 30000); the prefill path flags
-    an h beyond the fp16 range (scales of 30000 suffice)."""
-    _say(f"[overflow] T={T}")
-    wl, layer = _small_layer(7, d=256, f=128, E=8, k=2, types=("q8_0", "q8_0", "q8_0"))
+@pytest.mark.parametrize("T,fmt", [(2, "q8_0"), (80, "q8_0"), (64, "nvfp4")])
+def test_swiglu_overflow_is_flagged(T, fmt):
+    """Error bit 2: the decode path (T <= 64, also the prefill GEMMs' exact
+    mode there) keeps h in fp32 and scales each row into fp16 parts, so it
+    flags only an h that is not finite (here: tokens of 1e25 against gate /
+    up scales of 30000); the prefill path flags an h beyond the fp16 range
+    (scales of 30000 suffice)."""
+    _say(f"[overflow] T={T} {fmt}")
+    wl, layer = _small_layer(7, d=256, f=128, E=8, k=2, types=(fmt, fmt, fmt))
     for n in ("gate", "up"):
-        layer["routed"][n]["scales"].fill_(30000.0)
-        layer["shared"][n]["scales"].fill_(30000.0)
+        for grp in ("routed", "shared"):
+            m = layer[grp][n]
+            if fmt == "nvfp4":
+                m["tensor_scale"].fill_(30000.0)
+            else:
+                m["scales"].fill_(30000.0)
     x = torch.randn((T, wl.d)) * (1e25 if T <= 64 else 1.0)
     st, _ = _run_single(layer, x.to(torch.bfloat16), "bf16", "f32")
     assert int(st.bufs[0].plan.error.item()) & 2
@@ -388,14 +397,18 @@ def test_decode_path_small_activations(types, T):
     assert hmax < 1e-4
 
 
-@pytest.mark.parametrize("T", [5, 40, 100])
-def test_ffn_forward_with_dropped_pairs(T):
+@pytest.mark.parametrize("T,types", [(5, ("iq4_nl", "iq4_nl", "q8_0")), (40, ("iq4_nl", "iq4_nl", "q8_0")),
+                                     (100, ("iq4_nl", "iq4_nl", "q8_0")), (64, ("nvfp4", "nvfp4", "nvfp4"))],
+                         ids=lambda v: "-".join(v) if isinstance(v, tuple) else str(v))
+def test_ffn_forward_with_dropped_pairs(T, types):
     """A plan that dropped pairs (ids out of range, ids repeated within a
     token) through moe_ffn_forward: the dropped pairs contribute nothing, the
     others match the oracle, and nothing is written outside the buffers (the
-    workspace is bracketed by guard regions that must stay untouched)."""
-    _say(f"[dropped pairs] T={T}")
-    wl, layer = _small_layer(600 + T, d=256, f=128, E=16, k=4, types=("iq4_nl", "iq4_nl", "q8_0"))
+    workspace is bracketed by guard regions that must stay untouched).  The
+    NVFP4-style case at 64 tokens runs the prefill GEMMs' exact mode, whose
+    h rows of dropped pairs are never written."""
+    _say(f"[dropped pairs] T={T} {types}")
+    wl, layer = _small_layer(600 + T, d=256, f=128, E=16, k=4, types=types)
     g = np.random.default_rng(T)
     idx = np.stack([g.permutation(16)[:4] for _ in range(T)]).astype(np.int32)
     idx[0, 1] = -1

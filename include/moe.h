@@ -176,7 +176,11 @@ moe_status moe_plan(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
  * decode path runs: exact dequantisation, fp32 accumulation; tokens enter the
  * products as fp16 with a power-of-two scale per token (fp32 tokens as hi/lo
  * pairs), and each SwiGLU row h, formed in fp32, as fp16 hi/lo parts scaled by
- * a power of two per row (error bit 2 if an h is not finite).  For T > 64 the prefill
+ * a power of two per row (error bit 2 if an h is not finite).  Batches of 29
+ * to 64 bf16 tokens with NVFP4-style gate, up and down weights take the
+ * prefill GEMMs instead, in a mode with these same numerics (the weights are
+ * exact in fp16, h is kept in fp32 and split per row as above, the expert
+ * outputs are fp32), which is faster at those sizes.  For T > 64 the prefill
  * path runs: weights are rounded to fp16 (code times block scale, rounded
  * once: relative error at most 2^-11, never a lossy subnormal, since a
  * product below 2^-14 has a subnormal scale and is then an exact multiple of

@@ -699,8 +699,11 @@ hipError_t launch_gemm_nf(const PrefillArgs& a, int grid, hipStream_t s) {
 
 template <int FMT, bool GATEUP, bool EXACT = false>
 hipError_t launch_gemm_fmt(int nf, const PrefillArgs& a, int grid, hipStream_t s) {
-  if constexpr (GATEUP) return launch_gemm_nf<FMT, true, 4, EXACT>(a, grid, s);  // two gate and two up fragments
-  return nf == 4 ? launch_gemm_nf<FMT, false, 4, EXACT>(a, grid, s) : launch_gemm_nf<FMT, false, 2, EXACT>(a, grid, s);
+  // gate/up: two gate and two up fragments (NF = 4), or one of each (NF = 2)
+  if constexpr (GATEUP && !EXACT)
+    return launch_gemm_nf<FMT, true, 4, false>(a, grid, s);
+  else
+    return nf == 4 ? launch_gemm_nf<FMT, GATEUP, 4, EXACT>(a, grid, s) : launch_gemm_nf<FMT, GATEUP, 2, EXACT>(a, grid, s);
 }
 
 template <bool GATEUP>
@@ -793,10 +796,12 @@ hipError_t launch_prefill_stage(int stage, const FfnCall& c, hipStream_t s) {
     a.hout = w.h;
     a.hf = w.hf;
     a.hmax = w.hmax;
-    // two gate and two up fragments per wavefront: a tile of 128 f-rows
-    const long items = max_mtiles * (L.f / 128);
+    // two gate and two up fragments per wavefront: a tile of 128 f-rows (exact
+    // mode, few rows: one of each, 64 f-rows, twice the items)
+    const int nfg = exact ? 2 : 4;
+    const long items = max_mtiles * (L.f / (32 * nfg));
     const int grid = (int)(items < 8192 ? items : 8192) / kXcds * kXcds + kXcds;
-    return launch_gemm<true>(L.gate.type, 4, a, grid, s, exact);
+    return launch_gemm<true>(L.gate.type, nfg, a, grid, s, exact);
   }
   if (exact) {
     hipLaunchKernelGGL(k_pf_split_h, dim3(T * L.k + T), dim3(256), 0, s, w.hf, w.hmax, L.f, w.h, w.hx);
@@ -810,7 +815,7 @@ hipError_t launch_prefill_stage(int stage, const FfnCall& c, hipStream_t s) {
   a.hx = w.hx;
   a.of = w.of;
   // 256 d-rows per tile where d allows, else 128
-  const int nf = (L.d % 256 == 0) ? 4 : 2;
+  const int nf = (L.d % 256 == 0 && !exact) ? 4 : 2;
   const long items = max_mtiles * (L.d / (64 * nf));
   const int grid = (int)(items < 8192 ? items : 8192) / kXcds * kXcds + kXcds;
   return launch_gemm<false>(L.down.type, nf, a, grid, s, exact);

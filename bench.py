@@ -71,7 +71,7 @@ DOMINANT = {
                           [_CS + "moe_persist.hip", _CS + "moe_dq.h", _CS + "moe_device.h"]),
     "fused_gateup": ("k_fz_gateup (top-k + plan + gate/up + SwiGLU)", r"qre::k_fz_gateup<",
                      [_CS + "moe_fused.hip", _CS + "moe_dq.h", _CS + "moe_device.h"]),
-    "slots": ("k_pf_gemm gate/up (NVFP4, exact mode)", r"qre::k_pf_gemm<3, true, 4, true>",
+    "slots": ("k_pf_gemm gate/up (NVFP4, exact mode)", r"qre::k_pf_gemm<3, true, \d, true>",
               [_CS + "moe_prefill.hip", _CS + "moe_device.h"]),
     "prefill": ("k_pf_gemm gate/up (IQ4_NL)", r"qre::k_pf_gemm<2, true, 4, false>",
                 [_CS + "moe_prefill.hip", _CS + "moe_device.h"]),

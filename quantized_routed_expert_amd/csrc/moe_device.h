@@ -359,22 +359,12 @@ __device__ __forceinline__ void wave_topk_vals(const float (&lv)[NPL], int E, in
   int ng = 1;
   while (ng < k) ng <<= 1;
   const int g = 64 / ng;
-  // (every step runs and a uniform select keeps it or not: no branches to
-  // out-of-line blocks in the middle of the selection)
-  {
-    uint32_t t = max(gm, dpp_u32<kDppShr1, 0xf>(gm));
-    gm = g >= 2 ? t : gm;
-    t = max(gm, dpp_u32<kDppShr2, 0xf>(gm));
-    gm = g >= 4 ? t : gm;
-    t = max(gm, dpp_u32<kDppShr4, 0xf>(gm));
-    gm = g >= 8 ? t : gm;
-    t = max(gm, dpp_u32<kDppShr8, 0xf>(gm));
-    gm = g >= 16 ? t : gm;
-    t = max(gm, dpp_u32<kDppBcast15, 0xa>(gm));
-    gm = g >= 32 ? t : gm;
-    t = max(gm, dpp_u32<kDppBcast31, 0xc>(gm));
-    gm = g >= 64 ? t : gm;
-  }
+  if (g >= 2) gm = max(gm, dpp_u32<kDppShr1, 0xf>(gm));
+  if (g >= 4) gm = max(gm, dpp_u32<kDppShr2, 0xf>(gm));
+  if (g >= 8) gm = max(gm, dpp_u32<kDppShr4, 0xf>(gm));
+  if (g >= 16) gm = max(gm, dpp_u32<kDppShr8, 0xf>(gm));
+  if (g >= 32) gm = max(gm, dpp_u32<kDppBcast15, 0xa>(gm));
+  if (g >= 64) gm = max(gm, dpp_u32<kDppBcast31, 0xc>(gm));
   const bool rep = (lane & (g - 1)) == g - 1;  // this lane holds its group's maximum
   const uint32_t tau = ~wave_max_u32(rep ? ~gm : 0u);
 

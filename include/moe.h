@@ -293,9 +293,13 @@ moe_status moe_decode_stack(const moe_layer* layers, int32_t n_layers, float* h,
  * weight codes are issued up front: f a multiple of 128 up to 768, d a
  * multiple of 1024 up to 3072 (IQ4_NL / NVFP4-style gate/up) or 1024 (Q8_0
  * gate/up); unless the environment sets QRE_DECODE_LAUNCHES=1.
- * It computes the same layer with the same numerics, and a wait between its
- * workgroups that does not end within its poll bound sets error bit 16 in
- * every layer's record still to run. */
+ * It computes the same layer with the same numerics.  A wait between its
+ * workgroups that does not end within its poll bound (2^20 polls; the
+ * environment can lower it with QRE_PERSIST_SPIN_MAX=n, read at every call,
+ * to exercise this path) sets error bit 16 in the record of the layer it
+ * belongs to and an abort word that ends every other wait, so the step ends
+ * early: h and the records of that layer and later ones are then incomplete
+ * and must not be used. */
 int32_t moe_decode_stack_persistent(const moe_layer* layers, int32_t n_layers, int32_t T);
 
 /* Workspace bytes for moe_decode_stack on this layer shape with up to T_max

@@ -43,6 +43,7 @@
 // (the next layer's router row and shared-expert tile, a down tile's codes)
 // are issued before it.
 #include <algorithm>
+#include <cstdlib>
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -70,7 +71,7 @@ constexpr int kLnAbort = kLnTiles + kSubTiles;
 constexpr int kLnSlot = kLnAbort + 1;                   // kSubSlot lines per slot
 constexpr int kNumCnt = kLnSlot + kMaxSlots * kSubSlot;
 
-constexpr uint32_t kSpinMax = 1u << 20;  // polls of one wait before it gives up
+constexpr uint32_t kSpinMax = 1u << 20;  // polls of one wait before it gives up (the default bound)
 
 }  // namespace
 
@@ -106,6 +107,7 @@ struct PsArgs {
   float* rec_y;
   int32_t* rec_err;
   int32_t* err_ws;     // the error word when there are no per-layer records
+  uint32_t spin_max;   // polls of one wait before it gives up
 };
 
 __device__ __forceinline__ float ld_ag(const float* p) {
@@ -136,7 +138,7 @@ __device__ __forceinline__ void st_tag(uint64_t* p, uint32_t tag, float v) {
 // word is set).  Returns false when it gave up.  Ends with a barrier.
 template <int NE>
 __device__ __forceinline__ bool ps_poll(const uint64_t* p0, int step, uint32_t pend, uint32_t tag, float (&v)[NE],
-                                        int32_t* abort_w, int32_t* err) {
+                                        int32_t* abort_w, int32_t* err, uint32_t spin) {
   __shared__ int s_stop[2];
   const int tid = threadIdx.x;
   for (uint32_t n = 1;; ++n) {
@@ -155,7 +157,7 @@ __device__ __forceinline__ bool ps_poll(const uint64_t* p0, int step, uint32_t p
     if (tid == 0) {
       int stop = 0;
       if ((n & 15u) == 0u && __hip_atomic_load(abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) stop = 1;
-      if (n > kSpinMax) {
+      if (n > spin) {
         atomicOr(err, 16);
         __hip_atomic_store(abort_w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         stop = 1;
@@ -175,7 +177,7 @@ __device__ __forceinline__ bool ps_poll(const uint64_t* p0, int step, uint32_t p
 // instruction per round; the others wait at the barrier.  Returns false if the
 // wait ran out (error bit 16, abort word set) or another workgroup's did.
 __device__ __forceinline__ bool ps_wait(const int32_t* c, int nsub, int narr, int epoch, int32_t* abort_w,
-                                        int32_t* err) {
+                                        int32_t* err, uint32_t spin) {
   __shared__ int s_ok;
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
@@ -191,7 +193,7 @@ __device__ __forceinline__ bool ps_wait(const int32_t* c, int nsub, int narr, in
         ok = 0;
         break;
       }
-      if (++n > kSpinMax) {
+      if (++n > spin) {
         if (lane == 0) {
           atomicOr(err, 16);
           __hip_atomic_store(abort_w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -214,7 +216,7 @@ __device__ __forceinline__ bool ps_wait(const int32_t* c, int nsub, int narr, in
 // with a barrier (slog complete and visible) on success.
 template <int PT>
 __device__ __forceinline__ bool ps_poll_logits(const uint64_t* lg, int E, uint32_t tag, float* slog,
-                                               int32_t* abort_w, int32_t* err) {
+                                               int32_t* abort_w, int32_t* err, uint32_t spin) {
   __shared__ int s_stop[2];
   const int tid = threadIdx.x;
   uint32_t pend = 0u;
@@ -237,7 +239,7 @@ __device__ __forceinline__ bool ps_poll_logits(const uint64_t* lg, int E, uint32
     if (tid == 0) {
       int stop = 0;
       if ((n & 15u) == 0u && __hip_atomic_load(abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) stop = 1;
-      if (n > kSpinMax) {
+      if (n > spin) {
         atomicOr(err, 16);
         __hip_atomic_store(abort_w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         stop = 1;
@@ -682,7 +684,8 @@ __device__ __forceinline__ bool ps_combine(PsLds& S, const PsArgs& a, int l, int
   for (int i = 0; i < NE; ++i)
     if (q + 4 * i < nR) pend |= 1u << i;
   float v[NE];
-  if (!ps_poll<NE>(a.otg + (long)q * d + ct * 64 + c, 4 * d, pend, (uint32_t)(l + 1), v, abort_w, err)) return false;
+  if (!ps_poll<NE>(a.otg + (long)q * d + ct * 64 + c, 4 * d, pend, (uint32_t)(l + 1), v, abort_w, err, a.spin_max))
+    return false;
 #pragma unroll
   for (int i = 0; i < NE; ++i)
     if (q + 4 * i < nR) S.comb[q + 4 * i][c] = v[i];
@@ -745,7 +748,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
     // ---- glue and router (the logits first: they gate every routed item)
     if (has_x) {
-      if (l > 0 && !ps_wait(sync + kLnTiles * kLine, kSubTiles, dn_per, l, abort_w, err)) return;
+      if (l > 0 && !ps_wait(sync + kLnTiles * kLine, kSubTiles, dn_per, l, abort_w, err, a.spin_max)) return;
       f32x4 xv[4];
       ps_glue_x(S, r_in, l == 0 ? nullptr : a.ss[l & 1], d, a.eps,
                 (w == 0 && a.rec_x) ? a.rec_x + (long)l * d : nullptr, xv);
@@ -771,7 +774,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
     // ---- top-k and gate weights (every workgroup that needs them)
     if (needs_topk) {
-      if (!ps_poll_logits<PT>(lg, E, ltag, S.logit, abort_w, err)) return;
+      if (!ps_poll_logits<PT>(lg, E, ltag, S.logit, abort_w, err, a.spin_max)) return;
       // one wavefront selects (no barrier until the result is published)
       if (wid == 0) {
         wave_topk<PT * 4>(S.logit, E, k, lane, S.tk_key, S.tk_idx, S.idx, S.wv);
@@ -808,7 +811,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       const bool sh = slot < hs;
       DnCodes<DF> g;
       ps_dn_issue<DF>(sh ? P.m[kSDown] : P.m[kDown], sh ? 0 : S.idx[slot - hs], ct, f, d, g);
-      if (!ps_wait(sync + (kLnSlot + slot * kSubSlot) * kLine, kSubSlot, gu_per, l + 1, abort_w, err)) return;
+      if (!ps_wait(sync + (kLnSlot + slot * kSubSlot) * kLine, kSubSlot, gu_per, l + 1, abort_w, err, a.spin_max)) return;
       // the slot's h row, scaled by a power of two into fp16 hi / lo parts
       const float* hr = a.hrow + (long)slot * f;
       const f32x4 hv = tid * 4 < f ? ld_ag4(hr, tid * 16) : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1047,6 +1050,14 @@ hipError_t launch_persist_step(const moe_layer* layers, int n_layers, float* h, 
   a.rec_y = rec.y;
   a.rec_err = rec.error;
   a.err_ws = W.err_ws;
+  // The poll bound of every wait; a test can lower it through the
+  // environment (QRE_PERSIST_SPIN_MAX, read at every call) to drive the
+  // give-up path from the host.
+  a.spin_max = kSpinMax;
+  if (const char* v = getenv("QRE_PERSIST_SPIN_MAX")) {
+    const long n = strtol(v, nullptr, 10);
+    if (n >= 1 && n <= (long)kSpinMax) a.spin_max = (uint32_t)n;
+  }
   const int nS = L0.k + a.hs;
   int need = L0.E;
   need = need > nS * (L0.f / 16) ? need : nS * (L0.f / 16);

@@ -123,3 +123,29 @@ def test_persistent_repeatable_and_graph_replay():
         assert torch.equal(st.h, ref) and torch.equal(st.rec_idx, ref_idx)
         assert int(st.rec_error.abs().sum().item()) == 0
         _ = (torch.randn(1000, device=DEV) * 2).sum().item()
+
+
+def test_persistent_poll_bound_ends_the_step():
+    """Failure handling, forced from the host: with every wait's poll bound
+    lowered to one round (QRE_PERSIST_SPIN_MAX=1) the waits between
+    workgroups give up.  The launch still ends (every wait is bounded and the
+    abort word ends the others), error bit 16 is reported in a layer's record,
+    and the next step with the normal bound is exact again (the set-up launch
+    clears the counters, the abort word and the records)."""
+    wl = _wl(("iq4_nl", "iq4_nl", "iq4_nl"), 1024, 256, 64, 4, True, 4, 4242)
+    layers = [synth.make_layer(wl, l, DEV) for l in range(4)]
+    structs = [lib.layer_struct(L) for L in layers]
+    assert lib.moe_decode_stack_persistent(lib.layer_array(structs), 4, 1)
+    h0 = synth.make_tokens(wl, DEV)
+    os.environ["QRE_PERSIST_SPIN_MAX"] = "1"
+    try:
+        st = _step(layers, h0)
+    finally:
+        os.environ.pop("QRE_PERSIST_SPIN_MAX", None)
+    errs = st.rec_error.cpu().numpy()
+    _say(f"[persist poll bound 1] error words {errs.tolist()}")
+    assert (errs & 16).any(), "no wait reported giving up"
+    st2 = _step(layers, h0)
+    assert not (st2.rec_error.cpu().numpy() != 0).any()
+    stats = _check_fused(wl, layers, st2, TOL_DECODE)
+    _say(f"[persist after the forced give-up] {stats}")
